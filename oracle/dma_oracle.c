@@ -1,0 +1,340 @@
+/*
+ * CPU oracle for the forward hot path of Doge's Dynamic Mask Attention (DMA).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The product path
+ * (the HIP library and its Python binding) never links, loads or calls it, and
+ * this file shares no code, header or table with the HIP kernels.
+ *
+ * Source of every step: the gitcode blog page "Transformers 中的 Doge 小语言模型
+ * 完全指南：动态掩码注意力（DMA）与跨域 MoE（CDMoE）架构解析与实战" (called "the
+ * Doge guide" below), section "动态掩码注意力（DMA）：从缓存 value states 生成稀疏掩码"
+ * (forward chain, steps 3 and 4), and the DogeConfig parameter table in section
+ * "DogeConfig 全参数详解" (keep_window_size, num_key_value_heads).
+ *
+ * Everything is plain and slow on purpose: fp64 arithmetic on the exact stored
+ * input values, one qsort per query row for the top-w selection, no blocking,
+ * no fusion, no reuse between rows.  OpenMP only splits independent rows over
+ * host threads.
+ *
+ * Pins (checked by the CPU tests): the dt closed forms (W = 0 gives 2^A, A = 0
+ * gives 1, the softplus identity softplus(x) - softplus(-x) = x, one-hot V
+ * reads exactly one weight, inversion back to the projection), a literal NumPy
+ * brute force of the masked-softmax procedure on tiny shapes, the library SDPA
+ * routine when no row has more than w valid keys, and the selection
+ * invariants.  Every function below has at least one such pin.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* Read element i of a float32 or bfloat16 array as an exact double. */
+static double elem(const void *p, int dtype, size_t i)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)p)[i];
+    uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* softplus(x) = log(1 + e^x), written so that neither branch overflows. */
+static double softplus(double x)
+{
+    if (x > 0.0)
+        return x + log1p(exp(-x));
+    return log1p(exp(x));
+}
+
+/*
+ * dt for every (batch, kv head, position) -- Doge guide, DMA forward step 3:
+ * dt_proj maps the value states to num_key_value_heads scores, then
+ * dt = exp(A * softplus(dt_proj(V))).  dt_proj reads the value states of all
+ * kv heads of one token, concatenated head-major (input width Hkv*d), and has
+ * one output per kv head; bias is optional (attention_bias defaults to False).
+ *
+ *   V    [B][S][Hkv][d]   (dtype)
+ *   W    [Hkv][Hkv*d]     (dtype)
+ *   bias [Hkv] or NULL    (dtype)
+ *   A    [Hkv]            float32
+ *   out  [B][Hkv][S]      double
+ */
+void oracle_dt(const void *V, const void *W, const void *bias, const float *A,
+               int dtype, int B, int S, int Hkv, int d, double *out)
+{
+    const size_t width = (size_t)Hkv * d;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int s = 0; s < S; ++s) {
+            const size_t vrow = ((size_t)b * S + s) * width;
+            for (int h = 0; h < Hkv; ++h) {
+                double x = bias ? elem(bias, dtype, h) : 0.0;
+                for (size_t c = 0; c < width; ++c)
+                    x += elem(W, dtype, (size_t)h * width + c) * elem(V, dtype, vrow + c);
+                out[((size_t)b * Hkv + h) * S + s] = exp((double)A[h] * softplus(x));
+            }
+        }
+}
+
+/* One key of a query row: its dt (compared as a real number) and its index. */
+typedef struct {
+    float dt;
+    int32_t idx;
+} key_t_;
+
+/*
+ * Order of the top-w selection: larger dt first; among equal dt the lower key
+ * index first.  The Doge guide selects with torch.topk, whose order among
+ * equal scores is unspecified; the lower-index rule makes the kept set unique.
+ */
+static int better_first(const void *pa, const void *pb)
+{
+    const key_t_ *a = (const key_t_ *)pa, *b = (const key_t_ *)pb;
+    if (a->dt > b->dt)
+        return -1;
+    if (a->dt < b->dt)
+        return 1;
+    return (a->idx > b->idx) - (a->idx < b->idx);
+}
+
+/*
+ * Keys of query row i, in selection order, into buf (capacity >= i + 1).
+ * Valid keys are j <= i (causal mask) and j < L (right padding).  Returns how
+ * many of them the row keeps: all valid keys if there are at most w of them,
+ * else the first w in the order above (Doge guide, DMA forward step 3: the
+ * top-k branch keeps keep_window_size positions and masks the rest).
+ */
+static int row_kept(const float *dt_row, int i, int L, int w, key_t_ *buf)
+{
+    int n = (i + 1 < L) ? i + 1 : L;
+    for (int j = 0; j < n; ++j) {
+        buf[j].dt = dt_row[j];
+        buf[j].idx = j;
+    }
+    qsort(buf, (size_t)n, sizeof *buf, better_first);
+    return n < w ? n : w;
+}
+
+/*
+ * Threshold pair (tau_i, t_i) of each query row: the dt and index of the
+ * last (w-th) kept key.  A key j of row i is kept exactly when it is valid and
+ * (dt_j > tau_i, or dt_j == tau_i and j <= t_i).  Canonical forms: a row with
+ * at most w valid keys keeps them all and gets (-inf, -1); a padded row
+ * (i >= L) keeps nothing and gets (+inf, -1).
+ *
+ *   dt      [B][Hkv][S] float32
+ *   seqlens [B] int32 or NULL (then every batch has length S)
+ *   rows    list of nrows (b, g, i) triples, or NULL for every row
+ *   tau/tie one entry per requested row ([B][Hkv][S] when rows == NULL)
+ */
+void oracle_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w,
+                   const int32_t *rows, int64_t nrows, float *tau, int32_t *tie)
+{
+    const int64_t total = rows ? nrows : (int64_t)B * Hkv * S;
+#pragma omp parallel
+    {
+        key_t_ *buf = (key_t_ *)malloc(sizeof(key_t_) * (size_t)(S > 0 ? S : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < total; ++r) {
+            int b, g, i;
+            if (rows) {
+                b = rows[3 * r];
+                g = rows[3 * r + 1];
+                i = rows[3 * r + 2];
+            } else {
+                b = (int)(r / ((int64_t)Hkv * S));
+                g = (int)((r / S) % Hkv);
+                i = (int)(r % S);
+            }
+            const int L = seqlens ? seqlens[b] : S;
+            if (i >= L) {
+                tau[r] = INFINITY;
+                tie[r] = -1;
+                continue;
+            }
+            if (i + 1 <= w) {
+                tau[r] = -INFINITY;
+                tie[r] = -1;
+                continue;
+            }
+            int nk = row_kept(dt + ((size_t)b * Hkv + g) * S, i, L, w, buf);
+            tau[r] = buf[nk - 1].dt;
+            tie[r] = buf[nk - 1].idx;
+        }
+        free(buf);
+    }
+}
+
+/*
+ * Kept key indices of one query row, ascending, into out (capacity >= w).
+ * Returns their count.  Used by the tests to materialise kept sets.
+ */
+int oracle_kept_row(const float *dt, const int32_t *seqlens, int Hkv, int S, int w,
+                    int b, int g, int i, int32_t *out)
+{
+    const int L = seqlens ? seqlens[b] : S;
+    if (i >= L)
+        return 0;
+    key_t_ *buf = (key_t_ *)malloc(sizeof(key_t_) * (size_t)(i + 1));
+    int nk = row_kept(dt + ((size_t)b * Hkv + g) * S, i, L, w, buf);
+    /* report in index order */
+    int n = 0;
+    char *mark = (char *)calloc((size_t)i + 1, 1);
+    for (int k = 0; k < nk; ++k)
+        mark[buf[k].idx] = 1;
+    for (int j = 0; j <= i; ++j)
+        if (mark[j])
+            out[n++] = j;
+    free(mark);
+    free(buf);
+    return n;
+}
+
+/*
+ * Attention of one query vector over an explicit kept set -- Doge guide, DMA
+ * forward step 4: scores are scaled by head_dim**-0.5, the dt of each key is
+ * the additive mask value at kept positions (masked positions hold min_dtype
+ * and so contribute exactly zero weight), and the softmax is taken in full
+ * precision: o = sum_j p_j v_j / sum_j p_j with p_j = exp(s_j - max s).
+ *
+ *   q    d values at q (dtype), k/v base pointers with row stride kv_stride
+ *   keys nk kept key indices (nk >= 1), dtv the dt of each position
+ */
+static void attend(const void *q, size_t qoff, const void *K, const void *Vv, int dtype,
+                   size_t kv_base, size_t kv_stride, int d, const float *dtv,
+                   const key_t_ *keys, int nk, double *s_buf, double *o)
+{
+    const double scale = 1.0 / sqrt((double)d);
+    double m = -INFINITY;
+    for (int k = 0; k < nk; ++k) {
+        const size_t kr = kv_base + (size_t)keys[k].idx * kv_stride;
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e)
+            dot += elem(q, dtype, qoff + e) * elem(K, dtype, kr + e);
+        s_buf[k] = scale * dot + (double)dtv[keys[k].idx];
+        if (s_buf[k] > m)
+            m = s_buf[k];
+    }
+    double l = 0.0;
+    for (int e = 0; e < d; ++e)
+        o[e] = 0.0;
+    for (int k = 0; k < nk; ++k) {
+        const double p = exp(s_buf[k] - m);
+        l += p;
+        const size_t vr = kv_base + (size_t)keys[k].idx * kv_stride;
+        for (int e = 0; e < d; ++e)
+            o[e] += p * elem(Vv, dtype, vr + e);
+    }
+    for (int e = 0; e < d; ++e)
+        o[e] /= l;
+}
+
+/*
+ * Prefill attention with the dynamic mask, for all rows or for a list of
+ * (b, g, i) rows (each list entry produces the G query heads of kv head g).
+ * Query head hq uses kv head hq / G (contiguous groups, G = Hq / Hkv).  Padded
+ * rows (i >= L) produce zeros.
+ *
+ *   Q [B][S][Hq][d], K/V [B][S][Hkv][d] (dtype); dt [B][Hkv][S] float32
+ *   out: [B][S][Hq][d] double when rows == NULL, else [nrows][G][d]
+ */
+void oracle_attn(const void *Q, const void *K, const void *V, int dtype, const float *dt,
+                 const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d, int w,
+                 const int32_t *rows, int64_t nrows, double *out)
+{
+    const int G = Hq / Hkv;
+    const int64_t total = rows ? nrows : (int64_t)B * Hkv * S;
+#pragma omp parallel
+    {
+        key_t_ *buf = (key_t_ *)malloc(sizeof(key_t_) * (size_t)(S > 0 ? S : 1));
+        double *s_buf = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < total; ++r) {
+            int b, g, i;
+            if (rows) {
+                b = rows[3 * r];
+                g = rows[3 * r + 1];
+                i = rows[3 * r + 2];
+            } else {
+                b = (int)(r / ((int64_t)Hkv * S));
+                g = (int)((r / S) % Hkv);
+                i = (int)(r % S);
+            }
+            const int L = seqlens ? seqlens[b] : S;
+            for (int hh = 0; hh < G; ++hh) {
+                const int hq = g * G + hh;
+                double *o = rows ? out + ((size_t)r * G + hh) * d
+                                 : out + (((size_t)b * S + i) * Hq + hq) * d;
+                if (i >= L) {
+                    for (int e = 0; e < d; ++e)
+                        o[e] = 0.0;
+                    continue;
+                }
+                int nk = row_kept(dt + ((size_t)b * Hkv + g) * S, i, L, w, buf);
+                attend(Q, (((size_t)b * S + i) * Hq + hq) * d, K, V, dtype,
+                       ((size_t)b * S * Hkv + g) * d, (size_t)Hkv * d, d,
+                       dt + ((size_t)b * Hkv + g) * S, buf, nk, s_buf, o);
+            }
+        }
+        free(s_buf);
+        free(buf);
+    }
+}
+
+/*
+ * One decode step per batch over a KV cache: the query sits at position
+ * L_b - 1 and sees every cached position j < L_b; it keeps the top w of them
+ * by dt (all if L_b <= w), read from the dt cache -- dt is a function of each
+ * position's cached value state, so caching it per position equals
+ * re-projecting every cached value (Doge guide, DMA forward step 3, remark
+ * that dt comes from the cached value states).
+ *
+ *   q [B][Hq][d]; Kc/Vc [B][Lmax][Hkv][d] (dtype); dt_cache [B][Hkv][Lmax]
+ *   cache_lens [B] in [1, Lmax]
+ *   out [B][Hq][d] double; kept_idx [B][Hkv][w] int32 ascending, -1 padded
+ *   (kept_idx may be NULL)
+ */
+void oracle_decode(const void *q, const void *Kc, const void *Vc, int dtype,
+                   const float *dt_cache, const int32_t *cache_lens, int B, int Lmax,
+                   int Hq, int Hkv, int d, int w, double *out, int32_t *kept_idx)
+{
+    const int G = Hq / Hkv;
+#pragma omp parallel
+    {
+        key_t_ *buf = (key_t_ *)malloc(sizeof(key_t_) * (size_t)(Lmax > 0 ? Lmax : 1));
+        double *s_buf = (double *)malloc(sizeof(double) * (size_t)(Lmax > 0 ? Lmax : 1));
+#pragma omp for collapse(2) schedule(dynamic, 1)
+        for (int b = 0; b < B; ++b)
+            for (int g = 0; g < Hkv; ++g) {
+                const int L = cache_lens[b];
+                const float *drow = dt_cache + ((size_t)b * Hkv + g) * Lmax;
+                int nk = row_kept(drow, L - 1, L, w, buf);
+                if (kept_idx) {
+                    int32_t *ki = kept_idx + ((size_t)b * Hkv + g) * w;
+                    char *mark = (char *)calloc((size_t)L, 1);
+                    for (int k = 0; k < nk; ++k)
+                        mark[buf[k].idx] = 1;
+                    int n = 0;
+                    for (int j = 0; j < L; ++j)
+                        if (mark[j])
+                            ki[n++] = j;
+                    for (; n < w; ++n)
+                        ki[n] = -1;
+                    free(mark);
+                }
+                for (int hh = 0; hh < G; ++hh) {
+                    const int hq = g * G + hh;
+                    attend(q, ((size_t)b * Hq + hq) * d, Kc, Vc, dtype,
+                           ((size_t)b * Lmax * Hkv + g) * d, (size_t)Hkv * d, d, drow, buf,
+                           nk, s_buf, out + ((size_t)b * Hq + hq) * d);
+                }
+            }
+        free(s_buf);
+        free(buf);
+    }
+}
