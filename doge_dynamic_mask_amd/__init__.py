@@ -1,0 +1,200 @@
+"""Python binding of libdma.so, the MI355X forward hot path of Doge's Dynamic Mask Attention.
+
+Thin ctypes marshalling only: every step runs in the HIP kernels of
+``libdma.so``.  torch supplies device memory (outputs and workspace are
+allocated with torch on the inputs' device) and the current stream.  There is
+no CPU fallback: if the library is missing, importing the binding's functions
+raises.
+
+Functions mirror the C ABI in ``include/dma.h``:
+
+    dt(V, W, A, bias=None, out=None, out_pos=None)      -> dt [B, Hkv, S] float32
+    select(dt, w, seqlens=None)                         -> (tau, tie)
+    attn_fwd(Q, K, V, dt, tau, tie, w, seqlens=None)    -> O
+    decode(q, Kc, Vc, dt_cache, cache_lens, w, kept=False) -> out (, kept_idx)
+    prefill(Q, K, V, W, A, w, bias=None, seqlens=None)  -> (O, dt, tau, tie)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdma.so")
+
+F32 = 0
+BF16 = 1
+
+_STATUS = {
+    0: "DMA_OK", -1: "DMA_ERR_NULL", -2: "DMA_ERR_SHAPE", -3: "DMA_ERR_DTYPE",
+    -4: "DMA_ERR_UNSUPPORTED", -5: "DMA_ERR_WORKSPACE", -6: "DMA_ERR_HIP",
+}
+
+EXPORTS = ("dma_version", "dma_status_str", "dma_dt", "dma_select", "dma_attn_fwd",
+           "dma_decode_workspace_bytes", "dma_decode")
+
+
+class DmaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_STATUS.get(status, status)} ({lib().dma_status_str(status).decode()})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libdma.so (ctypes.CDLL) with argument types set."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m doge_dynamic_mask_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    L.dma_version.argtypes, L.dma_version.restype = [], I
+    L.dma_status_str.argtypes, L.dma_status_str.restype = [I], ctypes.c_char_p
+    L.dma_dt.argtypes = [P, P, P, P, I, I, I, I, I, P, I64, P, P]
+    L.dma_dt.restype = I
+    L.dma_select.argtypes = [P, P, I, I, I, I, P, P, P]
+    L.dma_select.restype = I
+    L.dma_attn_fwd.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, I, I, P, P]
+    L.dma_attn_fwd.restype = I
+    L.dma_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    L.dma_decode_workspace_bytes.restype = SZ
+    L.dma_decode.argtypes = [P, P, P, I, P, P, I, I, I, I, I, I, P, P, P, SZ, P]
+    L.dma_decode.restype = I
+    _lib = L
+    return L
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"expected bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t, name, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _call(status, what):
+    if status != 0:
+        raise DmaError(status, what)
+
+
+def dt(V, W, A, bias=None, out=None, out_pos=None):
+    """dt = exp(A * softplus(dt_proj(V))) -> float32 [B, Hkv, S] (or written into `out`)."""
+    _check(V, "V", ndim=4)
+    dev = V.device
+    _check(W, "W", V.dtype, 2, dev)
+    _check(A, "A", torch.float32, 1, dev)
+    if bias is not None:
+        _check(bias, "bias", V.dtype, 1, dev)
+    B, S, Hkv, d = V.shape
+    if out is None:
+        out = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
+    _check(out, "out", torch.float32, 3, dev)
+    if out_pos is not None:
+        _check(out_pos, "out_pos", torch.int32, 1, dev)
+    ld = out.shape[2]
+    _call(lib().dma_dt(_ptr(V), _ptr(W), _ptr(bias), _ptr(A), _dtype_code(V), B, S, Hkv, d,
+                       _ptr(out), ld, _ptr(out_pos), _stream(V)), "dma_dt")
+    return out
+
+
+def select(dt_, w, seqlens=None, tau=None, tie=None):
+    """Per-row threshold pairs (tau float32, tie int32), each [B, Hkv, S]."""
+    _check(dt_, "dt", torch.float32, 3)
+    B, Hkv, S = dt_.shape
+    if seqlens is not None:
+        _check(seqlens, "seqlens", torch.int32, 1, dt_.device)
+    if tau is None:
+        tau = torch.empty_like(dt_)
+    if tie is None:
+        tie = torch.empty((B, Hkv, S), dtype=torch.int32, device=dt_.device)
+    _call(lib().dma_select(_ptr(dt_), _ptr(seqlens), B, Hkv, S, int(w), _ptr(tau), _ptr(tie),
+                           _stream(dt_)), "dma_select")
+    return tau, tie
+
+
+def attn_fwd(Q, K, V, dt_, tau, tie, w, seqlens=None, out=None):
+    """Masked attention output O [B, S, Hq, d] in the dtype of Q."""
+    _check(Q, "Q", ndim=4)
+    dev = Q.device
+    _check(K, "K", Q.dtype, 4, dev)
+    _check(V, "V", Q.dtype, 4, dev)
+    B, S, Hq, d = Q.shape
+    Hkv = K.shape[2]
+    if tuple(K.shape) != (B, S, Hkv, d) or tuple(V.shape) != tuple(K.shape):
+        raise ValueError("K/V must be [B, S, Hkv, d] matching Q")
+    for name, t, dtp in (("dt", dt_, torch.float32), ("tau", tau, torch.float32), ("tie", tie, torch.int32)):
+        _check(t, name, dtp, 3, dev)
+        if tuple(t.shape) != (B, Hkv, S):
+            raise ValueError(f"{name} must be [B, Hkv, S]")
+    if seqlens is not None:
+        _check(seqlens, "seqlens", torch.int32, 1, dev)
+    if out is None:
+        out = torch.empty_like(Q)
+    _check(out, "out", Q.dtype, 4, dev)
+    _call(lib().dma_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), _ptr(dt_), _ptr(tau), _ptr(tie),
+                             _ptr(seqlens), B, S, Hq, Hkv, d, int(w), _ptr(out), _stream(Q)),
+          "dma_attn_fwd")
+    return out
+
+
+def decode_workspace_bytes(B, Lmax, Hq, Hkv, d, w):
+    return int(lib().dma_decode_workspace_bytes(B, Lmax, Hq, Hkv, d, w))
+
+
+def decode(q, Kc, Vc, dt_cache, cache_lens, w, kept=False, out=None, workspace=None):
+    """One decode step: out [B, Hq, d]; with kept=True also kept_idx [B, Hkv, w] int32."""
+    _check(q, "q", ndim=3)
+    dev = q.device
+    _check(Kc, "Kc", q.dtype, 4, dev)
+    _check(Vc, "Vc", q.dtype, 4, dev)
+    _check(dt_cache, "dt_cache", torch.float32, 3, dev)
+    _check(cache_lens, "cache_lens", torch.int32, 1, dev)
+    B, Hq, d = q.shape
+    Lmax, Hkv = Kc.shape[1], Kc.shape[2]
+    nbytes = decode_workspace_bytes(B, Lmax, Hq, Hkv, d, w)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    kept_idx = torch.empty((B, Hkv, int(w)), dtype=torch.int32, device=dev) if kept else None
+    _call(lib().dma_decode(_ptr(q), _ptr(Kc), _ptr(Vc), _dtype_code(q), _ptr(dt_cache), _ptr(cache_lens),
+                           B, Lmax, Hq, Hkv, d, int(w), _ptr(out), _ptr(kept_idx), _ptr(workspace),
+                           workspace.numel(), _stream(q)), "dma_decode")
+    return (out, kept_idx) if kept else out
+
+
+def prefill(Q, K, V, W, A, w, bias=None, seqlens=None):
+    """The whole prefill path: dt from V, per-row thresholds, masked attention."""
+    d_ = dt(V, W, A, bias)
+    tau, tie = select(d_, w, seqlens)
+    O = attn_fwd(Q, K, V, d_, tau, tie, w, seqlens)
+    return O, d_, tau, tie

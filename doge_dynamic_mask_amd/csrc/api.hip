@@ -1,0 +1,94 @@
+// C ABI of libdma.so: host-side validation, then one or more kernel launches
+// on the caller's stream.  Nothing here allocates, synchronises or keeps
+// state; every check happens before the first HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dma.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kAbiVersion = 100;
+
+bool aligned16(const void *p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+bool dtype_ok(int t) { return t == DMA_F32 || t == DMA_BF16; }
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? DMA_OK : DMA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int dma_version(void) { return kAbiVersion; }
+
+const char *dma_status_str(int status) {
+    switch (status) {
+        case DMA_OK: return "ok";
+        case DMA_ERR_NULL: return "a required pointer is NULL";
+        case DMA_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case DMA_ERR_DTYPE: return "dtype must be DMA_F32 or DMA_BF16";
+        case DMA_ERR_UNSUPPORTED: return "request outside the implemented kernels (head_dim, heads, alignment)";
+        case DMA_ERR_WORKSPACE: return "workspace missing or too small";
+        case DMA_ERR_HIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+int dma_dt(const void *V, const void *W, const void *bias, const float *A, int dtype, int B, int S,
+           int Hkv, int d, float *dt_out, int64_t ld_out, const int32_t *out_pos, void *stream) {
+    if (!V || !W || !A || !dt_out) return DMA_ERR_NULL;
+    if (!dtype_ok(dtype)) return DMA_ERR_DTYPE;
+    if (B < 1 || S < 1 || Hkv < 1 || d < 1 || ld_out < S) return DMA_ERR_SHAPE;
+    if (!head_dim_ok(d) || Hkv > dma::kMaxHkvDt) return DMA_ERR_UNSUPPORTED;
+    const size_t esize = dtype == DMA_BF16 ? 2 : 4;
+    if ((size_t)Hkv * Hkv * d * esize > dma::kDtLdsBytes) return DMA_ERR_UNSUPPORTED;
+    if (!aligned16(V) || !aligned16(W)) return DMA_ERR_UNSUPPORTED;
+    return from_hip(dma::launch_dt(V, W, bias, A, dtype, B, S, Hkv, d, dt_out, ld_out, out_pos,
+                                   (hipStream_t)stream));
+}
+
+int dma_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w, float *tau,
+               int32_t *tie, void *stream) {
+    if (!dt || !tau || !tie) return DMA_ERR_NULL;
+    if (B < 1 || Hkv < 1 || S < 1 || w < 1) return DMA_ERR_SHAPE;
+    if (B > 65535 || Hkv > 65535) return DMA_ERR_UNSUPPORTED;
+    return from_hip(dma::launch_select(dt, seqlens, B, Hkv, S, w, tau, tie, (hipStream_t)stream));
+}
+
+int dma_attn_fwd(const void *Q, const void *K, const void *V, int dtype, const float *dt,
+                 const float *tau, const int32_t *tie, const int32_t *seqlens, int B, int S, int Hq,
+                 int Hkv, int d, int w, void *O, void *stream) {
+    if (!Q || !K || !V || !dt || !tau || !tie || !O) return DMA_ERR_NULL;
+    if (!dtype_ok(dtype)) return DMA_ERR_DTYPE;
+    if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || d < 1 || w < 1 || Hq % Hkv != 0) return DMA_ERR_SHAPE;
+    if (!head_dim_ok(d) || Hq / Hkv > dma::kMaxGroupAttn) return DMA_ERR_UNSUPPORTED;
+    if (B > 65535 || Hkv > 65535) return DMA_ERR_UNSUPPORTED;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return DMA_ERR_UNSUPPORTED;
+    return from_hip(dma::launch_attn(Q, K, V, dtype, dt, tau, tie, seqlens, B, S, Hq, Hkv, d, w, O,
+                                     (hipStream_t)stream));
+}
+
+size_t dma_decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d, int w) {
+    if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || d < 1 || w < 1 || Hq % Hkv != 0) return 0;
+    return dma::decode_ws_bytes(B, Lmax, Hq, Hkv, d, w);
+}
+
+int dma_decode(const void *q, const void *Kc, const void *Vc, int dtype, const float *dt_cache,
+               const int32_t *cache_lens, int B, int Lmax, int Hq, int Hkv, int d, int w, void *out,
+               int32_t *kept_idx, void *ws, size_t ws_bytes, void *stream) {
+    if (!q || !Kc || !Vc || !dt_cache || !cache_lens || !out) return DMA_ERR_NULL;
+    if (!dtype_ok(dtype)) return DMA_ERR_DTYPE;
+    if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || d < 1 || w < 1 || Hq % Hkv != 0) return DMA_ERR_SHAPE;
+    if (!head_dim_ok(d) || Hq / Hkv > dma::kMaxGroupDecode) return DMA_ERR_UNSUPPORTED;
+    if (B > 65535 || Hkv > 65535) return DMA_ERR_UNSUPPORTED;
+    if (!aligned16(Kc) || !aligned16(Vc)) return DMA_ERR_UNSUPPORTED;
+    if (!ws) return DMA_ERR_WORKSPACE;
+    if (ws_bytes < dma::decode_ws_bytes(B, Lmax, Hq, Hkv, d, w)) return DMA_ERR_WORKSPACE;
+    return from_hip(dma::launch_decode(q, Kc, Vc, dtype, dt_cache, cache_lens, B, Lmax, Hq, Hkv, d, w,
+                                       out, kept_idx, ws, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// dt kernel: dt[b][h][s] = exp(A[h] * softplus(bias[h] + sum_c W[h][c] * V[b][s][c]))
+// Doge guide (gitcode), DMA section, forward step 3: dt_proj over the value
+// states of all kv heads of a token (input width Hkv*d, head-major), then
+// exp(A * softplus(.)).
+//
+// A skinny GEMV that streams V once from HBM: eight lanes share one token
+// row, each lane loading 16-byte vectors so that the eight lanes of a group
+// read 128 contiguous bytes per step.  W (at most 64 KiB) is staged once per
+// workgroup in LDS in its storage type.  Partial sums are reduced across the
+// eight lanes with xor shuffles; softplus and exp run in float32.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dma {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kLanesPerToken = 8;
+constexpr int kTokensPerBlock = kThreads / kLanesPerToken;
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4 &v, float *x);
+template <>
+__device__ __forceinline__ void unpack16<uint16_t>(const uint4 &v, float *x) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        x[2 * k] = __uint_as_float(w[k] << 16);
+        x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4 &v, float *x) {
+    x[0] = __uint_as_float(v.x);
+    x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z);
+    x[3] = __uint_as_float(v.w);
+}
+
+__device__ __forceinline__ float softplus_f32(float x) {
+    return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x));
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void dt_kernel(const T *__restrict__ V, const T *__restrict__ W,
+                                                      const T *__restrict__ bias,
+                                                      const float *__restrict__ A, int S, int Hkv,
+                                                      int d, int64_t ntok, float *__restrict__ out,
+                                                      int64_t ld, const int32_t *__restrict__ out_pos) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int EV = 16 / (int)sizeof(T);  // elements per 16-byte vector
+    const int width = Hkv * d;
+    const int nvec = width / EV;             // vectors per token row
+    uint4 *Ws = reinterpret_cast<uint4 *>(smem);
+    for (int v = threadIdx.x; v < Hkv * nvec; v += kThreads) Ws[v] = reinterpret_cast<const uint4 *>(W)[v];
+    __syncthreads();
+
+    const int q = threadIdx.x % kLanesPerToken;
+    for (int64_t t = (int64_t)blockIdx.x * kTokensPerBlock + threadIdx.x / kLanesPerToken; t < ntok;
+         t += (int64_t)gridDim.x * kTokensPerBlock) {
+        const uint4 *vrow = reinterpret_cast<const uint4 *>(V + t * width);
+        float acc[kMaxHkvDt];
+#pragma unroll
+        for (int h = 0; h < kMaxHkvDt; ++h) acc[h] = 0.f;
+        for (int v = q; v < nvec; v += kLanesPerToken) {
+            float x[EV];
+            unpack16<T>(vrow[v], x);
+#pragma unroll
+            for (int h = 0; h < kMaxHkvDt; ++h) {
+                if (h < Hkv) {
+                    float wv[EV];
+                    unpack16<T>(Ws[h * nvec + v], wv);
+                    float a = acc[h];
+#pragma unroll
+                    for (int e = 0; e < EV; ++e) a = fmaf(wv[e], x[e], a);
+                    acc[h] = a;
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < kMaxHkvDt; ++h) {
+            if (h < Hkv) {
+#pragma unroll
+                for (int o = 1; o < kLanesPerToken; o <<= 1) acc[h] += __shfl_xor(acc[h], o, kLanesPerToken);
+            }
+        }
+        const int b = (int)(t / S);
+        const int s = (int)(t - (int64_t)b * S);
+        const int64_t col = (out_pos ? (int64_t)out_pos[b] : 0) + s;
+#pragma unroll
+        for (int h = 0; h < kMaxHkvDt; ++h) {
+            if (h < Hkv && (h % kLanesPerToken) == q) {
+                const float x = acc[h] + (bias ? Elem<T>::load(bias, h) : 0.f);
+                out[((int64_t)b * Hkv + h) * ld + col] = expf(A[h] * softplus_f32(x));
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dt(const void *V, const void *W, const void *bias, const float *A, int dtype,
+                     int B, int S, int Hkv, int d, float *dt_out, int64_t ld_out,
+                     const int32_t *out_pos, hipStream_t stream) {
+    const int64_t ntok = (int64_t)B * S;
+    const int64_t want = (ntok + kTokensPerBlock - 1) / kTokensPerBlock;
+    const int grid = (int)(want < 2048 ? want : 2048);
+    const size_t esize = dtype == 1 ? 2 : 4;
+    const size_t lds = (size_t)Hkv * Hkv * d * esize;
+    if (dtype == 1) {
+        hipLaunchKernelGGL(dt_kernel<uint16_t>, dim3(grid), dim3(kThreads), lds, stream,
+                           (const uint16_t *)V, (const uint16_t *)W, (const uint16_t *)bias, A, S, Hkv,
+                           d, ntok, dt_out, ld_out, out_pos);
+    } else {
+        hipLaunchKernelGGL(dt_kernel<float>, dim3(grid), dim3(kThreads), lds, stream, (const float *)V,
+                           (const float *)W, (const float *)bias, A, S, Hkv, d, ntok, dt_out, ld_out,
+                           out_pos);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dma

@@ -1,0 +1,35 @@
+// Host-side launchers of the DMA kernels; called only from api.hip after the
+// arguments have been validated.  Each returns the HIP launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dma {
+
+hipError_t launch_dt(const void *V, const void *W, const void *bias, const float *A, int dtype,
+                     int B, int S, int Hkv, int d, float *dt_out, int64_t ld_out,
+                     const int32_t *out_pos, hipStream_t stream);
+
+hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w,
+                         float *tau, int32_t *tie, hipStream_t stream);
+
+hipError_t launch_attn(const void *Q, const void *K, const void *V, int dtype, const float *dt,
+                       const float *tau, const int32_t *tie, const int32_t *seqlens, int B, int S,
+                       int Hq, int Hkv, int d, int w, void *O, hipStream_t stream);
+
+size_t decode_ws_bytes(int B, int Lmax, int Hq, int Hkv, int d, int w);
+
+hipError_t launch_decode(const void *q, const void *Kc, const void *Vc, int dtype,
+                         const float *dt_cache, const int32_t *cache_lens, int B, int Lmax,
+                         int Hq, int Hkv, int d, int w, void *out, int32_t *kept_idx, void *ws,
+                         hipStream_t stream);
+
+// Limits the launchers rely on (checked by the ABI layer).
+constexpr int kMaxHkvDt = 16;          // dt kernel: heads accumulated in registers
+constexpr int kMaxGroupAttn = 128;     // prefill: query heads per kv head
+constexpr int kMaxGroupDecode = 16;    // decode: query heads per kv head
+constexpr size_t kDtLdsBytes = 65536;  // dt kernel: W staged in LDS
+
+}  // namespace dma

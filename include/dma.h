@@ -1,0 +1,162 @@
+/*
+ * dma.h -- C ABI of libdma.so, the MI355X (gfx950) forward hot path of Doge's
+ * Dynamic Mask Attention (DMA).
+ *
+ * The operations follow the gitcode page "Transformers 中的 Doge 小语言模型完全指南：
+ * 动态掩码注意力（DMA）与跨域 MoE（CDMoE）架构解析与实战" (the "Doge guide"), section
+ * "动态掩码注意力（DMA）：从缓存 value states 生成稀疏掩码", forward chain steps 3
+ * (dt from the value states, the broadcast dynamic mask and its top-k
+ * sparsification) and 4 (attention with head_dim**-0.5 scaling and an fp32
+ * softmax), with keep_window_size and num_key_value_heads from the DogeConfig
+ * table of the same page (section "DogeConfig 全参数详解").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor arguments are DEVICE pointers to caller-owned memory, dense
+ *    row-major in the layout stated per argument.  The library never
+ *    allocates, frees, or keeps a pointer after the call returns.
+ *  - Layouts: Q [B][S][Hq][d], K/V [B][S][Hkv][d] (token-major, heads
+ *    interleaved, as a projection writes them); dt, tau, tie [B][Hkv][S].
+ *  - dtype is DMA_F32 or DMA_BF16 and applies to Q, K, V, O, W and bias; A,
+ *    dt and tau are always float32, tie and lengths int32.
+ *  - Query head hq reads kv head hq / (Hq / Hkv) (contiguous GQA groups).
+ *  - Causal: query row i sees keys j <= i.  Right padding: with a lengths
+ *    array, batch b has L_b valid positions (1 <= L_b <= S); keys j >= L_b are
+ *    masked and query rows i >= L_b produce zeros.  A NULL lengths array
+ *    means L_b = S for every batch.
+ *  - Top-w selection order: larger dt first; among equal dt the lower key
+ *    index first.  dt values of valid keys must not be NaN (the method's
+ *    exp(.) never produces one); -0.0 and +0.0 compare equal.
+ *  - Every call validates its arguments on the host before any HIP call and
+ *    returns a dma_status; on error nothing is enqueued.  Work is enqueued on
+ *    `stream` (a hipStream_t; NULL is the default stream) and the call returns
+ *    without synchronising; kernel faults surface at the caller's next
+ *    synchronisation.  The library has no global mutable state; calls are
+ *    thread-safe.
+ */
+#ifndef DMA_H_
+#define DMA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dma_status {
+    DMA_OK = 0,
+    DMA_ERR_NULL = -1,        /* a required pointer is NULL */
+    DMA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+    DMA_ERR_DTYPE = -3,       /* dtype is not DMA_F32 / DMA_BF16 */
+    DMA_ERR_UNSUPPORTED = -4, /* valid request outside what the kernels implement */
+    DMA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
+    DMA_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+} dma_status;
+
+typedef enum dma_dtype { DMA_F32 = 0, DMA_BF16 = 1 } dma_dtype;
+
+/* Version of this ABI (major * 100 + minor). */
+int dma_version(void);
+
+/* Static text for a status code. */
+const char *dma_status_str(int status);
+
+/*
+ * dma_dt -- Doge guide, DMA forward step 3, first two bullets: dt_proj maps
+ * the value states to num_key_value_heads scores per token, then
+ * dt = exp(A * softplus(.)).  dt_proj reads all kv heads of one token,
+ * concatenated head-major (input width Hkv*d).
+ *
+ *   V       [B][S][Hkv][d]  dtype   value states
+ *   W       [Hkv][Hkv*d]    dtype   dt_proj weight (row h -> kv head h)
+ *   bias    [Hkv] dtype, or NULL (no bias)
+ *   A       [Hkv]           float32 per-kv-head scale
+ *   dt_out  float32; the result for (b, h, s) is written to
+ *           dt_out[(b*Hkv + h)*ld_out + (out_pos ? out_pos[b] : 0) + s]
+ *   ld_out  row stride of dt_out in elements (>= S; >= out_pos[b] + S)
+ *   out_pos [B] int32 device array or NULL: first column written per batch.
+ *           A decode step appends the new token's dt to a [B][Hkv][Lmax]
+ *           dt cache with S = 1, ld_out = Lmax, out_pos[b] = L_b - 1.
+ * Accumulation, softplus and exp are float32.  Supports Hkv <= 16,
+ * d in {64, 128}.
+ */
+int dma_dt(const void *V, const void *W, const void *bias, const float *A, int dtype,
+           int B, int S, int Hkv, int d, float *dt_out, int64_t ld_out,
+           const int32_t *out_pos, void *stream);
+
+/*
+ * dma_select -- Doge guide, DMA forward step 3, third bullet: every query row
+ * keeps the keep_window_size (= w) keys of largest dt among its valid keys and
+ * masks the rest; rows with at most w valid keys keep them all.
+ *
+ * The kept set of row i is encoded by a threshold pair: (tau[i], tie[i]) is
+ * the dt and index of the last (w-th) kept key, and key j is kept exactly when
+ * j is valid and (dt[j] > tau[i] or (dt[j] == tau[i] and j <= tie[i])).
+ * Canonical forms: (-inf, -1) when row i has at most w valid keys; (+inf, -1)
+ * for a padded row (i >= L_b).  The pair is exact: no floating-point
+ * arithmetic is done on dt, only comparisons.
+ *
+ *   dt      [B][Hkv][S] float32
+ *   seqlens [B] int32 or NULL
+ *   tau     [B][Hkv][S] float32 (out), tie [B][Hkv][S] int32 (out)
+ * Needs no workspace.
+ */
+int dma_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w,
+               float *tau, int32_t *tie, void *stream);
+
+/*
+ * dma_attn_fwd -- Doge guide, DMA forward step 4 with the mask of step 3:
+ * for query head hq of batch b at row i < L_b, with g = hq / (Hq/Hkv),
+ *   s_j = d**-0.5 * (q_i . k_j) + dt[b][g][j]    over the kept keys j of row i
+ *   o_i = sum_j softmax(s)_j v_j                 (softmax in float32)
+ * Rows i >= L_b are written as zeros.  The kept set comes from (tau, tie) as
+ * produced by dma_select for the same dt, seqlens and w.
+ *
+ *   Q [B][S][Hq][d], K/V [B][S][Hkv][d] dtype; dt/tau/tie [B][Hkv][S]
+ *   O [B][S][Hq][d] dtype (out)
+ *   w  keep_window_size used to produce (tau, tie)
+ * bf16 runs on matrix cores with float32 accumulation; the softmax weights
+ * are rounded once to bf16 for the weighted sum of V and the output is
+ * rounded to nearest-even.  Supports d in {64, 128}, Hq/Hkv <= 128.
+ * Needs no workspace.
+ */
+int dma_attn_fwd(const void *Q, const void *K, const void *V, int dtype, const float *dt,
+                 const float *tau, const int32_t *tie, const int32_t *seqlens, int B,
+                 int S, int Hq, int Hkv, int d, int w, void *O, void *stream);
+
+/*
+ * dma_decode_workspace_bytes -- bytes of device workspace dma_decode needs
+ * for these sizes (0 on invalid sizes).
+ */
+size_t dma_decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d, int w);
+
+/*
+ * dma_decode -- one decode step per batch: the query of batch b sits at
+ * position L_b - 1 (L_b = cache_lens[b]) and attends over the cached keys
+ * j < L_b that the top-w rule keeps (all of them when L_b <= w), using the
+ * per-position dt cache.  The dt of a position depends only on that
+ * position's cached value state (Doge guide, DMA forward step 3, remark that
+ * dt is projected from the cached value states), so the cache holds exactly
+ * what re-projecting every cached value each step would give.
+ *
+ *   q          [B][Hq][d] dtype
+ *   Kc, Vc     [B][Lmax][Hkv][d] dtype
+ *   dt_cache   [B][Hkv][Lmax] float32
+ *   cache_lens [B] int32, each in [1, Lmax]
+ *   out        [B][Hq][d] dtype (out)
+ *   kept_idx   [B][Hkv][w] int32 (out) or NULL: kept positions ascending,
+ *              padded with -1 when L_b < w
+ *   ws, ws_bytes  device workspace of at least dma_decode_workspace_bytes()
+ * Supports d in {64, 128}, Hq/Hkv <= 16.
+ */
+int dma_decode(const void *q, const void *Kc, const void *Vc, int dtype,
+               const float *dt_cache, const int32_t *cache_lens, int B, int Lmax, int Hq,
+               int Hkv, int d, int w, void *out, int32_t *kept_idx, void *ws,
+               size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMA_H_ */

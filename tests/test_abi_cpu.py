@@ -1,0 +1,101 @@
+"""The C ABI library without a GPU: it loads, exports every function that
+include/dma.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dma.h")
+LIB = os.path.join(ROOT, "doge_dynamic_mask_amd", "libdma.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libdma.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dma_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def dma():
+    import doge_dynamic_mask_amd as m
+    return m.lib()
+
+
+def test_exports_every_declared_symbol(dma):
+    names = declared_functions()
+    assert set(names) >= {"dma_dt", "dma_select", "dma_attn_fwd", "dma_decode",
+                          "dma_decode_workspace_bytes", "dma_status_str", "dma_version"}
+    for n in names:
+        assert hasattr(dma, n), n
+    import doge_dynamic_mask_amd as m
+    assert set(m.EXPORTS) == set(names)
+
+
+def test_version_and_status_strings(dma):
+    assert dma.dma_version() == 100
+    for s in range(-6, 1):
+        assert dma.dma_status_str(s)
+    assert dma.dma_status_str(-99) == b"unknown status"
+
+
+# Non-null, never-dereferenced stand-ins: every call below must fail host-side
+# validation before it could touch them.
+FAKE = ctypes.c_void_p(0x1000)
+FAKE2 = ctypes.c_void_p(0x2000)
+
+
+def test_dt_validation(dma):
+    ok = dict(V=FAKE, W=FAKE, bias=None, A=FAKE, dtype=1, B=1, S=8, Hkv=2, d=64, out=FAKE, ld=8, pos=None)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return dma.dma_dt(a["V"], a["W"], a["bias"], a["A"], a["dtype"], a["B"], a["S"], a["Hkv"], a["d"],
+                          a["out"], a["ld"], a["pos"], None)
+    assert call(V=None) == -1
+    assert call(out=None) == -1
+    assert call(A=None) == -1
+    assert call(dtype=7) == -3
+    assert call(B=0) == -2
+    assert call(ld=4) == -2
+    assert call(d=96) == -4
+    assert call(Hkv=17) == -4
+    assert call(V=ctypes.c_void_p(0x1004)) == -4  # misaligned
+
+
+def test_select_validation(dma):
+    assert dma.dma_select(None, None, 1, 1, 8, 2, FAKE, FAKE, None) == -1
+    assert dma.dma_select(FAKE, None, 1, 1, 8, 0, FAKE, FAKE, None) == -2
+    assert dma.dma_select(FAKE, None, 0, 1, 8, 2, FAKE, FAKE, None) == -2
+    assert dma.dma_select(FAKE, None, 1, 1, 0, 2, FAKE, FAKE, None) == -2
+
+
+def test_attn_validation(dma):
+    def call(Q=FAKE, dtype=1, B=1, S=8, Hq=4, Hkv=2, d=64, w=4, O=FAKE2):
+        return dma.dma_attn_fwd(Q, FAKE, FAKE, dtype, FAKE, FAKE, FAKE, None, B, S, Hq, Hkv, d, w, O, None)
+    assert call(Q=None) == -1
+    assert call(O=None) == -1
+    assert call(dtype=2) == -3
+    assert call(Hq=3) == -2
+    assert call(w=0) == -2
+    assert call(d=32) == -4
+    assert call(Hq=258, Hkv=2) == -4
+
+
+def test_decode_validation(dma):
+    need = dma.dma_decode_workspace_bytes(4, 2048, 8, 2, 128, 256)
+    assert need > 0
+    assert dma.dma_decode_workspace_bytes(0, 2048, 8, 2, 128, 256) == 0
+
+    def call(ws=FAKE2, nbytes=need, cache_lens=FAKE, d=128, Hq=8, Hkv=2):
+        return dma.dma_decode(FAKE, FAKE, FAKE, 1, FAKE, cache_lens, 4, 2048, Hq, Hkv, d, 256,
+                              FAKE, None, ws, nbytes, None)
+    assert call(cache_lens=None) == -1
+    assert call(ws=None) == -5
+    assert call(nbytes=need - 1) == -5
+    assert call(Hq=7) == -2
+    assert call(Hq=64, Hkv=2) == -4
+    assert call(d=80) == -4

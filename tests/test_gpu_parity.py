@@ -1,0 +1,312 @@
+"""GPU parity: every entry point of libdma.so against the CPU oracle on the same
+seeded inputs.
+
+Bars: dt within rel 1e-5; (tau, tie) and kept-index sets bit-exact; outputs
+within 2e-2 abs for bf16 and 1e-4 abs for fp32.  Small cases span several
+tiles with ragged tails and are compared element by element; the full
+workload sizes (launched exactly as the benchmark launches them) are compared
+on sampled rows that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+from tests.gpu_util import host_f64, sample_rows, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def dma():
+    import doge_dynamic_mask_amd as m
+    m.lib()
+    assert torch.cuda.is_available()
+    return m
+
+
+_INPUTS = {}
+
+
+def full_inputs(name):
+    if name not in _INPUTS:
+        _INPUTS[name] = si.make_inputs(si.WORKLOADS[name])
+    return _INPUTS[name]
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ dt ----
+@pytest.mark.parametrize("name", ["tiny", "c2", "long", "decode", "padded"])
+def test_dt_parity_full_size(dma, oracle_mod, name):
+    inp = full_inputs(name)
+    V = inp["Vc"] if si.WORKLOADS[name].decode else inp["V"]
+    got = to_host(dma.dt(to_dev(V), to_dev(inp["W"]), to_dev(inp["A"]), to_dev(inp["bias"])))
+    ref = oracle_mod.dt(V, inp["W"], inp["bias"], inp["A"])
+    rel = np.abs(got.astype(np.float64) - ref) / np.abs(ref)
+    assert rel.max() <= 1e-5, rel.max()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dt_no_bias_and_append(dma, oracle_mod, dtype):
+    rng = np.random.default_rng(5)
+    B, Lmax, Hkv, d = 3, 37, 4, 128
+    V = rng.standard_normal((B, 1, Hkv, d)).astype(np.float32)
+    W = rng.normal(0, 0.05, (Hkv, Hkv * d)).astype(np.float32)
+    A = rng.uniform(-2, 2, Hkv).astype(np.float32)
+    if dtype == "bf16":
+        V, W = si.to_bf16_bits(V), si.to_bf16_bits(W)
+    pos = np.array([0, 17, 36], np.int32)
+    cache = torch.full((B, Hkv, Lmax), -7.0, device="cuda:0")
+    dma.dt(to_dev(V), to_dev(W), to_dev(A), None, out=cache, out_pos=to_dev(pos))
+    got = to_host(cache)
+    ref = oracle_mod.dt(V, W, None, A)
+    for b in range(B):
+        np.testing.assert_allclose(got[b, :, pos[b]], ref[b, :, 0], rtol=1e-5)
+        mask = np.ones(Lmax, bool)
+        mask[pos[b]] = False
+        assert (got[b][:, mask] == -7.0).all()
+
+
+# -------------------------------------------------------------- select ----
+SELECT_CASES = [
+    # B, Hkv, S, w, kind, padded
+    (1, 1, 1, 1, "lognormal", False),
+    (1, 1, 2, 1, "lognormal", False),
+    (2, 2, 17, 4, "dyadic", True),
+    (2, 3, 64, 64, "lognormal", False),
+    (2, 2, 65, 64, "few", True),
+    (1, 2, 130, 7, "few", False),
+    (2, 2, 1000, 100, "lognormal", True),
+    (2, 2, 1000, 999, "dyadic", False),
+    (1, 1, 777, 1, "const", False),
+    (1, 1, 4096, 64, "const", False),
+    (1, 2, 3000, 2048, "few", True),
+    (2, 2, 500, 1000, "lognormal", False),
+    (1, 3, 5000, 300, "dyadic", False),
+    (1, 2, 2500, 63, "wide", True),
+    (1, 1, 1200, 65, "lognormal", False),
+]
+
+
+@pytest.mark.parametrize("B,Hkv,S,w,kind,padded", SELECT_CASES)
+def test_select_bit_exact(dma, oracle_mod, B, Hkv, S, w, kind, padded):
+    dt = si.make_dt((B, Hkv, S), kind, seed=S + w)
+    seq = si.make_lengths(B, 1, S, seed=w) if padded else None
+    tau, tie = dma.select(to_dev(dt), w, to_dev(seq))
+    rt, ri = oracle_mod.select(dt, w, seq)
+    np.testing.assert_array_equal(to_host(tie), ri)
+    np.testing.assert_array_equal(to_host(tau), rt)
+
+
+@pytest.mark.parametrize("name,kind", [("c2", "lognormal"), ("long", "dyadic"), ("padded", "lognormal"),
+                                       ("long", "few")])
+def test_select_full_size_sampled(dma, oracle_mod, name, kind):
+    wl = si.WORKLOADS[name]
+    seq = si.make_lengths(wl.B, wl.pad_lo, wl.pad_hi, seed=3) if wl.pad_hi else None
+    dt = si.make_dt((wl.B, wl.Hkv, wl.S), kind, seed=wl.seed)
+    tau, tie = dma.select(to_dev(dt), wl.w, to_dev(seq))
+    tau, tie = to_host(tau), to_host(tie)
+    rows = sample_rows(wl.B, wl.Hkv, wl.S, seq, 1500, seed=1, w=wl.w)
+    rt, ri = oracle_mod.select(dt, wl.w, seq, rows=rows)
+    b, g, i = rows.T
+    np.testing.assert_array_equal(tie[b, g, i], ri)
+    np.testing.assert_array_equal(tau[b, g, i], rt)
+    # every row's pair is monotone once rows hold more than w keys
+    for bb in range(wl.B):
+        L = wl.S if seq is None else int(seq[bb])
+        for gg in range(wl.Hkv):
+            t = tau[bb, gg, wl.w:L].astype(np.float64)
+            k = tie[bb, gg, wl.w:L].astype(np.int64)
+            assert ((t[1:] > t[:-1]) | ((t[1:] == t[:-1]) & (k[1:] <= k[:-1]))).all()
+            assert (tau[bb, gg, L:] == np.inf).all()
+
+
+# ----------------------------------------------------------- attention ----
+ATTN_CASES = [
+    # dtype, B, S, Hq, Hkv, d, w, kind, padded
+    ("f32", 1, 256, 2, 1, 64, 64, "lognormal", False),
+    ("f32", 2, 150, 4, 2, 128, 40, "dyadic", True),
+    ("bf16", 2, 300, 8, 4, 64, 64, "lognormal", True),
+    ("bf16", 1, 517, 16, 8, 128, 200, "lognormal", False),
+    ("bf16", 2, 200, 4, 4, 128, 300, "lognormal", False),
+    ("bf16", 1, 130, 2, 1, 128, 1, "few", False),
+    ("bf16", 1, 1, 2, 2, 64, 5, "lognormal", False),
+    ("bf16", 2, 1000, 32, 4, 128, 100, "lognormal", True),
+    ("bf16", 1, 700, 16, 1, 64, 50, "dyadic", False),
+    ("bf16", 1, 400, 4, 2, 128, 100, "const", False),
+    ("bf16", 1, 3000, 6, 2, 128, 2900, "wide", False),
+    ("bf16", 1, 2600, 4, 1, 64, 2500, "lognormal", True),
+]
+
+
+def _attn_case(dma, oracle_mod, dtype, B, S, Hq, Hkv, d, w, kind, padded, seed):
+    Q, K, V = si.make_qkv(B, S, Hq, Hkv, d, dtype, seed=seed)
+    dt = si.make_dt((B, Hkv, S), kind, seed=seed + 1)
+    seq = si.make_lengths(B, 1, S, seed=seed + 2) if padded else None
+    dts = to_dev(dt)
+    tau, tie = dma.select(dts, w, to_dev(seq))
+    O = dma.attn_fwd(to_dev(Q), to_dev(K), to_dev(V), dts, tau, tie, w, to_dev(seq))
+    return Q, K, V, dt, seq, to_host(O)
+
+
+@pytest.mark.parametrize("dtype,B,S,Hq,Hkv,d,w,kind,padded", ATTN_CASES)
+def test_attn_elementwise(dma, oracle_mod, dtype, B, S, Hq, Hkv, d, w, kind, padded):
+    Q, K, V, dt, seq, got = _attn_case(dma, oracle_mod, dtype, B, S, Hq, Hkv, d, w, kind, padded,
+                                       seed=S * 3 + w)
+    ref = oracle_mod.attn(Q, K, V, dt, w, seqlens=seq)
+    assert np.isfinite(got).all()
+    err = np.abs(got.astype(np.float64) - ref)
+    assert err.max() <= TOL[dtype], err.max()
+    if seq is not None:
+        for b in range(B):
+            assert (got[b, seq[b]:] == 0).all()
+
+
+@pytest.mark.parametrize("name", ["c2", "long", "padded"])
+def test_attn_full_size_sampled(dma, oracle_mod, name):
+    wl = si.WORKLOADS[name]
+    inp = full_inputs(name)
+    seq = inp["seqlens"]
+    dt = si.make_dt((wl.B, wl.Hkv, wl.S), "lognormal", seed=wl.seed + 7)
+    dts = to_dev(dt)
+    tau, tie = dma.select(dts, wl.w, to_dev(seq))
+    O = to_host(dma.attn_fwd(to_dev(inp["Q"]), to_dev(inp["K"]), to_dev(inp["V"]), dts, tau, tie, wl.w,
+                             to_dev(seq)))
+    rows = sample_rows(wl.B, wl.Hkv, wl.S, seq, 600, seed=2, w=wl.w)
+    ref = oracle_mod.attn(inp["Q"], inp["K"], inp["V"], dt, wl.w, seqlens=seq, rows=rows)
+    G = wl.Hq // wl.Hkv
+    for n, (b, g, i) in enumerate(rows):
+        got = O[b, i, g * G:(g + 1) * G].astype(np.float64)
+        assert np.abs(got - ref[n]).max() <= TOL[wl.dtype], (b, g, i)
+    if seq is not None:
+        for b in range(wl.B):
+            assert (O[b, seq[b]:] == 0).all()
+
+
+def test_attn_deterministic_and_gqa_equals_mha(dma, oracle_mod):
+    B, S, Hq, Hkv, d, w = 1, 700, 8, 2, 128, 150
+    Q, K, V = si.make_qkv(B, S, Hq, Hkv, d, "bf16", seed=31)
+    dt = si.make_dt((B, Hkv, S), "lognormal", seed=32)
+    dQ, dK, dV, ddt = to_dev(Q), to_dev(K), to_dev(V), to_dev(dt)
+    tau, tie = dma.select(ddt, w)
+    o1 = to_host(dma.attn_fwd(dQ, dK, dV, ddt, tau, tie, w))
+    o2 = to_host(dma.attn_fwd(dQ, dK, dV, ddt, tau, tie, w))
+    assert (o1 == o2).all()
+    G = Hq // Hkv
+    Kr, Vr, dtr = np.repeat(K, G, axis=2), np.repeat(V, G, axis=2), np.repeat(dt, G, axis=1)
+    dtr_d = to_dev(dtr)
+    tr, kr = dma.select(dtr_d, w)
+    o3 = to_host(dma.attn_fwd(dQ, to_dev(Kr), to_dev(Vr), dtr_d, tr, kr, w))
+    assert np.abs(o1.astype(np.float64) - o3).max() <= 2e-2
+
+
+def test_attn_padding_is_truncation_and_nan_safe(dma, oracle_mod):
+    B, S, Hq, Hkv, d, w = 2, 640, 8, 4, 128, 200
+    Q, K, V = si.make_qkv(B, S, Hq, Hkv, d, "bf16", seed=41)
+    dt = si.make_dt((B, Hkv, S), "lognormal", seed=42)
+    seq = np.array([640, 333], np.int32)
+    Kn, Vn, dtn = K.copy(), V.copy(), dt.copy()
+    Kn[1, 333:] = 0x7FC0  # bf16 NaN
+    Vn[1, 333:] = 0x7FC0
+    dtn[1, :, 333:] = np.nan
+    ddt = to_dev(dtn)
+    tau, tie = dma.select(ddt, w, to_dev(seq))
+    O = to_host(dma.attn_fwd(to_dev(Q), to_dev(Kn), to_dev(Vn), ddt, tau, tie, w, to_dev(seq)))
+    assert np.isfinite(O).all()
+    assert (O[1, 333:] == 0).all()
+    dtt = to_dev(np.ascontiguousarray(dt[1:, :, :333]))
+    t2, k2 = dma.select(dtt, w)
+    O2 = to_host(dma.attn_fwd(to_dev(np.ascontiguousarray(Q[1:, :333])), to_dev(np.ascontiguousarray(K[1:, :333])),
+                              to_dev(np.ascontiguousarray(V[1:, :333])), dtt, t2, k2, w))
+    assert np.abs(O[1:, :333].astype(np.float64) - O2).max() <= 2e-2
+
+
+# ---------------------------------------------------------------- decode ----
+def _decode_check(dma, oracle_mod, q, Kc, Vc, dtc, lens, w, tol):
+    out, kept = dma.decode(to_dev(q), to_dev(Kc), to_dev(Vc), to_dev(dtc), to_dev(lens), w, kept=True)
+    out, kept = to_host(out), to_host(kept)
+    ref, rkept = oracle_mod.decode(q, Kc, Vc, dtc, lens, w)
+    np.testing.assert_array_equal(kept, rkept)
+    err = np.abs(out.astype(np.float64) - ref)
+    assert err.max() <= tol, err.max()
+
+
+def test_decode_full_size(dma, oracle_mod):
+    wl = si.WORKLOADS["decode"]
+    inp = full_inputs("decode")
+    dtc = si.make_dt((wl.B, wl.Hkv, wl.S), "lognormal", seed=77)
+    _decode_check(dma, oracle_mod, inp["q"], inp["Kc"], inp["Vc"], dtc, inp["cache_lens"], wl.w, 2e-2)
+
+
+@pytest.mark.parametrize("dtype,kind,d,Hq,Hkv", [("bf16", "lognormal", 128, 8, 2), ("bf16", "dyadic", 64, 4, 4),
+                                                 ("bf16", "const", 128, 16, 1), ("f32", "few", 64, 6, 3),
+                                                 ("f32", "lognormal", 128, 4, 1)])
+def test_decode_edge_lengths(dma, oracle_mod, dtype, kind, d, Hq, Hkv):
+    B, Lmax, w = 6, 3000, 2048
+    rng = np.random.default_rng(d + Hq)
+    lens = np.array([1, 2, 2048, 2049, 3000, 1025], np.int32)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    Kc = rng.standard_normal((B, Lmax, Hkv, d)).astype(np.float32)
+    Vc = rng.standard_normal((B, Lmax, Hkv, d)).astype(np.float32)
+    if dtype == "bf16":
+        q, Kc, Vc = si.to_bf16_bits(q), si.to_bf16_bits(Kc), si.to_bf16_bits(Vc)
+    dtc = si.make_dt((B, Hkv, Lmax), kind, seed=d)
+    _decode_check(dma, oracle_mod, q, Kc, Vc, dtc, lens, w, TOL[dtype])
+
+
+def test_decode_matches_last_prefill_row(dma, oracle_mod):
+    B, S, Hq, Hkv, d, w = 3, 900, 8, 2, 128, 256
+    Q, K, V = si.make_qkv(B, S, Hq, Hkv, d, "bf16", seed=51)
+    dt = si.make_dt((B, Hkv, S), "lognormal", seed=52)
+    lens = np.array([900, 256, 611], np.int32)
+    ddt = to_dev(dt)
+    tau, tie = dma.select(ddt, w, to_dev(lens))
+    O = to_host(dma.attn_fwd(to_dev(Q), to_dev(K), to_dev(V), ddt, tau, tie, w, to_dev(lens)))
+    q = np.stack([Q[b, lens[b] - 1] for b in range(B)])
+    out = to_host(dma.decode(to_dev(q), to_dev(K), to_dev(V), ddt, to_dev(lens), w))
+    for b in range(B):
+        assert np.abs(out[b].astype(np.float64) - O[b, lens[b] - 1]).max() <= 2e-2
+
+
+# ------------------------------------------------------ end to end chain ----
+@pytest.mark.parametrize("name", ["tiny", "c2", "long", "padded"])
+def test_prefill_chain_from_value_states(dma, oracle_mod, name):
+    """dt -> select -> attention on the GPU against the oracle's own chain.
+    Rows whose kept set depends on a dt difference below the dt tolerance
+    (a near tie at the w-th place) are compared on the kept set of the GPU's
+    own dt and must be such near ties; every other row must match."""
+    wl = si.WORKLOADS[name]
+    inp = full_inputs(name)
+    seq = inp["seqlens"]
+    O, dtg, tau, tie = dma.prefill(to_dev(inp["Q"]), to_dev(inp["K"]), to_dev(inp["V"]), to_dev(inp["W"]),
+                                   to_dev(inp["A"]), wl.w, bias=to_dev(inp["bias"]), seqlens=to_dev(seq))
+    O, dtg, tau, tie = to_host(O), to_host(dtg), to_host(tau), to_host(tie)
+    ref_dt = oracle_mod.dt(inp["V"], inp["W"], inp["bias"], inp["A"])
+    assert (np.abs(dtg - ref_dt) / ref_dt).max() <= 1e-5
+    dt32 = ref_dt.astype(np.float32)
+    rows = sample_rows(wl.B, wl.Hkv, wl.S, seq, 400 if wl.S > 256 else 4 * wl.B * wl.Hkv * wl.S,
+                       seed=3, w=wl.w)
+    ref = oracle_mod.attn(inp["Q"], inp["K"], inp["V"], dt32, wl.w, seqlens=seq, rows=rows)
+    G = wl.Hq // wl.Hkv
+    near_ties = 0
+    for n, (b, g, i) in enumerate(rows):
+        got = O[b, i, g * G:(g + 1) * G].astype(np.float64)
+        ks_o = oracle_mod.kept_row(dt32, wl.w, b, g, i, seq)
+        # the GPU's kept set: its own threshold pair applied to its own dt
+        L = wl.S if seq is None else int(seq[b])
+        j = np.arange(min(i + 1, L))
+        x = dtg[b, g, j]
+        ks_g = j[(x > tau[b, g, i]) | ((x == tau[b, g, i]) & (j <= tie[b, g, i]))]
+        if ks_o.tolist() != ks_g.tolist():
+            diff = np.setxor1d(ks_o, ks_g)
+            d_ = ref_dt[b, g, diff]
+            assert (d_.max() - d_.min()) / d_.min() <= 4e-5, (b, g, i)
+            near_ties += 1
+            continue
+        assert np.abs(got - ref[n]).max() <= TOL[wl.dtype], (b, g, i)
+    assert near_ties <= max(2, len(rows) // 50)
