@@ -10,9 +10,12 @@ The 512 MiB scratch write before each decode evicts the kept K/V rows from
 the caches, so decode moves its bytes from HBM; it is outside the timed kernels.
 
 Printed: ONE JSON line.  value = prefill kept-key TFLOP/s (kept (query, key)
-pairs x 4*d flop over the three prefill kernels' GPU time); the decode GB/s
-(algorithmic bytes over dma_decode's GPU time) rides along under "decode".
-Kernel times come from HIP events recorded on the stream the kernels run on.
+pairs x 4*d flop over the GPU time of the three prefill kernels, replayed as
+one HIP graph); the decode GB/s (algorithmic bytes over dma_decode's GPU
+time) rides along under "decode".  ms_per_step = prefill + decode GPU time of
+one step (the cache flush between them is excluded); the wall-clock time per
+step including the flush is reported too.  Times come from HIP events
+recorded on the stream the kernels run on.
 """
 from __future__ import annotations
 
@@ -57,7 +60,7 @@ def to_dev(x, dev):
     return (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
 
 
-def cpu_baseline(pre_inp, wl_p, dec_inp, wl_d, dtc_host, min_seconds=10.0):
+def cpu_baseline(pre_inp, wl_p, min_seconds=10.0):
     """The oracle (plain C, fp64, OpenMP) timed on the host: full prefill of
     the same batch (dt, select, attention over every row), repeated until
     min_seconds have passed.  Reported in the metric's unit (kept-key TFLOP/s)."""
@@ -80,12 +83,50 @@ def cpu_baseline(pre_inp, wl_p, dec_inp, wl_d, dtc_host, min_seconds=10.0):
                       f"{reps} repetitions in {el:.1f} s, fp64"}
 
 
+def prefill_breakdown(dma, name, dev, reps=10):
+    """Per-kernel GPU time of one prefill workload (graph replays between events)."""
+    wl = si.WORKLOADS[name]
+    inp = si.make_inputs(wl)
+    Q, K, V = to_dev(inp["Q"], dev), to_dev(inp["K"], dev), to_dev(inp["V"], dev)
+    W, A, bias = to_dev(inp["W"], dev), to_dev(inp["A"], dev), to_dev(inp["bias"], dev)
+    seq = None if inp["seqlens"] is None else to_dev(inp["seqlens"], dev)
+    dt = torch.empty((wl.B, wl.Hkv, wl.S), dtype=torch.float32, device=dev)
+    tau, tie = torch.empty_like(dt), torch.empty(dt.shape, dtype=torch.int32, device=dev)
+    O = torch.empty_like(Q)
+    fns = {"dt": lambda: dma.dt(V, W, A, bias, out=dt),
+           "select": lambda: dma.select(dt, wl.w, seq, tau=tau, tie=tie),
+           "attn_fwd": lambda: dma.attn_fwd(Q, K, V, dt, tau, tie, wl.w, seq, out=O)}
+    res = {}
+    for n, f in fns.items():
+        f()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            f()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        res[n] = a.elapsed_time(b) / reps
+    flops = kept_flops(wl.B, wl.Hq, wl.S, wl.d, wl.w, inp["seqlens"])
+    tot = sum(res.values())
+    return {"ms": {k: round(v, 5) for k, v in res.items()}, "kept_flops": flops,
+            "tflops_prefill": round(flops / (tot * 1e-3) / 1e12, 2),
+            "tflops_attn": round(flops / (res["attn_fwd"] * 1e-3) / 1e12, 2),
+            "attn_frac_of_peak": round(flops / (res["attn_fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--other-configs", action="store_true",
+                    help="also time the other prefill workloads (long, padded, tiny) per kernel")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the DMA hot path has no cross-GPU step in this build "
@@ -121,51 +162,98 @@ def main():
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    names = ["dt", "select", "attn_fwd", "dt_append", "decode"]
-
-    def step(ev=None):
-        if ev: ev[0].record()
+    # Each stage is captured once into a HIP graph (the binding launches on
+    # torch's current stream, which is the capture stream), so a replay costs
+    # one launch and the events below time GPU work rather than Python.
+    def g_dt():
         dma.dt(V, W, A, bias, out=dt)
-        if ev: ev[1].record()
+
+    def g_select():
         dma.select(dt, wl_p.w, tau=tau, tie=tie)
-        if ev: ev[2].record()
+
+    def g_attn():
         dma.attn_fwd(Q, K, V, dt, tau, tie, wl_p.w, out=O)
-        if ev: ev[3].record()
-        flush.fill_(1.0)
-        if ev: ev[4].record()
+
+    def g_dt_append():
         dma.dt(v_new, Wd, Ad, biasd, out=dt_cache, out_pos=pos)
-        if ev: ev[5].record()
+
+    def g_decode():
         dma.decode(q, Kc, Vc, dt_cache, lens, wl_d.w, out=out, workspace=ws)
-        if ev: ev[6].record()
+
+    def capture(*fns):
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        return g
+
+    G_pre = capture(g_dt, g_select, g_attn)
+    G_dec = capture(g_dt_append, g_decode)
+    single = {"dt": capture(g_dt), "select": capture(g_select), "attn_fwd": capture(g_attn),
+              "dt_append": capture(g_dt_append), "decode": capture(g_decode)}
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step(e=None):
+        if e:
+            e[0].record()
+        G_pre.replay()
+        if e:
+            e[1].record()
+        flush.fill_(1.0)
+        if e:
+            e[2].record()
+        G_dec.replay()
+        if e:
+            e[3].record()
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[ev() for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms_pre = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_dec = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
 
-    per = {n: [] for n in names}
-    for ev in evs:
-        per["dt"].append(ev[0].elapsed_time(ev[1]))
-        per["select"].append(ev[1].elapsed_time(ev[2]))
-        per["attn_fwd"].append(ev[2].elapsed_time(ev[3]))
-        per["dt_append"].append(ev[4].elapsed_time(ev[5]))
-        per["decode"].append(ev[5].elapsed_time(ev[6]))
-    avg = {n: float(np.mean(v)) for n, v in per.items()}
-    med = {n: float(np.median(v)) for n, v in per.items()}
+    # Per-kernel average durations: REPS back-to-back replays of a one-kernel
+    # graph between two events; the decode kernels run after a cache flush.
+    REPS = 20
+    avg = {}
+    for n, g in single.items():
+        if n in ("dt_append", "decode"):
+            pairs = []
+            for _ in range(REPS):
+                flush.fill_(1.0)
+                a, b = ev(), ev()
+                a.record()
+                g.replay()
+                b.record()
+                pairs.append((a, b))
+            torch.cuda.synchronize()
+            avg[n] = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+        else:
+            a, b = ev(), ev()
+            a.record()
+            for _ in range(REPS):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            avg[n] = a.elapsed_time(b) / REPS
 
     flops = kept_flops(wl_p.B, wl_p.Hq, wl_p.S, wl_p.d, wl_p.w)
-    t_prefill = (avg["dt"] + avg["select"] + avg["attn_fwd"]) * 1e-3
-    value = flops / t_prefill / 1e12
+    value = flops / (ms_pre * 1e-3) / 1e12
     dbytes = decode_bytes(wl_d.B, wl_d.Hq, wl_d.Hkv, wl_d.d, wl_d.w, dec["cache_lens"])
     dec_gbs = dbytes / (avg["decode"] * 1e-3) / 1e9
     attn_tflops = flops / (avg["attn_fwd"] * 1e-3) / 1e12
-    ms_step = sum(avg[n] for n in names)
 
     line = {
         "metric": "DMA prefill kept-key TFLOP/s + decode GB/s, % of MI355X roofline",
@@ -174,7 +262,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(ms_pre + ms_dec, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -195,12 +283,15 @@ def main():
             "value": round(dec_gbs, 2), "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS,
             "frac": round(dec_gbs / PEAK_HBM_GBS, 5),
         },
+        "ms_prefill": round(ms_pre, 5),
+        "ms_decode_step": round(ms_dec, 5),
         "kernel_ms_avg": {n: round(v, 5) for n, v in avg.items()},
-        "kernel_ms_median": {n: round(v, 5) for n, v in med.items()},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
     }
+    if args.other_configs:
+        line["other_configs"] = {n: prefill_breakdown(dma, n, dev) for n in ("long", "padded")}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(pre, wl_p, dec, wl_d, None)
+        line["cpu_baseline"] = cpu_baseline(pre, wl_p)
     print(json.dumps(line), flush=True)
 
 

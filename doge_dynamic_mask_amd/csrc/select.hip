@@ -7,10 +7,12 @@
 //   (1) nesting: K_{i+1} is a subset of K_i plus {i+1}, so the w-th best key
 //       only moves towards better keys as i grows; and
 //   (2) for a chunk of C rows starting at r0, every row's kept set is the top
-//       w of (prefix [0, r0)) plus at most C new keys.  The best w-C keys of
-//       the prefix are therefore kept by every row of the chunk, prefix keys
-//       of rank >= w by none, and each row's threshold key lies in the "band"
-//       of prefix ranks [w-C, w) plus the chunk's own keys: at most 2C keys.
+//       w of (prefix [0, r0)) plus at most C new keys.  A prefix key of
+//       prefix rank k has between k and k + C better keys in a row's set, so
+//       the best w-C-1 prefix keys are kept by every row of the chunk and are
+//       never its w-th key, prefix keys of rank >= w are kept by none, and
+//       each row's threshold key lies in the "band" of prefix ranks
+//       [w-C-1, w) plus the chunk's own keys: at most 2C+1 keys.
 // One workgroup per (batch, kv head, chunk of 64 rows) finds the two band
 // limits with a two-target radix select over the prefix, gathers the band and
 // the chunk's keys into LDS, sorts them, and lets each row walk the sorted
@@ -25,7 +27,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunk = 64;
-constexpr int kSortN = 2 * kChunk;
+constexpr int kBand = kChunk + 1;  // band width: prefix ranks [w - kChunk - 1, w)
+constexpr int kSortN = 256;        // power of two >= kBand + kChunk
 
 __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restrict__ dt,
                                                           const int32_t *__restrict__ seqlens,
@@ -59,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
     if (lo >= hi) return;  // uniform across the workgroup
 
     const int P = r0;  // prefix [0, r0): all valid, as r0 < hi <= L
-    const int A0 = max(0, min(P, w - kChunk));
+    const int A0 = max(0, min(P, w - kChunk - 1));
     const int nb = min(P, w) - A0;
     if (tid == 0) ncand = 0;
     __syncthreads();
@@ -74,12 +77,12 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
             const uint64_t k = selkey(row[j], (uint32_t)j);
             if (k <= khi && k >= klo) {
                 const int at = atomicAdd(&ncand, 1);
-                if (at < kChunk) cand[at] = k;  // exactly nb <= kChunk keys match
+                if (at < kBand) cand[at] = k;  // exactly nb <= kBand keys match
             }
         }
     }
     __syncthreads();
-    const int nband = min(ncand, kChunk);
+    const int nband = min(ncand, kBand);
     const int nnew = hi - r0;
     for (int t = tid; t < kSortN; t += kThreads) {
         if (t >= nband && t < nband + nnew) {

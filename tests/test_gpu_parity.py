@@ -90,6 +90,9 @@ SELECT_CASES = [
     (1, 3, 5000, 300, "dyadic", False),
     (1, 2, 2500, 63, "wide", True),
     (1, 1, 1200, 65, "lognormal", False),
+    (1, 1, 3000, 700, "dyadic", False),   # a prefix key of rank w-C-1 can be the threshold
+    (2, 2, 2000, 129, "few", True),
+    (1, 2, 4000, 1000, "lognormal", False),
 ]
 
 
