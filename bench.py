@@ -6,8 +6,9 @@ One step = the whole hot path over one batch of synthetic input:
   prefill  B=4 Hq=8 Hkv=4 S=2048 d=64 w=512 bf16  (dma_dt -> dma_select -> dma_attn_fwd)
   decode   B=64 Hq=8 Hkv=2 d=128 w=2048, 16384 cached positions
            (dma_dt appends the new token's dt, then dma_decode)
-The 512 MiB scratch write before each decode evicts the kept K/V rows from
-the caches, so decode moves its bytes from HBM; it is outside the timed kernels.
+A 512 MiB read before each decode evicts the kept K/V rows from the caches
+(with clean lines, so no write-back traffic lands on the decode), so decode
+moves its bytes from HBM; the eviction is outside the timed kernels.
 
 Printed: ONE JSON line.  value = prefill kept-key TFLOP/s (kept (query, key)
 pairs x 4*d flop over the GPU time of the three prefill kernels, replayed as
@@ -159,7 +160,12 @@ def main():
     out = torch.empty_like(q)
     ws = torch.empty(dma.decode_workspace_bytes(wl_d.B, wl_d.S, wl_d.Hq, wl_d.Hkv, wl_d.d, wl_d.w),
                      dtype=torch.uint8, device=dev)
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    flush_buf = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def evict():
+        torch.sum(flush_buf, dim=0, out=flush_out)
+
     torch.cuda.synchronize()
 
     # Each stage is captured once into a HIP graph (the binding launches on
@@ -205,7 +211,7 @@ def main():
         G_pre.replay()
         if e:
             e[1].record()
-        flush.fill_(1.0)
+        evict()
         if e:
             e[2].record()
         G_dec.replay()
@@ -232,7 +238,7 @@ def main():
         if n in ("dt_append", "decode"):
             pairs = []
             for _ in range(REPS):
-                flush.fill_(1.0)
+                evict()
                 a, b = ev(), ev()
                 a.record()
                 g.replay()

@@ -84,6 +84,7 @@ int dma_decode(const void *q, const void *Kc, const void *Vc, int dtype, const f
     if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || d < 1 || w < 1 || Hq % Hkv != 0) return DMA_ERR_SHAPE;
     if (!head_dim_ok(d) || Hq / Hkv > dma::kMaxGroupDecode) return DMA_ERR_UNSUPPORTED;
     if (B > 65535 || Hkv > 65535) return DMA_ERR_UNSUPPORTED;
+    if ((Lmax < w ? Lmax : w) > dma::kMaxKeptDecode) return DMA_ERR_UNSUPPORTED;
     if (!aligned16(Kc) || !aligned16(Vc)) return DMA_ERR_UNSUPPORTED;
     if (!ws) return DMA_ERR_WORKSPACE;
     if (ws_bytes < dma::decode_ws_bytes(B, Lmax, Hq, Hkv, d, w)) return DMA_ERR_WORKSPACE;

@@ -5,19 +5,20 @@
 //
 // Three launches on the caller's stream:
 //  1. select: one workgroup per (batch, kv head) finds the w-th best cached
-//     position exactly (order: dt desc, index asc) and stores the threshold
-//     pair; optionally writes the kept positions in ascending order.  Rows of
-//     up to 32768 positions are held in registers (1024 threads) and resolved
-//     with one range-adapted 4096-bin histogram plus an exact rank of the few
+//     position exactly (order: dt desc, index asc) and writes the kept
+//     positions in ascending order (plus their dt) to the workspace, and to
+//     kept_idx when asked.  Rows of up to 32768 positions are held in
+//     registers (1024 threads, each owning consecutive positions) and resolved
+//     with a range-adapted 4096-bin histogram plus an exact rank of the few
 //     keys in the threshold bin; longer rows use the multi-pass radix select.
-//  2. attend: split over the cache: one workgroup per (batch, kv head, 1024
-//     positions) re-reads its dt slice, keeps the positions that pass the
-//     threshold test and gathers only their K/V rows, 64 at a time, into LDS
-//     with coalesced 16-byte loads (the next block's loads are issued before
-//     the current block's math).  Scores use 4 lanes per key; the weighted V
-//     sum uses lanes over head_dim.  It writes a partial (max, sum, output)
-//     per query head.
-//  3. combine: merges the partials of each (batch, kv head) into the output.
+//  2. attend: one workgroup per (batch, kv head, 64 kept positions) issues
+//     every K/V row load of its positions up front (coalesced, non-temporal
+//     16-byte loads: the rows are read once) and stages them in LDS; bf16
+//     runs the scores and the weighted V sum on 16x16x32 MFMA with the G
+//     query heads as the N dimension, fp32 uses VALU (4 lanes per key for the
+//     scores, lanes over head_dim for the sum); writes a partial (max, sum,
+//     output) per query head.
+//  3. combine: merges the partials of each (batch, query head).
 //     (A separate launch: merging inside the last attend workgroup would need
 //     device-scope fences, which on a multi-XCD part write back and
 //     invalidate L2 in every workgroup.)
@@ -31,27 +32,30 @@ namespace dma {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSplit = 1024;       // cache positions per attend workgroup
+constexpr int kKPC = 64;           // kept positions per attend workgroup
 constexpr int kSelThreads = 1024;  // select workgroup (register-resident rows)
 constexpr int kBins = 4096;
 constexpr int kCandCap = 1024;
 
-inline int nsplit_of(int Lmax) { return (Lmax + kSplit - 1) / kSplit; }
+inline int nchunk_of(int Lmax, int w) {
+    const int n = Lmax < w ? Lmax : w;
+    return (n + kKPC - 1) / kKPC;
+}
 
 struct WsLayout {
-    size_t thr_tau, thr_tie, pm, pl, po, total;
+    size_t kept, kdt, pm, pl, po, total;
 };
 
-inline WsLayout ws_layout(int B, int Lmax, int Hq, int Hkv, int d) {
+inline WsLayout ws_layout(int B, int Lmax, int Hq, int Hkv, int d, int w) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    const size_t ns = (size_t)nsplit_of(Lmax);
+    const size_t nc = (size_t)nchunk_of(Lmax, w);
     WsLayout l;
-    l.thr_tau = 0;
-    l.thr_tie = up(l.thr_tau + sizeof(float) * B * Hkv);
-    l.pm = up(l.thr_tie + sizeof(int32_t) * B * Hkv);
-    l.pl = up(l.pm + sizeof(float) * B * Hq * ns);
-    l.po = up(l.pl + sizeof(float) * B * Hq * ns);
-    l.total = up(l.po + sizeof(float) * B * Hq * ns * d);
+    l.kept = 0;
+    l.kdt = up(l.kept + sizeof(int32_t) * B * Hkv * w);
+    l.pm = up(l.kdt + sizeof(float) * B * Hkv * w);
+    l.pl = up(l.pm + sizeof(float) * B * Hq * nc);
+    l.po = up(l.pl + sizeof(float) * B * Hq * nc);
+    l.total = up(l.po + sizeof(float) * B * Hq * nc * d);
     return l;
 }
 
@@ -67,12 +71,16 @@ struct SelShared {
     uint64_t result;
 };
 
-// Exclusive prefix count of `flag` over threads (thread order), and the total.
-__device__ __forceinline__ uint32_t block_excl_count(bool flag, uint32_t &total, SelShared &sh) {
+// Exclusive prefix sum of v over the threads (thread order), and the total.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t &total, SelShared &sh) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint64_t bal = __ballot(flag);
-    const uint32_t pre = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) sh.red2[wave] = (uint32_t)__popcll(bal);
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) sh.red2[wave] = incl;
     __syncthreads();
     uint32_t off = 0, tot = 0;
 #pragma unroll
@@ -83,7 +91,7 @@ __device__ __forceinline__ uint32_t block_excl_count(bool flag, uint32_t &total,
     }
     __syncthreads();
     total = tot;
-    return off + pre;
+    return off + incl - v;
 }
 
 // Histogram of bin(key) for the keys with filter(key) true, then the bin that
@@ -95,7 +103,7 @@ __device__ void hist_find(const uint32_t *k, int L, uint32_t rr, BinF binf, Filt
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
-        const int j = it * kSelThreads + tid;
+        const int j = tid * ITEMS + it;
         if (j < L && filt(k[it])) atomicAdd(&sh.hist[binf(k[it])], 1u);
     }
     __syncthreads();
@@ -135,29 +143,52 @@ __device__ void hist_find(const uint32_t *k, int L, uint32_t rr, BinF binf, Filt
     __syncthreads();
 }
 
+// Kept positions (ascending) and their dt*log2(e) into the workspace lists;
+// also into kept_idx (padded with -1 up to w) when it is given.
+__device__ __forceinline__ void write_kept(int32_t *kl, float *kd, int32_t *kept_idx, uint32_t pos, int j,
+                                           float dtv, int w) {
+    if (pos < (uint32_t)w) {
+        kl[pos] = j;
+        kd[pos] = dtv * kLog2e;
+        if (kept_idx) kept_idx[pos] = j;
+    }
+}
+
 template <int ITEMS>
 __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(
     const float *__restrict__ dt_cache, const int32_t *__restrict__ cache_lens, int Hkv, int Lmax,
-    int w, float *__restrict__ thr_tau, int32_t *__restrict__ thr_tie, int32_t *__restrict__ kept_idx) {
+    int w, int32_t *__restrict__ kept_ws, float *__restrict__ kdt_ws, int32_t *__restrict__ kept_idx) {
+    static_assert(ITEMS % 4 == 0, "float4 loads");
     __shared__ SelShared sh;
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int L = cache_lens[b];
     const float *row = dt_cache + ((size_t)b * Hkv + g) * Lmax;
+    const int j0 = tid * ITEMS;  // this thread owns positions j0 .. j0 + ITEMS - 1
 
+    float dv[ITEMS];
     uint32_t k[ITEMS];
     uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
+    for (int q4 = 0; q4 < ITEMS / 4; ++q4) {
+        const int jj = j0 + 4 * q4;
+        if (jj + 3 < L && (((uintptr_t)(row + jj)) & 15u) == 0) {
+            const float4 v = *reinterpret_cast<const float4 *>(row + jj);
+            dv[4 * q4] = v.x; dv[4 * q4 + 1] = v.y; dv[4 * q4 + 2] = v.z; dv[4 * q4 + 3] = v.w;
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dv[4 * q4 + u] = jj + u < L ? row[jj + u] : 0.f;
+        }
+    }
+#pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
-        const int j = it * kSelThreads + tid;
-        k[it] = j < L ? ordkey(row[j]) : 0u;
-        if (j < L) {
+        const bool valid = j0 + it < L;
+        k[it] = valid ? ordkey(dv[it]) : 0u;
+        if (valid) {
             kmin = min(kmin, k[it]);
             kmax = max(kmax, k[it]);
         }
     }
     uint64_t result = 0;  // (ordkey << 32) | ~index of the w-th kept position
-    float t_tau = -INFINITY;
-    int t_tie = -1;
     if (L > w) {
         // block min / max of the keys
         const int lane = tid & 63, wave = tid >> 6;
@@ -209,7 +240,7 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(
             __syncthreads();
 #pragma unroll
             for (int it = 0; it < ITEMS; ++it) {
-                const int j = it * kSelThreads + tid;
+                const int j = j0 + it;
                 if (j < L && in_bin(k[it])) {
                     const uint32_t at = atomicAdd(&sh.ncand, 1u);
                     sh.cand[at] = ((uint64_t)k[it] << 32) | (uint64_t)(~(uint32_t)j);
@@ -223,53 +254,55 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(
                 if (rank == rr) sh.result = me;
             }
             __syncthreads();
-            result = sh.result;
         } else {
             // a single key value shared by more than kCandCap positions: the
-            // rr-th of them in index order.  Index order is item-major here.
+            // rr-th of them in index order (threads own consecutive positions)
             const uint32_t kv = bsel;
-            uint32_t seen = 0;
-            for (int it = 0; it < ITEMS; ++it) {
-                const int j = it * kSelThreads + tid;
-                const bool m = j < L && k[it] == kv;
-                uint32_t tot;
-                const uint32_t pre = block_excl_count(m, tot, sh);
-                if (seen + tot > rr) {
-                    if (m && seen + pre == rr) sh.result = ((uint64_t)kv << 32) | (uint64_t)(~(uint32_t)j);
-                    __syncthreads();
-                    break;
+            uint32_t c = 0;
+#pragma unroll
+            for (int it = 0; it < ITEMS; ++it) c += (j0 + it < L && k[it] == kv) ? 1u : 0u;
+            uint32_t tot;
+            const uint32_t before = block_excl_scan(c, tot, sh);
+            if (before <= rr && rr < before + c) {
+                uint32_t seen = before;
+#pragma unroll
+                for (int it = 0; it < ITEMS; ++it) {
+                    if (j0 + it < L && k[it] == kv) {
+                        if (seen == rr) sh.result = ((uint64_t)kv << 32) | (uint64_t)(~(uint32_t)(j0 + it));
+                        ++seen;
+                    }
                 }
-                seen += tot;
             }
-            result = sh.result;
+            __syncthreads();
         }
-        t_tie = (int)selkey_idx(result);
-        t_tau = row[t_tie];
+        result = sh.result;
     }
-    if (tid == 0) {
-        thr_tau[b * Hkv + g] = t_tau;
-        thr_tie[b * Hkv + g] = t_tie;
-    }
-    if (!kept_idx) return;
-    // kept positions in ascending order (item-major = index order)
-    int32_t *out = kept_idx + ((size_t)b * Hkv + g) * w;
-    const uint64_t thr = (L > w) ? result : 0ull;
-    uint32_t offset = 0;
+    // kept positions, ascending: per-thread counts, one block scan
+    uint32_t c = 0;
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it)
+        c += (j0 + it < L && ((((uint64_t)k[it] << 32) | (uint64_t)(~(uint32_t)(j0 + it))) >= result)) ? 1u : 0u;
+    uint32_t tot;
+    uint32_t pos = block_excl_scan(c, tot, sh);
+    int32_t *kl = kept_ws + ((size_t)b * Hkv + g) * w;
+    float *kd = kdt_ws + ((size_t)b * Hkv + g) * w;
+    int32_t *ki = kept_idx ? kept_idx + ((size_t)b * Hkv + g) * w : nullptr;
+#pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
-        const int j = it * kSelThreads + tid;
-        const bool keep = j < L && ((((uint64_t)k[it] << 32) | (uint64_t)(~(uint32_t)j)) >= thr);
-        uint32_t tot;
-        const uint32_t pre = block_excl_count(keep, tot, sh);
-        if (keep && offset + pre < (uint32_t)w) out[offset + pre] = j;
-        offset += tot;
+        const int j = j0 + it;
+        if (j < L && ((((uint64_t)k[it] << 32) | (uint64_t)(~(uint32_t)j)) >= result)) {
+            write_kept(kl, kd, ki, pos, j, dv[it], w);
+            ++pos;
+        }
     }
-    for (int q = min(L, w) + tid; q < w; q += kSelThreads) out[q] = -1;
+    if (ki)
+        for (int q = min(L, w) + tid; q < w; q += kSelThreads) ki[q] = -1;
 }
 
 // Rows longer than the register-resident path: multi-pass radix select.
 __global__ __launch_bounds__(kThreads) void decode_select_long_kernel(
     const float *__restrict__ dt_cache, const int32_t *__restrict__ cache_lens, int Hkv, int Lmax,
-    int w, float *__restrict__ thr_tau, int32_t *__restrict__ thr_tie, int32_t *__restrict__ kept_idx) {
+    int w, int32_t *__restrict__ kept_ws, float *__restrict__ kdt_ws, int32_t *__restrict__ kept_idx) {
     __shared__ RadixShared<kThreads> rs;
     __shared__ int wsum[kThreads / 64];
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -284,11 +317,6 @@ __global__ __launch_bounds__(kThreads) void decode_select_long_kernel(
         t_tie = (int)selkey_idx(keys[0]);
         t_tau = row[t_tie];
     }
-    if (tid == 0) {
-        thr_tau[b * Hkv + g] = t_tau;
-        thr_tie[b * Hkv + g] = t_tie;
-    }
-    if (!kept_idx) return;
     const int per = (L + kThreads - 1) / kThreads;
     const int j0 = min(tid * per, L), j1 = min(j0 + per, L);
     int cnt = 0;
@@ -304,224 +332,195 @@ __global__ __launch_bounds__(kThreads) void decode_select_long_kernel(
     __syncthreads();
     int off = incl - cnt;
     for (int w2 = 0; w2 < wave; ++w2) off += wsum[w2];
-    int32_t *out = kept_idx + ((size_t)b * Hkv + g) * w;
-    for (int j = j0; j < j1; ++j)
-        if (kept_test(row[j], j, t_tau, t_tie)) {
-            if (off < w) out[off] = j;
+    int32_t *kl = kept_ws + ((size_t)b * Hkv + g) * w;
+    float *kd = kdt_ws + ((size_t)b * Hkv + g) * w;
+    int32_t *ki = kept_idx ? kept_idx + ((size_t)b * Hkv + g) * w : nullptr;
+    for (int j = j0; j < j1; ++j) {
+        const float dj = row[j];
+        if (kept_test(dj, j, t_tau, t_tie)) {
+            write_kept(kl, kd, ki, (uint32_t)off, j, dj, w);
             ++off;
         }
-    for (int q = min(L, w) + tid; q < w; q += kThreads) out[q] = -1;
+    }
+    if (ki)
+        for (int q = min(L, w) + tid; q < w; q += kThreads) ki[q] = -1;
 }
 
 // ---------------------------------------------------------------- attend --
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streamed-once rows: non-temporal 16-byte loads, so the gather neither
+// allocates in nor evicts from the caches.
+__device__ __forceinline__ uint4 load_nt16(const void *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <typename T, int D, int GM>
 __global__ __launch_bounds__(kThreads) void decode_attend_kernel(
     const T *__restrict__ q, const T *__restrict__ Kc, const T *__restrict__ Vc,
-    const float *__restrict__ dt_cache, const int32_t *__restrict__ cache_lens, int Lmax, int Hq,
-    int Hkv, const float *__restrict__ thr_tau, const int32_t *__restrict__ thr_tie,
-    float *__restrict__ pm, float *__restrict__ pl, float *__restrict__ po, float qscale) {
+    const int32_t *__restrict__ cache_lens, int Lmax, int Hq, int Hkv, int w,
+    const int32_t *__restrict__ kept_ws, const float *__restrict__ kdt_ws, float *__restrict__ pm,
+    float *__restrict__ pl, float *__restrict__ po, float qscale) {
     constexpr int NW = kThreads / 64;
-    constexpr int BK = 64;                      // kept keys per block
+    constexpr int BK = kKPC;                    // kept keys per workgroup (one block)
     constexpr int EV = 16 / (int)sizeof(T);     // elements per 16-byte vector
     constexpr int RV = D / EV;                  // vectors per K/V row
     constexpr int P = D + EV;                   // LDS row pitch (elements), 16-byte pad
-    constexpr int NL = BK * RV / kThreads;      // row vectors per thread per block
+    constexpr int NL = BK * RV / kThreads;      // row vectors per thread
     constexpr int QD = D / 4;                   // head_dim quarter per lane (scores)
     constexpr int PER = D / 64;                 // output columns per lane (weighted sum)
-    static_assert(BK * RV % kThreads == 0, "block staging split");
+    static_assert(BK * RV % kThreads == 0 && BK == 64, "one 64-key block per workgroup");
     __shared__ __align__(16) float qs[GM][D];
     __shared__ __align__(16) T Ks[BK * P];
     __shared__ __align__(16) T Vs[BK * P];
-    __shared__ int c_idx[kSplit];
-    __shared__ float c_dtl[kSplit];
+    __shared__ float c_dtl[BK];
     __shared__ float zs[GM][BK];
-    __shared__ float hm[GM], halpha[GM], hl[GM];
+    __shared__ float hm[GM], hl[GM];
     __shared__ float ored[GM][D];
-    __shared__ int wcnt[NW];
 
-    const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int G = Hq / Hkv;
-    const int nsplit = gridDim.x;
+    const int nchunk = gridDim.x;
     const int L = cache_lens[b];
-    const int s0 = split * kSplit;
-    const int s1 = min(s0 + kSplit, L);
-    const float t_tau = thr_tau[b * Hkv + g];
-    const int t_tie = thr_tie[b * Hkv + g];
-    const float *row = dt_cache + ((size_t)b * Hkv + g) * Lmax;
+    const int c0 = chunk * BK;
+    const int n = max(0, min(min(L, w) - c0, BK));  // kept positions of this chunk
+    const size_t lbase = ((size_t)b * Hkv + g) * w + c0;
 
-    for (int x = tid; x < G * D; x += kThreads) {
-        const int hh = x / D, e = x % D;
-        qs[hh][e] = Elem<T>::load(q, ((size_t)b * Hq + g * G + hh) * D + e);
-        ored[hh][e] = 0.f;
-    }
-    if (tid < GM) {
-        hm[tid] = -INFINITY;
-        hl[tid] = 0.f;
-    }
-    // kept positions of this slice, in index order
-    int n = 0;
-    for (int base = s0; base < s1; base += kThreads) {
-        const int j = base + tid;
-        bool take = false;
-        float dj = 0.f;
-        if (j < s1) {
-            dj = row[j];
-            take = kept_test(dj, j, t_tau, t_tie);
-        }
-        const uint64_t bal = __ballot(take);
-        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0) wcnt[wave] = __popcll(bal);
-        __syncthreads();
-        int off = n, tot = 0;
+    // Issue every global load before anything waits on one: the query and
+    // the chunk's dt first, then all kept indices (16 lanes share each
+    // entry), then all K/V row loads.  Stores to LDS come after the issue.
+    constexpr int QPT = (GM * D + kThreads - 1) / kThreads;  // query values per thread
+    float qv[QPT];
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) {
-            const int c = wcnt[w2];
-            off += (w2 < wave) ? c : 0;
-            tot += c;
-        }
-        if (take) {
-            c_idx[off + pre] = j;
-            c_dtl[off + pre] = dj * kLog2e;
-        }
-        n += tot;
-        __syncthreads();
+    for (int u = 0; u < QPT; ++u) {  // clamped, unconditional loads: nothing waits yet
+        const int x = min(tid + u * kThreads, G * D - 1);
+        qv[u] = Elem<T>::load(q, ((size_t)b * Hq + g * G) * D + x);
     }
-    __syncthreads();
-
+    const float dlv = kdt_ws[lbase + min(tid, BK - 1)];
     const size_t kvs = (size_t)Hkv * D;
     const T *Kb = Kc + (size_t)b * Lmax * kvs + (size_t)g * D;
     const T *Vb = Vc + (size_t)b * Lmax * kvs + (size_t)g * D;
-
-    // coalesced staging: 16-byte vector v of the block is (row v / RV, column v % RV)
     uint4 rk[NL], rv[NL];
-    auto load_block = [&](int blk) {
+    if (n > 0) {
+        int jr[NL];
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
-            const int v = tid + u * kThreads;
-            const int kk = v / RV, cv = v % RV;
-            const int pos = blk + kk;
-            if (pos < n) {
-                const size_t off = (size_t)c_idx[pos] * kvs + (size_t)cv * EV;
-                rk[u] = *reinterpret_cast<const uint4 *>(Kb + off);
-                rv[u] = *reinterpret_cast<const uint4 *>(Vb + off);
+            const int kk = (tid + u * kThreads) / RV;
+            jr[u] = kept_ws[lbase + min(kk, n - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const size_t off = (size_t)jr[u] * kvs + (size_t)((tid + u * kThreads) % RV) * EV;
+            rk[u] = load_nt16(Kb + off);
+            rv[u] = load_nt16(Vb + off);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+        const int x = tid + u * kThreads;
+        if (x < G * D) {
+            qs[x / D][x % D] = qv[u];
+            ored[x / D][x % D] = 0.f;
+        }
+    }
+    if (tid < BK) c_dtl[tid] = tid < n ? dlv : 0.f;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+        const int v = tid + u * kThreads;
+        const int kk = v / RV, cv = v % RV;
+        const bool ok = kk < n;
+        *reinterpret_cast<uint4 *>(&Ks[kk * P + cv * EV]) = ok ? rk[u] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(&Vs[kk * P + cv * EV]) = ok ? rv[u] : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+
+    // scores: wave takes 16 keys, 4 lanes per key split head_dim in quarters
+    {
+        const int kk = wave * 16 + (lane >> 2);
+        const int qq = lane & 3;
+        float sc[GM];
+#pragma unroll
+        for (int hh = 0; hh < GM; ++hh) sc[hh] = 0.f;
+#pragma unroll
+        for (int e0 = 0; e0 < QD; e0 += 8) {
+            const int e = qq * QD + e0;
+            float x[8];
+            if constexpr (sizeof(T) == 2) {
+                const uint4 kv = *reinterpret_cast<const uint4 *>(&Ks[kk * P + e]);
+                const uint32_t w4[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    x[2 * r] = __uint_as_float(w4[r] << 16);
+                    x[2 * r + 1] = __uint_as_float(w4[r] & 0xffff0000u);
+                }
             } else {
-                rk[u] = make_uint4(0, 0, 0, 0);
-                rv[u] = make_uint4(0, 0, 0, 0);
+                const float4 a4 = *reinterpret_cast<const float4 *>(&Ks[kk * P + e]);
+                const float4 b4 = *reinterpret_cast<const float4 *>(&Ks[kk * P + e + 4]);
+                x[0] = a4.x; x[1] = a4.y; x[2] = a4.z; x[3] = a4.w;
+                x[4] = b4.x; x[5] = b4.y; x[6] = b4.z; x[7] = b4.w;
+            }
+#pragma unroll
+            for (int hh = 0; hh < GM; ++hh) {
+                if (hh < G) {
+                    const float4 qa = *reinterpret_cast<const float4 *>(&qs[hh][e]);
+                    const float4 qb = *reinterpret_cast<const float4 *>(&qs[hh][e + 4]);
+                    float a = sc[hh];
+                    a = fmaf(qa.x, x[0], a); a = fmaf(qa.y, x[1], a);
+                    a = fmaf(qa.z, x[2], a); a = fmaf(qa.w, x[3], a);
+                    a = fmaf(qb.x, x[4], a); a = fmaf(qb.y, x[5], a);
+                    a = fmaf(qb.z, x[6], a); a = fmaf(qb.w, x[7], a);
+                    sc[hh] = a;
+                }
             }
         }
-    };
+        const bool kval = kk < n;
+        const float dl = c_dtl[kk];
+#pragma unroll
+        for (int hh = 0; hh < GM; ++hh) {
+            if (hh < G) {
+                float a = sc[hh];
+                a += __shfl_xor(a, 1, 64);
+                a += __shfl_xor(a, 2, 64);
+                if (qq == 0) zs[hh][kk] = kval ? fmaf(a, qscale, dl) : -INFINITY;
+            }
+        }
+    }
+    __syncthreads();
+    // per head: max, probabilities, sum (wave hh % NW owns head hh)
+    for (int hh = wave; hh < G; hh += NW) {
+        const float z = zs[hh][lane];
+        const float mx = wave_max(z);
+        const float p = (mx == -INFINITY) ? 0.f : exp2f(z - mx);
+        zs[hh][lane] = p;
+        const float ps = wave_sum(p);
+        if (lane == 0) {
+            hm[hh] = mx;
+            hl[hh] = ps;
+        }
+    }
+    __syncthreads();
+    // weighted V rows: wave takes every NW-th key, lanes cover head_dim
     float acc[GM][PER];
 #pragma unroll
     for (int hh = 0; hh < GM; ++hh)
 #pragma unroll
         for (int u = 0; u < PER; ++u) acc[hh][u] = 0.f;
-
-    if (n > 0) load_block(0);
-    for (int blk = 0; blk < n; blk += BK) {
+    for (int kk = wave; kk < n; kk += NW) {
+        float v[PER];
 #pragma unroll
-        for (int u = 0; u < NL; ++u) {
-            const int v = tid + u * kThreads;
-            const int kk = v / RV, cv = v % RV;
-            *reinterpret_cast<uint4 *>(&Ks[kk * P + cv * EV]) = rk[u];
-            *reinterpret_cast<uint4 *>(&Vs[kk * P + cv * EV]) = rv[u];
-        }
-        __syncthreads();
-        if (blk + BK < n) load_block(blk + BK);
-
-        // scores: wave takes 16 keys, 4 lanes per key split head_dim in quarters
-        {
-            const int kk = wave * 16 + (lane >> 2);
-            const int qq = lane & 3;
-            float sc[GM];
+        for (int u = 0; u < PER; ++u) v[u] = Elem<T>::load(Vs, (size_t)kk * P + lane * PER + u);
 #pragma unroll
-            for (int hh = 0; hh < GM; ++hh) sc[hh] = 0.f;
-#pragma unroll
-            for (int e0 = 0; e0 < QD; e0 += 8) {
-                const int e = qq * QD + e0;
-                float x[8];
-                if constexpr (sizeof(T) == 2) {
-                    const uint4 kv = *reinterpret_cast<const uint4 *>(&Ks[kk * P + e]);
-                    const uint32_t w4[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        x[2 * r] = __uint_as_float(w4[r] << 16);
-                        x[2 * r + 1] = __uint_as_float(w4[r] & 0xffff0000u);
-                    }
-                } else {
-                    const float4 a4 = *reinterpret_cast<const float4 *>(&Ks[kk * P + e]);
-                    const float4 b4 = *reinterpret_cast<const float4 *>(&Ks[kk * P + e + 4]);
-                    x[0] = a4.x; x[1] = a4.y; x[2] = a4.z; x[3] = a4.w;
-                    x[4] = b4.x; x[5] = b4.y; x[6] = b4.z; x[7] = b4.w;
-                }
-#pragma unroll
-                for (int hh = 0; hh < GM; ++hh) {
-                    if (hh < G) {
-                        const float4 qa = *reinterpret_cast<const float4 *>(&qs[hh][e]);
-                        const float4 qb = *reinterpret_cast<const float4 *>(&qs[hh][e + 4]);
-                        float a = sc[hh];
-                        a = fmaf(qa.x, x[0], a); a = fmaf(qa.y, x[1], a);
-                        a = fmaf(qa.z, x[2], a); a = fmaf(qa.w, x[3], a);
-                        a = fmaf(qb.x, x[4], a); a = fmaf(qb.y, x[5], a);
-                        a = fmaf(qb.z, x[6], a); a = fmaf(qb.w, x[7], a);
-                        sc[hh] = a;
-                    }
-                }
-            }
-            const bool kval = blk + kk < n;
-            const float dl = kval ? c_dtl[blk + kk] : 0.f;
-#pragma unroll
-            for (int hh = 0; hh < GM; ++hh) {
-                if (hh < G) {
-                    float a = sc[hh];
-                    a += __shfl_xor(a, 1, 64);
-                    a += __shfl_xor(a, 2, 64);
-                    if (qq == 0) zs[hh][kk] = kval ? fmaf(a, qscale, dl) : -INFINITY;
-                }
-            }
-        }
-        __syncthreads();
-        // per head: block max, running max and rescale, probabilities
-        for (int hh = wave; hh < G; hh += NW) {
-            const float z = zs[hh][lane];
-            const float mo = hm[hh];
-            const float mn = fmaxf(mo, wave_max(z));
-            const float p = (mn == -INFINITY) ? 0.f : exp2f(z - mn);
-            zs[hh][lane] = p;
-            const float ps = wave_sum(p);
-            if (lane == 0) {
-                const float al = (mn == -INFINITY) ? 1.f : exp2f(mo - mn);
-                halpha[hh] = al;
-                hm[hh] = mn;
-                hl[hh] = hl[hh] * al + ps;
-            }
-        }
-        __syncthreads();
-        // weighted V rows: wave takes every NW-th key, lanes cover head_dim
-#pragma unroll
-        for (int hh = 0; hh < GM; ++hh)
+        for (int hh = 0; hh < GM; ++hh) {
             if (hh < G) {
-                const float al = halpha[hh];
+                const float p = zs[hh][kk];
 #pragma unroll
-                for (int u = 0; u < PER; ++u) acc[hh][u] *= al;
-            }
-        for (int kk = wave; kk < BK; kk += NW) {
-            float v[PER];
-#pragma unroll
-            for (int u = 0; u < PER; ++u) v[u] = Elem<T>::load(Vs, (size_t)kk * P + lane * PER + u);
-#pragma unroll
-            for (int hh = 0; hh < GM; ++hh) {
-                if (hh < G) {
-                    const float p = zs[hh][kk];
-#pragma unroll
-                    for (int u = 0; u < PER; ++u) acc[hh][u] = fmaf(p, v[u], acc[hh][u]);
-                }
+                for (int u = 0; u < PER; ++u) acc[hh][u] = fmaf(p, v[u], acc[hh][u]);
             }
         }
-        __syncthreads();
     }
-    // reduce over the waves and write this split's partials
 #pragma unroll
     for (int hh = 0; hh < GM; ++hh) {
         if (hh < G) {
@@ -532,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void decode_attend_kernel(
     __syncthreads();
     for (int x = tid; x < G * D; x += kThreads) {
         const int hh = x / D, e = x % D;
-        const size_t pidx = ((size_t)b * Hq + g * G + hh) * nsplit + split;
+        const size_t pidx = ((size_t)b * Hq + g * G + hh) * nchunk + chunk;
         po[pidx * D + e] = ored[hh][e];
         if (e == 0) {
             pm[pidx] = hm[hh];
@@ -541,40 +540,198 @@ __global__ __launch_bounds__(kThreads) void decode_attend_kernel(
     }
 }
 
-// Merge the split partials of one (batch, kv head): one thread per (head, column).
-template <typename T>
-__global__ __launch_bounds__(kThreads) void decode_combine_kernel(const float *__restrict__ pm,
-                                                                  const float *__restrict__ pl,
-                                                                  const float *__restrict__ po, int Hq,
-                                                                  int Hkv, int nsplit, int d,
-                                                                  T *__restrict__ out) {
-    const int g = blockIdx.x, b = blockIdx.y;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i receives
+// element (i % 4) of the 4 x 16-bit values at the address of lane (i/4 + 4s),
+// s = 0..3; lane k pointing at row r0 + k/4, columns c0 + 4*(k%4) of a
+// row-major tile gives lane i the column c0 + i of rows r0 .. r0+3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
+}
+
+// bf16 decode on matrix cores, one workgroup per (batch, kv head, 64 kept
+// positions).  16x16x32 MFMA layouts (wave64, l = lane):
+//   A[m = l%16][k = 8*(l/16) + 0..7], B[k = 8*(l/16) + 0..7][n = l%16],
+//   C[m = 4*(l/16) + i][n = l%16], i = 0..3.
+// Scores: S^T (16 keys x 16 heads) = K (keys x d) Q^T, wave w taking keys
+// 16w..16w+15; the G <= 16 query heads of the kv head fill the N dimension
+// (unused columns are zero).  Weighted sum: O (16 heads x 16 d) = P V with P
+// from LDS and V's column operand from LDS transpose reads of the row-major
+// V tile; wave w takes head_dim tiles w, w+4, ...
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_attend_mfma_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ Kc, const uint16_t *__restrict__ Vc,
+    const int32_t *__restrict__ cache_lens, int Lmax, int Hq, int Hkv, int w,
+    const int32_t *__restrict__ kept_ws, const float *__restrict__ kdt_ws, float *__restrict__ pm,
+    float *__restrict__ pl, float *__restrict__ po, float qscale) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    constexpr int NW = kThreads / 64;
+    constexpr int BK = kKPC;                 // 64 kept keys per workgroup
+    constexpr int RV = D / 8;                // 16-byte vectors per row
+    constexpr int KP = D + 8;                // K tile pitch (bf16)
+    constexpr int VP = D + 32;               // V tile pitch (bf16), transpose-read friendly
+    constexpr int PP = BK + 8;               // P tile pitch (bf16)
+    constexpr int NL = BK * RV / kThreads;   // row vectors per thread
+    static_assert(BK == 64 && BK * RV % kThreads == 0, "one 64-key block per workgroup");
+    __shared__ __align__(16) uint16_t Ks[BK * KP];
+    __shared__ __align__(16) uint16_t Vs[BK * VP];
+    __shared__ __align__(16) uint16_t Ps[16 * PP];
+    __shared__ float c_dtl[BK];
+    __shared__ float wmax[NW][16], wsum[NW][16];
+
+    const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int G = Hq / Hkv;
-    for (int x = threadIdx.x; x < G * d; x += kThreads) {
-        const int hh = x / d, e = x % d;
-        const size_t pbase = ((size_t)b * Hq + g * G + hh) * nsplit;
-        float M = -INFINITY;
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pm[pbase + s]);
-        float num = 0.f, den = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const float ms = pm[pbase + s];
-            if (ms == -INFINITY) continue;
-            const float f = exp2f(ms - M);
-            den = fmaf(pl[pbase + s], f, den);
-            num = fmaf(po[(pbase + s) * d + e], f, num);
+    const int nchunk = gridDim.x;
+    const int L = cache_lens[b];
+    const int c0 = chunk * BK;
+    const int n = max(0, min(min(L, w) - c0, BK));
+    const size_t lbase = ((size_t)b * Hkv + g) * w + c0;
+    const int col = lane & 15, grp = lane >> 4;
+
+    // global loads first: query fragments, dt, kept indices, then K/V rows
+    bf16x8 qf[D / 32];
+    {
+        const int hq = g * G + min(col, G - 1);
+        const uint16_t *qp = q + ((size_t)b * Hq + hq) * D + 8 * grp;
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+            qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
+            if (col >= G) qf[s] = bf16x8{};
         }
-        Elem<T>::store(out, ((size_t)b * Hq + g * G + hh) * d + e, den > 0.f ? num / den : 0.f);
+    }
+    const float dlv = kdt_ws[lbase + min(tid, BK - 1)];
+    const size_t kvs = (size_t)Hkv * D;
+    const uint16_t *Kb = Kc + (size_t)b * Lmax * kvs + (size_t)g * D;
+    const uint16_t *Vb = Vc + (size_t)b * Lmax * kvs + (size_t)g * D;
+    uint4 rk[NL], rv[NL];
+    if (n > 0) {
+        int jr[NL];
+#pragma unroll
+        for (int u = 0; u < NL; ++u) jr[u] = kept_ws[lbase + min((tid + u * kThreads) / RV, n - 1)];
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const size_t off = (size_t)jr[u] * kvs + (size_t)((tid + u * kThreads) % RV) * 8;
+            rk[u] = load_nt16(Kb + off);
+            rv[u] = load_nt16(Vb + off);
+        }
+    }
+    if (tid < BK) c_dtl[tid] = tid < n ? dlv : 0.f;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+        const int v = tid + u * kThreads;
+        const int kk = v / RV, cv = v % RV;
+        const bool ok = kk < n;
+        *reinterpret_cast<uint4 *>(&Ks[kk * KP + cv * 8]) = ok ? rk[u] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(&Vs[kk * VP + cv * 8]) = ok ? rv[u] : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+
+    // scores for keys 16*wave .. +15 (4 per lane), head = col
+    f32x4 sacc = f32x4{};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&Ks[(16 * wave + col) * KP + 32 * s + 8 * grp]);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], sacc, 0, 0, 0);
+    }
+    float z[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int kk = 16 * wave + 4 * grp + i;
+        z[i] = (kk < n && col < G) ? fmaf(sacc[i], qscale, c_dtl[kk]) : -INFINITY;
+        mx = fmaxf(mx, z[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (grp == 0) wmax[wave][col] = mx;
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, wmax[w2][col]);
+    const float msub = (M == -INFINITY) ? 0.f : M;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(z[i] - msub);
+        ps += p;
+        Ps[col * PP + 16 * wave + 4 * grp + i] = __builtin_bit_cast(uint16_t, (__bf16)p);
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    if (grp == 0) wsum[wave][col] = ps;
+    __syncthreads();
+
+    // O (16 heads x 16 columns per tile) = P V over the 64 keys
+    const int tr_k = lane & 15;
+    for (int t = wave; t < D / 16; t += NW) {
+        f32x4 oacc = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            const bf16x8 pa = *reinterpret_cast<const bf16x8 *>(&Ps[col * PP + 32 * ks + 8 * grp]);
+            const uint16_t *vp = &Vs[(32 * ks + 8 * grp + (tr_k >> 2)) * VP + 16 * t + 4 * (tr_k & 3)];
+            const i16x4 lo = lds_read_tr16(vp);
+            const i16x4 hi = lds_read_tr16(vp + 4 * VP);
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, oacc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hh = 4 * grp + i;
+            if (hh < G) {
+                const size_t pidx = ((size_t)b * Hq + g * G + hh) * nchunk + chunk;
+                po[pidx * D + 16 * t + col] = oacc[i];
+            }
+        }
+    }
+    if (tid < G) {
+        const size_t pidx = ((size_t)b * Hq + g * G + tid) * nchunk + chunk;
+        float l = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) l += wsum[w2][tid];
+        pm[pidx] = M == -INFINITY ? -INFINITY : M;
+        pl[pidx] = l;
+    }
+}
+
+// Merge the chunk partials of one (batch, query head): one thread per column.
+template <typename T>
+__global__ __launch_bounds__(128) void decode_combine_kernel(const float *__restrict__ pm,
+                                                            const float *__restrict__ pl,
+                                                            const float *__restrict__ po, int nchunk,
+                                                            int d, T *__restrict__ out) {
+    __shared__ float sf[1024];  // per-chunk weights (nchunk <= 1024)
+    __shared__ float sden;
+    const int bh = blockIdx.x;  // b * Hq + hq
+    const float *m = pm + (size_t)bh * nchunk;
+    const float *l = pl + (size_t)bh * nchunk;
+    float M = -INFINITY;
+    for (int s = 0; s < nchunk; ++s) M = fmaxf(M, m[s]);
+    for (int s = threadIdx.x; s < nchunk; s += blockDim.x) sf[s] = m[s] == -INFINITY ? 0.f : exp2f(m[s] - M);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float den = 0.f;
+        for (int s = 0; s < nchunk; ++s) den = fmaf(l[s], sf[s], den);
+        sden = den;
+    }
+    __syncthreads();
+    const float inv = sden > 0.f ? 1.f / sden : 0.f;
+    for (int e = threadIdx.x; e < d; e += blockDim.x) {
+        float num = 0.f;
+        for (int s = 0; s < nchunk; ++s) num = fmaf(po[((size_t)bh * nchunk + s) * d + e], sf[s], num);
+        Elem<T>::store(out, (size_t)bh * d + e, num * inv);
     }
 }
 
 template <typename T, int D>
 hipError_t launch_attend(int gm, dim3 grid, hipStream_t stream, const T *q, const T *Kc, const T *Vc,
-                         const float *dt_cache, const int32_t *cache_lens, int Lmax, int Hq, int Hkv,
-                         const float *thr_tau, const int32_t *thr_tie, float *pm, float *pl, float *po,
+                         const int32_t *cache_lens, int Lmax, int Hq, int Hkv, int w,
+                         const int32_t *kept_ws, const float *kdt_ws, float *pm, float *pl, float *po,
                          float qscale) {
 #define DMA_ATTEND(GMV)                                                                                  \
     hipLaunchKernelGGL((decode_attend_kernel<T, D, GMV>), grid, dim3(kThreads), 0, stream, q, Kc, Vc,    \
-                       dt_cache, cache_lens, Lmax, Hq, Hkv, thr_tau, thr_tie, pm, pl, po, qscale)
+                       cache_lens, Lmax, Hq, Hkv, w, kept_ws, kdt_ws, pm, pl, po, qscale)
     if (gm <= 4) DMA_ATTEND(4);
     else if (gm <= 8) DMA_ATTEND(8);
     else DMA_ATTEND(16);
@@ -586,44 +743,53 @@ template <typename T>
 hipError_t launch_decode_t(const T *q, const T *Kc, const T *Vc, const float *dt_cache,
                            const int32_t *cache_lens, int B, int Lmax, int Hq, int Hkv, int d, int w,
                            T *out, int32_t *kept_idx, void *ws, hipStream_t stream) {
-    const WsLayout lay = ws_layout(B, Lmax, Hq, Hkv, d);
+    const WsLayout lay = ws_layout(B, Lmax, Hq, Hkv, d, w);
     char *base = (char *)ws;
-    float *thr_tau = (float *)(base + lay.thr_tau);
-    int32_t *thr_tie = (int32_t *)(base + lay.thr_tie);
+    int32_t *kept_ws = (int32_t *)(base + lay.kept);
+    float *kdt_ws = (float *)(base + lay.kdt);
     float *pm = (float *)(base + lay.pm);
     float *pl = (float *)(base + lay.pl);
     float *po = (float *)(base + lay.po);
-    const int ns = nsplit_of(Lmax);
+    const int nc = nchunk_of(Lmax, w);
     const float qscale = (float)(1.0 / __builtin_sqrt((double)d) * 1.4426950408889634);
     const dim3 sgrid(Hkv, B);
     if (Lmax <= 16 * kSelThreads)
         hipLaunchKernelGGL(decode_select_kernel<16>, sgrid, dim3(kSelThreads), 0, stream, dt_cache,
-                           cache_lens, Hkv, Lmax, w, thr_tau, thr_tie, kept_idx);
+                           cache_lens, Hkv, Lmax, w, kept_ws, kdt_ws, kept_idx);
     else if (Lmax <= 32 * kSelThreads)
         hipLaunchKernelGGL(decode_select_kernel<32>, sgrid, dim3(kSelThreads), 0, stream, dt_cache,
-                           cache_lens, Hkv, Lmax, w, thr_tau, thr_tie, kept_idx);
+                           cache_lens, Hkv, Lmax, w, kept_ws, kdt_ws, kept_idx);
     else
         hipLaunchKernelGGL(decode_select_long_kernel, sgrid, dim3(kThreads), 0, stream, dt_cache,
-                           cache_lens, Hkv, Lmax, w, thr_tau, thr_tie, kept_idx);
+                           cache_lens, Hkv, Lmax, w, kept_ws, kdt_ws, kept_idx);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 agrid(ns, Hkv, B);
+    const dim3 agrid(nc, Hkv, B);
     const int G = Hq / Hkv;
-    e = d == 128 ? launch_attend<T, 128>(G, agrid, stream, q, Kc, Vc, dt_cache, cache_lens, Lmax, Hq, Hkv,
-                                         thr_tau, thr_tie, pm, pl, po, qscale)
-                 : launch_attend<T, 64>(G, agrid, stream, q, Kc, Vc, dt_cache, cache_lens, Lmax, Hq, Hkv,
-                                        thr_tau, thr_tie, pm, pl, po, qscale);
+    if constexpr (sizeof(T) == 2) {
+        if (d == 128)
+            hipLaunchKernelGGL(decode_attend_mfma_kernel<128>, agrid, dim3(kThreads), 0, stream, q, Kc, Vc,
+                               cache_lens, Lmax, Hq, Hkv, w, kept_ws, kdt_ws, pm, pl, po, qscale);
+        else
+            hipLaunchKernelGGL(decode_attend_mfma_kernel<64>, agrid, dim3(kThreads), 0, stream, q, Kc, Vc,
+                               cache_lens, Lmax, Hq, Hkv, w, kept_ws, kdt_ws, pm, pl, po, qscale);
+        e = hipGetLastError();
+    } else {
+        e = d == 128 ? launch_attend<T, 128>(G, agrid, stream, q, Kc, Vc, cache_lens, Lmax, Hq, Hkv, w,
+                                             kept_ws, kdt_ws, pm, pl, po, qscale)
+                     : launch_attend<T, 64>(G, agrid, stream, q, Kc, Vc, cache_lens, Lmax, Hq, Hkv, w,
+                                            kept_ws, kdt_ws, pm, pl, po, qscale);
+    }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(Hkv, B), dim3(kThreads), 0, stream, pm, pl, po, Hq,
-                       Hkv, ns, d, out);
+    hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(B * Hq), dim3(d), 0, stream, pm, pl, po, nc, d,
+                       out);
     return hipGetLastError();
 }
 
 }  // namespace
 
 size_t decode_ws_bytes(int B, int Lmax, int Hq, int Hkv, int d, int w) {
-    (void)w;
-    return ws_layout(B, Lmax, Hq, Hkv, d).total;
+    return ws_layout(B, Lmax, Hq, Hkv, d, w).total;
 }
 
 hipError_t launch_decode(const void *q, const void *Kc, const void *Vc, int dtype,

@@ -30,6 +30,7 @@ hipError_t launch_decode(const void *q, const void *Kc, const void *Vc, int dtyp
 constexpr int kMaxHkvDt = 16;          // dt kernel: heads accumulated in registers
 constexpr int kMaxGroupAttn = 128;     // prefill: query heads per kv head
 constexpr int kMaxGroupDecode = 16;    // decode: query heads per kv head
+constexpr int kMaxKeptDecode = 131072; // decode: kept positions per (batch, kv head)
 constexpr size_t kDtLdsBytes = 65536;  // dt kernel: W staged in LDS
 
 }  // namespace dma

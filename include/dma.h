@@ -148,7 +148,7 @@ size_t dma_decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d, int w
  *   kept_idx   [B][Hkv][w] int32 (out) or NULL: kept positions ascending,
  *              padded with -1 when L_b < w
  *   ws, ws_bytes  device workspace of at least dma_decode_workspace_bytes()
- * Supports d in {64, 128}, Hq/Hkv <= 16.
+ * Supports d in {64, 128}, Hq/Hkv <= 16, min(Lmax, w) <= 131072.
  */
 int dma_decode(const void *q, const void *Kc, const void *Vc, int dtype,
                const float *dt_cache, const int32_t *cache_lens, int B, int Lmax, int Hq,

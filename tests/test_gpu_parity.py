@@ -262,6 +262,18 @@ def test_decode_edge_lengths(dma, oracle_mod, dtype, kind, d, Hq, Hkv):
     _decode_check(dma, oracle_mod, q, Kc, Vc, dtc, lens, w, TOL[dtype])
 
 
+@pytest.mark.parametrize("Lmax,lens,w", [(20000, [20000, 9000, 16385], 2048),   # 32 positions per thread
+                                         (40000, [40000, 2049, 33000], 1500)])  # multi-pass radix path
+def test_decode_long_caches(dma, oracle_mod, Lmax, lens, w):
+    B, Hq, Hkv, d = len(lens), 4, 2, 128
+    rng = np.random.default_rng(Lmax)
+    q = si.to_bf16_bits(rng.standard_normal((B, Hq, d)).astype(np.float32))
+    Kc = si.to_bf16_bits(rng.standard_normal((B, Lmax, Hkv, d)).astype(np.float32))
+    Vc = si.to_bf16_bits(rng.standard_normal((B, Lmax, Hkv, d)).astype(np.float32))
+    dtc = si.make_dt((B, Hkv, Lmax), "dyadic", seed=Lmax + 1)
+    _decode_check(dma, oracle_mod, q, Kc, Vc, dtc, np.array(lens, np.int32), w, 2e-2)
+
+
 def test_decode_matches_last_prefill_row(dma, oracle_mod):
     B, S, Hq, Hkv, d, w = 3, 900, 8, 2, 128, 256
     Q, K, V = si.make_qkv(B, S, Hq, Hkv, d, "bf16", seed=51)
