@@ -17,6 +17,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kLanesPerToken = 8;
 constexpr int kTokensPerBlock = kThreads / kLanesPerToken;
+constexpr int kBatch = 8;  // 16-byte vectors per lane loaded together
 
 template <typename T>
 __device__ __forceinline__ void unpack16(const uint4 &v, float *x);
@@ -48,32 +49,54 @@ __global__ __launch_bounds__(kThreads) void dt_kernel(const T *__restrict__ V, c
                                                       int d, int64_t ntok, float *__restrict__ out,
                                                       int64_t ld, const int32_t *__restrict__ out_pos) {
     extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ float As[kMaxHkvDt], bs[kMaxHkvDt];
     constexpr int EV = 16 / (int)sizeof(T);  // elements per 16-byte vector
     const int width = Hkv * d;
     const int nvec = width / EV;             // vectors per token row
     uint4 *Ws = reinterpret_cast<uint4 *>(smem);
+    // W, A and bias are staged together so that their load latencies overlap
     for (int v = threadIdx.x; v < Hkv * nvec; v += kThreads) Ws[v] = reinterpret_cast<const uint4 *>(W)[v];
+    if (threadIdx.x < (unsigned)Hkv) {
+        As[threadIdx.x] = A[threadIdx.x];
+        bs[threadIdx.x] = bias ? Elem<T>::load(bias, threadIdx.x) : 0.f;
+    }
     __syncthreads();
 
     const int q = threadIdx.x % kLanesPerToken;
     for (int64_t t = (int64_t)blockIdx.x * kTokensPerBlock + threadIdx.x / kLanesPerToken; t < ntok;
          t += (int64_t)gridDim.x * kTokensPerBlock) {
         const uint4 *vrow = reinterpret_cast<const uint4 *>(V + t * width);
+        const int b = (int)(t / S);
+        const int s = (int)(t - (int64_t)b * S);
+        const int64_t col = (out_pos ? (int64_t)out_pos[b] : 0) + s;  // loaded with the rows
         float acc[kMaxHkvDt];
 #pragma unroll
         for (int h = 0; h < kMaxHkvDt; ++h) acc[h] = 0.f;
-        for (int v = q; v < nvec; v += kLanesPerToken) {
-            float x[EV];
-            unpack16<T>(vrow[v], x);
+        // this lane's vectors of the token, kBatch at a time, all loaded
+        // before any is used so that their latencies overlap
+        for (int v0 = q; v0 < nvec; v0 += kBatch * kLanesPerToken) {
+            uint4 vb[kBatch];
 #pragma unroll
-            for (int h = 0; h < kMaxHkvDt; ++h) {
-                if (h < Hkv) {
-                    float wv[EV];
-                    unpack16<T>(Ws[h * nvec + v], wv);
-                    float a = acc[h];
+            for (int k = 0; k < kBatch; ++k) {
+                const int v = v0 + k * kLanesPerToken;
+                if (v < nvec) vb[k] = vrow[v];
+            }
 #pragma unroll
-                    for (int e = 0; e < EV; ++e) a = fmaf(wv[e], x[e], a);
-                    acc[h] = a;
+            for (int k = 0; k < kBatch; ++k) {
+                const int v = v0 + k * kLanesPerToken;
+                if (v >= nvec) break;
+                float x[EV];
+                unpack16<T>(vb[k], x);
+#pragma unroll
+                for (int h = 0; h < kMaxHkvDt; ++h) {
+                    if (h < Hkv) {
+                        float wv[EV];
+                        unpack16<T>(Ws[h * nvec + v], wv);
+                        float a = acc[h];
+#pragma unroll
+                        for (int e = 0; e < EV; ++e) a = fmaf(wv[e], x[e], a);
+                        acc[h] = a;
+                    }
                 }
             }
         }
@@ -84,14 +107,11 @@ __global__ __launch_bounds__(kThreads) void dt_kernel(const T *__restrict__ V, c
                 for (int o = 1; o < kLanesPerToken; o <<= 1) acc[h] += __shfl_xor(acc[h], o, kLanesPerToken);
             }
         }
-        const int b = (int)(t / S);
-        const int s = (int)(t - (int64_t)b * S);
-        const int64_t col = (out_pos ? (int64_t)out_pos[b] : 0) + s;
 #pragma unroll
         for (int h = 0; h < kMaxHkvDt; ++h) {
             if (h < Hkv && (h % kLanesPerToken) == q) {
-                const float x = acc[h] + (bias ? Elem<T>::load(bias, h) : 0.f);
-                out[((int64_t)b * Hkv + h) * ld + col] = expf(A[h] * softplus_f32(x));
+                const float x = acc[h] + bs[h];
+                out[((int64_t)b * Hkv + h) * ld + col] = expf(As[h] * softplus_f32(x));
             }
         }
     }

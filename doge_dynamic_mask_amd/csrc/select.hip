@@ -9,15 +9,22 @@
 //   (2) for a chunk of C rows starting at r0, every row's kept set is the top
 //       w of (prefix [0, r0)) plus at most C new keys.  A prefix key of
 //       prefix rank k has between k and k + C better keys in a row's set, so
-//       the best w-C-1 prefix keys are kept by every row of the chunk and are
-//       never its w-th key, prefix keys of rank >= w are kept by none, and
-//       each row's threshold key lies in the "band" of prefix ranks
-//       [w-C-1, w) plus the chunk's own keys: at most 2C+1 keys.
-// One workgroup per (batch, kv head, chunk of 64 rows) finds the two band
-// limits with a two-target radix select over the prefix, gathers the band and
-// the chunk's keys into LDS, sorts them, and lets each row walk the sorted
-// list to its threshold.  Output per row: (tau, tie) = (dt, index) of the
-// w-th kept key, or the canonical (-inf, -1) / (+inf, -1).
+//       the best A0 = w-C-1 prefix keys are kept by every row of the chunk and
+//       are never its w-th key, prefix keys of rank >= w are kept by none, and
+//       each row's threshold key lies in the "band" of prefix ranks [A0, w)
+//       plus the chunk's own keys: at most 2C+1 candidates.
+// One workgroup per (batch, kv head, chunk of C rows), C = 64 for rows up to
+// 4096 and 128 beyond:
+//   a. finds the band: min/max of the prefix keys, one histogram pass with
+//      4096 bins spanning that range, the bins holding ranks A0 and w-1, and
+//      an exact rank of the keys gathered from those bins (a multi-pass radix
+//      select over the prefix when those bins hold too many keys, e.g. under
+//      heavy ties);
+//   b. lets each candidate find the rows it is the threshold of: at row i
+//      the threshold is the candidate with exactly w-A0-1 better candidates
+//      that row already sees (band keys always; new key j from row j on).
+// Output per row: (tau, tie) = (dt, index) of the w-th kept key, or the
+// canonical (-inf, -1) / (+inf, -1).  Only comparisons touch dt.
 #include "common.hpp"
 #include "launch.hpp"
 #include "radix_select.hpp"
@@ -26,28 +33,66 @@ namespace dma {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 64;
-constexpr int kBand = kChunk + 1;  // band width: prefix ranks [w - kChunk - 1, w)
-constexpr int kSortN = 256;        // power of two >= kBand + kChunk
+constexpr int kBins = 4096;
+constexpr int kCollectCap = 512;    // boundary-bin keys ranked exactly in LDS
+constexpr int kUnroll = 16;         // prefix keys per thread per pass step (loads in flight)
+constexpr int kStage = 8192;        // prefixes up to this many keys are kept in LDS
 
+template <int C>
+struct SelectShared {
+    RadixShared<kThreads> rs;       // fallback radix select
+    uint32_t hist[kBins];
+    uint64_t col[kCollectCap];
+    uint64_t cand[2 * C + 1];       // band (by rank) then the chunk's own keys
+    uint32_t red[2][kThreads / 64];
+    uint32_t ncol, nfound;
+    uint32_t binA, binB, aboveA;
+    uint32_t keys[kStage];          // prefix order keys, when P <= kStage
+};
+
+// f(j, dt[j]) for every prefix position j < P, kUnroll positions per thread
+// per step with all of their loads issued before any is used.
+template <typename F>
+__device__ __forceinline__ void for_prefix(const float *__restrict__ row, int P, F f) {
+    for (int j0 = 0; j0 < P; j0 += kUnroll * kThreads) {
+        float v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int j = j0 + u * kThreads + (int)threadIdx.x;
+            v[u] = j < P ? row[j] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int j = j0 + u * kThreads + (int)threadIdx.x;
+            if (j < P) f(j, v[u]);
+        }
+    }
+}
+
+// f(j, key_j) over the prefix from the LDS copy of its order keys.
+template <typename F>
+__device__ __forceinline__ void for_staged(const uint32_t *keys, int P, F f) {
+    for (int j = threadIdx.x; j < P; j += kThreads) f(j, keys[j]);
+}
+
+// C: rows per chunk (the band holds C+1 prefix keys)
+template <int C>
 __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restrict__ dt,
                                                           const int32_t *__restrict__ seqlens,
                                                           int Hkv, int S, int w,
                                                           float *__restrict__ tau,
                                                           int32_t *__restrict__ tie) {
-    __shared__ RadixShared<kThreads> rs;
-    __shared__ uint64_t cand[kSortN];
-    __shared__ int ncand;
-
-    const int tid = threadIdx.x;
+    constexpr int kChunk = C;
+    __shared__ SelectShared<C> sh;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = blockIdx.y, b = blockIdx.z;
     const int r0 = blockIdx.x * kChunk;
     const int L = seqlens ? seqlens[b] : S;
     const size_t base = ((size_t)b * Hkv + g) * S;
     const float *row = dt + base;
     const int rend = min(r0 + kChunk, S);
-    const int lo = max(r0, w);       // first row holding more than w valid keys
-    const int hi = min(rend, L);     // end of the valid rows of this chunk
+    const int lo = max(r0, w);    // first row holding more than w valid keys
+    const int hi = min(rend, L);  // end of the valid rows of this chunk
 
     for (int t = tid; t < rend - r0; t += kThreads) {
         const int i = r0 + t;
@@ -63,65 +108,160 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
 
     const int P = r0;  // prefix [0, r0): all valid, as r0 < hi <= L
     const int A0 = max(0, min(P, w - kChunk - 1));
-    const int nb = min(P, w) - A0;
-    if (tid == 0) ncand = 0;
-    __syncthreads();
+    const int nb = min(P, w) - A0;  // band size, 0 when the prefix is empty
     if (nb > 0) {
-        const uint32_t ranks[2] = {(uint32_t)A0, (uint32_t)(A0 + nb - 1)};
-        uint64_t keys[2];
-        const int nt = nb > 1 ? 2 : 1;
-        radix_select<kThreads>(row, P, nt, ranks, keys, rs);
-        const uint64_t khi = keys[0];
-        const uint64_t klo = nt > 1 ? keys[1] : keys[0];
-        for (int j = tid; j < P; j += kThreads) {
-            const uint64_t k = selkey(row[j], (uint32_t)j);
-            if (k <= khi && k >= klo) {
-                const int at = atomicAdd(&ncand, 1);
-                if (at < kBand) cand[at] = k;  // exactly nb <= kBand keys match
-            }
+        const uint32_t rankA = (uint32_t)A0, rankB = (uint32_t)(A0 + nb - 1);
+        // ---- a1: key range of the prefix
+        const bool staged = P <= kStage;
+        uint32_t kmin = 0xffffffffu, kmax = 0u;
+        for_prefix(row, P, [&](int j, float x) {
+            const uint32_t k = ordkey(x);
+            kmin = min(kmin, k);
+            kmax = max(kmax, k);
+            if (staged) sh.keys[j] = k;
+        });
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            kmin = min(kmin, (uint32_t)__shfl_xor(kmin, o, 64));
+            kmax = max(kmax, (uint32_t)__shfl_xor(kmax, o, 64));
         }
-    }
-    __syncthreads();
-    const int nband = min(ncand, kBand);
-    const int nnew = hi - r0;
-    for (int t = tid; t < kSortN; t += kThreads) {
-        if (t >= nband && t < nband + nnew) {
-            const int j = r0 + (t - nband);
-            cand[t] = selkey(row[j], (uint32_t)j);
-        } else if (t >= nband + nnew) {
-            cand[t] = 0ull;  // sorts last; never counted (see below)
+        if (lane == 0) {
+            sh.red[0][wave] = kmin;
+            sh.red[1][wave] = kmax;
         }
-    }
-    __syncthreads();
-    // bitonic sort, descending
-    for (int k = 2; k <= kSortN; k <<= 1) {
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-            if (tid < kSortN / 2) {
-                const int i = (tid / jj) * 2 * jj + (tid % jj);
-                const int p = i + jj;
-                const uint64_t a = cand[i], c = cand[p];
-                const bool desc = (i & k) == 0;
-                if (desc ? (a < c) : (a > c)) {
-                    cand[i] = c;
-                    cand[p] = a;
-                }
+        for (int x = tid; x < kBins; x += kThreads) sh.hist[x] = 0u;
+        if (tid == 0) {
+            sh.ncol = 0u;
+            sh.nfound = 0u;
+        }
+        __syncthreads();
+        kmin = 0xffffffffu;
+        kmax = 0u;
+#pragma unroll
+        for (int q = 0; q < kThreads / 64; ++q) {
+            kmin = min(kmin, sh.red[0][q]);
+            kmax = max(kmax, sh.red[1][q]);
+        }
+        const uint32_t range = kmax - kmin;
+        const int bw = range == 0u ? 0 : 32 - __clz(range);
+        const int shift = bw > 12 ? bw - 12 : 0;
+        // ---- a2: histogram, then the bins of ranks A0 and w-1 (descending)
+        if (staged)
+            for_staged(sh.keys, P, [&](int, uint32_t k) { atomicAdd(&sh.hist[(k - kmin) >> shift], 1u); });
+        else
+            for_prefix(row, P, [&](int, float x) { atomicAdd(&sh.hist[(ordkey(x) - kmin) >> shift], 1u); });
+        __syncthreads();
+        {
+            constexpr int PER = kBins / kThreads;  // 16 bins per thread, descending
+            uint32_t c[PER], s = 0;
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                c[q] = sh.hist[kBins - 1 - (PER * tid + q)];
+                s += c[q];
             }
+            uint32_t incl = s;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += y;
+            }
+            if (lane == 63) sh.red[0][wave] = incl;
             __syncthreads();
+            uint32_t excl = incl - s;
+            for (int q = 0; q < wave; ++q) excl += sh.red[0][q];
+            uint32_t run = excl;
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                const uint32_t bin = (uint32_t)(kBins - 1 - (PER * tid + q));
+                if (run <= rankA && rankA < run + c[q]) {
+                    sh.binA = bin;
+                    sh.aboveA = run;
+                }
+                if (run <= rankB && rankB < run + c[q]) sh.binB = bin;
+                run += c[q];
+            }
+        }
+        __syncthreads();
+        const uint32_t binA = sh.binA, binB = sh.binB, aboveA = sh.aboveA;
+        // ---- a3: keys of bins [binB, binA] into LDS, ranked exactly
+        auto collect = [&](int j, uint32_t k) {
+            const uint32_t bin = (k - kmin) >> shift;
+            if (bin >= binB && bin <= binA) {
+                const uint32_t at = atomicAdd(&sh.ncol, 1u);
+                if (at < (uint32_t)kCollectCap) sh.col[at] = ((uint64_t)k << 32) | (uint64_t)(~(uint32_t)j);
+            }
+        };
+        if (staged)
+            for_staged(sh.keys, P, collect);
+        else
+            for_prefix(row, P, [&](int j, float x) { collect(j, ordkey(x)); });
+        __syncthreads();
+        const uint32_t m = sh.ncol;
+        if (m <= (uint32_t)kCollectCap) {
+            for (uint32_t x = tid; x < m; x += kThreads) {
+                const uint64_t me = sh.col[x];
+                uint32_t r = aboveA;
+                for (uint32_t u = 0; u < m; ++u) r += sh.col[u] > me ? 1u : 0u;
+                if (r >= rankA && r <= rankB) sh.cand[r - rankA] = me;
+            }
+        } else {
+            // fallback: exact two-target radix select, then the keys between
+            const uint32_t ranks[2] = {rankA, rankB};
+            uint64_t keys[2];
+            const int nt = nb > 1 ? 2 : 1;
+            radix_select<kThreads>(row, P, nt, ranks, keys, sh.rs);
+            const uint64_t khi = keys[0];
+            const uint64_t klo = nt > 1 ? keys[1] : keys[0];
+            for_prefix(row, P, [&](int j, float x) {
+                const uint64_t k = selkey(x, (uint32_t)j);
+                if (k <= khi && k >= klo) {
+                    const uint32_t at = atomicAdd(&sh.nfound, 1u);
+                    if (at < (uint32_t)kCollectCap) sh.col[at] = k;
+                }
+            });
+            __syncthreads();
+            const uint32_t f = min(sh.nfound, (uint32_t)kCollectCap);  // == nb
+            for (uint32_t x = tid; x < f; x += kThreads) {
+                const uint64_t me = sh.col[x];
+                uint32_t r = 0;
+                for (uint32_t u = 0; u < f; ++u) r += sh.col[u] > me ? 1u : 0u;
+                if (r < (uint32_t)nb) sh.cand[r] = me;
+            }
         }
     }
-    const int total = nband + nnew;
-    for (int t = tid; t < kChunk; t += kThreads) {
-        const int i = r0 + t;
-        if (i < lo || i >= hi) continue;
-        const int need = w - A0;  // rank of the threshold inside band + new keys
-        int cnt = 0;
-        for (int e = 0; e < total; ++e) {
-            const uint32_t j = selkey_idx(cand[e]);
-            if ((int)j <= i && ++cnt == need) {
-                tau[base + i] = row[j];
-                tie[base + i] = (int32_t)j;
-                break;
+    // the chunk's own keys after the band
+    const int nnew = hi - r0;
+    for (int t = tid; t < nnew; t += kThreads) {
+        const int j = r0 + t;
+        sh.cand[nb + t] = selkey(row[j], (uint32_t)j);
+    }
+    __syncthreads();
+
+    // ---- b: each candidate marks the rows it is the threshold of
+    const int need = w - A0 - 1;  // better candidates a row's w-th key has
+    const int ncand = nb + nnew;
+    for (int x = tid; x < ncand; x += kThreads) {
+        const uint64_t kx = sh.cand[x];
+        const int jx = (int)selkey_idx(kx);
+        int better;
+        int first;  // first row that sees this candidate
+        if (x < nb) {
+            better = x;  // band keys are stored by rank
+            first = lo;
+        } else {
+            better = 0;
+            for (int u = 0; u < nb; ++u) better += sh.cand[u] > kx ? 1 : 0;
+            first = max(jx, lo);
+        }
+        if (better > need) continue;
+        for (int t = 0; t < nnew; ++t) {
+            const int i = r0 + t;
+            better += (sh.cand[nb + t] > kx) ? 1 : 0;
+            if (i >= first && better == need) {
+                tau[base + i] = row[jx];
+                tie[base + i] = jx;
             }
+            if (better > need) break;
         }
     }
 }
@@ -130,9 +270,16 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
 
 hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w,
                          float *tau, int32_t *tie, hipStream_t stream) {
-    const dim3 grid((S + kChunk - 1) / kChunk, Hkv, B);
-    hipLaunchKernelGGL(select_kernel, grid, dim3(kThreads), 0, stream, dt, seqlens, Hkv, S, w, tau,
-                       tie);
+    // short rows: more, smaller chunks; long rows: half the prefix passes
+    if (S <= 4096) {
+        const dim3 grid((S + 63) / 64, Hkv, B);
+        hipLaunchKernelGGL(select_kernel<64>, grid, dim3(kThreads), 0, stream, dt, seqlens, Hkv, S, w,
+                           tau, tie);
+    } else {
+        const dim3 grid((S + 127) / 128, Hkv, B);
+        hipLaunchKernelGGL(select_kernel<128>, grid, dim3(kThreads), 0, stream, dt, seqlens, Hkv, S, w,
+                           tau, tie);
+    }
     return hipGetLastError();
 }
 
