@@ -1,6 +1,7 @@
 """Benchmark of the DMA forward hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--other-configs]
+    python bench.py --copy-calibration     (a plain 256 MiB copy, for counter scaling)
 
 One step = the whole hot path over one batch of synthetic input:
   prefill  B=4 Hq=8 Hkv=4 S=2048 d=64 w=512 bf16  (dma_dt -> dma_select -> dma_attn_fwd)
@@ -8,15 +9,17 @@ One step = the whole hot path over one batch of synthetic input:
            (dma_dt appends the new token's dt, then dma_decode)
 A 512 MiB read before each decode evicts the kept K/V rows from the caches
 (with clean lines, so no write-back traffic lands on the decode), so decode
-moves its bytes from HBM; the eviction is outside the timed kernels.
+moves its bytes from HBM; a 512 MiB read before the prefill does the same
+for the prefill inputs.  The evictions are outside the timed kernels.
 
 Printed: ONE JSON line.  value = prefill kept-key TFLOP/s (kept (query, key)
-pairs x 4*d flop over the GPU time of the three prefill kernels, replayed as
-one HIP graph); the decode GB/s (algorithmic bytes over dma_decode's GPU
-time) rides along under "decode".  ms_per_step = prefill + decode GPU time of
-one step (the cache flush between them is excluded); the wall-clock time per
-step including the flush is reported too.  Times come from HIP events
-recorded on the stream the kernels run on.
+pairs x 4*d flop over the GPU time of the three prefill calls, launched back
+to back); the decode GB/s (algorithmic bytes over dma_decode's GPU time)
+rides along under "decode".  ms_per_step = prefill + decode GPU time of one
+step (the cache evictions are excluded); the wall-clock time per step
+including them is reported too.  Times come from HIP events recorded between
+the calls on the stream the kernels run on; the prefill replayed as one HIP
+graph is timed as well.
 """
 from __future__ import annotations
 
@@ -36,6 +39,39 @@ import synth_inputs as si  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+
+# HBM bytes per launch of the prefill attention kernel on this workload, from
+# two rocprofv3 counter runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB
+# per dispatch), each scaled by copy_bytes / counter reading of a plain copy of
+# known size (--copy-calibration); the runs and their readings are in
+# profiles/dma_kernels_prefill_b4s2048_decode_b64l16384_hbm_counters.md.  The
+# figure holds only for the attention source it was measured on: when the
+# hash of those files differs, traffic is reported as null.
+ATTN_TRAFFIC = {"bytes": 25674240,
+                "sources_sha256": "0bc3fdb3595f83e3cb29101350d6e5658b81b39cce40afc7dfc8db57c9f03994"}
+ATTN_SOURCES = ("doge_dynamic_mask_amd/csrc/attn.hip", "doge_dynamic_mask_amd/csrc/common.hpp")
+COPY_CAL_BYTES = 256 * 1024 * 1024
+
+
+def sources_sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def copy_calibration():
+    """Five plain device-to-device copies of COPY_CAL_BYTES, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each": COPY_CAL_BYTES, "copies": 5}), flush=True)
 
 
 def kept_flops(B, Hq, S, d, w, seqlens=None):
@@ -84,8 +120,11 @@ def cpu_baseline(pre_inp, wl_p, min_seconds=10.0):
                       f"{reps} repetitions in {el:.1f} s, fp64"}
 
 
-def prefill_breakdown(dma, name, dev, reps=10):
-    """Per-kernel GPU time of one prefill workload (graph replays between events)."""
+def prefill_breakdown(dma, name, dev, evict, R=8, rounds=4):
+    """Per-call GPU time of one prefill workload, timed like the main
+    workload's calls: after an eviction, R back-to-back launches between two
+    events, each on its own copy of the inputs (enough copies that every
+    launch reads from HBM)."""
     wl = si.WORKLOADS[name]
     inp = si.make_inputs(wl)
     Q, K, V = to_dev(inp["Q"], dev), to_dev(inp["K"], dev), to_dev(inp["V"], dev)
@@ -94,27 +133,47 @@ def prefill_breakdown(dma, name, dev, reps=10):
     dt = torch.empty((wl.B, wl.Hkv, wl.S), dtype=torch.float32, device=dev)
     tau, tie = torch.empty_like(dt), torch.empty(dt.shape, dtype=torch.int32, device=dev)
     O = torch.empty_like(Q)
-    fns = {"dt": lambda: dma.dt(V, W, A, bias, out=dt),
-           "select": lambda: dma.select(dt, wl.w, seq, tau=tau, tie=tie),
-           "attn_fwd": lambda: dma.attn_fwd(Q, K, V, dt, tau, tie, wl.w, seq, out=O)}
+    dma.dt(V, W, A, bias, out=dt)
+    dma.select(dt, wl.w, seq, tau=tau, tie=tie)
+    first = (Q, K, V, dt, tau, tie)
+    set_bytes = sum(t.numel() * t.element_size() for t in first)
+    nsets = 1 + -(-300 * 2**20 // set_bytes)
+    sets = [first] + [tuple(t.clone() for t in first) for _ in range(nsets - 1)]
+    rot = [0]
+
+    def nxt():
+        rot[0] += 1
+        return sets[rot[0] % nsets]
+
+    def c_dt():
+        s_ = nxt()
+        dma.dt(s_[2], W, A, bias, out=s_[3])
+
+    def c_select():
+        s_ = nxt()
+        dma.select(s_[3], wl.w, seq, tau=s_[4], tie=s_[5])
+
+    def c_attn():
+        s_ = nxt()
+        dma.attn_fwd(*s_, wl.w, seq, out=O)
+
     res = {}
-    for n, f in fns.items():
-        f()
+    for n, f in (("dt", c_dt), ("select", c_select), ("attn_fwd", c_attn)):
+        pairs = []
+        for _ in range(rounds):
+            evict()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(R):
+                f()
+            b.record()
+            pairs.append((a, b))
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            f()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g.replay()
-        a.record()
-        for _ in range(reps):
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        res[n] = a.elapsed_time(b) / reps
+        res[n] = float(np.mean([a.elapsed_time(b) for a, b in pairs])) / R
+    del sets
     flops = kept_flops(wl.B, wl.Hq, wl.S, wl.d, wl.w, inp["seqlens"])
     tot = sum(res.values())
-    return {"ms": {k: round(v, 5) for k, v in res.items()}, "kept_flops": flops,
+    return {"ms": {k: round(v, 5) for k, v in res.items()}, "kept_flops": flops, "input_copies": nsets,
             "tflops_prefill": round(flops / (tot * 1e-3) / 1e12, 2),
             "tflops_attn": round(flops / (res["attn_fwd"] * 1e-3) / 1e12, 2),
             "attn_frac_of_peak": round(flops / (res["attn_fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
@@ -128,7 +187,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--other-configs", action="store_true",
                     help="also time the other prefill workloads (long, padded, tiny) per kernel")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain copies of known size (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the DMA hot path has no cross-GPU step in this build "
               "(--gpus must be 1)", file=sys.stderr)
@@ -168,9 +232,8 @@ def main():
 
     torch.cuda.synchronize()
 
-    # Each stage is captured once into a HIP graph (the binding launches on
-    # torch's current stream, which is the capture stream), so a replay costs
-    # one launch and the events below time GPU work rather than Python.
+    # The stages, each one call of the C ABI through the binding, which
+    # launches on torch's current stream (the stream the events record on).
     def g_dt():
         dma.dt(V, W, A, bias, out=dt)
 
@@ -197,31 +260,40 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    G_pre = capture(g_dt, g_select, g_attn)
-    G_dec = capture(g_dt_append, g_decode)
-    single = {"dt": capture(g_dt), "select": capture(g_select), "attn_fwd": capture(g_attn),
-              "dt_append": capture(g_dt_append), "decode": capture(g_decode)}
-
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    # One step: evict, the three prefill calls back to back, evict, the two
+    # decode calls.  The eviction keeps the GPU busy for ~0.14 ms while Python
+    # enqueues what follows, so the events see GPU work rather than host
+    # launch latency (host_enqueue_ms_per_step reports the enqueue time).
+    PRE = (g_dt, g_select, g_attn)
+    DEC = (g_dt_append, g_decode)
+    host_ms = []
+
     def step(e=None):
+        evict()
+        h0 = time.perf_counter()
         if e:
             e[0].record()
-        G_pre.replay()
+        for f in PRE:
+            f()
         if e:
             e[1].record()
         evict()
         if e:
             e[2].record()
-        G_dec.replay()
+        for f in DEC:
+            f()
         if e:
             e[3].record()
+        host_ms.append((time.perf_counter() - h0) * 1e3)
 
     for _ in range(args.warmup):
         step()
     evs = [[ev() for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    host_ms.clear()
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(evs[k])
@@ -230,30 +302,77 @@ def main():
     ms_pre = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     ms_dec = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
 
-    # Per-kernel average durations: REPS back-to-back replays of a one-kernel
-    # graph between two events; the decode kernels run after a cache flush.
-    REPS = 20
-    avg = {}
-    for n, g in single.items():
-        if n in ("dt_append", "decode"):
-            pairs = []
-            for _ in range(REPS):
-                evict()
-                a, b = ev(), ev()
-                a.record()
-                g.replay()
-                b.record()
-                pairs.append((a, b))
-            torch.cuda.synchronize()
-            avg[n] = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
-        else:
+    # Average launch duration per call: after an eviction, R back-to-back
+    # launches of one call between two events, ROUNDS times.  Each launch
+    # reads its own copy of the inputs, rotating over enough copies that the
+    # data read in between exceeds the 256 MB last-level cache, so that every
+    # launch reads from HBM as in the steps above.
+    R, ROUNDS = 12, 5
+    NPRE = 20    # prefill input sets of ~16.4 MB
+    NDEC = 4     # decode caches (~134 MB of kept rows each)
+    pre_sets = [(Q, K, V, dt, tau, tie)] + [
+        tuple(t.clone() for t in (Q, K, V, dt, tau, tie)) for _ in range(NPRE - 1)]
+    dec_sets = [(Kc, Vc, dt_cache)] + [
+        tuple(t.clone() for t in (Kc, Vc, dt_cache)) for _ in range(NDEC - 1)]
+    rot = [0]
+
+    def nxt(sets):
+        rot[0] += 1
+        return sets[rot[0] % len(sets)]
+
+    def c_dt():
+        _, _, v, d, _, _ = nxt(pre_sets)
+        dma.dt(v, W, A, bias, out=d)
+
+    def c_select():
+        _, _, _, d, ta, ti = nxt(pre_sets)
+        dma.select(d, wl_p.w, tau=ta, tie=ti)
+
+    def c_attn():
+        q_, k_, v_, d, ta, ti = nxt(pre_sets)
+        dma.attn_fwd(q_, k_, v_, d, ta, ti, wl_p.w, out=O)
+
+    def c_dt_append():
+        dma.dt(v_new, Wd, Ad, biasd, out=nxt(dec_sets)[2], out_pos=pos)
+
+    def c_decode():
+        kc, vc, dc = nxt(dec_sets)
+        dma.decode(q, kc, vc, dc, lens, wl_d.w, out=out, workspace=ws)
+
+    calls = (("dt", c_dt), ("select", c_select), ("attn_fwd", c_attn),
+             ("dt_append", c_dt_append), ("decode", c_decode))
+    avg, host_launch_ms = {}, {}
+    for n, f in calls:
+        pairs = []
+        hs = []
+        for _ in range(ROUNDS):
+            evict()
             a, b = ev(), ev()
             a.record()
-            for _ in range(REPS):
-                g.replay()
+            h0 = time.perf_counter()
+            for _ in range(R):
+                f()
+            hs.append((time.perf_counter() - h0) * 1e3 / R)
             b.record()
-            torch.cuda.synchronize()
-            avg[n] = a.elapsed_time(b) / REPS
+            pairs.append((a, b))
+        torch.cuda.synchronize()
+        avg[n] = float(np.mean([a.elapsed_time(b) for a, b in pairs])) / R
+        host_launch_ms[n] = float(np.mean(hs))
+    del pre_sets, dec_sets
+
+    # The same prefill replayed as one HIP graph (one launch for three
+    # kernels), timed after an eviction in the same way; reported beside.
+    G_pre = capture(g_dt, g_select, g_attn)
+    gpairs = []
+    for _ in range(args.steps):
+        evict()
+        a, b = ev(), ev()
+        a.record()
+        G_pre.replay()
+        b.record()
+        gpairs.append((a, b))
+    torch.cuda.synchronize()
+    ms_pre_graph = float(np.mean([a.elapsed_time(b) for a, b in gpairs]))
 
     flops = kept_flops(wl_p.B, wl_p.Hq, wl_p.S, wl_p.d, wl_p.w)
     value = flops / (ms_pre * 1e-3) / 1e12
@@ -283,7 +402,10 @@ def main():
         "roofline": {
             "bound": "mfma", "kernel": "dma_attn_fwd (attn_bf16_kernel<64>)",
             "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 5), "traffic": None,
+            "ms_per_launch": round(avg["attn_fwd"], 5), "flop_per_launch": flops,
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 5),
+            "traffic": (ATTN_TRAFFIC["bytes"]
+                        if ATTN_TRAFFIC["sources_sha256"] == sources_sha256(ATTN_SOURCES) else None),
         },
         "decode": {
             "value": round(dec_gbs, 2), "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS,
@@ -292,10 +414,13 @@ def main():
         "ms_prefill": round(ms_pre, 5),
         "ms_decode_step": round(ms_dec, 5),
         "kernel_ms_avg": {n: round(v, 5) for n, v in avg.items()},
+        "ms_prefill_as_one_graph": round(ms_pre_graph, 5),
+        "host_enqueue_ms_per_step": round(float(np.mean(host_ms)), 4),
+        "host_ms_per_launch": {n: round(v, 5) for n, v in host_launch_ms.items()},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
     }
     if args.other_configs:
-        line["other_configs"] = {n: prefill_breakdown(dma, n, dev) for n in ("long", "padded")}
+        line["other_configs"] = {n: prefill_breakdown(dma, n, dev, evict) for n in ("long", "padded")}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre, wl_p)
     print(json.dumps(line), flush=True)
