@@ -9,14 +9,19 @@
 // mask (which depends only on the kv head and the row).
 //
 // Gathered keys instead of dense key tiles: by nesting, the union of the kept
-// sets of rows [i0, i0+Bq) lies inside K_{i0} plus the keys (i0, i0+Bq).  The
-// workgroup scans dt[0..i_last] once, keeps keys passing row i0's threshold
-// test (or newer than i0) and compacts their indices into LDS (ballot +
-// popcount).  It then walks that candidate list in blocks of 64 keys: gather
-// the K and V rows (row-major, plain 16-byte copies) into LDS, S^T = K Q^T on
-// 32x32x16 bf16 MFMA, the exact per-row kept test and the dt bias in
-// registers, an online softmax in base 2, and O^T += V^T P^T on MFMA with P
-// rounded once to bf16.  The V^T operand is read straight from the row-major
+// sets of rows [i0, i_last] lies inside K_{i0} plus the keys (i0, i_last].
+// The workgroup scans dt[0..i_last] and compacts those candidate keys into
+// LDS in two passes (count per wave and 1024-key step with all loads in
+// flight, one scan, then write with ballot offsets), in index order and split
+// in two groups: "full" keys, kept by every row of the tile (a key j <= i0
+// kept by i_last is kept by every row in between, by nesting), first, and the
+// "partial" rest after them (at most 2*Bq keys: each row drops at most one
+// key, plus the tile's own keys), each with the run of tile rows that keeps
+// it.  It then walks the candidates in blocks of 64 keys: gather the K and V
+// rows (row-major, plain 16-byte copies) into LDS, S^T = K Q^T on 32x32x16
+// bf16 MFMA, the dt bias (plus, in blocks holding partial keys only, the
+// row-run test) in registers, an online softmax in base 2, and O^T += V^T P^T
+// on MFMA with P rounded once to bf16.  The V^T operand is read straight from the row-major
 // V tile with the gfx950 LDS transpose read (ds_read_b64_tr_b16).  Only
 // ~w + Bq keys are touched per tile instead of the dense causal prefix.
 //
@@ -37,7 +42,11 @@ constexpr int kThreads = 256;
 constexpr int kRowsPerWG = 128;  // stacked (row, head) pairs per workgroup
 constexpr int kBK = 64;          // keys per block
 constexpr int kCap = 2560;       // candidate slots in LDS (multiple of kBK)
-constexpr int kFillPer = 2;      // consecutive keys per thread per fill step
+constexpr int kFillKeys = 4;     // consecutive keys per thread per fill step
+constexpr int kStepKeys = kThreads * kFillKeys;  // keys per fill step
+constexpr int kMaxSteps = 32;    // fill steps counted per round (32768 keys)
+constexpr int kBatchSteps = 8;   // fill steps whose loads are issued together
+constexpr int kPartCap = 2 * kRowsPerWG + 2 * kBK;  // slots of the masked region
 
 template <int D>
 struct Tiles {
@@ -82,13 +91,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     constexpr int NL = kBK * RV / kThreads;      // K (and V) vectors per thread per block
     static_assert(kBK * RV % kThreads == 0, "block staging split");
     __shared__ __align__(16) int c_idx[kCap];
-    __shared__ __align__(16) int c_lo[kCap];     // first tile row (offset) keeping the key
-    __shared__ __align__(16) int c_span[kCap];   // number of consecutive rows keeping it
-    __shared__ __align__(16) float c_dtl[kCap];  // dt * log2(e)
-    __shared__ uint64_t thr[kRowsPerWG];           // threshold key of each tile row
+    __shared__ __align__(16) float c_dtl[kCap];     // dt * log2(e)
+    __shared__ __align__(16) int c_lo[kPartCap];    // masked region: first tile row keeping the key
+    __shared__ __align__(16) int c_span[kPartCap];  // masked region: rows keeping it
+    __shared__ uint64_t thr[kRowsPerWG];            // threshold key of each tile row
+    __shared__ uint32_t cnt[kMaxSteps * 4];         // per (fill step, wave): full | partial << 16
+    __shared__ int fill_info[3];                    // steps used, full count, partial count
     __shared__ __align__(16) uint16_t Ks[kBK * T::KP];
     __shared__ __align__(16) uint16_t Vs[kBK * T::VP];
-    __shared__ int wcnt[2][kThreads / 64];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int h = lane >> 5, ql = lane & 31;
@@ -136,10 +146,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         for (int ks = 0; ks < D / 16; ++ks) qf[ks] = bf16x8{};
     }
 
-    const float tau0 = tau[urow + i0];
-    const int tie0 = tie[urow + i0];
+    // thresholds of the first and the last row of the tile
+    const float tau0 = tau[urow + i0], taul = tau[urow + i_last];
+    const int tie0 = tie[urow + i0], tiel = tie[urow + i_last];
     const float *dtrow = dt + urow;
-    const size_t kvs = (size_t)Hkv * D;
+    const uint32_t kvs = (uint32_t)(Hkv * D);
     const uint16_t *Kb = K + (size_t)b * S * kvs + (size_t)g * D;
     const uint16_t *Vb = V + (size_t)b * S * kvs + (size_t)g * D;
 
@@ -148,31 +159,49 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
 
-    // next block, staged in registers: vector v = tid + u*256 is row v / RV,
-    // 16-byte column v % RV of both the K and the V tile
-    uint4 pk[NL], pv[NL];
-    auto load_block = [&](int blk, int n) {
+    // candidate class of key j: 0 not a candidate, 1 kept by every tile row,
+    // 2 kept by some tile rows
+    auto cls_of = [&](float dv, int j) __attribute__((always_inline)) -> int {
+        if (j > i_last) return 0;
+        if (j > i0) return 2;
+        if (!kept_test(dv, j, tau0, tie0)) return 0;
+        return kept_test(dv, j, taul, tiel) ? 1 : 2;
+    };
+    // the fill step's keys of this thread: scan + step*kStepKeys + 4*tid + e
+    auto load_step_keys = [&](float (&dv)[kBatchSteps][kFillKeys], int scan, int s0, int nsteps)
+        __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < NL; ++u) {
-            const int v = tid + u * kThreads;
-            const int pos = blk + v / RV;
-            if (pos < n) {
-                const size_t off = (size_t)c_idx[pos] * kvs + (v % RV) * 8;
-                pk[u] = *reinterpret_cast<const uint4 *>(Kb + off);
-                pv[u] = *reinterpret_cast<const uint4 *>(Vb + off);
-            } else {
-                pk[u] = make_uint4(0, 0, 0, 0);
-                pv[u] = make_uint4(0, 0, 0, 0);
+        for (int bb = 0; bb < kBatchSteps; ++bb) {
+#pragma unroll
+            for (int e = 0; e < kFillKeys; ++e) {
+                const int j = scan + (s0 + bb) * kStepKeys + kFillKeys * tid + e;
+                dv[bb][e] = (s0 + bb < nsteps && j <= i_last) ? dtrow[j] : 0.f;
             }
         }
     };
-    auto store_block = [&]() {
+
+    // next block, staged in registers: vector v = tid + u*256 is row v / RV,
+    // 16-byte column v % RV of both the K and the V tile.  Positions past the
+    // last candidate repeat it (a real row; its weight is masked to zero).
+    u32x4 pk[NL], pv[NL];
+    auto load_block = [&](int blk, int n) __attribute__((always_inline)) {
+        int idx[NL];
+#pragma unroll
+        for (int u = 0; u < NL; ++u) idx[u] = c_idx[min(blk + (tid + u * kThreads) / RV, n - 1)];
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const size_t off = (size_t)(uint32_t)idx[u] * kvs + ((tid + u * kThreads) % RV) * 8;
+            pk[u] = *reinterpret_cast<const u32x4 *>(Kb + off);
+            pv[u] = *reinterpret_cast<const u32x4 *>(Vb + off);
+        }
+    };
+    auto store_block = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
             const int v = tid + u * kThreads;
             const int kk = v / RV, cv = v % RV;
-            *reinterpret_cast<uint4 *>(&Ks[kk * T::KP + cv * 8]) = pk[u];
-            *reinterpret_cast<uint4 *>(&Vs[kk * T::VP + cv * 8]) = pv[u];
+            *reinterpret_cast<u32x4 *>(&Ks[kk * T::KP + cv * 8]) = pk[u];
+            *reinterpret_cast<u32x4 *>(&Vs[kk * T::VP + cv * 8]) = pv[u];
         }
     };
 
@@ -181,70 +210,110 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     // column 16*((l>>4)&1) + 4*(k&3) (+32t).
     const int tr_k = lane & 15;
     const int tr_off = (4 * h + (tr_k >> 2)) * T::VP + 16 * ((lane >> 4) & 1) + 4 * (tr_k & 3);
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
 
     int scan = 0;
     while (scan <= i_last) {
-        // ---- fill: compact the candidate keys of this tile into LDS, two
-        // consecutive keys per thread, one barrier per 512 keys
-        int n = 0, par = 0;
-        while (scan <= i_last && n + kFillPer * kThreads <= kCap) {
-            const int j0 = scan + kFillPer * tid;
-            float dj[kFillPer];
-            bool take[kFillPer];
-            int cnt = 0;
+        // ---- fill pass 1: candidates per (step, wave), loads of kBatchSteps
+        // steps in flight
+        const int nsteps = min((i_last - scan) / kStepKeys + 1, kMaxSteps);
+        for (int s0 = 0; s0 < nsteps; s0 += kBatchSteps) {
+            float dv[kBatchSteps][kFillKeys];
+            load_step_keys(dv, scan, s0, nsteps);
 #pragma unroll
-            for (int u = 0; u < kFillPer; ++u) {
-                const int j = j0 + u;
-                dj[u] = j <= i_last ? dtrow[j] : 0.f;
-                take[u] = j <= i_last && ((j > i0) || kept_test(dj[u], j, tau0, tie0));
-                cnt += take[u] ? 1 : 0;
-            }
-            int incl = cnt;
+            for (int bb = 0; bb < kBatchSteps; ++bb) {
+                if (s0 + bb >= nsteps) break;
+                uint32_t nf = 0, np = 0;
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(incl, o, 64);
-                if (lane >= o) incl += y;
-            }
-            if (lane == 63) wcnt[par][wave] = incl;
-            __syncthreads();
-            int off = n + incl - cnt, tot = 0;
-#pragma unroll
-            for (int w2 = 0; w2 < kThreads / 64; ++w2) {
-                const int c = wcnt[par][w2];
-                off += (w2 < wave) ? c : 0;
-                tot += c;
-            }
-#pragma unroll
-            for (int u = 0; u < kFillPer; ++u) {
-                if (take[u]) {
-                    c_idx[off] = j0 + u;
-                    c_dtl[off] = dj[u];
-                    ++off;
+                for (int e = 0; e < kFillKeys; ++e) {
+                    const int c = cls_of(dv[bb][e], scan + (s0 + bb) * kStepKeys + kFillKeys * tid + e);
+                    nf += (uint32_t)__popcll(__ballot(c == 1));
+                    np += (uint32_t)__popcll(__ballot(c == 2));
                 }
+                if (lane == 0) cnt[(s0 + bb) * 4 + wave] = nf | (np << 16);
             }
-            n += tot;
-            scan += kFillPer * kThreads;
-            par ^= 1;
         }
         __syncthreads();
-        // ---- per candidate: the run of tile rows that keep it.  By nesting a
-        // key kept by row r is kept by every earlier row >= its own index, so
-        // it is kept exactly on rows [lo, lo + span) (offsets from i0).
-        const int npad = (n + kBK - 1) / kBK * kBK;
-        for (int k = tid; k < npad; k += kThreads) {
-            int lo = 0, span = 0;
-            float dl = 0.f;
-            if (k < n) {
-                const int j = c_idx[k];
-                const float dv = c_dtl[k];
-                lo = j > i0 ? j - i0 : 0;
-                span = first_row_above(thr, lo, nrows, selkey(dv, (uint32_t)j)) - lo;
-                dl = dv * kLog2e;
+        // ---- exclusive scan over (step, wave) in key order; the steps whose
+        // candidates fit in kCap are used this round
+        if (wave == 0) {
+            const int e0 = 2 * lane, ne = 4 * nsteps;
+            const uint32_t v0 = e0 < ne ? cnt[e0] : 0u, v1 = e0 + 1 < ne ? cnt[e0 + 1] : 0u;
+            uint32_t incl = v0 + v1;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += y;
             }
-            c_lo[k] = lo;
-            c_span[k] = span;
-            c_dtl[k] = dl;
+            if (e0 < ne) cnt[e0] = incl - v0 - v1;
+            if (e0 + 1 < ne) cnt[e0 + 1] = incl - v1;
+            // lane 2s+1 holds the running total through the end of step s
+            const bool fits = (lane & 1) && (lane >> 1) < nsteps && (incl & 0xffffu) + (incl >> 16) <= (uint32_t)kCap;
+            const int used = __popcll(__ballot(fits));  // >= 1: one step never exceeds kCap
+            const uint32_t tot = __shfl(incl, 2 * used - 1, 64);
+            if (lane == 0) {
+                fill_info[0] = used;
+                fill_info[1] = (int)(tot & 0xffffu);
+                fill_info[2] = (int)(tot >> 16);
+            }
         }
+        __syncthreads();
+        const int used = fill_info[0], nF = fill_info[1], n = nF + fill_info[2];
+        const int pbase = nF / kBK * kBK;           // first block holding a partial key
+        const int npad = (n + kBK - 1) / kBK * kBK;
+        // ---- fill pass 2: write the candidates (full first, partial after)
+        for (int s0 = 0; s0 < used; s0 += kBatchSteps) {
+            float dv[kBatchSteps][kFillKeys];
+            load_step_keys(dv, scan, s0, used);
+#pragma unroll
+            for (int bb = 0; bb < kBatchSteps; ++bb) {
+                if (s0 + bb >= used) break;
+                const uint32_t base = cnt[(s0 + bb) * 4 + wave];
+                int of = (int)(base & 0xffffu), op = nF + (int)(base >> 16);
+                const int jb = scan + (s0 + bb) * kStepKeys + kFillKeys * tid;
+                int c[kFillKeys];
+#pragma unroll
+                for (int e = 0; e < kFillKeys; ++e) {
+                    c[e] = cls_of(dv[bb][e], jb + e);
+                    of += (int)__popcll(__ballot(c[e] == 1) & lt_mask);
+                    op += (int)__popcll(__ballot(c[e] == 2) & lt_mask);
+                }
+#pragma unroll
+                for (int e = 0; e < kFillKeys; ++e) {
+                    const int j = jb + e;
+                    if (c[e] == 1) {
+                        c_idx[of] = j;
+                        c_dtl[of] = dv[bb][e] * kLog2e;
+                        ++of;
+                    } else if (c[e] == 2) {
+                        c_idx[op] = j;
+                        c_dtl[op] = dv[bb][e] * kLog2e;
+                        ++op;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // row runs of the masked region: a partial key j is kept on the tile
+        // rows [lo, lo + span) (by nesting a run: from its own row, or from
+        // i0, until the first row whose threshold passes it); full keys
+        // sharing a block with partial ones keep every row; slots past the
+        // last candidate keep none
+        for (int k = pbase + tid; k < npad; k += kThreads) {
+            int lo = 0, span = 0;
+            if (k < nF) {
+                span = nrows;
+            } else if (k < n) {
+                const int j = c_idx[k];
+                lo = j > i0 ? j - i0 : 0;
+                span = first_row_above(thr, lo, nrows, selkey(dtrow[j], (uint32_t)j)) - lo;
+            } else {
+                c_dtl[k] = 0.f;
+            }
+            c_lo[k - pbase] = lo;
+            c_span[k - pbase] = span;
+        }
+        scan += used * kStepKeys;
         __syncthreads();
 
         // ---- attend over the candidates, 64 keys at a time
@@ -274,26 +343,45 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 a1 = n1;
             }
 
-            // mask (row runs), dt bias, online softmax in base 2
+            // dt bias (and, where partial keys are, the row-run test), then
+            // the online softmax in base 2
             float z[2][16];
             float mloc = -INFINITY;
+            if (blk < pbase) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+                for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int pos = blk + 32 * kt + 8 * r4 + 4 * h;
-                    const int4 lo4 = *reinterpret_cast<const int4 *>(&c_lo[pos]);
-                    const int4 sp4 = *reinterpret_cast<const int4 *>(&c_span[pos]);
-                    const float4 dl4 = *reinterpret_cast<const float4 *>(&c_dtl[pos]);
-                    const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
-                    const int sps[4] = {sp4.x, sp4.y, sp4.z, sp4.w};
-                    const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int pos = blk + 32 * kt + 8 * r4 + 4 * h;
+                        const float4 dl4 = *reinterpret_cast<const float4 *>(&c_dtl[pos]);
+                        const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const bool ok = (unsigned)(r - los[e]) < (unsigned)sps[e];
-                        const float zz = fmaf(sacc[kt][4 * r4 + e], qscale, ok ? dls[e] : -INFINITY);
-                        z[kt][4 * r4 + e] = zz;
-                        mloc = fmaxf(mloc, zz);
+                        for (int e = 0; e < 4; ++e) {
+                            const float zz = fmaf(sacc[kt][4 * r4 + e], qscale, dls[e]);
+                            z[kt][4 * r4 + e] = zz;
+                            mloc = fmaxf(mloc, zz);
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int pos = blk + 32 * kt + 8 * r4 + 4 * h;
+                        const int4 lo4 = *reinterpret_cast<const int4 *>(&c_lo[pos - pbase]);
+                        const int4 sp4 = *reinterpret_cast<const int4 *>(&c_span[pos - pbase]);
+                        const float4 dl4 = *reinterpret_cast<const float4 *>(&c_dtl[pos]);
+                        const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
+                        const int sps[4] = {sp4.x, sp4.y, sp4.z, sp4.w};
+                        const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const bool ok = (unsigned)(r - los[e]) < (unsigned)sps[e];
+                            const float zz = fmaf(sacc[kt][4 * r4 + e], qscale, ok ? dls[e] : -INFINITY);
+                            z[kt][4 * r4 + e] = zz;
+                            mloc = fmaxf(mloc, zz);
+                        }
                     }
                 }
             }
@@ -312,28 +400,31 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
             }
             const float msub = (mrow == -INFINITY) ? 0.f : mrow;
-            float psum = 0.f;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(z[kt][e] - msub);
-                    z[kt][e] = p;
-                    psum += p;
-                }
+                for (int e = 0; e < 16; ++e) z[kt][e] = __builtin_amdgcn_exp2f(z[kt][e] - msub);
             }
-            lrow += psum;
 
             // O^T += V^T P^T.  PV call c covers keys 16c..16c+15; lane half h
             // holds, in k-slots 0..7, keys 16c + 8*(j/4) + 4h + j%4, which are
             // exactly its score registers z[c/2][8*(c%2) + j].  The V^T operand
             // comes from two transpose reads (rows 16c + 4h + {0..3} and
-            // 16c + 8 + 4h + {0..3}).
+            // 16c + 8 + 4h + {0..3}).  The softmax denominator sums the same
+            // bf16-rounded weights that multiply V, so that the rounding of P
+            // perturbs the weights of a normalised average (an output
+            // dominated by one key keeps that key's value).
+            float psum = 0.f;
+            const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 bf16x8 pb;
 #pragma unroll
                 for (int jx = 0; jx < 8; ++jx) pb[jx] = (__bf16)z[c >> 1][8 * (c & 1) + jx];
+                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), one2, psum, false);
+                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one2, psum, false);
+                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one2, psum, false);
+                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), one2, psum, false);
 #pragma unroll
                 for (int t = 0; t < D / 32; ++t) {
                     const uint16_t *vp = &Vs[16 * c * T::VP + 32 * t + tr_off];
@@ -343,6 +434,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                     oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, oacc[t], 0, 0, 0);
                 }
             }
+            lrow += psum;
             __syncthreads();  // LDS tiles are rewritten next
         }
     }

@@ -3,11 +3,16 @@
 // states of all kv heads of a token (input width Hkv*d, head-major), then
 // exp(A * softplus(.)).
 //
-// A skinny GEMV that streams V once from HBM: eight lanes share one token
-// row, each lane loading 16-byte vectors so that the eight lanes of a group
-// read 128 contiguous bytes per step.  W (at most 64 KiB) is staged once per
-// workgroup in LDS in its storage type.  Partial sums are reduced across the
-// eight lanes with xor shuffles; softplus and exp run in float32.
+// A skinny matrix product X[tokens][Hkv] = V[tokens][Hkv*d] * W^T that must
+// stream V once from HBM.  bf16 runs on matrix cores: one wave takes 16
+// tokens, v_mfma_f32_16x16x32_bf16 with the tokens as M, the (zero-padded)
+// kv heads as N and the channels as K, so V is fed to the MFMA straight from
+// its 16-byte loads with no conversion; W is staged once per workgroup in LDS
+// with a padded pitch.  The contraction order over channels is free, so each
+// lane owns 32 consecutive channels per 128-channel chunk (64 contiguous
+// bytes of its token row) and the same channel permutation is applied to W.
+// float32 uses VALU: eight lanes per token, 16-byte vectors, xor-shuffle
+// reduction.  softplus and exp run in float32 in both.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -21,15 +26,6 @@ constexpr int kBatch = 8;  // 16-byte vectors per lane loaded together
 
 template <typename T>
 __device__ __forceinline__ void unpack16(const uint4 &v, float *x);
-template <>
-__device__ __forceinline__ void unpack16<uint16_t>(const uint4 &v, float *x) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        x[2 * k] = __uint_as_float(w[k] << 16);
-        x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-    }
-}
 template <>
 __device__ __forceinline__ void unpack16<float>(const uint4 &v, float *x) {
     x[0] = __uint_as_float(v.x);
@@ -117,21 +113,103 @@ __global__ __launch_bounds__(kThreads) void dt_kernel(const T *__restrict__ V, c
     }
 }
 
+constexpr int kMfmaThreads = 128;     // two waves, one 16-token tile each
+constexpr int kChunk = 128;           // channels per lane group pass (4 lanes x 32)
+constexpr int kChunksPerBatch = 4;    // chunks loaded before the first multiply
+
+// bf16 dt on matrix cores.  16x16x32 bf16 operand layouts (l = lane):
+//   A[m = l%16][k = 8*(l/16) + j], B[k = 8*(l/16) + j][n = l%16],
+//   C[m = 4*(l/16) + i][n = l%16], i = 0..3.
+// Channel of k-slot (kg = l/16, j) in step s of chunk c: c*128 + 32*kg + 8*s + j.
+__global__ __launch_bounds__(kMfmaThreads) void dt_mfma_kernel(
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ W, const uint16_t *__restrict__ bias,
+    const float *__restrict__ A, int S, int Hkv, int width, int pitch, int64_t ntok,
+    float *__restrict__ out, int64_t ld, const int32_t *__restrict__ out_pos) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ float As[kMaxHkvDt], bs[kMaxHkvDt];
+    uint16_t *Ws = reinterpret_cast<uint16_t *>(smem);  // [Hkv][pitch]
+    const int rv = width / 8;     // 16-byte vectors per W row
+    for (int v = threadIdx.x; v < Hkv * rv; v += kMfmaThreads) {
+        const int hh = v / rv, c = v - hh * rv;
+        *reinterpret_cast<uint4 *>(Ws + hh * pitch + 8 * c) = reinterpret_cast<const uint4 *>(W)[v];
+    }
+    if (threadIdx.x < (unsigned)Hkv) {
+        As[threadIdx.x] = A[threadIdx.x];
+        bs[threadIdx.x] = bias ? bf16_to_f32(bias[threadIdx.x]) : 0.f;
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int mr = lane & 15, kg = lane >> 4;
+    const int nchunk = (width + kChunk - 1) / kChunk;
+    const bool head_ok = mr < Hkv;
+    const int64_t ntiles = (ntok + 15) / 16;
+    for (int64_t tile = (int64_t)blockIdx.x * (kMfmaThreads / 64) + wave; tile < ntiles;
+         tile += (int64_t)gridDim.x * (kMfmaThreads / 64)) {
+        const int64_t t = tile * 16 + mr;
+        const bool tok_ok = t < ntok;
+        const uint16_t *vrow = V + (tok_ok ? t : 0) * (int64_t)width;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int c0 = 0; c0 < nchunk; c0 += kChunksPerBatch) {
+            uint4 va[kChunksPerBatch][4];
+#pragma unroll
+            for (int cc = 0; cc < kChunksPerBatch; ++cc) {
+                const int base = (c0 + cc) * kChunk + 32 * kg;
+                const bool ok = tok_ok && base < width;
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+                    va[cc][st] = ok ? *reinterpret_cast<const uint4 *>(vrow + base + 8 * st) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int cc = 0; cc < kChunksPerBatch; ++cc) {
+                const int base = (c0 + cc) * kChunk + 32 * kg;
+                if (c0 + cc >= nchunk) break;
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    bf16x8 bw = {};
+                    if (head_ok && base < width) bw = *reinterpret_cast<const bf16x8 *>(Ws + mr * pitch + base + 8 * st);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va[cc][st]), bw, acc, 0, 0, 0);
+                }
+            }
+        }
+        if (head_ok) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t tok = tile * 16 + 4 * kg + i;
+                if (tok < ntok) {
+                    const int b = (int)(tok / S);
+                    const int s = (int)(tok - (int64_t)b * S);
+                    const int64_t col = (out_pos ? (int64_t)out_pos[b] : 0) + s;
+                    const float x = acc[i] + bs[mr];
+                    out[((int64_t)b * Hkv + mr) * ld + col] = expf(As[mr] * softplus_f32(x));
+                }
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_dt(const void *V, const void *W, const void *bias, const float *A, int dtype,
                      int B, int S, int Hkv, int d, float *dt_out, int64_t ld_out,
                      const int32_t *out_pos, hipStream_t stream) {
     const int64_t ntok = (int64_t)B * S;
-    const int64_t want = (ntok + kTokensPerBlock - 1) / kTokensPerBlock;
-    const int grid = (int)(want < 2048 ? want : 2048);
-    const size_t esize = dtype == 1 ? 2 : 4;
-    const size_t lds = (size_t)Hkv * Hkv * d * esize;
     if (dtype == 1) {
-        hipLaunchKernelGGL(dt_kernel<uint16_t>, dim3(grid), dim3(kThreads), lds, stream,
+        const int width = Hkv * d;
+        const int64_t ntiles = (ntok + 15) / 16;
+        const int64_t want = (ntiles + kMfmaThreads / 64 - 1) / (kMfmaThreads / 64);
+        const int grid = (int)(want < 4096 ? want : 4096);
+        // W rows padded by 16 bytes so that the heads read by one lane group
+        // fall in different banks, unless that would pass 64 KiB of LDS
+        const int pitch = (size_t)Hkv * (width + 8) * sizeof(uint16_t) <= kDtLdsBytes ? width + 8 : width;
+        const size_t lds = (size_t)Hkv * pitch * sizeof(uint16_t);
+        hipLaunchKernelGGL(dt_mfma_kernel, dim3(grid), dim3(kMfmaThreads), lds, stream,
                            (const uint16_t *)V, (const uint16_t *)W, (const uint16_t *)bias, A, S, Hkv,
-                           d, ntok, dt_out, ld_out, out_pos);
+                           width, pitch, ntok, dt_out, ld_out, out_pos);
     } else {
+        const int64_t want = (ntok + kTokensPerBlock - 1) / kTokensPerBlock;
+        const int grid = (int)(want < 2048 ? want : 2048);
+        const size_t lds = (size_t)Hkv * Hkv * d * sizeof(float);
         hipLaunchKernelGGL(dt_kernel<float>, dim3(grid), dim3(kThreads), lds, stream, (const float *)V,
                            (const float *)W, (const float *)bias, A, S, Hkv, d, ntok, dt_out, ld_out,
                            out_pos);

@@ -72,6 +72,28 @@ def test_dt_no_bias_and_append(dma, oracle_mod, dtype):
         assert (got[b][:, mask] == -7.0).all()
 
 
+@pytest.mark.parametrize("dtype,B,S,Hkv,d", [
+    ("bf16", 1, 1, 1, 64),      # width 64: half of a 128-channel chunk
+    ("bf16", 3, 37, 1, 64),     # ragged 16-token tiles across batch boundaries
+    ("bf16", 2, 333, 16, 128),  # largest head count and width (W fills 64 KiB of LDS)
+    ("bf16", 1, 100, 3, 128),   # head count not a power of two
+    ("f32", 2, 45, 8, 64),
+    ("f32", 1, 70, 5, 128),
+])
+def test_dt_shapes(dma, oracle_mod, dtype, B, S, Hkv, d):
+    rng = np.random.default_rng(B * 1000 + S + Hkv)
+    V = rng.standard_normal((B, S, Hkv, d)).astype(np.float32)
+    W = rng.normal(0, 0.02, (Hkv, Hkv * d)).astype(np.float32)
+    bias = rng.normal(0, 0.5, Hkv).astype(np.float32)
+    A = rng.uniform(-2, 2, Hkv).astype(np.float32)
+    if dtype == "bf16":
+        V, W, bias = si.to_bf16_bits(V), si.to_bf16_bits(W), si.to_bf16_bits(bias)
+    got = to_host(dma.dt(to_dev(V), to_dev(W), to_dev(A), to_dev(bias)))
+    ref = oracle_mod.dt(V, W, bias, A)
+    rel = np.abs(got.astype(np.float64) - ref) / np.abs(ref)
+    assert rel.max() <= 1e-5, rel.max()
+
+
 # -------------------------------------------------------------- select ----
 SELECT_CASES = [
     # B, Hkv, S, w, kind, padded
@@ -189,6 +211,24 @@ def test_attn_full_size_sampled(dma, oracle_mod, name):
     if seq is not None:
         for b in range(wl.B):
             assert (O[b, seq[b]:] == 0).all()
+
+
+@pytest.mark.parametrize("S,w,Hq,Hkv,d", [(40000, 100, 4, 2, 64),     # prefix scan over two fill rounds
+                                         (70000, 3000, 2, 1, 128)])  # candidates beyond the LDS capacity too
+def test_attn_long_rows_sampled(dma, oracle_mod, S, w, Hq, Hkv, d):
+    Q, K, V = si.make_qkv(1, S, Hq, Hkv, d, "bf16", seed=S + w)
+    dt = si.make_dt((1, Hkv, S), "lognormal", seed=S + w + 1)
+    dts = to_dev(dt)
+    tau, tie = dma.select(dts, w)
+    O = to_host(dma.attn_fwd(to_dev(Q), to_dev(K), to_dev(V), dts, tau, tie, w))
+    rng = np.random.default_rng(S)
+    picks = sorted(set(rng.integers(0, S, 60).tolist()) | {0, w - 1, w, 32767, 32768, S - 1})
+    rows = [(0, g, i) for g in range(Hkv) for i in picks if i < S]
+    ref = oracle_mod.attn(Q, K, V, dt, w, rows=rows)
+    G = Hq // Hkv
+    for n, (b, g, i) in enumerate(rows):
+        got = O[b, i, g * G:(g + 1) * G].astype(np.float64)
+        assert np.abs(got - ref[n]).max() <= TOL["bf16"], (g, i)
 
 
 def test_attn_deterministic_and_gqa_equals_mha(dma, oracle_mod):
