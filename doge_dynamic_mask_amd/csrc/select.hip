@@ -237,10 +237,22 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
     }
     __syncthreads();
 
-    // ---- b: each candidate marks the rows it is the threshold of
+    // ---- b: each candidate marks the rows it is the threshold of.  One wave
+    // per candidate at a time: the chunk's new keys sit one per lane (rows
+    // t = lane and t = lane + 64), so "new keys of rows <= t better than the
+    // candidate" is a ballot and a masked bit count per lane, and every lane
+    // checks its own rows.
     const int need = w - A0 - 1;  // better candidates a row's w-th key has
     const int ncand = nb + nnew;
-    for (int x = tid; x < ncand; x += kThreads) {
+    const uint64_t nk0 = lane < nnew ? sh.cand[nb + lane] : 0ull;  // 0: below every key
+    const uint64_t nk1 = (C > 64 && lane + 64 < nnew) ? sh.cand[nb + 64 + lane] : 0ull;
+    uint64_t bk[(C + 1 + 63) / 64 + 1];
+#pragma unroll
+    for (int q = 0; q < (int)(sizeof(bk) / sizeof(bk[0])); ++q)
+        bk[q] = 64 * q + lane < nb ? sh.cand[64 * q + lane] : 0ull;
+    const uint64_t le_mask = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);  // bits 0..lane
+    const int t0 = lane, t1 = lane + 64;  // this lane's rows (chunk offsets)
+    for (int x = wave; x < ncand; x += kThreads / 64) {
         const uint64_t kx = sh.cand[x];
         const int jx = (int)selkey_idx(kx);
         int better;
@@ -250,18 +262,27 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
             first = lo;
         } else {
             better = 0;
-            for (int u = 0; u < nb; ++u) better += sh.cand[u] > kx ? 1 : 0;
+#pragma unroll
+            for (int q = 0; q < (int)(sizeof(bk) / sizeof(bk[0])); ++q) better += __popcll(__ballot(bk[q] > kx));
             first = max(jx, lo);
         }
-        if (better > need) continue;
-        for (int t = 0; t < nnew; ++t) {
-            const int i = r0 + t;
-            better += (sh.cand[nb + t] > kx) ? 1 : 0;
-            if (i >= first && better == need) {
-                tau[base + i] = row[jx];
-                tie[base + i] = jx;
-            }
-            if (better > need) break;
+        const int need_x = need - better;  // better new keys the row must see
+        if (need_x < 0) continue;          // uniform: the band alone outranks it
+        const uint64_t m0 = __ballot(nk0 > kx);
+        const uint64_t m1 = C > 64 ? __ballot(nk1 > kx) : 0ull;
+        const int c0 = __popcll(m0 & le_mask);
+        const int c1 = __popcll(m0) + __popcll(m1 & le_mask);
+        const bool hit0 = c0 == need_x && r0 + t0 >= first && r0 + t0 < hi;
+        const bool hit1 = C > 64 && c1 == need_x && r0 + t1 >= first && r0 + t1 < hi;
+        if (__ballot(hit0 || hit1) == 0ull) continue;
+        const float vx = row[jx];
+        if (hit0) {
+            tau[base + r0 + t0] = vx;
+            tie[base + r0 + t0] = jx;
+        }
+        if (hit1) {
+            tau[base + r0 + t1] = vx;
+            tie[base + r0 + t1] = jx;
         }
     }
 }
