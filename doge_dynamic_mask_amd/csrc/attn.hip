@@ -32,6 +32,8 @@
 // S^T = K Q^T puts one query per lane (n) and 32 keys per lane, so row max /
 // sum need only a swap between the two lane halves.  O^T = V^T P^T keeps one
 // query per lane, so the online-softmax rescale is lane-local.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -47,6 +49,8 @@ constexpr int kStepKeys = kThreads * kFillKeys;  // keys per fill step
 constexpr int kMaxSteps = 32;    // fill steps counted per round (32768 keys)
 constexpr int kBatchSteps = 8;   // fill steps whose loads are issued together
 constexpr int kPartCap = 2 * kRowsPerWG + 2 * kBK;  // slots of the masked region
+constexpr int kCarrySlots = kCap / kThreads;         // carried candidates per thread
+constexpr int kTargetItems = 1024;                   // workgroups a launch aims for
 
 template <int D>
 struct Tiles {
@@ -84,12 +88,13 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const float *__restrict__ dt, const float *__restrict__ tau, const int32_t *__restrict__ tie,
-    const int32_t *__restrict__ seqlens, int S, int Hq, int Hkv, int G, int Bq, int ntiles,
+    const int32_t *__restrict__ seqlens, int S, int Hq, int Hkv, int G, int Bq, int ntiles, int tpw,
     uint16_t *__restrict__ O, float qscale) {
     using T = Tiles<D>;
     constexpr int RV = D / 8;                    // 16-byte vectors per K/V row
     constexpr int NL = kBK * RV / kThreads;      // K (and V) vectors per thread per block
     static_assert(kBK * RV % kThreads == 0, "block staging split");
+    static_assert(4 * (kCarrySlots + 1) <= 64 && 4 * (kCarrySlots + 1) <= 4 * kMaxSteps, "carry scan");
     __shared__ __align__(16) int c_idx[kCap];
     __shared__ __align__(16) float c_dtl[kCap];     // dt * log2(e)
     __shared__ __align__(16) int c_lo[kPartCap];    // masked region: first tile row keeping the key
@@ -102,62 +107,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int h = lane >> 5, ql = lane & 31;
+    // Work item = (batch, kv head, group of tpw consecutive query tiles).
     // XCD-aware order: workgroup ids go round-robin over the 8 XCDs, so hand
-    // each XCD a contiguous run of (batch, kv head, tile) work items; nearby
-    // tiles of one kv head share most candidate K/V rows in that XCD's L2.
+    // each XCD a contiguous run of work items; nearby tiles of one kv head
+    // share most candidate K/V rows in that XCD's L2.
+    const int ngroups = (ntiles + tpw - 1) / tpw;
     const int nwg = gridDim.x;
     const int per_xcd = nwg >> 3;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int item = (slot < per_xcd && (nwg & 7) == 0) ? xcd * per_xcd + slot : blockIdx.x;
-    const int tile = item % ntiles;
-    const int g = (item / ntiles) % Hkv;
-    const int b = item / (ntiles * Hkv);
-    const int i0 = tile * Bq;
+    const int grp = item % ngroups;
+    const int g = (item / ngroups) % Hkv;
+    const int b = item / (ngroups * Hkv);
     const int L = seqlens ? seqlens[b] : S;
 
     const int m = wave * 32 + ql;  // stacked (row, head) pair of this lane
     const int r = m / G, hh = m - r * G;
-    const int i = i0 + r;
-    const bool active = (r < Bq) && (i < S);
     const int hq = g * G + hh;
-    uint16_t *orow = O + (((size_t)b * S + (active ? i : 0)) * Hq + hq) * D;
-
-    if (i0 >= L) {  // the whole tile is padding: zero rows
-        if (active) {
-            for (int c = h * (D / 2); c < (h + 1) * (D / 2); c += 8)
-                *reinterpret_cast<uint4 *>(orow + c) = make_uint4(0, 0, 0, 0);
-        }
-        return;
-    }
-
     const size_t urow = ((size_t)b * Hkv + g) * S;
-    const bool live = active && i < L;
-    const int i_last = min(i0 + Bq, L) - 1;
-    const int nrows = i_last - i0 + 1;
-    for (int t = tid; t < nrows; t += kThreads) thr[t] = selkey(tau[urow + i0 + t], (uint32_t)tie[urow + i0 + t]);
-
-    bf16x8 qf[D / 16];
-    if (live) {
-        const uint16_t *qp = Q + (((size_t)b * S + i) * Hq + hq) * D + 8 * h;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qp + 16 * ks);
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = bf16x8{};
-    }
-
-    // thresholds of the first and the last row of the tile
-    const float tau0 = tau[urow + i0], taul = tau[urow + i_last];
-    const int tie0 = tie[urow + i0], tiel = tie[urow + i_last];
     const float *dtrow = dt + urow;
     const uint32_t kvs = (uint32_t)(Hkv * D);
     const uint16_t *Kb = K + (size_t)b * S * kvs + (size_t)g * D;
     const uint16_t *Vb = V + (size_t)b * S * kvs + (size_t)g * D;
 
-    float mrow = -INFINITY, lrow = 0.f;
-    f32x16 oacc[D / 32];
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
+    // the current tile: first and last valid row, and their thresholds
+    int i0 = 0, i_last = 0, nrows = 0;
+    float tau0 = 0.f, taul = 0.f;
+    int tie0 = 0, tiel = 0;
 
     // candidate class of key j: 0 not a candidate, 1 kept by every tile row,
     // 2 kept by some tile rows
@@ -212,246 +188,352 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const int tr_off = (4 * h + (tr_k >> 2)) * T::VP + 16 * ((lane >> 4) & 1) + 4 * (tr_k & 3);
     const uint64_t lt_mask = (1ull << lane) - 1ull;
 
-    int scan = 0;
-    while (scan <= i_last) {
-        // ---- fill pass 1: candidates per (step, wave), loads of kBatchSteps
-        // steps in flight
-        const int nsteps = min((i_last - scan) / kStepKeys + 1, kMaxSteps);
-        for (int s0 = 0; s0 < nsteps; s0 += kBatchSteps) {
-            float dv[kBatchSteps][kFillKeys];
-            load_step_keys(dv, scan, s0, nsteps);
-#pragma unroll
-            for (int bb = 0; bb < kBatchSteps; ++bb) {
-                if (s0 + bb >= nsteps) break;
-                uint32_t nf = 0, np = 0;
-#pragma unroll
-                for (int e = 0; e < kFillKeys; ++e) {
-                    const int c = cls_of(dv[bb][e], scan + (s0 + bb) * kStepKeys + kFillKeys * tid + e);
-                    nf += (uint32_t)__popcll(__ballot(c == 1));
-                    np += (uint32_t)__popcll(__ballot(c == 2));
-                }
-                if (lane == 0) cnt[(s0 + bb) * 4 + wave] = nf | (np << 16);
+    int n = 0, nF = 0;    // candidates in LDS: nF full ones, then the partial ones
+    bool carry = false;   // LDS holds the whole candidate list of the previous tile
+
+    const int t_end = min(ntiles, (grp + 1) * tpw);
+    for (int tile = grp * tpw; tile < t_end; ++tile) {
+        i0 = tile * Bq;
+        const int i = i0 + r;
+        const bool active = (r < Bq) && (i < S);
+        uint16_t *orow = O + (((size_t)b * S + (active ? i : 0)) * Hq + hq) * D;
+        if (i0 >= L) {  // the whole tile is padding (so are the later ones): zero rows
+            if (active) {
+                for (int c = h * (D / 2); c < (h + 1) * (D / 2); c += 8)
+                    *reinterpret_cast<uint4 *>(orow + c) = make_uint4(0, 0, 0, 0);
             }
+            continue;
         }
-        __syncthreads();
-        // ---- exclusive scan over (step, wave) in key order; the steps whose
-        // candidates fit in kCap are used this round
-        if (wave == 0) {
-            const int e0 = 2 * lane, ne = 4 * nsteps;
-            const uint32_t v0 = e0 < ne ? cnt[e0] : 0u, v1 = e0 + 1 < ne ? cnt[e0 + 1] : 0u;
-            uint32_t incl = v0 + v1;
+        const bool live = active && i < L;
+        i_last = min(i0 + Bq, L) - 1;
+        nrows = i_last - i0 + 1;
+        tau0 = tau[urow + i0];
+        taul = tau[urow + i_last];
+        tie0 = tie[urow + i0];
+        tiel = tie[urow + i_last];
+        // (the previous tile's readers of thr have all passed a barrier since)
+        for (int t = tid; t < nrows; t += kThreads) thr[t] = selkey(tau[urow + i0 + t], (uint32_t)tie[urow + i0 + t]);
+
+        float mrow = -INFINITY, lrow = 0.f;
+        f32x16 oacc[D / 32];
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t y = __shfl_up(incl, o, 64);
-                if (lane >= o) incl += y;
-            }
-            if (e0 < ne) cnt[e0] = incl - v0 - v1;
-            if (e0 + 1 < ne) cnt[e0 + 1] = incl - v1;
-            // lane 2s+1 holds the running total through the end of step s
-            const bool fits = (lane & 1) && (lane >> 1) < nsteps && (incl & 0xffffu) + (incl >> 16) <= (uint32_t)kCap;
-            const int used = __popcll(__ballot(fits));  // >= 1: one step never exceeds kCap
-            const uint32_t tot = __shfl(incl, 2 * used - 1, 64);
-            if (lane == 0) {
-                fill_info[0] = used;
-                fill_info[1] = (int)(tot & 0xffffu);
-                fill_info[2] = (int)(tot >> 16);
-            }
-        }
-        __syncthreads();
-        const int used = fill_info[0], nF = fill_info[1], n = nF + fill_info[2];
-        const int pbase = nF / kBK * kBK;           // first block holding a partial key
-        const int npad = (n + kBK - 1) / kBK * kBK;
-        // ---- fill pass 2: write the candidates (full first, partial after)
-        for (int s0 = 0; s0 < used; s0 += kBatchSteps) {
-            float dv[kBatchSteps][kFillKeys];
-            load_step_keys(dv, scan, s0, used);
+        for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
+        bf16x8 qf[D / 16];
+
+        int scan = 0, rounds = 0;
+        while (scan <= i_last) {
+            if (rounds == 0 && carry) {
+                // ---- carried list: by nesting, this tile's candidates are the
+                // previous tile's candidates plus this tile's own keys,
+                // re-classified against this tile's first and last rows
+                int jc[kCarrySlots + 1];
+                float dc[kCarrySlots + 1];
 #pragma unroll
-            for (int bb = 0; bb < kBatchSteps; ++bb) {
-                if (s0 + bb >= used) break;
-                const uint32_t base = cnt[(s0 + bb) * 4 + wave];
-                int of = (int)(base & 0xffffu), op = nF + (int)(base >> 16);
-                const int jb = scan + (s0 + bb) * kStepKeys + kFillKeys * tid;
-                int c[kFillKeys];
-#pragma unroll
-                for (int e = 0; e < kFillKeys; ++e) {
-                    c[e] = cls_of(dv[bb][e], jb + e);
-                    of += (int)__popcll(__ballot(c[e] == 1) & lt_mask);
-                    op += (int)__popcll(__ballot(c[e] == 2) & lt_mask);
+                for (int q = 0; q < kCarrySlots; ++q) {
+                    const int k = tid + q * kThreads;
+                    jc[q] = k < n ? c_idx[k] : -1;
                 }
+                jc[kCarrySlots] = tid < nrows ? i0 + tid : -1;
 #pragma unroll
-                for (int e = 0; e < kFillKeys; ++e) {
-                    const int j = jb + e;
-                    if (c[e] == 1) {
-                        c_idx[of] = j;
-                        c_dtl[of] = dv[bb][e] * kLog2e;
-                        ++of;
-                    } else if (c[e] == 2) {
-                        c_idx[op] = j;
-                        c_dtl[op] = dv[bb][e] * kLog2e;
-                        ++op;
+                for (int q = 0; q <= kCarrySlots; ++q) dc[q] = jc[q] >= 0 ? dtrow[jc[q]] : 0.f;
+                int cc[kCarrySlots + 1];
+#pragma unroll
+                for (int q = 0; q <= kCarrySlots; ++q) {
+                    cc[q] = jc[q] >= 0 ? cls_of(dc[q], jc[q]) : 0;
+                    const uint32_t nf = (uint32_t)__popcll(__ballot(cc[q] == 1));
+                    const uint32_t np = (uint32_t)__popcll(__ballot(cc[q] == 2));
+                    if (lane == 0) cnt[q * 4 + wave] = nf | (np << 16);
+                }
+                __syncthreads();  // counts visible; every read of the old list done
+                if (wave == 0) {
+                    constexpr int ne = 4 * (kCarrySlots + 1);
+                    const uint32_t v = lane < ne ? cnt[lane] : 0u;
+                    uint32_t incl = v;
+#pragma unroll
+                    for (int o = 1; o < 64; o <<= 1) {
+                        const uint32_t y = __shfl_up(incl, o, 64);
+                        if (lane >= o) incl += y;
+                    }
+                    if (lane < ne) cnt[lane] = incl - v;
+                    const uint32_t tot = __shfl(incl, 63, 64);
+                    if (lane == 0) {
+                        fill_info[1] = (int)(tot & 0xffffu);
+                        fill_info[2] = (int)(tot >> 16);
                     }
                 }
-            }
-        }
-        __syncthreads();
-        // row runs of the masked region: a partial key j is kept on the tile
-        // rows [lo, lo + span) (by nesting a run: from its own row, or from
-        // i0, until the first row whose threshold passes it); full keys
-        // sharing a block with partial ones keep every row; slots past the
-        // last candidate keep none
-        for (int k = pbase + tid; k < npad; k += kThreads) {
-            int lo = 0, span = 0;
-            if (k < nF) {
-                span = nrows;
-            } else if (k < n) {
-                const int j = c_idx[k];
-                lo = j > i0 ? j - i0 : 0;
-                span = first_row_above(thr, lo, nrows, selkey(dtrow[j], (uint32_t)j)) - lo;
+                __syncthreads();
+                nF = fill_info[1];
+                n = nF + fill_info[2];
+#pragma unroll
+                for (int q = 0; q <= kCarrySlots; ++q) {
+                    const uint32_t base = cnt[q * 4 + wave];
+                    const int of = (int)(base & 0xffffu) + (int)__popcll(__ballot(cc[q] == 1) & lt_mask);
+                    const int op = nF + (int)(base >> 16) + (int)__popcll(__ballot(cc[q] == 2) & lt_mask);
+                    if (cc[q] == 1) {
+                        c_idx[of] = jc[q];
+                        c_dtl[of] = dc[q] * kLog2e;
+                    } else if (cc[q] == 2) {
+                        c_idx[op] = jc[q];
+                        c_dtl[op] = dc[q] * kLog2e;
+                    }
+                }
+                scan = i_last + 1;
             } else {
-                c_dtl[k] = 0.f;
+            // ---- fill pass 1: candidates per (step, wave), loads of kBatchSteps
+            // steps in flight
+            const int nsteps = min((i_last - scan) / kStepKeys + 1, kMaxSteps);
+            for (int s0 = 0; s0 < nsteps; s0 += kBatchSteps) {
+                float dv[kBatchSteps][kFillKeys];
+                load_step_keys(dv, scan, s0, nsteps);
+    #pragma unroll
+                for (int bb = 0; bb < kBatchSteps; ++bb) {
+                    if (s0 + bb >= nsteps) break;
+                    uint32_t nf = 0, np = 0;
+    #pragma unroll
+                    for (int e = 0; e < kFillKeys; ++e) {
+                        const int c = cls_of(dv[bb][e], scan + (s0 + bb) * kStepKeys + kFillKeys * tid + e);
+                        nf += (uint32_t)__popcll(__ballot(c == 1));
+                        np += (uint32_t)__popcll(__ballot(c == 2));
+                    }
+                    if (lane == 0) cnt[(s0 + bb) * 4 + wave] = nf | (np << 16);
+                }
             }
-            c_lo[k - pbase] = lo;
-            c_span[k - pbase] = span;
-        }
-        scan += used * kStepKeys;
-        __syncthreads();
-
-        // ---- attend over the candidates, 64 keys at a time
-        if (n > 0) load_block(0, n);
-        for (int blk = 0; blk < n; blk += kBK) {
-            store_block();
             __syncthreads();
-            if (blk + kBK < n) load_block(blk + kBK, n);  // in flight during the math below
-
-            // S^T = K Q^T for two 32-key halves of the block; the K fragments
-            // of step ks+1 are read while step ks multiplies
-            f32x16 sacc[2] = {f32x16{}, f32x16{}};
-            const uint16_t *kp0 = &Ks[ql * T::KP + 8 * h];
-            const uint16_t *kp1 = &Ks[(32 + ql) * T::KP + 8 * h];
-            bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kp0);
-            bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(kp1);
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                bf16x8 n0 = a0, n1 = a1;
-                if (ks + 1 < D / 16) {
-                    n0 = *reinterpret_cast<const bf16x8 *>(kp0 + 16 * (ks + 1));
-                    n1 = *reinterpret_cast<const bf16x8 *>(kp1 + 16 * (ks + 1));
+            // ---- exclusive scan over (step, wave) in key order; the steps whose
+            // candidates fit in kCap are used this round
+            if (wave == 0) {
+                const int e0 = 2 * lane, ne = 4 * nsteps;
+                const uint32_t v0 = e0 < ne ? cnt[e0] : 0u, v1 = e0 + 1 < ne ? cnt[e0 + 1] : 0u;
+                uint32_t incl = v0 + v1;
+    #pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t y = __shfl_up(incl, o, 64);
+                    if (lane >= o) incl += y;
                 }
-                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], sacc[0], 0, 0, 0);
-                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], sacc[1], 0, 0, 0);
-                a0 = n0;
-                a1 = n1;
+                if (e0 < ne) cnt[e0] = incl - v0 - v1;
+                if (e0 + 1 < ne) cnt[e0 + 1] = incl - v1;
+                // lane 2s+1 holds the running total through the end of step s
+                const bool fits = (lane & 1) && (lane >> 1) < nsteps && (incl & 0xffffu) + (incl >> 16) <= (uint32_t)kCap;
+                const int used = __popcll(__ballot(fits));  // >= 1: one step never exceeds kCap
+                const uint32_t tot = __shfl(incl, 2 * used - 1, 64);
+                if (lane == 0) {
+                    fill_info[0] = used;
+                    fill_info[1] = (int)(tot & 0xffffu);
+                    fill_info[2] = (int)(tot >> 16);
+                }
             }
-
-            // dt bias (and, where partial keys are, the row-run test), then
-            // the online softmax in base 2
-            float z[2][16];
-            float mloc = -INFINITY;
-            if (blk < pbase) {
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const int pos = blk + 32 * kt + 8 * r4 + 4 * h;
-                        const float4 dl4 = *reinterpret_cast<const float4 *>(&c_dtl[pos]);
-                        const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float zz = fmaf(sacc[kt][4 * r4 + e], qscale, dls[e]);
-                            z[kt][4 * r4 + e] = zz;
-                            mloc = fmaxf(mloc, zz);
-                        }
+            __syncthreads();
+                const int used = fill_info[0];
+                nF = fill_info[1];
+                n = nF + fill_info[2];
+            // ---- fill pass 2: write the candidates (full first, partial after)
+            for (int s0 = 0; s0 < used; s0 += kBatchSteps) {
+                float dv[kBatchSteps][kFillKeys];
+                load_step_keys(dv, scan, s0, used);
+    #pragma unroll
+                for (int bb = 0; bb < kBatchSteps; ++bb) {
+                    if (s0 + bb >= used) break;
+                    const uint32_t base = cnt[(s0 + bb) * 4 + wave];
+                    int of = (int)(base & 0xffffu), op = nF + (int)(base >> 16);
+                    const int jb = scan + (s0 + bb) * kStepKeys + kFillKeys * tid;
+                    int c[kFillKeys];
+    #pragma unroll
+                    for (int e = 0; e < kFillKeys; ++e) {
+                        c[e] = cls_of(dv[bb][e], jb + e);
+                        of += (int)__popcll(__ballot(c[e] == 1) & lt_mask);
+                        op += (int)__popcll(__ballot(c[e] == 2) & lt_mask);
                     }
-                }
-            } else {
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const int pos = blk + 32 * kt + 8 * r4 + 4 * h;
-                        const int4 lo4 = *reinterpret_cast<const int4 *>(&c_lo[pos - pbase]);
-                        const int4 sp4 = *reinterpret_cast<const int4 *>(&c_span[pos - pbase]);
-                        const float4 dl4 = *reinterpret_cast<const float4 *>(&c_dtl[pos]);
-                        const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
-                        const int sps[4] = {sp4.x, sp4.y, sp4.z, sp4.w};
-                        const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const bool ok = (unsigned)(r - los[e]) < (unsigned)sps[e];
-                            const float zz = fmaf(sacc[kt][4 * r4 + e], qscale, ok ? dls[e] : -INFINITY);
-                            z[kt][4 * r4 + e] = zz;
-                            mloc = fmaxf(mloc, zz);
+    #pragma unroll
+                    for (int e = 0; e < kFillKeys; ++e) {
+                        const int j = jb + e;
+                        if (c[e] == 1) {
+                            c_idx[of] = j;
+                            c_dtl[of] = dv[bb][e] * kLog2e;
+                            ++of;
+                        } else if (c[e] == 2) {
+                            c_idx[op] = j;
+                            c_dtl[op] = dv[bb][e] * kLog2e;
+                            ++op;
                         }
                     }
                 }
             }
-            // Lazy rescale: the running max only moves when a block raises it
-            // by more than 8 (base 2), so p stays <= 256 and most blocks skip
-            // the O rescale.  The final normalisation uses the same max, so
-            // the result is the softmax whatever max was used.
-            const float mblk = half_swap_max(mloc);
-            const bool upd = mblk > mrow + 8.f;
-            if (__any(upd)) {
-                const float mnew = upd ? mblk : mrow;
-                const float alpha = upd ? __builtin_amdgcn_exp2f(mrow - mnew) : 1.f;
-                mrow = mnew;
-                lrow *= alpha;
-#pragma unroll
-                for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
+                scan += used * kStepKeys;
             }
-            const float msub = (mrow == -INFINITY) ? 0.f : mrow;
+            ++rounds;
+            if (rounds == 1) {  // Q of the tile, loaded while the row runs are found
+                if (live) {
+                    const uint16_t *qp = Q + (((size_t)b * S + i) * Hq + hq) * D + 8 * h;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+                    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qp + 16 * ks);
+                } else {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) z[kt][e] = __builtin_amdgcn_exp2f(z[kt][e] - msub);
-            }
-
-            // O^T += V^T P^T.  PV call c covers keys 16c..16c+15; lane half h
-            // holds, in k-slots 0..7, keys 16c + 8*(j/4) + 4h + j%4, which are
-            // exactly its score registers z[c/2][8*(c%2) + j].  The V^T operand
-            // comes from two transpose reads (rows 16c + 4h + {0..3} and
-            // 16c + 8 + 4h + {0..3}).  The softmax denominator sums the same
-            // bf16-rounded weights that multiply V, so that the rounding of P
-            // perturbs the weights of a normalised average (an output
-            // dominated by one key keeps that key's value).
-            float psum = 0.f;
-            const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                bf16x8 pb;
-#pragma unroll
-                for (int jx = 0; jx < 8; ++jx) pb[jx] = (__bf16)z[c >> 1][8 * (c & 1) + jx];
-                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), one2, psum, false);
-                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one2, psum, false);
-                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one2, psum, false);
-                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), one2, psum, false);
-#pragma unroll
-                for (int t = 0; t < D / 32; ++t) {
-                    const uint16_t *vp = &Vs[16 * c * T::VP + 32 * t + tr_off];
-                    const i16x4 lo = lds_read_tr16(vp);
-                    const i16x4 hi = lds_read_tr16(vp + 8 * T::VP);
-                    const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, oacc[t], 0, 0, 0);
+                    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = bf16x8{};
                 }
             }
-            lrow += psum;
-            __syncthreads();  // LDS tiles are rewritten next
+            const int pbase = nF / kBK * kBK;           // first block holding a partial key
+            const int npad = (n + kBK - 1) / kBK * kBK;
+            __syncthreads();
+            // row runs of the masked region: a partial key j is kept on the tile
+            // rows [lo, lo + span) (by nesting a run: from its own row, or from
+            // i0, until the first row whose threshold passes it); full keys
+            // sharing a block with partial ones keep every row; slots past the
+            // last candidate keep none
+            for (int k = pbase + tid; k < npad; k += kThreads) {
+                int lo = 0, span = 0;
+                if (k < nF) {
+                    span = nrows;
+                } else if (k < n) {
+                    const int j = c_idx[k];
+                    lo = j > i0 ? j - i0 : 0;
+                    span = first_row_above(thr, lo, nrows, selkey(dtrow[j], (uint32_t)j)) - lo;
+                } else {
+                    c_dtl[k] = 0.f;
+                }
+                c_lo[k - pbase] = lo;
+                c_span[k - pbase] = span;
+            }
+            __syncthreads();
+
+            // ---- attend over the candidates, 64 keys at a time
+            if (n > 0) load_block(0, n);
+            for (int blk = 0; blk < n; blk += kBK) {
+                store_block();
+                __syncthreads();
+                if (blk + kBK < n) load_block(blk + kBK, n);  // in flight during the math below
+
+                // S^T = K Q^T for two 32-key halves of the block; the K fragments
+                // of step ks+1 are read while step ks multiplies
+                f32x16 sacc[2] = {f32x16{}, f32x16{}};
+                const uint16_t *kp0 = &Ks[ql * T::KP + 8 * h];
+                const uint16_t *kp1 = &Ks[(32 + ql) * T::KP + 8 * h];
+                bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kp0);
+                bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(kp1);
+    #pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    bf16x8 n0 = a0, n1 = a1;
+                    if (ks + 1 < D / 16) {
+                        n0 = *reinterpret_cast<const bf16x8 *>(kp0 + 16 * (ks + 1));
+                        n1 = *reinterpret_cast<const bf16x8 *>(kp1 + 16 * (ks + 1));
+                    }
+                    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], sacc[0], 0, 0, 0);
+                    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], sacc[1], 0, 0, 0);
+                    a0 = n0;
+                    a1 = n1;
+                }
+
+                // dt bias (and, where partial keys are, the row-run test), then
+                // the online softmax in base 2
+                float z[2][16];
+                float mloc = -INFINITY;
+                if (blk < pbase) {
+    #pragma unroll
+                    for (int kt = 0; kt < 2; ++kt) {
+    #pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const int pos = blk + 32 * kt + 8 * r4 + 4 * h;
+                            const float4 dl4 = *reinterpret_cast<const float4 *>(&c_dtl[pos]);
+                            const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float zz = fmaf(sacc[kt][4 * r4 + e], qscale, dls[e]);
+                                z[kt][4 * r4 + e] = zz;
+                                mloc = fmaxf(mloc, zz);
+                            }
+                        }
+                    }
+                } else {
+    #pragma unroll
+                    for (int kt = 0; kt < 2; ++kt) {
+    #pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const int pos = blk + 32 * kt + 8 * r4 + 4 * h;
+                            const int4 lo4 = *reinterpret_cast<const int4 *>(&c_lo[pos - pbase]);
+                            const int4 sp4 = *reinterpret_cast<const int4 *>(&c_span[pos - pbase]);
+                            const float4 dl4 = *reinterpret_cast<const float4 *>(&c_dtl[pos]);
+                            const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
+                            const int sps[4] = {sp4.x, sp4.y, sp4.z, sp4.w};
+                            const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const bool ok = (unsigned)(r - los[e]) < (unsigned)sps[e];
+                                const float zz = fmaf(sacc[kt][4 * r4 + e], qscale, ok ? dls[e] : -INFINITY);
+                                z[kt][4 * r4 + e] = zz;
+                                mloc = fmaxf(mloc, zz);
+                            }
+                        }
+                    }
+                }
+                // Lazy rescale: the running max only moves when a block raises it
+                // by more than 8 (base 2), so p stays <= 256 and most blocks skip
+                // the O rescale.  The final normalisation uses the same max, so
+                // the result is the softmax whatever max was used.
+                const float mblk = half_swap_max(mloc);
+                const bool upd = mblk > mrow + 8.f;
+                if (__any(upd)) {
+                    const float mnew = upd ? mblk : mrow;
+                    const float alpha = upd ? __builtin_amdgcn_exp2f(mrow - mnew) : 1.f;
+                    mrow = mnew;
+                    lrow *= alpha;
+    #pragma unroll
+                    for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
+                }
+                const float msub = (mrow == -INFINITY) ? 0.f : mrow;
+    #pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+    #pragma unroll
+                    for (int e = 0; e < 16; ++e) z[kt][e] = __builtin_amdgcn_exp2f(z[kt][e] - msub);
+                }
+
+                // O^T += V^T P^T.  PV call c covers keys 16c..16c+15; lane half h
+                // holds, in k-slots 0..7, keys 16c + 8*(j/4) + 4h + j%4, which are
+                // exactly its score registers z[c/2][8*(c%2) + j].  The V^T operand
+                // comes from two transpose reads (rows 16c + 4h + {0..3} and
+                // 16c + 8 + 4h + {0..3}).  The softmax denominator sums the same
+                // bf16-rounded weights that multiply V, so that the rounding of P
+                // perturbs the weights of a normalised average (an output
+                // dominated by one key keeps that key's value).
+                float psum = 0.f;
+                const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    #pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    bf16x8 pb;
+    #pragma unroll
+                    for (int jx = 0; jx < 8; ++jx) pb[jx] = (__bf16)z[c >> 1][8 * (c & 1) + jx];
+                    psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), one2, psum, false);
+                    psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one2, psum, false);
+                    psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one2, psum, false);
+                    psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), one2, psum, false);
+    #pragma unroll
+                    for (int t = 0; t < D / 32; ++t) {
+                        const uint16_t *vp = &Vs[16 * c * T::VP + 32 * t + tr_off];
+                        const i16x4 lo = lds_read_tr16(vp);
+                        const i16x4 hi = lds_read_tr16(vp + 8 * T::VP);
+                        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, oacc[t], 0, 0, 0);
+                    }
+                }
+                lrow += psum;
+                __syncthreads();  // LDS tiles are rewritten next
+            }
         }
-    }
 
-    const float ltot = half_swap_sum(lrow);
-    const float inv = (live && ltot > 0.f) ? 1.f / ltot : 0.f;
-    if (active) {
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int col = 32 * t + 8 * r4 + 4 * h;
-                const uint32_t w0 = (uint32_t)f32_to_bf16(oacc[t][4 * r4 + 0] * inv) |
-                                    ((uint32_t)f32_to_bf16(oacc[t][4 * r4 + 1] * inv) << 16);
-                const uint32_t w1 = (uint32_t)f32_to_bf16(oacc[t][4 * r4 + 2] * inv) |
-                                    ((uint32_t)f32_to_bf16(oacc[t][4 * r4 + 3] * inv) << 16);
-                *reinterpret_cast<uint2 *>(orow + col) = make_uint2(w0, w1);
+        carry = rounds == 1 && n + Bq <= kCap;
+
+        const float ltot = half_swap_sum(lrow);
+        const float inv = (live && ltot > 0.f) ? 1.f / ltot : 0.f;
+        if (active) {
+    #pragma unroll
+            for (int t = 0; t < D / 32; ++t) {
+    #pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int col = 32 * t + 8 * r4 + 4 * h;
+                    const uint32_t w0 = (uint32_t)f32_to_bf16(oacc[t][4 * r4 + 0] * inv) |
+                                        ((uint32_t)f32_to_bf16(oacc[t][4 * r4 + 1] * inv) << 16);
+                    const uint32_t w1 = (uint32_t)f32_to_bf16(oacc[t][4 * r4 + 2] * inv) |
+                                        ((uint32_t)f32_to_bf16(oacc[t][4 * r4 + 3] * inv) << 16);
+                    *reinterpret_cast<uint2 *>(orow + col) = make_uint2(w0, w1);
+                }
             }
         }
     }
@@ -533,17 +615,22 @@ hipError_t launch_attn(const void *Q, const void *K, const void *V, int dtype, c
         const int G = Hq / Hkv;
         const int Bq = kRowsPerWG / G;
         const int ntiles = (S + Bq - 1) / Bq;
-        const int64_t items = (int64_t)ntiles * Hkv * B;
+        // consecutive tiles per workgroup: enough work items to fill the chip
+        // about four times over, and the prefix scan of a tile's first
+        // candidate list amortised over the rest of its group
+        const int64_t total = (int64_t)ntiles * Hkv * B;
+        const int tpw = (int)std::max<int64_t>(1, std::min<int64_t>(total / kTargetItems, ntiles));
+        const int64_t items = (int64_t)((ntiles + tpw - 1) / tpw) * Hkv * B;
         if (items > 0x7fffffff) return hipErrorInvalidValue;
         const dim3 grid((unsigned)items);
         if (d == 128)
             hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(kThreads), 0, stream,
                                (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau,
-                               tie, seqlens, S, Hq, Hkv, G, Bq, ntiles, (uint16_t *)O, qscale);
+                               tie, seqlens, S, Hq, Hkv, G, Bq, ntiles, tpw, (uint16_t *)O, qscale);
         else
             hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(kThreads), 0, stream,
                                (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau,
-                               tie, seqlens, S, Hq, Hkv, G, Bq, ntiles, (uint16_t *)O, qscale);
+                               tie, seqlens, S, Hq, Hkv, G, Bq, ntiles, tpw, (uint16_t *)O, qscale);
     } else {
         const int64_t waves = (int64_t)B * Hq * S;
         const int64_t blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);

@@ -231,6 +231,29 @@ def test_attn_long_rows_sampled(dma, oracle_mod, S, w, Hq, Hkv, d):
         assert np.abs(got - ref[n]).max() <= TOL["bf16"], (g, i)
 
 
+@pytest.mark.parametrize("B,S,Hq,Hkv,d,w,kind,padded", [
+    (2, 4096, 32, 16, 64, 300, "lognormal", True),   # two tiles per workgroup, carried lists
+    (4, 4096, 32, 16, 128, 700, "dyadic", False),    # four tiles per workgroup, ties
+    (2, 8192, 16, 16, 64, 2500, "few", True),        # lists too long to carry: rescans
+])
+def test_attn_multi_tile_sampled(dma, oracle_mod, B, S, Hq, Hkv, d, w, kind, padded):
+    Q, K, V = si.make_qkv(B, S, Hq, Hkv, d, "bf16", seed=S + w + d)
+    dt = si.make_dt((B, Hkv, S), kind, seed=S + w + d + 1)
+    seq = si.make_lengths(B, S // 2, S, seed=S + w + d + 2) if padded else None
+    dts = to_dev(dt)
+    tau, tie = dma.select(dts, w, to_dev(seq))
+    O = to_host(dma.attn_fwd(to_dev(Q), to_dev(K), to_dev(V), dts, tau, tie, w, to_dev(seq)))
+    rows = sample_rows(B, Hkv, S, seq, 400, seed=S + w, w=w)
+    ref = oracle_mod.attn(Q, K, V, dt, w, seqlens=seq, rows=rows)
+    G = Hq // Hkv
+    for n, (b, g, i) in enumerate(rows):
+        got = O[b, i, g * G:(g + 1) * G].astype(np.float64)
+        assert np.abs(got - ref[n]).max() <= TOL["bf16"], (b, g, i)
+    if seq is not None:
+        for b in range(B):
+            assert (O[b, seq[b]:] == 0).all()
+
+
 def test_attn_deterministic_and_gqa_equals_mha(dma, oracle_mod):
     B, S, Hq, Hkv, d, w = 1, 700, 8, 2, 128, 150
     Q, K, V = si.make_qkv(B, S, Hq, Hkv, d, "bf16", seed=31)
