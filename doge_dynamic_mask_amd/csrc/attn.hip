@@ -282,14 +282,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
             // ---- fill pass 1: candidates per (step, wave), loads of kBatchSteps
             // steps in flight
             const int nsteps = min((i_last - scan) / kStepKeys + 1, kMaxSteps);
+            // with d = 64 the keys of a round of at most kBatchSteps steps stay
+            // in registers for pass 2 (with d = 128 there is no room for them)
+            constexpr bool kKeepKeys = D <= 64;
+            float dv[kBatchSteps][kFillKeys];
             for (int s0 = 0; s0 < nsteps; s0 += kBatchSteps) {
-                float dv[kBatchSteps][kFillKeys];
                 load_step_keys(dv, scan, s0, nsteps);
-    #pragma unroll
+#pragma unroll
                 for (int bb = 0; bb < kBatchSteps; ++bb) {
                     if (s0 + bb >= nsteps) break;
                     uint32_t nf = 0, np = 0;
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < kFillKeys; ++e) {
                         const int c = cls_of(dv[bb][e], scan + (s0 + bb) * kStepKeys + kFillKeys * tid + e);
                         nf += (uint32_t)__popcll(__ballot(c == 1));
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 const int e0 = 2 * lane, ne = 4 * nsteps;
                 const uint32_t v0 = e0 < ne ? cnt[e0] : 0u, v1 = e0 + 1 < ne ? cnt[e0 + 1] : 0u;
                 uint32_t incl = v0 + v1;
-    #pragma unroll
+#pragma unroll
                 for (int o = 1; o < 64; o <<= 1) {
                     const uint32_t y = __shfl_up(incl, o, 64);
                     if (lane >= o) incl += y;
@@ -328,22 +331,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 n = nF + fill_info[2];
             // ---- fill pass 2: write the candidates (full first, partial after)
             for (int s0 = 0; s0 < used; s0 += kBatchSteps) {
-                float dv[kBatchSteps][kFillKeys];
-                load_step_keys(dv, scan, s0, used);
-    #pragma unroll
+                if (!kKeepKeys || nsteps > kBatchSteps) load_step_keys(dv, scan, s0, used);
+#pragma unroll
                 for (int bb = 0; bb < kBatchSteps; ++bb) {
                     if (s0 + bb >= used) break;
                     const uint32_t base = cnt[(s0 + bb) * 4 + wave];
                     int of = (int)(base & 0xffffu), op = nF + (int)(base >> 16);
                     const int jb = scan + (s0 + bb) * kStepKeys + kFillKeys * tid;
                     int c[kFillKeys];
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < kFillKeys; ++e) {
                         c[e] = cls_of(dv[bb][e], jb + e);
                         of += (int)__popcll(__ballot(c[e] == 1) & lt_mask);
                         op += (int)__popcll(__ballot(c[e] == 2) & lt_mask);
                     }
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < kFillKeys; ++e) {
                         const int j = jb + e;
                         if (c[e] == 1) {
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 const uint16_t *kp1 = &Ks[(32 + ql) * T::KP + 8 * h];
                 bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kp0);
                 bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(kp1);
-    #pragma unroll
+#pragma unroll
                 for (int ks = 0; ks < D / 16; ++ks) {
                     bf16x8 n0 = a0, n1 = a1;
                     if (ks + 1 < D / 16) {
@@ -427,14 +429,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 float z[2][16];
                 float mloc = -INFINITY;
                 if (blk < pbase) {
-    #pragma unroll
+#pragma unroll
                     for (int kt = 0; kt < 2; ++kt) {
-    #pragma unroll
+#pragma unroll
                         for (int r4 = 0; r4 < 4; ++r4) {
                             const int pos = blk + 32 * kt + 8 * r4 + 4 * h;
                             const float4 dl4 = *reinterpret_cast<const float4 *>(&c_dtl[pos]);
                             const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
-    #pragma unroll
+#pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const float zz = fmaf(sacc[kt][4 * r4 + e], qscale, dls[e]);
                                 z[kt][4 * r4 + e] = zz;
@@ -443,9 +445,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                         }
                     }
                 } else {
-    #pragma unroll
+#pragma unroll
                     for (int kt = 0; kt < 2; ++kt) {
-    #pragma unroll
+#pragma unroll
                         for (int r4 = 0; r4 < 4; ++r4) {
                             const int pos = blk + 32 * kt + 8 * r4 + 4 * h;
                             const int4 lo4 = *reinterpret_cast<const int4 *>(&c_lo[pos - pbase]);
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                             const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
                             const int sps[4] = {sp4.x, sp4.y, sp4.z, sp4.w};
                             const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
-    #pragma unroll
+#pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const bool ok = (unsigned)(r - los[e]) < (unsigned)sps[e];
                                 const float zz = fmaf(sacc[kt][4 * r4 + e], qscale, ok ? dls[e] : -INFINITY);
@@ -475,13 +477,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                     const float alpha = upd ? __builtin_amdgcn_exp2f(mrow - mnew) : 1.f;
                     mrow = mnew;
                     lrow *= alpha;
-    #pragma unroll
+#pragma unroll
                     for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
                 }
                 const float msub = (mrow == -INFINITY) ? 0.f : mrow;
-    #pragma unroll
+#pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < 16; ++e) z[kt][e] = __builtin_amdgcn_exp2f(z[kt][e] - msub);
                 }
 
@@ -495,16 +497,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 // dominated by one key keeps that key's value).
                 float psum = 0.f;
                 const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-    #pragma unroll
+#pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     bf16x8 pb;
-    #pragma unroll
+#pragma unroll
                     for (int jx = 0; jx < 8; ++jx) pb[jx] = (__bf16)z[c >> 1][8 * (c & 1) + jx];
                     psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), one2, psum, false);
                     psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one2, psum, false);
                     psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one2, psum, false);
                     psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), one2, psum, false);
-    #pragma unroll
+#pragma unroll
                     for (int t = 0; t < D / 32; ++t) {
                         const uint16_t *vp = &Vs[16 * c * T::VP + 32 * t + tr_off];
                         const i16x4 lo = lds_read_tr16(vp);
@@ -523,9 +525,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         const float ltot = half_swap_sum(lrow);
         const float inv = (live && ltot > 0.f) ? 1.f / ltot : 0.f;
         if (active) {
-    #pragma unroll
+#pragma unroll
             for (int t = 0; t < D / 32; ++t) {
-    #pragma unroll
+#pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
                     const int col = 32 * t + 8 * r4 + 4 * h;
                     const uint32_t w0 = (uint32_t)f32_to_bf16(oacc[t][4 * r4 + 0] * inv) |

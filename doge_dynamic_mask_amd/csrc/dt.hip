@@ -128,6 +128,33 @@ __global__ __launch_bounds__(kMfmaThreads) void dt_mfma_kernel(
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float As[kMaxHkvDt], bs[kMaxHkvDt];
     uint16_t *Ws = reinterpret_cast<uint16_t *>(smem);  // [Hkv][pitch]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int mr = lane & 15, kg = lane >> 4;
+    const int nchunk = (width + kChunk - 1) / kChunk;
+    const bool head_ok = mr < Hkv;
+    const int64_t ntiles = (ntok + 15) / 16;
+    const int64_t stride = (int64_t)gridDim.x * (kMfmaThreads / 64);
+
+    // this lane's 16-byte vectors of chunks c0 .. c0 + kChunksPerBatch - 1 of
+    // its token row (zeros past the row or the last token)
+    uint4 va[kChunksPerBatch][4];
+    auto load_batch = [&](int64_t tile, int c0) __attribute__((always_inline)) {
+        const int64_t t = tile * 16 + mr;
+        const bool tok_ok = t < ntok;
+        const uint16_t *vrow = V + (tok_ok ? t : 0) * (int64_t)width;
+#pragma unroll
+        for (int cc = 0; cc < kChunksPerBatch; ++cc) {
+            const int base = (c0 + cc) * kChunk + 32 * kg;
+            const bool ok = tok_ok && base < width;
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                va[cc][st] = ok ? *reinterpret_cast<const uint4 *>(vrow + base + 8 * st) : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    // the first rows are requested before W is staged, so both latencies overlap
+    int64_t tile = (int64_t)blockIdx.x * (kMfmaThreads / 64) + wave;
+    if (tile < ntiles) load_batch(tile, 0);
     const int rv = width / 8;     // 16-byte vectors per W row
     for (int v = threadIdx.x; v < Hkv * rv; v += kMfmaThreads) {
         const int hh = v / rv, c = v - hh * rv;
@@ -139,27 +166,10 @@ __global__ __launch_bounds__(kMfmaThreads) void dt_mfma_kernel(
     }
     __syncthreads();
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int mr = lane & 15, kg = lane >> 4;
-    const int nchunk = (width + kChunk - 1) / kChunk;
-    const bool head_ok = mr < Hkv;
-    const int64_t ntiles = (ntok + 15) / 16;
-    for (int64_t tile = (int64_t)blockIdx.x * (kMfmaThreads / 64) + wave; tile < ntiles;
-         tile += (int64_t)gridDim.x * (kMfmaThreads / 64)) {
-        const int64_t t = tile * 16 + mr;
-        const bool tok_ok = t < ntok;
-        const uint16_t *vrow = V + (tok_ok ? t : 0) * (int64_t)width;
+    for (; tile < ntiles; tile += stride) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int c0 = 0; c0 < nchunk; c0 += kChunksPerBatch) {
-            uint4 va[kChunksPerBatch][4];
-#pragma unroll
-            for (int cc = 0; cc < kChunksPerBatch; ++cc) {
-                const int base = (c0 + cc) * kChunk + 32 * kg;
-                const bool ok = tok_ok && base < width;
-#pragma unroll
-                for (int st = 0; st < 4; ++st)
-                    va[cc][st] = ok ? *reinterpret_cast<const uint4 *>(vrow + base + 8 * st) : make_uint4(0, 0, 0, 0);
-            }
+            if (c0 > 0) load_batch(tile, c0);  // the first batch is already in flight
 #pragma unroll
             for (int cc = 0; cc < kChunksPerBatch; ++cc) {
                 const int base = (c0 + cc) * kChunk + 32 * kg;
@@ -172,6 +182,7 @@ __global__ __launch_bounds__(kMfmaThreads) void dt_mfma_kernel(
                 }
             }
         }
+        if (tile + stride < ntiles) load_batch(tile + stride, 0);  // next tile's rows in flight
         if (head_ok) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

@@ -16,7 +16,8 @@
 // One workgroup per (batch, kv head, chunk of C rows), C = 64 for rows up to
 // 4096 and 128 beyond:
 //   a. finds the band: min/max of the prefix keys, one histogram pass with
-//      4096 bins spanning that range, the bins holding ranks A0 and w-1, and
+//      1024 (short rows) or 4096 bins spanning that range, the bins holding
+//      ranks A0 and w-1, and
 //      an exact rank of the keys gathered from those bins (a multi-pass radix
 //      select over the prefix when those bins hold too many keys, e.g. under
 //      heavy ties);
@@ -33,15 +34,14 @@ namespace dma {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBins = 4096;
 constexpr int kCollectCap = 512;    // boundary-bin keys ranked exactly in LDS
 constexpr int kUnroll = 16;         // prefix keys per thread per pass step (loads in flight)
 constexpr int kStage = 8192;        // prefixes up to this many keys are kept in LDS
 
-template <int C>
+template <int C, int NB>
 struct SelectShared {
     RadixShared<kThreads> rs;       // fallback radix select
-    uint32_t hist[kBins];
+    uint32_t hist[NB];
     uint64_t col[kCollectCap];
     uint64_t cand[2 * C + 1];       // band (by rank) then the chunk's own keys
     uint32_t red[2][kThreads / 64];
@@ -75,15 +75,15 @@ __device__ __forceinline__ void for_staged(const uint32_t *keys, int P, F f) {
     for (int j = threadIdx.x; j < P; j += kThreads) f(j, keys[j]);
 }
 
-// C: rows per chunk (the band holds C+1 prefix keys)
-template <int C>
+// C: rows per chunk (the band holds C+1 prefix keys); NB: histogram bins
+template <int C, int NB>
 __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restrict__ dt,
                                                           const int32_t *__restrict__ seqlens,
                                                           int Hkv, int S, int w,
                                                           float *__restrict__ tau,
                                                           int32_t *__restrict__ tie) {
     constexpr int kChunk = C;
-    __shared__ SelectShared<C> sh;
+    __shared__ SelectShared<C, NB> sh;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = blockIdx.y, b = blockIdx.z;
     const int r0 = blockIdx.x * kChunk;
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
             sh.red[0][wave] = kmin;
             sh.red[1][wave] = kmax;
         }
-        for (int x = tid; x < kBins; x += kThreads) sh.hist[x] = 0u;
+        for (int x = tid; x < NB; x += kThreads) sh.hist[x] = 0u;
         if (tid == 0) {
             sh.ncol = 0u;
             sh.nfound = 0u;
@@ -144,7 +144,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
         }
         const uint32_t range = kmax - kmin;
         const int bw = range == 0u ? 0 : 32 - __clz(range);
-        const int shift = bw > 12 ? bw - 12 : 0;
+        constexpr int kLogBins = __builtin_ctz(NB);
+        const int shift = bw > kLogBins ? bw - kLogBins : 0;
         // ---- a2: histogram, then the bins of ranks A0 and w-1 (descending)
         if (staged)
             for_staged(sh.keys, P, [&](int, uint32_t k) { atomicAdd(&sh.hist[(k - kmin) >> shift], 1u); });
@@ -152,11 +153,11 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
             for_prefix(row, P, [&](int, float x) { atomicAdd(&sh.hist[(ordkey(x) - kmin) >> shift], 1u); });
         __syncthreads();
         {
-            constexpr int PER = kBins / kThreads;  // 16 bins per thread, descending
+            constexpr int PER = NB / kThreads;  // bins per thread, descending
             uint32_t c[PER], s = 0;
 #pragma unroll
             for (int q = 0; q < PER; ++q) {
-                c[q] = sh.hist[kBins - 1 - (PER * tid + q)];
+                c[q] = sh.hist[NB - 1 - (PER * tid + q)];
                 s += c[q];
             }
             uint32_t incl = s;
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
             uint32_t run = excl;
 #pragma unroll
             for (int q = 0; q < PER; ++q) {
-                const uint32_t bin = (uint32_t)(kBins - 1 - (PER * tid + q));
+                const uint32_t bin = (uint32_t)(NB - 1 - (PER * tid + q));
                 if (run <= rankA && rankA < run + c[q]) {
                     sh.binA = bin;
                     sh.aboveA = run;
@@ -294,11 +295,11 @@ hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv
     // short rows: more, smaller chunks; long rows: half the prefix passes
     if (S <= 4096) {
         const dim3 grid((S + 63) / 64, Hkv, B);
-        hipLaunchKernelGGL(select_kernel<64>, grid, dim3(kThreads), 0, stream, dt, seqlens, Hkv, S, w,
+        hipLaunchKernelGGL((select_kernel<64, 1024>), grid, dim3(kThreads), 0, stream, dt, seqlens, Hkv, S, w,
                            tau, tie);
     } else {
         const dim3 grid((S + 127) / 128, Hkv, B);
-        hipLaunchKernelGGL(select_kernel<128>, grid, dim3(kThreads), 0, stream, dt, seqlens, Hkv, S, w,
+        hipLaunchKernelGGL((select_kernel<128, 4096>), grid, dim3(kThreads), 0, stream, dt, seqlens, Hkv, S, w,
                            tau, tie);
     }
     return hipGetLastError();
