@@ -5,19 +5,20 @@
 //
 // Three launches on the caller's stream:
 //  1. select: one workgroup per (batch, kv head) finds the w-th best cached
-//     position exactly (order: dt desc, index asc) and writes the kept
-//     positions in ascending order (plus their dt) to the workspace, and to
-//     kept_idx when asked.  Rows of up to 32768 positions are held in
-//     registers (1024 threads, each owning consecutive positions) and resolved
-//     with a range-adapted 4096-bin histogram plus an exact rank of the few
-//     keys in the threshold bin; longer rows use the multi-pass radix select.
-//  2. attend: one workgroup per (batch, kv head, 64 kept positions) issues
-//     every K/V row load of its positions up front (coalesced, non-temporal
-//     16-byte loads: the rows are read once) and stages them in LDS; bf16
-//     runs the scores and the weighted V sum on 16x16x32 MFMA with the G
-//     query heads as the N dimension, fp32 uses VALU (4 lanes per key for the
-//     scores, lanes over head_dim for the sum); writes a partial (max, sum,
-//     output) per query head.
+//     position exactly (order: dt desc, index asc) and writes its selection
+//     key to the workspace (and, when asked or for the float32 path, the kept
+//     positions in ascending order).  Rows of up to 32768 positions are held
+//     in registers (1024 threads, each owning consecutive positions) and
+//     resolved with a range-adapted 4096-bin histogram plus an exact rank of
+//     the few keys in the threshold bin; longer rows use the multi-pass radix
+//     select.
+//  2. attend: bf16 takes one workgroup per (contiguous range of positions,
+//     kv head, batch), compacts the range's kept positions in LDS from the
+//     threshold and walks them 64 at a time (non-temporal 16-byte gathers of
+//     the K/V rows, the next block in flight, scores and P V on 16x16x32 MFMA
+//     with the G query heads as the N dimension, online softmax across
+//     blocks); float32 takes one workgroup per 64 kept positions of the list
+//     and uses VALU.  Each writes a partial (max, sum, output) per query head.
 //  3. combine: merges the partials of each (batch, query head).
 //     (A separate launch: merging inside the last attend workgroup would need
 //     device-scope fences, which on a multi-XCD part write back and
@@ -43,14 +44,15 @@ inline int nchunk_of(int Lmax, int w) {
 }
 
 struct WsLayout {
-    size_t kept, kdt, pm, pl, po, total;
+    size_t thr, kept, kdt, pm, pl, po, total;
 };
 
 inline WsLayout ws_layout(int B, int Lmax, int Hq, int Hkv, int d, int w) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t nc = (size_t)nchunk_of(Lmax, w);
     WsLayout l;
-    l.kept = 0;
+    l.thr = 0;
+    l.kept = up(l.thr + sizeof(uint64_t) * B * Hkv);
     l.kdt = up(l.kept + sizeof(int32_t) * B * Hkv * w);
     l.pm = up(l.kdt + sizeof(float) * B * Hkv * w);
     l.pl = up(l.pm + sizeof(float) * B * Hq * nc);
@@ -148,8 +150,10 @@ __device__ void hist_find(const uint32_t *k, int L, uint32_t rr, BinF binf, Filt
 __device__ __forceinline__ void write_kept(int32_t *kl, float *kd, int32_t *kept_idx, uint32_t pos, int j,
                                            float dtv, int w) {
     if (pos < (uint32_t)w) {
-        kl[pos] = j;
-        kd[pos] = dtv * kLog2e;
+        if (kl) {
+            kl[pos] = j;
+            kd[pos] = dtv * kLog2e;
+        }
         if (kept_idx) kept_idx[pos] = j;
     }
 }
@@ -157,7 +161,8 @@ __device__ __forceinline__ void write_kept(int32_t *kl, float *kd, int32_t *kept
 template <int ITEMS>
 __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(
     const float *__restrict__ dt_cache, const int32_t *__restrict__ cache_lens, int Hkv, int Lmax,
-    int w, int32_t *__restrict__ kept_ws, float *__restrict__ kdt_ws, int32_t *__restrict__ kept_idx) {
+    int w, uint64_t *__restrict__ thr_ws, int32_t *__restrict__ kept_ws, float *__restrict__ kdt_ws,
+    int32_t *__restrict__ kept_idx) {
     static_assert(ITEMS % 4 == 0, "float4 loads");
     __shared__ SelShared sh;
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -277,6 +282,9 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(
         }
         result = sh.result;
     }
+    // the w-th kept key (0, below every key, when all positions are kept)
+    if (tid == 0) thr_ws[(size_t)b * Hkv + g] = result;
+    if (!kept_ws && !kept_idx) return;  // uniform: no list asked for
     // kept positions, ascending: per-thread counts, one block scan
     uint32_t c = 0;
 #pragma unroll
@@ -284,8 +292,8 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(
         c += (j0 + it < L && ((((uint64_t)k[it] << 32) | (uint64_t)(~(uint32_t)(j0 + it))) >= result)) ? 1u : 0u;
     uint32_t tot;
     uint32_t pos = block_excl_scan(c, tot, sh);
-    int32_t *kl = kept_ws + ((size_t)b * Hkv + g) * w;
-    float *kd = kdt_ws + ((size_t)b * Hkv + g) * w;
+    int32_t *kl = kept_ws ? kept_ws + ((size_t)b * Hkv + g) * w : nullptr;
+    float *kd = kept_ws ? kdt_ws + ((size_t)b * Hkv + g) * w : nullptr;
     int32_t *ki = kept_idx ? kept_idx + ((size_t)b * Hkv + g) * w : nullptr;
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
@@ -302,7 +310,8 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(
 // Rows longer than the register-resident path: multi-pass radix select.
 __global__ __launch_bounds__(kThreads) void decode_select_long_kernel(
     const float *__restrict__ dt_cache, const int32_t *__restrict__ cache_lens, int Hkv, int Lmax,
-    int w, int32_t *__restrict__ kept_ws, float *__restrict__ kdt_ws, int32_t *__restrict__ kept_idx) {
+    int w, uint64_t *__restrict__ thr_ws, int32_t *__restrict__ kept_ws, float *__restrict__ kdt_ws,
+    int32_t *__restrict__ kept_idx) {
     __shared__ RadixShared<kThreads> rs;
     __shared__ int wsum[kThreads / 64];
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -310,13 +319,17 @@ __global__ __launch_bounds__(kThreads) void decode_select_long_kernel(
     const float *row = dt_cache + ((size_t)b * Hkv + g) * Lmax;
     float t_tau = -INFINITY;
     int t_tie = -1;
+    uint64_t result = 0;  // selection key of the w-th kept position (0: all kept)
     if (L > w) {
         const uint32_t ranks[2] = {(uint32_t)(w - 1), 0u};
         uint64_t keys[2];
         radix_select<kThreads>(row, L, 1, ranks, keys, rs);
+        result = keys[0];
         t_tie = (int)selkey_idx(keys[0]);
         t_tau = row[t_tie];
     }
+    if (tid == 0) thr_ws[(size_t)b * Hkv + g] = result;
+    if (!kept_ws && !kept_idx) return;  // uniform: no list asked for
     const int per = (L + kThreads - 1) / kThreads;
     const int j0 = min(tid * per, L), j1 = min(j0 + per, L);
     int cnt = 0;
@@ -332,8 +345,8 @@ __global__ __launch_bounds__(kThreads) void decode_select_long_kernel(
     __syncthreads();
     int off = incl - cnt;
     for (int w2 = 0; w2 < wave; ++w2) off += wsum[w2];
-    int32_t *kl = kept_ws + ((size_t)b * Hkv + g) * w;
-    float *kd = kdt_ws + ((size_t)b * Hkv + g) * w;
+    int32_t *kl = kept_ws ? kept_ws + ((size_t)b * Hkv + g) * w : nullptr;
+    float *kd = kept_ws ? kdt_ws + ((size_t)b * Hkv + g) * w : nullptr;
     int32_t *ki = kept_idx ? kept_idx + ((size_t)b * Hkv + g) * w : nullptr;
     for (int j = j0; j < j1; ++j) {
         const float dj = row[j];
@@ -550,148 +563,244 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
 }
 
-// bf16 decode on matrix cores, one workgroup per (batch, kv head, 64 kept
-// positions).  16x16x32 MFMA layouts (wave64, l = lane):
-//   A[m = l%16][k = 8*(l/16) + 0..7], B[k = 8*(l/16) + 0..7][n = l%16],
-//   C[m = 4*(l/16) + i][n = l%16], i = 0..3.
-// Scores: S^T (16 keys x 16 heads) = K (keys x d) Q^T, wave w taking keys
-// 16w..16w+15; the G <= 16 query heads of the kv head fill the N dimension
-// (unused columns are zero).  Weighted sum: O (16 heads x 16 d) = P V with P
-// from LDS and V's column operand from LDS transpose reads of the row-major
-// V tile; wave w takes head_dim tiles w, w+4, ...
+constexpr int kRange = 1024;            // positions compacted per pass
+constexpr int kTargetSplitWGs = 1024;   // attend workgroups a launch aims for
+
+// bf16 attend, wave-independent: one workgroup per (range of positions, kv
+// head, batch) compacts the range's kept positions into LDS (one barrier per
+// pass); then each wave takes every fourth block of 32 kept keys with no
+// further barrier until the end.  A block's K and V rows are gathered with
+// whole-row, non-temporal 16-byte loads (16 lanes per row) into the wave's own
+// LDS region; scores S^T = K Q^T on 16x16x32 MFMA leave each lane the 8 keys
+// kappa(g, j) = 16*(j/4) + 4g + j%4 of head l%16 (g = l/16), which are exactly
+// the k-slots of the P operand of O = P V, so P never leaves registers; V
+// comes back as the B operand by transpose reads.  The next block's rows are
+// in flight while a block is computed.  Each wave keeps its own online
+// softmax state; the four are merged in LDS into one partial per query head.
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_attend_mfma_kernel(
+__global__ __launch_bounds__(kThreads, 2) void decode_attend_wave_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ Kc, const uint16_t *__restrict__ Vc,
-    const int32_t *__restrict__ cache_lens, int Lmax, int Hq, int Hkv, int w,
-    const int32_t *__restrict__ kept_ws, const float *__restrict__ kdt_ws, float *__restrict__ pm,
-    float *__restrict__ pl, float *__restrict__ po, float qscale) {
+    const float *__restrict__ dt_cache, const int32_t *__restrict__ cache_lens, int Lmax, int Hq,
+    int Hkv, const uint64_t *__restrict__ thr_ws, float *__restrict__ pm, float *__restrict__ pl,
+    float *__restrict__ po, float qscale) {
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     constexpr int NW = kThreads / 64;
-    constexpr int BK = kKPC;                 // 64 kept keys per workgroup
+    constexpr int KB = 32;                   // kept keys per wave block
+    constexpr int NS = D / 32;               // 32-wide head_dim slices
+    constexpr int KP = D + 8;                // K and V row pitch in LDS (bf16): 16-byte pad
     constexpr int RV = D / 8;                // 16-byte vectors per row
-    constexpr int KP = D + 8;                // K tile pitch (bf16)
-    constexpr int VP = D + 32;               // V tile pitch (bf16), transpose-read friendly
-    constexpr int PP = BK + 8;               // P tile pitch (bf16)
-    constexpr int NL = BK * RV / kThreads;   // row vectors per thread
-    static_assert(BK == 64 && BK * RV % kThreads == 0, "one 64-key block per workgroup");
-    __shared__ __align__(16) uint16_t Ks[BK * KP];
-    __shared__ __align__(16) uint16_t Vs[BK * VP];
-    __shared__ __align__(16) uint16_t Ps[16 * PP];
-    __shared__ float c_dtl[BK];
-    __shared__ float wmax[NW][16], wsum[NW][16];
+    constexpr int NU = KB * RV / 64;         // row vectors per lane per block
+    constexpr int PER = kRange / kThreads;   // positions per thread per compaction pass
+    constexpr int NT = D / 16;               // output column tiles
+    static_assert(2 * NW * KB * KP * 2 >= NW * 16 * D * 4, "the merge buffer fits in the row regions");
+    __shared__ int l_idx[kRange];
+    __shared__ float l_dtl[kRange];
+    __shared__ uint32_t wcnt[NW];
+    __shared__ __align__(16) uint16_t KVw[NW][2][KB * KP];  // per-wave K, V rows; reused for the merge
+    __shared__ float mw[NW][16], lw[NW][16];
 
-    const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int nsplit = gridDim.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int G = Hq / Hkv;
-    const int nchunk = gridDim.x;
-    const int L = cache_lens[b];
-    const int c0 = chunk * BK;
-    const int n = max(0, min(min(L, w) - c0, BK));
-    const size_t lbase = ((size_t)b * Hkv + g) * w + c0;
     const int col = lane & 15, grp = lane >> 4;
+    const int L = cache_lens[b];
+    const int len = (L + nsplit - 1) / nsplit;
+    const int jbeg = min(split * len, L), jend = min(jbeg + len, L);
+    const uint64_t thr = thr_ws[(size_t)b * Hkv + g];
+    const float *drow = dt_cache + ((size_t)b * Hkv + g) * Lmax;
+    const size_t kvs = (size_t)Hkv * D;
+    const uint16_t *Kb = Kc + (size_t)b * Lmax * kvs + (size_t)g * D;
+    const uint16_t *Vb = Vc + (size_t)b * Lmax * kvs + (size_t)g * D;
+    uint16_t *kw = KVw[wave][0];
+    uint16_t *vw = KVw[wave][1];
 
-    // global loads first: query fragments, dt, kept indices, then K/V rows
-    bf16x8 qf[D / 32];
+    bf16x8 qf[NS];
     {
         const int hq = g * G + min(col, G - 1);
         const uint16_t *qp = q + ((size_t)b * Hq + hq) * D + 8 * grp;
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
+        for (int s = 0; s < NS; ++s) {
             qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
             if (col >= G) qf[s] = bf16x8{};
         }
     }
-    const float dlv = kdt_ws[lbase + min(tid, BK - 1)];
-    const size_t kvs = (size_t)Hkv * D;
-    const uint16_t *Kb = Kc + (size_t)b * Lmax * kvs + (size_t)g * D;
-    const uint16_t *Vb = Vc + (size_t)b * Lmax * kvs + (size_t)g * D;
-    uint4 rk[NL], rv[NL];
-    if (n > 0) {
-        int jr[NL];
+
+    float m_run = -INFINITY, l_run = 0.f;  // head `col`
+    f32x4 oacc[NT];                        // rows: heads 4*grp + i; columns 16t + col
 #pragma unroll
-        for (int u = 0; u < NL; ++u) jr[u] = kept_ws[lbase + min((tid + u * kThreads) / RV, n - 1)];
+    for (int t = 0; t < NT; ++t) oacc[t] = f32x4{};
+
+    // rows of a block: vector v = lane + 64u is row v / RV, 16-byte column v % RV
+    u32x4 kr[NU], vr[NU], kn[NU], vn[NU];
+    auto load_rows = [&](u32x4 (&kx)[NU], u32x4 (&vx)[NU], int kb, int n) __attribute__((always_inline)) {
+        int jr[NU];
 #pragma unroll
-        for (int u = 0; u < NL; ++u) {
-            const size_t off = (size_t)jr[u] * kvs + (size_t)((tid + u * kThreads) % RV) * 8;
-            rk[u] = load_nt16(Kb + off);
-            rv[u] = load_nt16(Vb + off);
+        for (int u = 0; u < NU; ++u) jr[u] = l_idx[min(kb + (lane + 64 * u) / RV, n - 1)];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const size_t off = (size_t)(uint32_t)jr[u] * kvs + (size_t)((lane + 64 * u) % RV) * 8;
+            kx[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(Kb + off));
+            vx[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(Vb + off));
         }
-    }
-    if (tid < BK) c_dtl[tid] = tid < n ? dlv : 0.f;
+    };
+    // one block: S, online softmax, O += P V
+    auto block = [&](const u32x4 (&kx)[NU], const u32x4 (&vx)[NU], int kb, int n) __attribute__((always_inline)) {
+        const int nb = min(KB, n - kb);
 #pragma unroll
-    for (int u = 0; u < NL; ++u) {
-        const int v = tid + u * kThreads;
-        const int kk = v / RV, cv = v % RV;
-        const bool ok = kk < n;
-        *reinterpret_cast<uint4 *>(&Ks[kk * KP + cv * 8]) = ok ? rk[u] : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4 *>(&Vs[kk * VP + cv * 8]) = ok ? rv[u] : make_uint4(0, 0, 0, 0);
-    }
-    __syncthreads();
-
-    // scores for keys 16*wave .. +15 (4 per lane), head = col
-    f32x4 sacc = f32x4{};
+        for (int u = 0; u < NU; ++u) {
+            const int v = lane + 64 * u;
+            *reinterpret_cast<u32x4 *>(&kw[(v / RV) * KP + (v % RV) * 8]) = kx[u];
+            *reinterpret_cast<u32x4 *>(&vw[(v / RV) * KP + (v % RV) * 8]) = vx[u];
+        }
+        float z[2][4];
+        float mx = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&Ks[(16 * wave + col) * KP + 32 * s + 8 * grp]);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], sacc, 0, 0, 0);
-    }
-    float z[4];
-    float mx = -INFINITY;
+        for (int c = 0; c < 2; ++c) {
+            f32x4 sacc = f32x4{};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int kk = 16 * wave + 4 * grp + i;
-        z[i] = (kk < n && col < G) ? fmaf(sacc[i], qscale, c_dtl[kk]) : -INFINITY;
-        mx = fmaxf(mx, z[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (grp == 0) wmax[wave][col] = mx;
-    __syncthreads();
-    float M = -INFINITY;
+            for (int s = 0; s < NS; ++s)
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    *reinterpret_cast<const bf16x8 *>(&kw[(16 * c + col) * KP + 32 * s + 8 * grp]), qf[s], sacc, 0, 0, 0);
 #pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, wmax[w2][col]);
-    const float msub = (M == -INFINITY) ? 0.f : M;
-    float ps = 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int kk = 16 * c + 4 * grp + i;
+                z[c][i] = (kk < nb && col < G) ? fmaf(sacc[i], qscale, l_dtl[kb + kk]) : -INFINITY;
+                mx = fmaxf(mx, z[c][i]);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float msub = m_new == -INFINITY ? 0.f : m_new;
+        bf16x8 pa;
+        float ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(z[i] - msub);
-        ps += p;
-        Ps[col * PP + 16 * wave + 4 * grp + i] = __builtin_bit_cast(uint16_t, (__bf16)p);
-    }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    if (grp == 0) wsum[wave][col] = ps;
-    __syncthreads();
-
-    // O (16 heads x 16 columns per tile) = P V over the 64 keys
-    const int tr_k = lane & 15;
-    for (int t = wave; t < D / 16; t += NW) {
-        f32x4 oacc = f32x4{};
+        for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-            const bf16x8 pa = *reinterpret_cast<const bf16x8 *>(&Ps[col * PP + 32 * ks + 8 * grp]);
-            const uint16_t *vp = &Vs[(32 * ks + 8 * grp + (tr_k >> 2)) * VP + 16 * t + 4 * (tr_k & 3)];
+            for (int i = 0; i < 4; ++i) {
+                const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(z[c][i] - msub);
+                pa[4 * c + i] = pb;
+                ps += (float)pb;  // the denominator sums the same rounded weights
+            }
+        }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        l_run = l_run * alpha + ps;
+        m_run = m_new;
+        float ar[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * grp + i, 64);
+        const int tr_k = lane & 15;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oacc[t][i] *= ar[i];
+            const uint16_t *vp = &vw[(4 * grp + (tr_k >> 2)) * KP + 16 * t + 4 * (tr_k & 3)];
             const i16x4 lo = lds_read_tr16(vp);
-            const i16x4 hi = lds_read_tr16(vp + 4 * VP);
+            const i16x4 hi = lds_read_tr16(vp + 16 * KP);
             const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, oacc, 0, 0, 0);
+            oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, oacc[t], 0, 0, 0);
+        }
+    };
+
+    for (int jb = jbeg; jb < jend; jb += kRange) {
+        // ---- compaction: this thread's PER consecutive positions, block scan
+        const int je = min(jb + kRange, jend);
+        float dv[PER];
+        bool kp[PER];
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int j = jb + PER * tid + u;
+            dv[u] = j < je ? drow[j] : 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hh = 4 * grp + i;
-            if (hh < G) {
-                const size_t pidx = ((size_t)b * Hq + g * G + hh) * nchunk + chunk;
-                po[pidx * D + 16 * t + col] = oacc[i];
+        for (int u = 0; u < PER; ++u) {
+            const int j = jb + PER * tid + u;
+            kp[u] = j < je && selkey(dv[u], (uint32_t)j) >= thr;
+            cnt += kp[u] ? 1u : 0u;
+        }
+        uint32_t incl = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        __syncthreads();  // the previous pass's readers of the list are done
+        if (lane == 63) wcnt[wave] = incl;
+        __syncthreads();
+        uint32_t off = incl - cnt;
+        int n = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+            off += w2 < wave ? wcnt[w2] : 0u;
+            n += (int)wcnt[w2];
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            if (kp[u]) {
+                l_idx[off] = jb + PER * tid + u;
+                l_dtl[off] = dv[u] * kLog2e;
+                ++off;
+            }
+        }
+        __syncthreads();
+
+        // ---- this wave's blocks: kb = (wave + NW*k) * KB, two at a time so
+        // that the register sets alternate without copies.  The next block's
+        // rows are requested unconditionally (indices clamp to the last kept
+        // position, so past the end they repeat cached rows): a conditional
+        // request would make the compiler wait for it before the current
+        // block's math.
+        int kb = wave * KB;
+        if (kb < n) {
+            load_rows(kr, vr, kb, n);
+            for (;;) {
+                load_rows(kn, vn, kb + NW * KB, n);
+                block(kr, vr, kb, n);
+                kb += NW * KB;
+                if (kb >= n) break;
+                load_rows(kr, vr, kb + NW * KB, n);
+                block(kn, vn, kb, n);
+                kb += NW * KB;
+                if (kb >= n) break;
             }
         }
     }
-    if (tid < G) {
-        const size_t pidx = ((size_t)b * Hq + g * G + tid) * nchunk + chunk;
-        float l = 0.f;
+
+    // ---- merge the four waves' states into one partial per query head
+    __syncthreads();  // the V regions are reused below
+    float *om = reinterpret_cast<float *>(&KVw[0][0][0]);  // [NW][16][D]
+    if (grp == 0) {
+        mw[wave][col] = m_run;
+        lw[wave][col] = l_run;
+    }
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) l += wsum[w2][tid];
-        pm[pidx] = M == -INFINITY ? -INFINITY : M;
-        pl[pidx] = l;
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) om[(wave * 16 + 4 * grp + i) * D + 16 * t + col] = oacc[t][i];
+    }
+    __syncthreads();
+    for (int x = tid; x < G * D; x += kThreads) {
+        const int hh = x / D, e = x - hh * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, mw[w2][hh]);
+        float lsum = 0.f, osum = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+            const float f = mw[w2][hh] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w2][hh] - M);
+            lsum = fmaf(lw[w2][hh], f, lsum);
+            osum = fmaf(om[(w2 * 16 + hh) * D + e], f, osum);
+        }
+        const size_t pidx = ((size_t)b * Hq + g * G + hh) * nsplit + split;
+        po[pidx * D + e] = osum;
+        if (e == 0) {
+            pm[pidx] = M;
+            pl[pidx] = lsum;
+        }
     }
 }
 
@@ -752,36 +861,45 @@ hipError_t launch_decode_t(const T *q, const T *Kc, const T *Vc, const float *dt
     float *po = (float *)(base + lay.po);
     const int nc = nchunk_of(Lmax, w);
     const float qscale = (float)(1.0 / __builtin_sqrt((double)d) * 1.4426950408889634);
+    uint64_t *thr_ws = (uint64_t *)(base + lay.thr);
+    constexpr bool kRangeAttend = sizeof(T) == 2;  // bf16: attend scans ranges, no lists
+    int32_t *lists = kRangeAttend ? nullptr : kept_ws;
     const dim3 sgrid(Hkv, B);
     if (Lmax <= 16 * kSelThreads)
         hipLaunchKernelGGL(decode_select_kernel<16>, sgrid, dim3(kSelThreads), 0, stream, dt_cache,
-                           cache_lens, Hkv, Lmax, w, kept_ws, kdt_ws, kept_idx);
+                           cache_lens, Hkv, Lmax, w, thr_ws, lists, kdt_ws, kept_idx);
     else if (Lmax <= 32 * kSelThreads)
         hipLaunchKernelGGL(decode_select_kernel<32>, sgrid, dim3(kSelThreads), 0, stream, dt_cache,
-                           cache_lens, Hkv, Lmax, w, kept_ws, kdt_ws, kept_idx);
+                           cache_lens, Hkv, Lmax, w, thr_ws, lists, kdt_ws, kept_idx);
     else
         hipLaunchKernelGGL(decode_select_long_kernel, sgrid, dim3(kThreads), 0, stream, dt_cache,
-                           cache_lens, Hkv, Lmax, w, kept_ws, kdt_ws, kept_idx);
+                           cache_lens, Hkv, Lmax, w, thr_ws, lists, kdt_ws, kept_idx);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 agrid(nc, Hkv, B);
-    const int G = Hq / Hkv;
-    if constexpr (sizeof(T) == 2) {
+    int nparts = nc;  // partials per (batch, query head)
+    if constexpr (kRangeAttend) {
+        // ranges per (batch, kv head): about kTargetSplitWGs workgroups in
+        // all, never more partials than the workspace holds
+        const int want = (kTargetSplitWGs + B * Hkv - 1) / (B * Hkv);
+        nparts = want < 1 ? 1 : (want > nc ? nc : want);
+        const dim3 rgrid(nparts, Hkv, B);
         if (d == 128)
-            hipLaunchKernelGGL(decode_attend_mfma_kernel<128>, agrid, dim3(kThreads), 0, stream, q, Kc, Vc,
-                               cache_lens, Lmax, Hq, Hkv, w, kept_ws, kdt_ws, pm, pl, po, qscale);
+            hipLaunchKernelGGL(decode_attend_wave_kernel<128>, rgrid, dim3(kThreads), 0, stream, q, Kc, Vc,
+                               dt_cache, cache_lens, Lmax, Hq, Hkv, thr_ws, pm, pl, po, qscale);
         else
-            hipLaunchKernelGGL(decode_attend_mfma_kernel<64>, agrid, dim3(kThreads), 0, stream, q, Kc, Vc,
-                               cache_lens, Lmax, Hq, Hkv, w, kept_ws, kdt_ws, pm, pl, po, qscale);
+            hipLaunchKernelGGL(decode_attend_wave_kernel<64>, rgrid, dim3(kThreads), 0, stream, q, Kc, Vc,
+                               dt_cache, cache_lens, Lmax, Hq, Hkv, thr_ws, pm, pl, po, qscale);
         e = hipGetLastError();
     } else {
+        const dim3 agrid(nc, Hkv, B);
+        const int G = Hq / Hkv;
         e = d == 128 ? launch_attend<T, 128>(G, agrid, stream, q, Kc, Vc, cache_lens, Lmax, Hq, Hkv, w,
                                              kept_ws, kdt_ws, pm, pl, po, qscale)
                      : launch_attend<T, 64>(G, agrid, stream, q, Kc, Vc, cache_lens, Lmax, Hq, Hkv, w,
                                             kept_ws, kdt_ws, pm, pl, po, qscale);
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(B * Hq), dim3(d), 0, stream, pm, pl, po, nc, d,
+    hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(B * Hq), dim3(d), 0, stream, pm, pl, po, nparts, d,
                        out);
     return hipGetLastError();
 }
