@@ -6,11 +6,11 @@
 // A skinny matrix product X[tokens][Hkv] = V[tokens][Hkv*d] * W^T that must
 // stream V once from HBM.  bf16 runs on matrix cores: one wave takes 16
 // tokens, v_mfma_f32_16x16x32_bf16 with the tokens as M, the (zero-padded)
-// kv heads as N and the channels as K, so V is fed to the MFMA straight from
-// its 16-byte loads with no conversion; W is staged once per workgroup in LDS
-// with a padded pitch.  The contraction order over channels is free, so each
-// lane owns 32 consecutive channels per 128-channel chunk (64 contiguous
-// bytes of its token row) and the same channel permutation is applied to W.
+// kv heads as N and the channels as K, so V and W are fed to the MFMA
+// straight from their 16-byte loads with no conversion.  The contraction
+// order over channels is free, so each lane owns 32 consecutive channels per
+// 128-channel chunk (64 contiguous bytes of its token row) and W uses the
+// same order.
 // float32 uses VALU: eight lanes per token, 16-byte vectors, xor-shuffle
 // reduction.  softplus and exp run in float32 in both.
 #include "common.hpp"
@@ -117,69 +117,87 @@ constexpr int kMfmaThreads = 128;     // two waves, one 16-token tile each
 constexpr int kChunk = 128;           // channels per lane group pass (4 lanes x 32)
 constexpr int kChunksPerBatch = 4;    // chunks loaded before the first multiply
 
+// softplus and exp on the hardware exp2 / log2: softplus(x) = max(x, 0) +
+// ln(1 + e^-|x|) and e^y, with an absolute error in softplus of a few 1e-8
+// and a relative error in e^y of about |y| * 2^-23, far inside the float32
+// tolerance of dt (which is relative to exp of their product).
+__device__ __forceinline__ float dt_from_x(float a, float x) {
+    constexpr float kLn2 = 0.6931471805599453f;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+    const float sp = fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + e) * kLn2;
+    return __builtin_amdgcn_exp2f(a * sp * kLog2e);
+}
+
 // bf16 dt on matrix cores.  16x16x32 bf16 operand layouts (l = lane):
 //   A[m = l%16][k = 8*(l/16) + j], B[k = 8*(l/16) + j][n = l%16],
 //   C[m = 4*(l/16) + i][n = l%16], i = 0..3.
 // Channel of k-slot (kg = l/16, j) in step s of chunk c: c*128 + 32*kg + 8*s + j.
+// Both operands come straight from global memory (W is small and stays in
+// the caches), so no LDS and no barrier stand between the loads and the math.
 __global__ __launch_bounds__(kMfmaThreads) void dt_mfma_kernel(
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ W, const uint16_t *__restrict__ bias,
-    const float *__restrict__ A, int S, int Hkv, int width, int pitch, int64_t ntok,
+    const float *__restrict__ A, int S, int Hkv, int width, int64_t ntok,
     float *__restrict__ out, int64_t ld, const int32_t *__restrict__ out_pos) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ float As[kMaxHkvDt], bs[kMaxHkvDt];
-    uint16_t *Ws = reinterpret_cast<uint16_t *>(smem);  // [Hkv][pitch]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int mr = lane & 15, kg = lane >> 4;
     const int nchunk = (width + kChunk - 1) / kChunk;
     const bool head_ok = mr < Hkv;
+    const int hc = head_ok ? mr : 0;  // clamped head for the (unused) W loads
     const int64_t ntiles = (ntok + 15) / 16;
     const int64_t stride = (int64_t)gridDim.x * (kMfmaThreads / 64);
+    const float a_h = A[hc];
+    const float b_h = bias ? bf16_to_f32(bias[hc]) : 0.f;
 
     // this lane's 16-byte vectors of chunks c0 .. c0 + kChunksPerBatch - 1 of
-    // its token row (zeros past the row or the last token)
-    uint4 va[kChunksPerBatch][4];
+    // its token row and of W's row for head l%16 (zeros past the row, the last
+    // token or the last head).  Requests are unconditional from clamped, valid
+    // addresses: a conditional load would be a branch of its own.
+    uint4 va[kChunksPerBatch][4], wa[kChunksPerBatch][4];
     auto load_batch = [&](int64_t tile, int c0) __attribute__((always_inline)) {
         const int64_t t = tile * 16 + mr;
         const bool tok_ok = t < ntok;
-        const uint16_t *vrow = V + (tok_ok ? t : 0) * (int64_t)width;
+        const uint16_t *vrow = V + (tok_ok ? t : ntok - 1) * (int64_t)width;
+        const uint16_t *wrow = W + (size_t)hc * width;
 #pragma unroll
         for (int cc = 0; cc < kChunksPerBatch; ++cc) {
             const int base = (c0 + cc) * kChunk + 32 * kg;
-            const bool ok = tok_ok && base < width;
+            const bool in = base < width;
+            const int cb = in ? base : width - 32;
 #pragma unroll
-            for (int st = 0; st < 4; ++st)
-                va[cc][st] = ok ? *reinterpret_cast<const uint4 *>(vrow + base + 8 * st) : make_uint4(0, 0, 0, 0);
+            for (int st = 0; st < 4; ++st) {
+                const uint4 x = *reinterpret_cast<const uint4 *>(vrow + cb + 8 * st);
+                const uint4 y = *reinterpret_cast<const uint4 *>(wrow + cb + 8 * st);
+                va[cc][st] = (tok_ok && in) ? x : make_uint4(0, 0, 0, 0);
+                wa[cc][st] = (head_ok && in) ? y : make_uint4(0, 0, 0, 0);
+            }
         }
     };
 
-    // the first rows are requested before W is staged, so both latencies overlap
     int64_t tile = (int64_t)blockIdx.x * (kMfmaThreads / 64) + wave;
     if (tile < ntiles) load_batch(tile, 0);
-    const int rv = width / 8;     // 16-byte vectors per W row
-    for (int v = threadIdx.x; v < Hkv * rv; v += kMfmaThreads) {
-        const int hh = v / rv, c = v - hh * rv;
-        *reinterpret_cast<uint4 *>(Ws + hh * pitch + 8 * c) = reinterpret_cast<const uint4 *>(W)[v];
-    }
-    if (threadIdx.x < (unsigned)Hkv) {
-        As[threadIdx.x] = A[threadIdx.x];
-        bs[threadIdx.x] = bias ? bf16_to_f32(bias[threadIdx.x]) : 0.f;
-    }
-    __syncthreads();
-
     for (; tile < ntiles; tile += stride) {
+        // batch and column of this lane's four output tokens, out_pos loaded
+        // now so that its latency hides behind the products
+        int ob[4], os[4];
+        int64_t ocol[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t tok = tile * 16 + 4 * kg + i;
+            const int64_t tc = tok < ntok ? tok : ntok - 1;
+            ob[i] = ntok <= 0x7fffffff ? (int)((uint32_t)tc / (uint32_t)S) : (int)(tc / S);
+            os[i] = (int)(tc - (int64_t)ob[i] * S);
+            ocol[i] = out_pos ? (int64_t)out_pos[ob[i]] : 0;
+        }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int c0 = 0; c0 < nchunk; c0 += kChunksPerBatch) {
             if (c0 > 0) load_batch(tile, c0);  // the first batch is already in flight
 #pragma unroll
             for (int cc = 0; cc < kChunksPerBatch; ++cc) {
-                const int base = (c0 + cc) * kChunk + 32 * kg;
                 if (c0 + cc >= nchunk) break;
 #pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    bf16x8 bw = {};
-                    if (head_ok && base < width) bw = *reinterpret_cast<const bf16x8 *>(Ws + mr * pitch + base + 8 * st);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va[cc][st]), bw, acc, 0, 0, 0);
-                }
+                for (int st = 0; st < 4; ++st)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va[cc][st]),
+                                                                  __builtin_bit_cast(bf16x8, wa[cc][st]), acc, 0, 0, 0);
             }
         }
         if (tile + stride < ntiles) load_batch(tile + stride, 0);  // next tile's rows in flight
@@ -187,13 +205,8 @@ __global__ __launch_bounds__(kMfmaThreads) void dt_mfma_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t tok = tile * 16 + 4 * kg + i;
-                if (tok < ntok) {
-                    const int b = (int)(tok / S);
-                    const int s = (int)(tok - (int64_t)b * S);
-                    const int64_t col = (out_pos ? (int64_t)out_pos[b] : 0) + s;
-                    const float x = acc[i] + bs[mr];
-                    out[((int64_t)b * Hkv + mr) * ld + col] = expf(As[mr] * softplus_f32(x));
-                }
+                if (tok < ntok)
+                    out[((int64_t)ob[i] * Hkv + mr) * ld + ocol[i] + os[i]] = dt_from_x(a_h, acc[i] + b_h);
             }
         }
     }
@@ -210,13 +223,9 @@ hipError_t launch_dt(const void *V, const void *W, const void *bias, const float
         const int64_t ntiles = (ntok + 15) / 16;
         const int64_t want = (ntiles + kMfmaThreads / 64 - 1) / (kMfmaThreads / 64);
         const int grid = (int)(want < 4096 ? want : 4096);
-        // W rows padded by 16 bytes so that the heads read by one lane group
-        // fall in different banks, unless that would pass 64 KiB of LDS
-        const int pitch = (size_t)Hkv * (width + 8) * sizeof(uint16_t) <= kDtLdsBytes ? width + 8 : width;
-        const size_t lds = (size_t)Hkv * pitch * sizeof(uint16_t);
-        hipLaunchKernelGGL(dt_mfma_kernel, dim3(grid), dim3(kMfmaThreads), lds, stream,
+        hipLaunchKernelGGL(dt_mfma_kernel, dim3(grid), dim3(kMfmaThreads), 0, stream,
                            (const uint16_t *)V, (const uint16_t *)W, (const uint16_t *)bias, A, S, Hkv,
-                           width, pitch, ntok, dt_out, ld_out, out_pos);
+                           width, ntok, dt_out, ld_out, out_pos);
     } else {
         const int64_t want = (ntok + kTokensPerBlock - 1) / kTokensPerBlock;
         const int grid = (int)(want < 2048 ? want : 2048);
