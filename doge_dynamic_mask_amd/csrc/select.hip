@@ -238,53 +238,68 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
     }
     __syncthreads();
 
-    // ---- b: each candidate marks the rows it is the threshold of.  One wave
-    // per candidate at a time: the chunk's new keys sit one per lane (rows
-    // t = lane and t = lane + 64), so "new keys of rows <= t better than the
-    // candidate" is a ballot and a masked bit count per lane, and every lane
-    // checks its own rows.
+    // ---- b: each candidate finds the rows it is the threshold of.  The
+    // chunk's new keys sit one per lane (rows t = lane and t = lane + 64), so
+    // "new keys of rows <= t better than the candidate" is a ballot and a
+    // masked bit count per lane.  Band keys are distinct and held by rank, so
+    // the band ballots count x keys above the band key of rank x, and its
+    // position lies before the chunk: one formula serves both kinds.  A wave
+    // takes kUnrollB candidates per step with no branch between them, so
+    // their dependency chains overlap; each lane keeps the position found for
+    // its rows in registers and stores the pair once at the end.
+    constexpr int kWaves = kThreads / 64;
+    constexpr int kUnrollB = 4;
     const int need = w - A0 - 1;  // better candidates a row's w-th key has
     const int ncand = nb + nnew;
     const uint64_t nk0 = lane < nnew ? sh.cand[nb + lane] : 0ull;  // 0: below every key
     const uint64_t nk1 = (C > 64 && lane + 64 < nnew) ? sh.cand[nb + 64 + lane] : 0ull;
-    uint64_t bk[(C + 1 + 63) / 64 + 1];
+    uint64_t bk[(C + 1 + 63) / 64];  // the band holds at most C + 1 keys
 #pragma unroll
     for (int q = 0; q < (int)(sizeof(bk) / sizeof(bk[0])); ++q)
         bk[q] = 64 * q + lane < nb ? sh.cand[64 * q + lane] : 0ull;
-    const uint64_t le_mask = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);  // bits 0..lane
     const int t0 = lane, t1 = lane + 64;  // this lane's rows (chunk offsets)
-    for (int x = wave; x < ncand; x += kThreads / 64) {
-        const uint64_t kx = sh.cand[x];
-        const int jx = (int)selkey_idx(kx);
-        int better;
-        int first;  // first row that sees this candidate
-        if (x < nb) {
-            better = x;  // band keys are stored by rank
-            first = lo;
-        } else {
-            better = 0;
+    const bool v0 = r0 + t0 >= lo && r0 + t0 < hi;
+    const bool v1 = C > 64 && r0 + t1 >= lo && r0 + t1 < hi;
+    int h0 = -1, h1 = -1;  // threshold position of rows t0, t1 if this wave has it
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    for (int xb = wv; xb < ncand; xb += kWaves * kUnrollB) {
+        uint64_t kx[kUnrollB];
 #pragma unroll
-            for (int q = 0; q < (int)(sizeof(bk) / sizeof(bk[0])); ++q) better += __popcll(__ballot(bk[q] > kx));
-            first = max(jx, lo);
+        for (int u = 0; u < kUnrollB; ++u) {
+            // past the end the read repeats the last candidate, whose second
+            // pass sets the same positions again
+            kx[u] = sh.cand[min(xb + kWaves * u, ncand - 1)];
         }
-        const int need_x = need - better;  // better new keys the row must see
-        if (need_x < 0) continue;          // uniform: the band alone outranks it
-        const uint64_t m0 = __ballot(nk0 > kx);
-        const uint64_t m1 = C > 64 ? __ballot(nk1 > kx) : 0ull;
-        const int c0 = __popcll(m0 & le_mask);
-        const int c1 = __popcll(m0) + __popcll(m1 & le_mask);
-        const bool hit0 = c0 == need_x && r0 + t0 >= first && r0 + t0 < hi;
-        const bool hit1 = C > 64 && c1 == need_x && r0 + t1 >= first && r0 + t1 < hi;
-        if (__ballot(hit0 || hit1) == 0ull) continue;
-        const float vx = row[jx];
-        if (hit0) {
-            tau[base + r0 + t0] = vx;
-            tie[base + r0 + t0] = jx;
+#pragma unroll
+        for (int u = 0; u < kUnrollB; ++u) {
+            const int jx = (int)selkey_idx(kx[u]);
+            int better = 0;
+#pragma unroll
+            for (int q = 0; q < (int)(sizeof(bk) / sizeof(bk[0])); ++q) better += __popcll(__ballot(bk[q] > kx[u]));
+            const int need_x = need - better;  // better new keys the row must see
+            const uint64_t m0 = __ballot(nk0 > kx[u]);
+            const uint64_t m1 = C > 64 ? __ballot(nk1 > kx[u]) : 0ull;
+            // set bits of m at lanes 0..lane: those of m >> 1 below the lane,
+            // plus bit 0
+            const int c0 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m0 >> 33),
+                                 __builtin_amdgcn_mbcnt_lo((uint32_t)(m0 >> 1), 0u)) + (int)(m0 & 1);
+            const int c1 = C > 64 ? __popcll(m0) + (int)(m1 & 1) +
+                                        (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m1 >> 33),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)(m1 >> 1), 0u))
+                                  : 0;
+            // the candidate is visible to rows at or after its own position
+            h0 = (v0 & (c0 == need_x) & (r0 + t0 >= jx)) ? jx : h0;
+            if (C > 64) h1 = (v1 & (c1 == need_x) & (r0 + t1 >= jx)) ? jx : h1;
         }
-        if (hit1) {
-            tau[base + r0 + t1] = vx;
-            tie[base + r0 + t1] = jx;
-        }
+    }
+    // every row in [lo, hi) has exactly one threshold, found by one wave
+    if (h0 >= 0) {
+        tau[base + r0 + t0] = row[h0];
+        tie[base + r0 + t0] = h0;
+    }
+    if (C > 64 && h1 >= 0) {
+        tau[base + r0 + t1] = row[h1];
+        tie[base + r0 + t1] = h1;
     }
 }
 
