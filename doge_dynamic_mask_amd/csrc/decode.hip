@@ -564,7 +564,7 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t *p) {
 }
 
 constexpr int kRange = 1024;            // positions compacted per pass
-constexpr int kTargetSplitWGs = 1024;   // attend workgroups a launch aims for
+constexpr int kTargetSplitWGs = 512;   // attend workgroups a launch aims for
 
 // bf16 attend, wave-independent: one workgroup per (range of positions, kv
 // head, batch) compacts the range's kept positions into LDS (one barrier per
@@ -705,17 +705,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_wave_kernel(
         }
     };
 
+    // dt of a pass's positions; positions past the range load the range's
+    // last one (never kept there), so no load is conditional.  The next
+    // pass's loads are issued before this pass's blocks.
+    float dv[PER], dnx[PER];
+    auto load_dt = [&](float (&x)[PER], int jb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) x[u] = drow[min(jb + PER * tid + u, jend - 1)];
+    };
+    if (jbeg < jend) load_dt(dv, jbeg);
     for (int jb = jbeg; jb < jend; jb += kRange) {
         // ---- compaction: this thread's PER consecutive positions, block scan
         const int je = min(jb + kRange, jend);
-        float dv[PER];
         bool kp[PER];
         uint32_t cnt = 0;
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int j = jb + PER * tid + u;
-            dv[u] = j < je ? drow[j] : 0.f;
-        }
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
             const int j = jb + PER * tid + u;
@@ -747,6 +750,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_wave_kernel(
             }
         }
         __syncthreads();
+        if (jb + kRange < jend) load_dt(dnx, jb + kRange);
 
         // ---- this wave's blocks: kb = (wave + NW*k) * KB, two at a time so
         // that the register sets alternate without copies.  The next block's
@@ -768,6 +772,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_wave_kernel(
                 if (kb >= n) break;
             }
         }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) dv[u] = dnx[u];
     }
 
     // ---- merge the four waves' states into one partial per query head
@@ -810,27 +816,45 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float *__rest
                                                             const float *__restrict__ pl,
                                                             const float *__restrict__ po, int nchunk,
                                                             int d, T *__restrict__ out) {
-    __shared__ float sf[1024];  // per-chunk weights (nchunk <= 1024)
-    __shared__ float sden;
+    // Thread e merges column e of the partials of one (batch, query head),
+    // kGroup partials at a time with all of their loads in flight together;
+    // every thread forms the same weights.  Slots past the last partial
+    // repeat it with weight zero, so no load is conditional.
+    constexpr int kGroup = 8;
     const int bh = blockIdx.x;  // b * Hq + hq
+    const int e = min((int)threadIdx.x, d - 1);
     const float *m = pm + (size_t)bh * nchunk;
     const float *l = pl + (size_t)bh * nchunk;
-    float M = -INFINITY;
-    for (int s = 0; s < nchunk; ++s) M = fmaxf(M, m[s]);
-    for (int s = threadIdx.x; s < nchunk; s += blockDim.x) sf[s] = m[s] == -INFINITY ? 0.f : exp2f(m[s] - M);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float den = 0.f;
-        for (int s = 0; s < nchunk; ++s) den = fmaf(l[s], sf[s], den);
-        sden = den;
+    const float *o = po + (size_t)bh * nchunk * d + e;
+    float M = -INFINITY, den = 0.f, num = 0.f;
+    for (int s0 = 0; s0 < nchunk; s0 += kGroup) {
+        float mv[kGroup], lv[kGroup], ov[kGroup];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            const int s = min(s0 + u, nchunk - 1);
+            mv[u] = m[s];
+            lv[u] = l[s];
+            ov[u] = o[(size_t)s * d];
+        }
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u)
+            if (s0 + u >= nchunk) mv[u] = -INFINITY;
+        float Mn = M;
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) Mn = fmaxf(Mn, mv[u]);
+        if (Mn == -INFINITY) continue;  // nothing kept so far
+        const float c = M == -INFINITY ? 0.f : exp2f(M - Mn);
+        den *= c;
+        num *= c;
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            const float f = mv[u] == -INFINITY ? 0.f : exp2f(mv[u] - Mn);
+            den = fmaf(lv[u], f, den);
+            num = fmaf(ov[u], f, num);
+        }
+        M = Mn;
     }
-    __syncthreads();
-    const float inv = sden > 0.f ? 1.f / sden : 0.f;
-    for (int e = threadIdx.x; e < d; e += blockDim.x) {
-        float num = 0.f;
-        for (int s = 0; s < nchunk; ++s) num = fmaf(po[((size_t)bh * nchunk + s) * d + e], sf[s], num);
-        Elem<T>::store(out, (size_t)bh * d + e, num * inv);
-    }
+    if ((int)threadIdx.x < d) Elem<T>::store(out, (size_t)bh * d + threadIdx.x, den > 0.f ? num / den : 0.f);
 }
 
 template <typename T, int D>
