@@ -563,7 +563,7 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
 }
 
-constexpr int kRange = 1024;            // positions compacted per pass
+constexpr int kRange = 4096;            // positions compacted per pass
 constexpr int kTargetSplitWGs = 512;   // attend workgroups a launch aims for
 
 // bf16 attend, wave-independent: one workgroup per (range of positions, kv
@@ -592,11 +592,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_wave_kernel(
     constexpr int NU = KB * RV / 64;         // row vectors per lane per block
     constexpr int PER = kRange / kThreads;   // positions per thread per compaction pass
     constexpr int NT = D / 16;               // output column tiles
-    static_assert(2 * NW * KB * KP * 2 >= NW * 16 * D * 4, "the merge buffer fits in the row regions");
+    static_assert(NW * KB * KP * 2 >= NW * 16 * D * 4, "the merge buffer fits in the row regions");
     __shared__ int l_idx[kRange];
     __shared__ float l_dtl[kRange];
     __shared__ uint32_t wcnt[NW];
-    __shared__ __align__(16) uint16_t KVw[NW][2][KB * KP];  // per-wave K, V rows; reused for the merge
+    __shared__ __align__(16) uint16_t KVw[NW][KB * KP];  // per-wave V rows; reused for the merge
     __shared__ float mw[NW][16], lw[NW][16];
 
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -612,8 +612,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_wave_kernel(
     const size_t kvs = (size_t)Hkv * D;
     const uint16_t *Kb = Kc + (size_t)b * Lmax * kvs + (size_t)g * D;
     const uint16_t *Vb = Vc + (size_t)b * Lmax * kvs + (size_t)g * D;
-    uint16_t *kw = KVw[wave][0];
-    uint16_t *vw = KVw[wave][1];
+    uint16_t *vw = KVw[wave];
 
     bf16x8 qf[NS];
     {
@@ -631,26 +630,36 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_wave_kernel(
 #pragma unroll
     for (int t = 0; t < NT; ++t) oacc[t] = f32x4{};
 
-    // rows of a block: vector v = lane + 64u is row v / RV, 16-byte column v % RV
-    u32x4 kr[NU], vr[NU], kn[NU], vn[NU];
-    auto load_rows = [&](u32x4 (&kx)[NU], u32x4 (&vx)[NU], int kb, int n) __attribute__((always_inline)) {
-        int jr[NU];
+    // K of a block goes straight to registers in the layout of the score
+    // MFMA's A operand: lane (col, grp) takes key 16c + col, columns
+    // 32s + 8grp .. +7 (NK = 2 * NS pieces).  V rows go through LDS for the
+    // transpose reads: vector v = lane + 64u is row v / RV, 16-byte column v % RV.
+    constexpr int NK = 2 * NS;
+    u32x4 kr[NK], vr[NU], kn[NK], vn[NU];
+    auto load_rows = [&](u32x4 (&kx)[NK], u32x4 (&vx)[NU], int kb, int n) __attribute__((always_inline)) {
+        int jk[2], jr[NU];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) jk[c] = l_idx[min(kb + 16 * c + col, n - 1)];
 #pragma unroll
         for (int u = 0; u < NU; ++u) jr[u] = l_idx[min(kb + (lane + 64 * u) / RV, n - 1)];
 #pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int s2 = 0; s2 < NS; ++s2)
+                kx[c * NS + s2] = *reinterpret_cast<const u32x4 *>(Kb + (size_t)(uint32_t)jk[c] * kvs + 32 * s2 + 8 * grp);
+        }
+#pragma unroll
         for (int u = 0; u < NU; ++u) {
             const size_t off = (size_t)(uint32_t)jr[u] * kvs + (size_t)((lane + 64 * u) % RV) * 8;
-            kx[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(Kb + off));
             vx[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(Vb + off));
         }
     };
     // one block: S, online softmax, O += P V
-    auto block = [&](const u32x4 (&kx)[NU], const u32x4 (&vx)[NU], int kb, int n) __attribute__((always_inline)) {
+    auto block = [&](const u32x4 (&kx)[NK], const u32x4 (&vx)[NU], int kb, int n) __attribute__((always_inline)) {
         const int nb = min(KB, n - kb);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int v = lane + 64 * u;
-            *reinterpret_cast<u32x4 *>(&kw[(v / RV) * KP + (v % RV) * 8]) = kx[u];
             *reinterpret_cast<u32x4 *>(&vw[(v / RV) * KP + (v % RV) * 8]) = vx[u];
         }
         float z[2][4];
@@ -661,7 +670,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_wave_kernel(
 #pragma unroll
             for (int s = 0; s < NS; ++s)
                 sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    *reinterpret_cast<const bf16x8 *>(&kw[(16 * c + col) * KP + 32 * s + 8 * grp]), qf[s], sacc, 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, kx[c * NS + s]), qf[s], sacc, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int kk = 16 * c + 4 * grp + i;
@@ -778,7 +787,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_wave_kernel(
 
     // ---- merge the four waves' states into one partial per query head
     __syncthreads();  // the V regions are reused below
-    float *om = reinterpret_cast<float *>(&KVw[0][0][0]);  // [NW][16][D]
+    float *om = reinterpret_cast<float *>(&KVw[0][0]);  // [NW][16][D]
     if (grp == 0) {
         mw[wave][col] = m_run;
         lw[wave][col] = l_run;
