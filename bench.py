@@ -92,6 +92,16 @@ def decode_bytes(B, Hq, Hkv, d, w, lens, esize=2):
     return total
 
 
+def decode_state_bytes_moved(B, Hq, Hkv, d, w, lens, esize=2):
+    """Per incremental decode step: the selection key and K/V row of every kept
+    slot, the new token's rows and dt, q and out."""
+    total = 0
+    for L in lens:
+        n = min(int(L) + 1, w)
+        total += Hkv * (n * (8 + 2 * d * esize) + 2 * d * esize + 4) + 2 * Hq * d * esize
+    return total
+
+
 def to_dev(x, dev):
     t = torch.from_numpy(np.ascontiguousarray(x))
     return (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
@@ -339,8 +349,24 @@ def main():
         kc, vc, dc = nxt(dec_sets)
         dma.decode(q, kc, vc, dc, lens, wl_d.w, out=out, workspace=ws)
 
+    # The incremental decode: the state of the cache without its last token
+    # (kept keys and their K/V rows, 137 MB), then steps that append that
+    # token; three states in turn, so that each step reads its rows from HBM.
+    NST = 3
+    ar = torch.arange(wl_d.B, device=dev)
+    k_last, v_last = Kc[ar, pos.long()].contiguous(), Vc[ar, pos.long()].contiguous()
+    dt_last = dt_cache[ar, :, pos.long()].contiguous()
+    states = [dma.decode_state_init(Kc, Vc, dt_cache, pos, wl_d.w) for _ in range(NST)]
+    ws_step = torch.empty(dma.decode_step_workspace_bytes(wl_d.B, wl_d.Hq, wl_d.Hkv, wl_d.d, wl_d.w),
+                          dtype=torch.uint8, device=dev)
+    rot_st = [0]
+
+    def c_decode_step():
+        rot_st[0] += 1
+        dma.decode_step(q, k_last, v_last, dt_last, states[rot_st[0] % NST], out=out, workspace=ws_step)
+
     calls = (("dt", c_dt), ("select", c_select), ("attn_fwd", c_attn),
-             ("dt_append", c_dt_append), ("decode", c_decode))
+             ("dt_append", c_dt_append), ("decode", c_decode), ("decode_step", c_decode_step))
     avg, host_launch_ms = {}, {}
     for n, f in calls:
         pairs = []
@@ -358,7 +384,7 @@ def main():
         torch.cuda.synchronize()
         avg[n] = float(np.mean([a.elapsed_time(b) for a, b in pairs])) / R
         host_launch_ms[n] = float(np.mean(hs))
-    del pre_sets, dec_sets
+    del pre_sets, dec_sets, states
 
     # The same prefill replayed as one HIP graph (one launch for three
     # kernels), timed after an eviction in the same way; reported beside.
@@ -379,6 +405,8 @@ def main():
     dbytes = decode_bytes(wl_d.B, wl_d.Hq, wl_d.Hkv, wl_d.d, wl_d.w, dec["cache_lens"])
     dec_gbs = dbytes / (avg["decode"] * 1e-3) / 1e9
     attn_tflops = flops / (avg["attn_fwd"] * 1e-3) / 1e12
+    sbytes = decode_state_bytes_moved(wl_d.B, wl_d.Hq, wl_d.Hkv, wl_d.d, wl_d.w, pos.cpu().numpy())
+    step_gbs = sbytes / (avg["decode_step"] * 1e-3) / 1e9
 
     line = {
         "metric": "DMA prefill kept-key TFLOP/s + decode GB/s, % of MI355X roofline",
@@ -410,6 +438,12 @@ def main():
         "decode": {
             "value": round(dec_gbs, 2), "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS,
             "frac": round(dec_gbs / PEAK_HBM_GBS, 5),
+        },
+        "decode_incremental": {
+            "value": round(step_gbs, 2), "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS,
+            "frac": round(step_gbs / PEAK_HBM_GBS, 5), "bytes": sbytes, "ms": round(avg["decode_step"], 5),
+            "tokens_per_s": round(wl_d.B / (avg["decode_step"] * 1e-3), 1),
+            "note": "dma_decode_step: kept set carried across steps, the kept K/V rows stored compactly",
         },
         "ms_prefill": round(ms_pre, 5),
         "ms_decode_step": round(ms_dec, 5),

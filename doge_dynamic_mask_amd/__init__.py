@@ -33,7 +33,9 @@ _STATUS = {
 }
 
 EXPORTS = ("dma_version", "dma_status_str", "dma_dt", "dma_select", "dma_attn_fwd",
-           "dma_decode_workspace_bytes", "dma_decode")
+           "dma_decode_workspace_bytes", "dma_decode", "dma_decode_state_bytes",
+           "dma_decode_step_workspace_bytes", "dma_decode_state_init", "dma_decode_step",
+           "dma_decode_state_kept")
 
 
 class DmaError(RuntimeError):
@@ -66,6 +68,15 @@ def lib():
     L.dma_decode_workspace_bytes.restype = SZ
     L.dma_decode.argtypes = [P, P, P, I, P, P, I, I, I, I, I, I, P, P, P, SZ, P]
     L.dma_decode.restype = I
+    L.dma_decode_state_bytes.argtypes, L.dma_decode_state_bytes.restype = [I, I, I, I], SZ
+    L.dma_decode_step_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.dma_decode_step_workspace_bytes.restype = SZ
+    L.dma_decode_state_init.argtypes = [P, P, I, P, P, I, I, I, I, I, P, SZ, P, SZ, P]
+    L.dma_decode_state_init.restype = I
+    L.dma_decode_step.argtypes = [P, P, P, I, P, I, I, I, I, I, P, SZ, P, P, SZ, P]
+    L.dma_decode_step.restype = I
+    L.dma_decode_state_kept.argtypes = [P, SZ, I, I, I, I, P, P, P]
+    L.dma_decode_state_kept.restype = I
     _lib = L
     return L
 
@@ -198,3 +209,71 @@ def prefill(Q, K, V, W, A, w, bias=None, seqlens=None):
     tau, tie = select(d_, w, seqlens)
     O = attn_fwd(Q, K, V, d_, tau, tie, w, seqlens)
     return O, d_, tau, tie
+
+
+class DecodeState:
+    """Kept keys of every (batch, kv head), carried from one decode step to the next.
+
+    Built from a cache by decode_state_init(); advanced one token per batch by
+    decode_step().  Holds the device buffers and the sizes they were made for."""
+
+    def __init__(self, B, Hkv, d, w, device):
+        self.B, self.Hkv, self.d, self.w = B, Hkv, d, int(w)
+        n = int(lib().dma_decode_state_bytes(B, Hkv, d, self.w))
+        if n == 0:
+            raise ValueError("invalid decode state sizes")
+        self.buf = torch.empty(n, dtype=torch.uint8, device=device)
+
+    def kept(self):
+        """(kept positions [B, Hkv, w] int32 in slot order, -1 padded; lengths [B, Hkv] int32)."""
+        dev = self.buf.device
+        kept_idx = torch.empty((self.B, self.Hkv, self.w), dtype=torch.int32, device=dev)
+        lens = torch.empty((self.B, self.Hkv), dtype=torch.int32, device=dev)
+        _call(lib().dma_decode_state_kept(_ptr(self.buf), self.buf.numel(), self.B, self.Hkv, self.d, self.w,
+                                          _ptr(kept_idx), _ptr(lens), _stream(self.buf)), "dma_decode_state_kept")
+        return kept_idx, lens
+
+
+def decode_step_workspace_bytes(B, Hq, Hkv, d, w):
+    return int(lib().dma_decode_step_workspace_bytes(B, Hq, Hkv, d, w))
+
+
+def decode_state_init(Kc, Vc, dt_cache, cache_lens, w, state=None, workspace=None):
+    """The DecodeState of a cache of cache_lens[b] positions (bf16 K/V)."""
+    _check(Kc, "Kc", torch.bfloat16, 4)
+    dev = Kc.device
+    _check(Vc, "Vc", torch.bfloat16, 4, dev)
+    _check(dt_cache, "dt_cache", torch.float32, 3, dev)
+    _check(cache_lens, "cache_lens", torch.int32, 1, dev)
+    B, Lmax, Hkv, d = Kc.shape
+    if state is None:
+        state = DecodeState(B, Hkv, d, w, dev)
+    nbytes = decode_step_workspace_bytes(B, Hkv, Hkv, d, w)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _call(lib().dma_decode_state_init(_ptr(Kc), _ptr(Vc), BF16, _ptr(dt_cache), _ptr(cache_lens), B, Lmax, Hkv, d,
+                                      int(w), _ptr(state.buf), state.buf.numel(), _ptr(workspace),
+                                      workspace.numel(), _stream(Kc)), "dma_decode_state_init")
+    return state
+
+
+def decode_step(q, k_new, v_new, dt_new, state, out=None, workspace=None):
+    """Append one token per batch (rows k_new/v_new [B, Hkv, d], dt_new [B, Hkv]) and decode q [B, Hq, d]."""
+    _check(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _check(k_new, "k_new", torch.bfloat16, 3, dev)
+    _check(v_new, "v_new", torch.bfloat16, 3, dev)
+    _check(dt_new, "dt_new", torch.float32, 2, dev)
+    B, Hq, d = q.shape
+    Hkv = k_new.shape[1]
+    if (B, Hkv, d) != (state.B, state.Hkv, state.d):
+        raise ValueError("q / k_new do not match the decode state")
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = decode_step_workspace_bytes(B, Hq, Hkv, d, state.w)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _call(lib().dma_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), BF16, _ptr(dt_new), B, Hq, Hkv, d, state.w,
+                                _ptr(state.buf), state.buf.numel(), _ptr(out), _ptr(workspace), workspace.numel(),
+                                _stream(q)), "dma_decode_step")
+    return out

@@ -92,4 +92,53 @@ int dma_decode(const void *q, const void *Kc, const void *Vc, int dtype, const f
                                        out, kept_idx, ws, (hipStream_t)stream));
 }
 
+size_t dma_decode_state_bytes(int B, int Hkv, int d, int w) {
+    if (B < 1 || Hkv < 1 || w < 1 || !head_dim_ok(d)) return 0;
+    return dma::decode_state_bytes(B, Hkv, d, w);
+}
+
+size_t dma_decode_step_workspace_bytes(int B, int Hq, int Hkv, int d, int w) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || w < 1 || Hq % Hkv != 0 || !head_dim_ok(d)) return 0;
+    return dma::decode_step_ws_bytes(B, Hq, Hkv, d, w);
+}
+
+int dma_decode_state_init(const void *Kc, const void *Vc, int dtype, const float *dt_cache,
+                          const int32_t *cache_lens, int B, int Lmax, int Hkv, int d, int w, void *state,
+                          size_t state_bytes, void *ws, size_t ws_bytes, void *stream) {
+    if (!Kc || !Vc || !dt_cache || !cache_lens || !state) return DMA_ERR_NULL;
+    if (!dtype_ok(dtype)) return DMA_ERR_DTYPE;
+    if (B < 1 || Lmax < 1 || Hkv < 1 || d < 1 || w < 1) return DMA_ERR_SHAPE;
+    if (dtype != DMA_BF16 || !head_dim_ok(d)) return DMA_ERR_UNSUPPORTED;
+    if (B > 65535 || Hkv > 65535 || w > dma::kMaxKeptDecode) return DMA_ERR_UNSUPPORTED;
+    if (!aligned16(Kc) || !aligned16(Vc) || !aligned16(state)) return DMA_ERR_UNSUPPORTED;
+    if (state_bytes < dma::decode_state_bytes(B, Hkv, d, w)) return DMA_ERR_WORKSPACE;
+    if (!ws || ws_bytes < dma::decode_step_ws_bytes(B, Hkv, Hkv, d, w)) return DMA_ERR_WORKSPACE;
+    return from_hip(dma::launch_decode_state_init(Kc, Vc, dt_cache, cache_lens, B, Lmax, Hkv, d, w, state, ws,
+                                                  (hipStream_t)stream));
+}
+
+int dma_decode_step(const void *q, const void *k_new, const void *v_new, int dtype, const float *dt_new,
+                    int B, int Hq, int Hkv, int d, int w, void *state, size_t state_bytes, void *out, void *ws,
+                    size_t ws_bytes, void *stream) {
+    if (!q || !k_new || !v_new || !dt_new || !state || !out) return DMA_ERR_NULL;
+    if (!dtype_ok(dtype)) return DMA_ERR_DTYPE;
+    if (B < 1 || Hq < 1 || Hkv < 1 || d < 1 || w < 1 || Hq % Hkv != 0) return DMA_ERR_SHAPE;
+    if (dtype != DMA_BF16 || !head_dim_ok(d) || Hq / Hkv > dma::kMaxGroupDecode) return DMA_ERR_UNSUPPORTED;
+    if (B > 65535 || Hkv > 65535 || w > dma::kMaxKeptDecode) return DMA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(state)) return DMA_ERR_UNSUPPORTED;
+    if (state_bytes < dma::decode_state_bytes(B, Hkv, d, w)) return DMA_ERR_WORKSPACE;
+    if (!ws || ws_bytes < dma::decode_step_ws_bytes(B, Hq, Hkv, d, w)) return DMA_ERR_WORKSPACE;
+    return from_hip(dma::launch_decode_step(q, k_new, v_new, dt_new, B, Hq, Hkv, d, w, state, out, ws,
+                                            (hipStream_t)stream));
+}
+
+int dma_decode_state_kept(const void *state, size_t state_bytes, int B, int Hkv, int d, int w, int32_t *kept_idx,
+                          int32_t *lens, void *stream) {
+    if (!state || !kept_idx) return DMA_ERR_NULL;
+    if (B < 1 || Hkv < 1 || d < 1 || w < 1) return DMA_ERR_SHAPE;
+    if (!head_dim_ok(d) || B > 65535 || Hkv > 65535) return DMA_ERR_UNSUPPORTED;
+    if (state_bytes < dma::decode_state_bytes(B, Hkv, d, w)) return DMA_ERR_WORKSPACE;
+    return from_hip(dma::launch_decode_state_kept(state, B, Hkv, d, w, kept_idx, lens, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -939,6 +939,21 @@ hipError_t launch_decode_t(const T *q, const T *Kc, const T *Vc, const float *dt
 
 }  // namespace
 
+hipError_t launch_decode_thresholds(const float *dt_cache, const int32_t *cache_lens, int B, int Lmax, int Hkv,
+                                    int w, uint64_t *thr, hipStream_t stream) {
+    const dim3 sgrid(Hkv, B);
+    if (Lmax <= 16 * kSelThreads)
+        hipLaunchKernelGGL(decode_select_kernel<16>, sgrid, dim3(kSelThreads), 0, stream, dt_cache, cache_lens, Hkv,
+                           Lmax, w, thr, (int32_t *)nullptr, (float *)nullptr, (int32_t *)nullptr);
+    else if (Lmax <= 32 * kSelThreads)
+        hipLaunchKernelGGL(decode_select_kernel<32>, sgrid, dim3(kSelThreads), 0, stream, dt_cache, cache_lens, Hkv,
+                           Lmax, w, thr, (int32_t *)nullptr, (float *)nullptr, (int32_t *)nullptr);
+    else
+        hipLaunchKernelGGL(decode_select_long_kernel, sgrid, dim3(kThreads), 0, stream, dt_cache, cache_lens, Hkv,
+                           Lmax, w, thr, (int32_t *)nullptr, (float *)nullptr, (int32_t *)nullptr);
+    return hipGetLastError();
+}
+
 size_t decode_ws_bytes(int B, int Lmax, int Hq, int Hkv, int d, int w) {
     return ws_layout(B, Lmax, Hq, Hkv, d, w).total;
 }

@@ -26,6 +26,22 @@ hipError_t launch_decode(const void *q, const void *Kc, const void *Vc, int dtyp
                          int Hq, int Hkv, int d, int w, void *out, int32_t *kept_idx, void *ws,
                          hipStream_t stream);
 
+// The selection key of the w-th kept position of each (batch, kv head) of a
+// decode cache (0 when every position is kept), as dma_decode's first step.
+hipError_t launch_decode_thresholds(const float *dt_cache, const int32_t *cache_lens, int B, int Lmax, int Hkv,
+                                    int w, uint64_t *thr, hipStream_t stream);
+
+// Incremental decode state (decode_state.hip).
+size_t decode_state_bytes(int B, int Hkv, int d, int w);
+size_t decode_step_ws_bytes(int B, int Hq, int Hkv, int d, int w);
+hipError_t launch_decode_state_init(const void *Kc, const void *Vc, const float *dt_cache, const int32_t *cache_lens,
+                                    int B, int Lmax, int Hkv, int d, int w, void *state, void *ws,
+                                    hipStream_t stream);
+hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_new, const float *dt_new, int B,
+                              int Hq, int Hkv, int d, int w, void *state, void *out, void *ws, hipStream_t stream);
+hipError_t launch_decode_state_kept(const void *state, int B, int Hkv, int d, int w, int32_t *kept_idx,
+                                    int32_t *lens, hipStream_t stream);
+
 // Limits the launchers rely on (checked by the ABI layer).
 constexpr int kMaxHkvDt = 16;          // dt kernel: heads accumulated in registers
 constexpr int kMaxGroupAttn = 128;     // prefill: query heads per kv head

@@ -155,6 +155,62 @@ int dma_decode(const void *q, const void *Kc, const void *Vc, int dtype,
                int Hkv, int d, int w, void *out, int32_t *kept_idx, void *ws,
                size_t ws_bytes, void *stream);
 
+/*
+ * Incremental decode -- Doge guide, DMA section, forward steps 3 and 4 at
+ * inference, one token at a time.  The kept sets nest (under dt desc, index
+ * asc, the kept set of position p is a subset of that of p-1 plus {p}), so
+ * a state that holds each (batch, kv head)'s kept keys -- their selection
+ * keys, positions and K/V rows, compacted into w slots -- is enough to
+ * decode the next token exactly: the new key enters iff fewer than w keys
+ * are kept or it beats the worst kept key (a tie in dt loses), and then
+ * replaces it.  A step reads the w kept rows per kv head, not the cache.
+ * bf16 only (DMA_BF16); d in {64, 128}; Hq/Hkv <= 16.
+ *
+ * dma_decode_state_bytes -- bytes of the state for these sizes (0 on
+ * invalid sizes).  The state is caller-owned device memory, 16-byte aligned,
+ * written only by dma_decode_state_init and dma_decode_step.
+ */
+size_t dma_decode_state_bytes(int B, int Hkv, int d, int w);
+
+/*
+ * dma_decode_step_workspace_bytes -- device workspace of dma_decode_step and
+ * dma_decode_state_init (0 on invalid sizes).
+ */
+size_t dma_decode_step_workspace_bytes(int B, int Hq, int Hkv, int d, int w);
+
+/*
+ * dma_decode_state_init -- the state of a cache of cache_lens[b] positions
+ * (0 <= cache_lens[b] <= Lmax): the kept set of its last position, found
+ * exactly as dma_decode does, with the K/V rows copied into the slots.
+ *   Kc, Vc [B][Lmax][Hkv][d] bf16, dt_cache [B][Hkv][Lmax] float32,
+ *   cache_lens [B] int32; state/ws of at least the sizes above.
+ */
+int dma_decode_state_init(const void *Kc, const void *Vc, int dtype, const float *dt_cache,
+                          const int32_t *cache_lens, int B, int Lmax, int Hkv, int d, int w,
+                          void *state, size_t state_bytes, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dma_decode_step -- appends one token per batch at position L_b (the
+ * state's length) and decodes it: out[b] = the attention of q[b] over the
+ * kept keys of positions <= L_b, exactly what dma_decode returns for the
+ * cache extended by that token with cache_lens = L_b + 1.  The state then
+ * describes the extended cache.
+ *   q [B][Hq][d], k_new / v_new [B][Hkv][d] bf16 (the new token's rows),
+ *   dt_new [B][Hkv] float32 (its dt, e.g. from dma_dt on its value row),
+ *   out [B][Hq][d] bf16.
+ */
+int dma_decode_step(const void *q, const void *k_new, const void *v_new, int dtype, const float *dt_new,
+                    int B, int Hq, int Hkv, int d, int w, void *state, size_t state_bytes, void *out,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dma_decode_state_kept -- the kept positions of every (batch, kv head) in
+ * slot order (not sorted), padded with -1: kept_idx [B][Hkv][w] int32; and
+ * the cache length of each (batch, kv head) into lens [B][Hkv] (nullable).
+ */
+int dma_decode_state_kept(const void *state, size_t state_bytes, int B, int Hkv, int d, int w,
+                          int32_t *kept_idx, int32_t *lens, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -99,3 +99,35 @@ def test_decode_validation(dma):
     assert call(Hq=7) == -2
     assert call(Hq=64, Hkv=2) == -4
     assert call(d=80) == -4
+
+
+def test_decode_state_validation(dma):
+    nst = dma.dma_decode_state_bytes(2, 2, 128, 64)
+    nws = dma.dma_decode_step_workspace_bytes(2, 8, 2, 128, 64)
+    assert nst > 0 and nws > 0
+    assert dma.dma_decode_state_bytes(2, 2, 96, 64) == 0
+    assert dma.dma_decode_step_workspace_bytes(2, 7, 2, 128, 64) == 0
+
+    def init(Kc=FAKE, dtype=1, state=FAKE2, sb=nst, ws=FAKE2, wb=nws, d=128, w=64):
+        return dma.dma_decode_state_init(Kc, FAKE, dtype, FAKE, FAKE, 2, 100, 2, d, w, state, sb, ws, wb, None)
+    assert init(Kc=None) == -1
+    assert init(state=None) == -1
+    assert init(dtype=5) == -3
+    assert init(dtype=0) == -4        # float32 K/V: the state path is bf16 only
+    assert init(w=0) == -2
+    assert init(d=80) == -4
+    assert init(sb=nst - 1) == -5
+    assert init(ws=None) == -5
+
+    def step(q=FAKE, dtype=1, Hq=8, sb=nst, wb=nws, out=FAKE2):
+        return dma.dma_decode_step(q, FAKE, FAKE, dtype, FAKE, 2, Hq, 2, 128, 64, FAKE2, sb, out, FAKE2, wb, None)
+    assert step(q=None) == -1
+    assert step(out=None) == -1
+    assert step(dtype=0) == -4
+    assert step(Hq=7) == -2
+    assert step(Hq=64) == -4
+    assert step(sb=nst - 1) == -5
+    assert step(wb=nws - 1) == -5
+    assert step(q=ctypes.c_void_p(0x1008)) == -4
+    assert dma.dma_decode_state_kept(None, nst, 2, 2, 128, 64, FAKE, None, None) == -1
+    assert dma.dma_decode_state_kept(FAKE, nst - 1, 2, 2, 128, 64, FAKE, None, None) == -5

@@ -337,6 +337,82 @@ def test_decode_long_caches(dma, oracle_mod, Lmax, lens, w):
     _decode_check(dma, oracle_mod, q, Kc, Vc, dtc, np.array(lens, np.int32), w, 2e-2)
 
 
+def _state_kept_sorted(st):
+    kept, lens = st.kept()
+    kept = to_host(kept)
+    out = np.full_like(kept, -1)
+    for b in range(kept.shape[0]):
+        for g in range(kept.shape[1]):
+            v = np.sort(kept[b, g][kept[b, g] >= 0])
+            out[b, g, :len(v)] = v
+    return out, to_host(lens)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,w,lens,kind", [
+    (3, 8, 2, 128, 100, [0, 99, 301], "few"),      # ties with the worst kept key
+    (2, 4, 4, 64, 37, [37, 500], "lognormal"),
+    (2, 2, 1, 128, 1, [5, 1], "few"),              # w = 1: the running best
+    (1, 16, 1, 64, 600, [250], "dyadic"),          # every position kept throughout
+    (2, 8, 2, 64, 64, [3000, 64], "const"),        # all dt equal: the first w positions stay
+])
+def test_decode_state_steps(dma, oracle_mod, B, Hq, Hkv, d, w, lens, kind):
+    """Steps of the incremental decode against the oracle's decode of the
+    cache extended by each new token: outputs within tolerance, kept sets
+    exactly."""
+    T = 24
+    lens = np.array(lens, np.int32)
+    Lmax = int(lens.max()) + T
+    rng = np.random.default_rng(d * 7 + w)
+    Kc = si.to_bf16_bits(rng.standard_normal((B, Lmax, Hkv, d)).astype(np.float32))
+    Vc = si.to_bf16_bits(rng.standard_normal((B, Lmax, Hkv, d)).astype(np.float32))
+    dtc = si.make_dt((B, Hkv, Lmax), kind, seed=w + 3)
+    st = dma.decode_state_init(to_dev(Kc), to_dev(Vc), to_dev(dtc), to_dev(lens), w)
+    kept0, slens = _state_kept_sorted(st)
+    _, rkept0 = oracle_mod.decode(np.zeros((B, Hq, d), np.uint16), Kc, Vc, dtc, np.maximum(lens, 1), w)
+    for b in range(B):
+        assert (slens[b] == lens[b]).all()
+        if lens[b] > 0:
+            np.testing.assert_array_equal(kept0[b], rkept0[b])
+    for _ in range(T):
+        q = si.to_bf16_bits(rng.standard_normal((B, Hq, d)).astype(np.float32))
+        ar = np.arange(B)
+        k_new, v_new = Kc[ar, lens], Vc[ar, lens]          # [B, Hkv, d]: the token at position lens[b]
+        dt_new = np.ascontiguousarray(dtc[ar, :, lens])     # [B, Hkv]
+        out = to_host(dma.decode_step(to_dev(q), to_dev(k_new), to_dev(v_new), to_dev(dt_new), st))
+        lens = lens + 1
+        ref, rkept = oracle_mod.decode(q, Kc, Vc, dtc, lens, w)
+        assert np.abs(out.astype(np.float64) - ref).max() <= 2e-2
+        kept, slens = _state_kept_sorted(st)
+        np.testing.assert_array_equal(kept, rkept)
+        assert (slens == lens[:, None]).all()
+
+
+def test_decode_state_full_size(dma, oracle_mod):
+    """The decode workload: the state of the cache without its last token, then
+    one step with that token, against dma_decode of the whole cache (kept sets
+    exactly, outputs within tolerance) and the oracle on sampled batches."""
+    wl = si.WORKLOADS["decode"]
+    inp = full_inputs("decode")
+    dtc = si.make_dt((wl.B, wl.Hkv, wl.S), "lognormal", seed=91)
+    lens = inp["cache_lens"]
+    Kc, Vc, q = to_dev(inp["Kc"]), to_dev(inp["Vc"]), to_dev(inp["q"])
+    dtd = to_dev(dtc)
+    ar = torch.arange(wl.B, device=Kc.device)
+    last = to_dev(lens).long() - 1
+    st = dma.decode_state_init(Kc, Vc, dtd, to_dev(lens - 1), wl.w)
+    out = dma.decode_step(q, Kc[ar, last].contiguous(), Vc[ar, last].contiguous(),
+                          dtd[ar, :, last].contiguous(), st)
+    ref, kept_ref = dma.decode(q, Kc, Vc, dtd, to_dev(lens), wl.w, kept=True)
+    kept, slens = _state_kept_sorted(st)
+    np.testing.assert_array_equal(kept, to_host(kept_ref))
+    assert (slens == lens[:, None]).all()
+    got = to_host(out).astype(np.float64)
+    assert np.abs(got - to_host(ref)).max() <= 2e-2
+    bs = [0, 17, 63]
+    r, _ = oracle_mod.decode(inp["q"][bs], inp["Kc"][bs], inp["Vc"][bs], dtc[bs], lens[bs], wl.w)
+    assert np.abs(got[bs] - r).max() <= 2e-2
+
+
 def test_decode_matches_last_prefill_row(dma, oracle_mod):
     B, S, Hq, Hkv, d, w = 3, 900, 8, 2, 128, 256
     Q, K, V = si.make_qkv(B, S, Hq, Hkv, d, "bf16", seed=51)
