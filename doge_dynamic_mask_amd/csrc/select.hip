@@ -50,6 +50,12 @@ struct SelectShared {
     uint32_t keys[kStage];          // prefix order keys, when P <= kStage
 };
 
+// The float of order bits o = ordkey(f): f itself, except that -0.0 comes
+// back as +0.0.
+__device__ __forceinline__ float order_value(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
 // f(j, dt[j]) for every prefix position j < P, kUnroll positions per thread
 // per step with all of their loads issued before any is used.
 template <typename F>
@@ -93,6 +99,9 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
     const int rend = min(r0 + kChunk, S);
     const int lo = max(r0, w);    // first row holding more than w valid keys
     const int hi = min(rend, L);  // end of the valid rows of this chunk
+    // this thread's key of the chunk (C <= kThreads), requested before the
+    // prefix work so that its latency is hidden there
+    const float own = row[min(r0 + tid, S - 1)];
 
     for (int t = tid; t < rend - r0; t += kThreads) {
         const int i = r0 + t;
@@ -232,10 +241,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
     }
     // the chunk's own keys after the band
     const int nnew = hi - r0;
-    for (int t = tid; t < nnew; t += kThreads) {
-        const int j = r0 + t;
-        sh.cand[nb + t] = selkey(row[j], (uint32_t)j);
-    }
+    if (tid < nnew) sh.cand[nb + tid] = selkey(own, (uint32_t)(r0 + tid));
     __syncthreads();
 
     // ---- b: each candidate finds the rows it is the threshold of.  The
@@ -261,6 +267,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
     const bool v0 = r0 + t0 >= lo && r0 + t0 < hi;
     const bool v1 = C > 64 && r0 + t1 >= lo && r0 + t1 < hi;
     int h0 = -1, h1 = -1;  // threshold position of rows t0, t1 if this wave has it
+    uint32_t o0 = 0, o1 = 0;  // and its dt order bits
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     for (int xb = wv; xb < ncand; xb += kWaves * kUnrollB) {
         uint64_t kx[kUnrollB];
@@ -288,17 +295,25 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
                                              __builtin_amdgcn_mbcnt_lo((uint32_t)(m1 >> 1), 0u))
                                   : 0;
             // the candidate is visible to rows at or after its own position
-            h0 = (v0 & (c0 == need_x) & (r0 + t0 >= jx)) ? jx : h0;
-            if (C > 64) h1 = (v1 & (c1 == need_x) & (r0 + t1 >= jx)) ? jx : h1;
+            const bool g0 = v0 & (c0 == need_x) & (r0 + t0 >= jx);
+            h0 = g0 ? jx : h0;
+            o0 = g0 ? (uint32_t)(kx[u] >> 32) : o0;
+            if (C > 64) {
+                const bool g1 = v1 & (c1 == need_x) & (r0 + t1 >= jx);
+                h1 = g1 ? jx : h1;
+                o1 = g1 ? (uint32_t)(kx[u] >> 32) : o1;
+            }
         }
     }
-    // every row in [lo, hi) has exactly one threshold, found by one wave
+    // every row in [lo, hi) has exactly one threshold, found by one wave;
+    // its value comes back from the order bits (only a zero, whose sign the
+    // order folds, is read again)
     if (h0 >= 0) {
-        tau[base + r0 + t0] = row[h0];
+        tau[base + r0 + t0] = o0 == 0x80000000u ? row[h0] : order_value(o0);
         tie[base + r0 + t0] = h0;
     }
     if (C > 64 && h1 >= 0) {
-        tau[base + r0 + t1] = row[h1];
+        tau[base + r0 + t1] = o1 == 0x80000000u ? row[h1] : order_value(o1);
         tie[base + r0 + t1] = h1;
     }
 }
