@@ -143,14 +143,22 @@ __device__ __forceinline__ uint32_t init_excl_scan(uint32_t v, uint32_t &total, 
 // threads, a multiple of 64) gets it.
 __device__ __forceinline__ void worst_key(const uint64_t *keys, int n, int sub, uint64_t key_sub, int nt,
                                           uint64_t &kmin, int &smin, uint64_t *red_k, int *red_s) {
+    constexpr int kBatch = 16;  // keys per thread whose loads are in flight together
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint64_t mk = ~0ull;
     int ms = -1;
-    for (int s = threadIdx.x; s < n; s += nt) {
-        const uint64_t k = s == sub ? key_sub : keys[s];
-        if (k < mk) {
-            mk = k;
-            ms = s;
+    for (int s0 = threadIdx.x; s0 < n; s0 += nt * kBatch) {
+        uint64_t k[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) k[u] = keys[min(s0 + u * nt, n - 1)];  // past n: a repeat, skipped below
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int s = s0 + u * nt;
+            const uint64_t ku = s == sub ? key_sub : k[u];
+            if (s < n && ku < mk) {
+                mk = ku;
+                ms = s;
+            }
         }
     }
 #pragma unroll
