@@ -306,11 +306,6 @@ __global__ __launch_bounds__(kThreads, 2) void state_attend_kernel(
     const uint16_t *vn_row = v_new + bg * D;
     uint16_t *vw = Vw[wave];
 
-    for (int x = tid; x < cnt; x += kThreads) {
-        const int s = s0 + x;
-        l_dtl[x] = (s == adm ? dtn : key_dt(kb_keys[s])) * kLog2e;
-    }
-
     bf16x8 qf[NS];
     {
         const int hq = g * G + min(col, G - 1);
@@ -406,14 +401,20 @@ __global__ __launch_bounds__(kThreads, 2) void state_attend_kernel(
             oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, oacc[t], 0, 0, 0);
         }
     };
+    // this wave's first block is requested before the keys of the dt bias:
+    // both depend only on the header
+    int kb = wave * KB;
+    if (kb < cnt) load_rows(kr, vr, kb);
+    for (int x = tid; x < cnt; x += kThreads) {
+        const int s = s0 + x;
+        l_dtl[x] = (s == adm ? dtn : key_dt(kb_keys[s])) * kLog2e;
+    }
     __syncthreads();  // l_dtl visible
 
     // this wave's blocks: kb = (wave + NW*k) * KB, two register sets in turn;
     // the next block is requested unconditionally (offsets clamp to the last
     // slot), so no request waits on a branch
-    int kb = wave * KB;
     if (kb < cnt) {
-        load_rows(kr, vr, kb);
         for (;;) {
             load_rows(kn, vn, kb + NW * KB);
             block(kr, vr, kb);
