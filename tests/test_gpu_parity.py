@@ -354,6 +354,7 @@ def _state_kept_sorted(st):
     (2, 2, 1, 128, 1, [5, 1], "few"),              # w = 1: the running best
     (1, 16, 1, 64, 600, [250], "dyadic"),          # every position kept throughout
     (2, 8, 2, 64, 64, [3000, 64], "const"),        # all dt equal: the first w positions stay
+    (1, 4, 1, 128, 3000, [5000], "lognormal"),     # w above one workgroup's 2048 slots
 ])
 def test_decode_state_steps(dma, oracle_mod, B, Hq, Hkv, d, w, lens, kind):
     """Steps of the incremental decode against the oracle's decode of the
