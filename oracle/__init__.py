@@ -58,6 +58,8 @@ def _load():
         lib.oracle_attn.restype = None
         lib.oracle_decode.argtypes = [P, P, P, I, P, P, I, I, I, I, I, I, P, P]
         lib.oracle_decode.restype = None
+        lib.oracle_qk_norm_rope.argtypes = [P, P, I, ctypes.c_double, ctypes.c_double, P, I64, I, P]
+        lib.oracle_qk_norm_rope.restype = None
         _lib = lib
     return _lib
 
@@ -162,3 +164,21 @@ def decode(q, Kc, Vc, dt_cache, cache_lens, w):
     _load().oracle_decode(_ptr(q), _ptr(Kc), _ptr(Vc), tq, _ptr(dt_cache), _ptr(lens), B, Lmax, Hq,
                           Hkv, d, int(w), _ptr(out), _ptr(kept))
     return out, kept
+
+
+def qk_norm_rope(x, w, eps, theta, positions):
+    """RMSNorm over the last axis (weight w) then the rotary embedding, fp64.
+
+    x: [..., d] (float32 or bf16 bit patterns), w: [d] of the same type,
+    positions: int array broadcastable to x.shape[:-1] (the position of each
+    row).  Doge guide, DMA forward step 1 (q_norm / k_norm, rotary)."""
+    x, tx = _elem_array(x)
+    w, tw = _elem_array(w)
+    assert tx == tw
+    d = x.shape[-1]
+    assert w.shape == (d,) and d % 2 == 0
+    pos = np.ascontiguousarray(np.broadcast_to(np.asarray(positions, np.int32), x.shape[:-1]), dtype=np.int32)
+    n = int(np.prod(x.shape[:-1]))
+    out = np.empty(x.shape, dtype=np.float64)
+    _load().oracle_qk_norm_rope(_ptr(x), _ptr(w), tx, float(eps), float(theta), _ptr(pos), n, d, _ptr(out))
+    return out

@@ -338,3 +338,38 @@ void oracle_decode(const void *q, const void *Kc, const void *Vc, int dtype,
         free(buf);
     }
 }
+
+/*
+ * Q/K normalisation and rotary position embedding -- Doge guide, DMA forward
+ * step 1: after q_proj/k_proj, Q and K go through q_norm/k_norm, an RMSNorm
+ * over head_dim with one learnable weight per element (the T5 layer norm of
+ * the Llama code it reuses; eps = rms_norm_eps), and then the rotary position
+ * embedding reused from Llama.  Reading of the rotary step (the guide names
+ * it only): element e < d/2 pairs with e + d/2, the pair turns by the angle
+ * pos * theta^(-2e/d):
+ *   out_e       = y_e cos(a) - y_{e+d/2} sin(a)
+ *   out_{e+d/2} = y_{e+d/2} cos(a) + y_e sin(a)
+ * x: nrows rows of d elements (dtype), row r at position pos[r]; w: d
+ * weights (dtype); out: fp64, nrows x d.
+ */
+void oracle_qk_norm_rope(const void *x, const void *w, int dtype, double eps, double theta,
+                         const int32_t *pos, int64_t nrows, int d, double *out)
+{
+    const int h = d / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+        double ss = 0.0;
+        for (int e = 0; e < d; ++e) {
+            const double v = elem(x, dtype, (size_t)r * d + e);
+            ss += v * v;
+        }
+        const double inv = 1.0 / sqrt(ss / d + eps);
+        for (int e = 0; e < h; ++e) {
+            const double a = (double)pos[r] * pow(theta, -2.0 * e / d);
+            const double y0 = elem(x, dtype, (size_t)r * d + e) * inv * elem(w, dtype, e);
+            const double y1 = elem(x, dtype, (size_t)r * d + e + h) * inv * elem(w, dtype, e + h);
+            out[(size_t)r * d + e] = y0 * cos(a) - y1 * sin(a);
+            out[(size_t)r * d + e + h] = y1 * cos(a) + y0 * sin(a);
+        }
+    }
+}
