@@ -13,6 +13,9 @@ Functions mirror the C ABI in ``include/dma.h``:
     attn_fwd(Q, K, V, dt, tau, tie, w, seqlens=None)    -> O
     decode(q, Kc, Vc, dt_cache, cache_lens, w, kept=False) -> out (, kept_idx)
     prefill(Q, K, V, W, A, w, bias=None, seqlens=None)  -> (O, dt, tau, tie)
+    qk_norm_rope(Q, K, q_norm_w, k_norm_w, ...)         -> (Q', K')
+    prologue(Q, K, V, q_norm_w, k_norm_w, W, A, ...)    -> (Q', K', dt)
+    DecodeState, decode_state_init(...), decode_step(...)  incremental decode
 """
 from __future__ import annotations
 
@@ -35,7 +38,7 @@ _STATUS = {
 EXPORTS = ("dma_version", "dma_status_str", "dma_dt", "dma_select", "dma_attn_fwd",
            "dma_decode_workspace_bytes", "dma_decode", "dma_decode_state_bytes",
            "dma_decode_step_workspace_bytes", "dma_decode_state_init", "dma_decode_step",
-           "dma_decode_state_kept")
+           "dma_decode_state_kept", "dma_qk_norm_rope", "dma_prologue")
 
 
 class DmaError(RuntimeError):
@@ -77,6 +80,11 @@ def lib():
     L.dma_decode_step.restype = I
     L.dma_decode_state_kept.argtypes = [P, SZ, I, I, I, I, P, P, P]
     L.dma_decode_state_kept.restype = I
+    D = ctypes.c_double
+    L.dma_qk_norm_rope.argtypes = [P, P, I, P, P, ctypes.c_float, D, P, I, I, I, I, I, P, P, P]
+    L.dma_qk_norm_rope.restype = I
+    L.dma_prologue.argtypes = [P, P, P, I, P, P, ctypes.c_float, D, P, P, P, P, I, I, I, I, I, P, P, P, P]
+    L.dma_prologue.restype = I
     _lib = L
     return L
 
@@ -277,3 +285,61 @@ def decode_step(q, k_new, v_new, dt_new, state, out=None, workspace=None):
                                 _ptr(state.buf), state.buf.numel(), _ptr(out), _ptr(workspace), workspace.numel(),
                                 _stream(q)), "dma_decode_step")
     return out
+
+
+def _qk_args(Q, K, q_norm_w, k_norm_w, positions, Q_out, K_out):
+    _check(Q, "Q", ndim=4)
+    dev = Q.device
+    _check(K, "K", Q.dtype, 4, dev)
+    B, S, Hq, d = Q.shape
+    Hkv = K.shape[2]
+    if tuple(K.shape) != (B, S, Hkv, d):
+        raise ValueError("K must be [B, S, Hkv, d] matching Q")
+    _check(q_norm_w, "q_norm_w", Q.dtype, 1, dev)
+    _check(k_norm_w, "k_norm_w", Q.dtype, 1, dev)
+    if q_norm_w.shape[0] != d or k_norm_w.shape[0] != d:
+        raise ValueError("q_norm_w / k_norm_w must have head_dim elements")
+    if positions is not None:
+        _check(positions, "positions", torch.int32, 2, dev)
+        if tuple(positions.shape) != (B, S):
+            raise ValueError("positions must be [B, S]")
+    Q_out = torch.empty_like(Q) if Q_out is None else Q_out
+    K_out = torch.empty_like(K) if K_out is None else K_out
+    _check(Q_out, "Q_out", Q.dtype, 4, dev)
+    _check(K_out, "K_out", Q.dtype, 4, dev)
+    if Q_out.shape != Q.shape or K_out.shape != K.shape:
+        raise ValueError("Q_out / K_out must have the shapes of Q / K")
+    return B, S, Hq, Hkv, d, Q_out, K_out
+
+
+def qk_norm_rope(Q, K, q_norm_w, k_norm_w, eps=1e-6, rope_theta=10000.0, positions=None, Q_out=None, K_out=None):
+    """RMSNorm over head_dim (weights q_norm_w / k_norm_w) then rotary embedding of Q [B,S,Hq,d] and
+    K [B,S,Hkv,d] at positions [B,S] int32 (None: position s).  Q_out=Q, K_out=K runs in place."""
+    B, S, Hq, Hkv, d, Q_out, K_out = _qk_args(Q, K, q_norm_w, k_norm_w, positions, Q_out, K_out)
+    _call(lib().dma_qk_norm_rope(_ptr(Q), _ptr(K), _dtype_code(Q), _ptr(q_norm_w), _ptr(k_norm_w), float(eps),
+                                 float(rope_theta), _ptr(positions), B, S, Hq, Hkv, d, _ptr(Q_out), _ptr(K_out),
+                                 _stream(Q)), "dma_qk_norm_rope")
+    return Q_out, K_out
+
+
+def prologue(Q, K, V, q_norm_w, k_norm_w, W, A, bias=None, eps=1e-6, rope_theta=10000.0, positions=None,
+             Q_out=None, K_out=None, dt_out=None):
+    """qk_norm_rope on Q and K plus dt from V, in one call -> (Q', K', dt [B, Hkv, S] float32)."""
+    B, S, Hq, Hkv, d, Q_out, K_out = _qk_args(Q, K, q_norm_w, k_norm_w, positions, Q_out, K_out)
+    dev = Q.device
+    _check(V, "V", Q.dtype, 4, dev)
+    if tuple(V.shape) != tuple(K.shape):
+        raise ValueError("V must be [B, S, Hkv, d] matching K")
+    _check(W, "W", Q.dtype, 2, dev)
+    _check(A, "A", torch.float32, 1, dev)
+    if bias is not None:
+        _check(bias, "bias", Q.dtype, 1, dev)
+    if dt_out is None:
+        dt_out = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
+    _check(dt_out, "dt_out", torch.float32, 3, dev)
+    if tuple(dt_out.shape) != (B, Hkv, S):
+        raise ValueError("dt_out must be [B, Hkv, S]")
+    _call(lib().dma_prologue(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), _ptr(q_norm_w), _ptr(k_norm_w), float(eps),
+                             float(rope_theta), _ptr(positions), _ptr(W), _ptr(bias), _ptr(A), B, S, Hq, Hkv, d,
+                             _ptr(Q_out), _ptr(K_out), _ptr(dt_out), _stream(Q)), "dma_prologue")
+    return Q_out, K_out, dt_out

@@ -42,6 +42,11 @@ hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_ne
 hipError_t launch_decode_state_kept(const void *state, int B, int Hkv, int d, int w, int32_t *kept_idx,
                                     int32_t *lens, hipStream_t stream);
 
+// Q/K RMSNorm over head_dim and rotary embedding (prologue.hip).
+hipError_t launch_qk_norm_rope(const void *Q, const void *K, int dtype, const void *wq, const void *wk, float eps,
+                               double rope_theta, const int32_t *positions, int B, int S, int Hq, int Hkv, int d,
+                               void *Qo, void *Ko, hipStream_t stream);
+
 // Limits the launchers rely on (checked by the ABI layer).
 constexpr int kMaxHkvDt = 16;          // dt kernel: heads accumulated in registers
 constexpr int kMaxGroupAttn = 128;     // prefill: query heads per kv head

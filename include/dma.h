@@ -211,6 +211,42 @@ int dma_decode_step(const void *q, const void *k_new, const void *v_new, int dty
 int dma_decode_state_kept(const void *state, size_t state_bytes, int B, int Hkv, int d, int w,
                           int32_t *kept_idx, int32_t *lens, void *stream);
 
+/*
+ * dma_qk_norm_rope -- Doge guide, DMA section, forward step 1: q_norm /
+ * k_norm (an RMSNorm over head_dim with one weight per element) and then the
+ * rotary position embedding that Doge takes from Llama (section on the
+ * modular file's imports).  For every head row x of Q and of K (weight wq for
+ * Q rows, wk for K rows) at position p:
+ *   y_e = w_e * x_e / sqrt(mean_e(x_e^2) + eps)
+ *   a_e = p * rope_theta^(-2e/d)                       for e < d/2
+ *   out_e       = y_e cos a_e - y_{e+d/2} sin a_e
+ *   out_{e+d/2} = y_{e+d/2} cos a_e + y_e sin a_e
+ *
+ *   Q [B][S][Hq][d], K [B][S][Hkv][d] dtype
+ *   q_norm_w, k_norm_w [d] dtype
+ *   eps        rms_norm_eps (>= 0; the DogeConfig default is 1e-6)
+ *   rope_theta rope base (> 1; Llama's default is 10000)
+ *   positions  [B][S] int32 device array, or NULL for p = s
+ *   Q_out, K_out  same shapes and dtype (out); they may be Q and K
+ *                 themselves (in place), but must not overlap them otherwise
+ * Arithmetic is float32 with the angle reduced modulo a turn in float64;
+ * the output is rounded once.  Supports d in {64, 128}.
+ */
+int dma_qk_norm_rope(const void *Q, const void *K, int dtype, const void *q_norm_w, const void *k_norm_w, float eps,
+                     double rope_theta, const int32_t *positions, int B, int S, int Hq, int Hkv, int d, void *Q_out,
+                     void *K_out, void *stream);
+
+/*
+ * dma_prologue -- the per-token work upstream of the selection, from the
+ * projected Q, K and V of B*S tokens: dma_qk_norm_rope on Q and K, then dt
+ * from V exactly as dma_dt with ld_out = S and no out_pos (dt_out
+ * [B][Hkv][S] float32).  Both are validated before either is launched.
+ */
+int dma_prologue(const void *Q, const void *K, const void *V, int dtype, const void *q_norm_w, const void *k_norm_w,
+                 float eps, double rope_theta, const int32_t *positions, const void *W, const void *bias,
+                 const float *A, int B, int S, int Hq, int Hkv, int d, void *Q_out, void *K_out, float *dt_out,
+                 void *stream);
+
 #ifdef __cplusplus
 }
 #endif

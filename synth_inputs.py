@@ -158,3 +158,30 @@ def make_lengths(B, lo, hi, seed) -> np.ndarray:
     """Right-padding lengths ~ U[lo, hi] (inclusive)."""
     rng = np.random.default_rng(seed)
     return rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+
+
+def make_norm_weights(d, dtype, seed):
+    """q_norm and k_norm weights, each [d] ~ U(0.5, 1.5), stored as float32 or bf16
+    bits (RMSNorm weights start at ones; trained ones spread around that)."""
+    rng = np.random.default_rng(seed)
+    wq = rng.uniform(0.5, 1.5, size=d).astype(np.float32)
+    wk = rng.uniform(0.5, 1.5, size=d).astype(np.float32)
+    return _store(wq, dtype), _store(wk, dtype)
+
+
+def make_positions(B, S, kind, seed) -> np.ndarray:
+    """Token positions [B, S] int32.
+
+    kinds:
+      offset  s + o_b with o_b ~ U[0, 2^20]: a chunk after o_b cached tokens
+      large   independent ~ U[0, 2^30): angles far from the first turns
+    """
+    rng = np.random.default_rng(seed)
+    if kind == "offset":
+        o = rng.integers(0, 1 << 20, size=(B, 1), endpoint=True)
+        p = o + np.arange(S)[None, :]
+    elif kind == "large":
+        p = rng.integers(0, 1 << 30, size=(B, S))
+    else:
+        raise ValueError(kind)
+    return np.ascontiguousarray(p, dtype=np.int32)

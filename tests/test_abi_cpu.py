@@ -131,3 +131,30 @@ def test_decode_state_validation(dma):
     assert step(q=ctypes.c_void_p(0x1008)) == -4
     assert dma.dma_decode_state_kept(None, nst, 2, 2, 128, 64, FAKE, None, None) == -1
     assert dma.dma_decode_state_kept(FAKE, nst - 1, 2, 2, 128, 64, FAKE, None, None) == -5
+
+
+def test_qk_norm_rope_validation(dma):
+    def call(Q=FAKE, dtype=1, wq=FAKE, eps=1e-6, theta=10000.0, B=2, S=8, Hq=4, Hkv=2, d=64, Qo=FAKE2):
+        return dma.dma_qk_norm_rope(Q, FAKE, dtype, wq, FAKE, eps, theta, None, B, S, Hq, Hkv, d, Qo, FAKE2, None)
+    assert call(Q=None) == -1
+    assert call(wq=None) == -1
+    assert call(Qo=None) == -1
+    assert call(dtype=3) == -3
+    assert call(B=0) == -2
+    assert call(S=0) == -2
+    assert call(eps=-1.0) == -2
+    assert call(eps=float("nan")) == -2
+    assert call(theta=1.0) == -2
+    assert call(B=65536, S=65536) == -2       # more tokens than an int32 counts
+    assert call(d=96) == -4
+    assert call(Qo=ctypes.c_void_p(0x2008)) == -4
+
+    def pro(V=FAKE, W=FAKE, A=FAKE, dt=FAKE2, Hkv=2, d=64, Q=FAKE):
+        return dma.dma_prologue(Q, FAKE, V, 1, FAKE, FAKE, 1e-6, 10000.0, None, W, None, A, 2, 8, 4, Hkv, d,
+                                FAKE2, FAKE2, dt, None)
+    assert pro(V=None) == -1
+    assert pro(A=None) == -1
+    assert pro(dt=None) == -1
+    assert pro(Q=None) == -1
+    assert pro(Hkv=17) == -4
+    assert pro(W=ctypes.c_void_p(0x1004)) == -4
