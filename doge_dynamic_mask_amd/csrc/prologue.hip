@@ -58,9 +58,41 @@ template <> struct Lanes<float> {
     }
 };
 
-// D: head_dim; NS: row steps whose loads are issued together (a step covers
-// 64 / (lanes per row) rows of the token).
-template <int D, typename T, int NS>
+// Cross-lane moves inside a row's group of LR lanes (LR in {8, 16, 32},
+// groups aligned to LR): DPP where the pattern exists, else ds_swizzle.
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int PATTERN> __device__ __forceinline__ float swz(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), PATTERN));
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowMirror = 0x140, kRowHalfMirror = 0x141;
+constexpr int kSwzXor16 = (0x10 << 10) | 0x1F, kSwzXor31 = (0x1F << 10) | 0x1F;
+
+// sum over the LR lanes of the group, in every lane
+template <int LR> __device__ __forceinline__ float group_sum(float v) {
+    v += dpp<kQuadXor1>(v);
+    v += dpp<kQuadXor2>(v);
+    v += dpp<kRowHalfMirror>(v);                     // lane i <-> 7 - i: the other quad
+    if constexpr (LR >= 16) v += dpp<kRowMirror>(v);  // lane i <-> 15 - i: the other half row
+    if constexpr (LR >= 32) v += swz<kSwzXor16>(v);
+    return v;
+}
+// the value of the mirror lane LR - 1 - i of the group
+template <int LR> __device__ __forceinline__ float group_mirror(float v) {
+    if constexpr (LR == 8) return dpp<kRowHalfMirror>(v);
+    else if constexpr (LR == 16) return dpp<kRowMirror>(v);
+    else return swz<kSwzXor31>(v);
+}
+
+// D: head_dim; NS: row steps per chunk (a step covers 64 / (lanes per row)
+// rows of a token); MULTI: the token's Hq + Hkv rows take more than one chunk.
+//
+// Lane i of a row's group holds 16-byte chunk i of the row's first half if
+// i < LR/2, else chunk LR/2 + (LR - 1 - i) of its second half: the rotation
+// partner of every element then sits in the mirror lane LR - 1 - i, one DPP
+// move away.
+template <int D, typename T, int NS, bool MULTI>
 __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
     const T *Q, const T *K, const T *__restrict__ wq, const T *__restrict__ wk, float eps, double log2_theta,
     const int32_t *__restrict__ positions, int S, int Hq, int Hkv, int ntok, T *Qo, T *Ko) {
@@ -69,91 +101,113 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
     constexpr int LR = D / E;      // lanes per row
     constexpr int RW = 64 / LR;    // rows per step
     constexpr int H = D / 2;       // distinct angles per token
-    static_assert(LR >= 2 && LR <= 64 && 64 % LR == 0 && H <= 64 && H % E == 0, "row split");
+    static_assert(LR == 8 || LR == 16 || LR == 32, "row split");
+    static_assert(H <= 64 && H % E == 0, "angles");
     // turns per position of frequency e: theta^(-2e/d) / (2 pi)
     __shared__ double turns[H];
-    // per wave: cosines then sines of the token's d/2 angles
+    // per wave: cosines then sines of the current token's d/2 angles
     __shared__ __align__(16) float trig[kWaves][2][H];
 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int tok_raw = blockIdx.x * kWaves + wv;
-    const int tok = min(tok_raw, ntok - 1);
     const int li = lane % LR, ri = lane / LR;
-    const int e0 = E * li;         // this lane's first element
-    const bool low = e0 < H;       // first half: out = y cos - partner sin
+    const bool low = li < LR / 2;  // first half: out = y cos - partner sin
+    const int e0 = E * (low ? li : LR / 2 + (LR - 1 - li));  // this lane's first element
     const int nrows = Hq + Hkv;
+    const int nch = (nrows + NS * RW - 1) / (NS * RW);  // chunks per token
+    const int t_raw = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wv);
+    const int t = min(t_raw, ntok - 1);  // the wave's token
 
-    // the loads of NS row steps are issued together; rows past the last
-    // repeat it and are not stored
-    u32x4 xr[NS];
-    size_t off[NS];
-    bool isq[NS];
-    auto load_rows = [&](int r0) __attribute__((always_inline)) {
+    // Element offset of this lane's 16 bytes of row r of token t in Q (r < Hq)
+    // or K.  Rows past the last are clamped to it: such lanes load and store
+    // the last row with the very values its own lanes hold.
+    auto row_off = [&](int t, int r) __attribute__((always_inline)) {
+        const bool q = r < Hq;
+        const int64_t row = (int64_t)t * (q ? Hq : Hkv) + (q ? r : r - Hq);
+        return row * D + e0;
+    };
+    auto load = [&](u32x4 (&x)[NS], int t, int c) __attribute__((always_inline)) {
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-            const int r = min(r0 + st * RW + ri, nrows - 1);
-            isq[st] = r < Hq;
-            off[st] = isq[st] ? ((size_t)tok * Hq + r) * D + e0 : ((size_t)tok * Hkv + (r - Hq)) * D + e0;
-            xr[st] = *reinterpret_cast<const u32x4 *>((isq[st] ? Q : K) + off[st]);
+            const int r = min(c * NS * RW + st * RW + ri, nrows - 1);
+            x[st] = *reinterpret_cast<const u32x4 *>((r < Hq ? Q : K) + row_off(t, r));
         }
     };
-    // the first rows are requested before anything else, so that their
-    // latency overlaps the position load and the angle work
-    load_rows(0);
-    const int pos = positions ? positions[tok] : tok % S;
+
     const u32x4 wqr = *reinterpret_cast<const u32x4 *>(wq + e0);
     const u32x4 wkr = *reinterpret_cast<const u32x4 *>(wk + e0);
+    u32x4 xa[NS], xb[NS];
+    load(xa, t, 0);
+    const int pos = positions ? positions[t] : t % S;
     if (threadIdx.x < H) turns[threadIdx.x] = exp2(-(2.0 * threadIdx.x / D) * log2_theta) * 0.15915494309189535;
     __syncthreads();
-    if (tok_raw >= ntok) return;  // uniform per wave, after the only block barrier
+    if (t_raw >= ntok) return;      // uniform per wave, after the only block barrier
 
-    {
-        const int e = lane % H;   // lanes past d/2 repeat the first d/2 (same values, same slots)
-        const double a = (double)pos * turns[e];
-        const float r = (float)(a - rint(a)) * 6.283185307179586f;  // in [-pi, pi]
-        float s, c;
-        sincosf(r, &s, &c);
-        trig[wv][0][e] = c;
-        trig[wv][1][e] = s;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float cs[E], sn[E], wqv[E], wkv[E];
-#pragma unroll
-    for (int i = 0; i < E; i += 4) {
-        const float4 c4 = *reinterpret_cast<const float4 *>(&trig[wv][0][e0 % H + i]);
-        const float4 s4 = *reinterpret_cast<const float4 *>(&trig[wv][1][e0 % H + i]);
-        cs[i] = c4.x; cs[i + 1] = c4.y; cs[i + 2] = c4.z; cs[i + 3] = c4.w;
-        sn[i] = s4.x; sn[i + 1] = s4.y; sn[i + 2] = s4.z; sn[i + 3] = s4.w;
-    }
+    float wqv[E], wkv[E], cs[E], sn[E];
     L::unpack(wqr, wqv);
     L::unpack(wkr, wkv);
 
-    for (int r0 = 0;;) {
+    // the sine and cosine of this lane's elements at position p: lane l
+    // works out angle l % (d/2), the wave exchanges them through LDS
+    auto angles = [&](int p) __attribute__((always_inline)) {
+        const int e = lane % H;     // lanes past d/2 repeat the first d/2 (same values, same slots)
+        const double a = (double)p * turns[e];
+        const float r = (float)(a - rint(a)) * 6.283185307179586f;  // in [-pi, pi]
+        float sv, cv;
+        sincosf(r, &sv, &cv);
+        trig[wv][0][e] = cv;
+        trig[wv][1][e] = sv;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int i = 0; i < E; i += 4) {
+            const float4 c4 = *reinterpret_cast<const float4 *>(&trig[wv][0][e0 % H + i]);
+            const float4 s4 = *reinterpret_cast<const float4 *>(&trig[wv][1][e0 % H + i]);
+            cs[i] = c4.x; cs[i + 1] = c4.y; cs[i + 2] = c4.z; cs[i + 3] = c4.w;
+            sn[i] = s4.x; sn[i + 1] = s4.y; sn[i + 2] = s4.z; sn[i + 3] = s4.w;
+        }
+    };
+
+    auto compute = [&](const u32x4 (&x)[NS], int t, int c) __attribute__((always_inline)) {
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-            float x[E];
-            L::unpack(xr[st], x);
+            const int r = min(c * NS * RW + st * RW + ri, nrows - 1);
+            const bool q = r < Hq;
+            float xv[E];
+            L::unpack(x[st], xv);
             float ss = 0.f;
 #pragma unroll
-            for (int i = 0; i < E; ++i) ss = fmaf(x[i], x[i], ss);
-#pragma unroll
-            for (int o = 1; o < LR; o <<= 1) ss += __shfl_xor(ss, o, 64);
+            for (int i = 0; i < E; ++i) ss = fmaf(xv[i], xv[i], ss);
+            ss = group_sum<LR>(ss);
             const float inv = rsqrtf(ss / (float)D + eps);
             float y[E], out[E];
 #pragma unroll
-            for (int i = 0; i < E; ++i) y[i] = x[i] * inv * (isq[st] ? wqv[i] : wkv[i]);
+            for (int i = 0; i < E; ++i) y[i] = xv[i] * inv * (q ? wqv[i] : wkv[i]);
 #pragma unroll
             for (int i = 0; i < E; ++i) {
-                const float p = __shfl_xor(y[i], LR / 2, 64);  // element e + d/2 (or e - d/2)
-                out[i] = fmaf(y[i], cs[i], (low ? -p : p) * sn[i]);
+                const float pv = group_mirror<LR>(y[i]);  // element e + d/2 (or e - d/2)
+                out[i] = fmaf(y[i], cs[i], (low ? -pv : pv) * sn[i]);
             }
-            if (r0 + st * RW + ri < nrows) *reinterpret_cast<u32x4 *>((isq[st] ? Qo : Ko) + off[st]) = L::pack(out);
+            *reinterpret_cast<u32x4 *>((q ? Qo : Ko) + row_off(t, r)) = L::pack(out);
         }
-        r0 += NS * RW;
-        if (r0 >= nrows) break;
-        load_rows(r0);
+    };
+
+    angles(pos);
+    if constexpr (!MULTI) {
+        compute(xa, t, 0);
+    } else {
+        // chunk c is worked on while chunk c + 1 is in flight; past the last
+        // chunk the request repeats it, so that requests and stores are
+        // unconditional and the wait for a chunk counts exactly the memory
+        // operations issued after it
+        for (int c = 0;;) {
+            load(xb, t, min(c + 1, nch - 1));
+            compute(xa, t, c);
+            if (++c >= nch) break;
+            load(xa, t, min(c + 1, nch - 1));
+            compute(xb, t, c);
+            if (++c >= nch) break;
+        }
     }
 }
 
@@ -162,19 +216,29 @@ void launch_t(const void *Q, const void *K, const void *wq, const void *wk, floa
               const int32_t *positions, int S, int Hq, int Hkv, int ntok, void *Qo, void *Ko, hipStream_t stream) {
     constexpr int RW = 64 / (D / Lanes<T>::kElems);
     const int steps = (Hq + Hkv + RW - 1) / RW;
+    // a token's rows in as few chunks of at most 4 steps as possible, each
+    // of equal size
+    const int nchunk = (steps + 3) / 4;
+    const int ns = (steps + nchunk - 1) / nchunk;
     const unsigned grid = (unsigned)((ntok + kWaves - 1) / kWaves);
-#define DMA_QKNR(NS)                                                                                         \
-    hipLaunchKernelGGL((qk_norm_rope_kernel<D, T, NS>), dim3(grid), dim3(kThreads), 0, stream, (const T *)Q, \
-                       (const T *)K, (const T *)wq, (const T *)wk, eps, log2_theta, positions, S, Hq, Hkv, ntok, \
-                       (T *)Qo, (T *)Ko)
-    if (steps <= 1)
-        DMA_QKNR(1);
-    else if (steps <= 2)
-        DMA_QKNR(2);
-    else if (steps <= 4)
-        DMA_QKNR(4);
-    else
-        DMA_QKNR(8);
+#define DMA_QKNR(NS, MULTI)                                                                                   \
+    hipLaunchKernelGGL((qk_norm_rope_kernel<D, T, NS, MULTI>), dim3(grid), dim3(kThreads), 0, stream,         \
+                       (const T *)Q, (const T *)K, (const T *)wq, (const T *)wk, eps, log2_theta, positions, S, Hq, \
+                       Hkv, ntok, (T *)Qo, (T *)Ko)
+    if (nchunk == 1) {
+        switch (ns) {
+            case 1: DMA_QKNR(1, false); break;
+            case 2: DMA_QKNR(2, false); break;
+            case 3: DMA_QKNR(3, false); break;
+            default: DMA_QKNR(4, false); break;
+        }
+    } else {
+        switch (ns) {
+            case 2: DMA_QKNR(2, true); break;
+            case 3: DMA_QKNR(3, true); break;
+            default: DMA_QKNR(4, true); break;
+        }
+    }
 #undef DMA_QKNR
 }
 
