@@ -60,6 +60,10 @@ def _load():
         lib.oracle_decode.restype = None
         lib.oracle_qk_norm_rope.argtypes = [P, P, I, ctypes.c_double, ctypes.c_double, P, I64, I, P]
         lib.oracle_qk_norm_rope.restype = None
+        lib.oracle_attn_bwd.argtypes = [P, P, P, I, P, P, P, I, I, I, I, I, I, P, P, P, P]
+        lib.oracle_attn_bwd.restype = None
+        lib.oracle_dt_bwd.argtypes = [P, P, P, P, I, I, I, I, I, P, P, P, P, P]
+        lib.oracle_dt_bwd.restype = None
         _lib = lib
     return _lib
 
@@ -182,3 +186,49 @@ def qk_norm_rope(x, w, eps, theta, positions):
     out = np.empty(x.shape, dtype=np.float64)
     _load().oracle_qk_norm_rope(_ptr(x), _ptr(w), tx, float(eps), float(theta), _ptr(pos), n, d, _ptr(out))
     return out
+
+
+def attn_bwd(Q, K, V, dt32, w, dO, seqlens=None):
+    """fp64 gradients (dQ, dK, dV, ddt) of attn() for an upstream gradient dO [B,S,Hq,d]
+    (same storage type as Q).  Kept sets are the forward's; selection has no gradient."""
+    Q, tq = _elem_array(Q)
+    K, tk = _elem_array(K)
+    V, tv = _elem_array(V)
+    dO, to = _elem_array(dO)
+    assert tq == tk == tv == to
+    dt32 = np.ascontiguousarray(dt32, dtype=np.float32)
+    B, S, Hq, d = Q.shape
+    Hkv = K.shape[2]
+    assert K.shape == (B, S, Hkv, d) and V.shape == K.shape and dO.shape == Q.shape and Hq % Hkv == 0
+    assert dt32.shape == (B, Hkv, S)
+    dQ = np.empty((B, S, Hq, d))
+    dK = np.empty((B, S, Hkv, d))
+    dV = np.empty((B, S, Hkv, d))
+    ddt = np.empty((B, Hkv, S))
+    seq = _seq(seqlens)
+    _load().oracle_attn_bwd(_ptr(Q), _ptr(K), _ptr(V), tq, _ptr(dt32), _ptr(seq), _ptr(dO), B, S, Hq, Hkv, d,
+                            int(w), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ddt))
+    return dQ, dK, dV, ddt
+
+
+def dt_bwd(V, W, bias, A, ddt):
+    """fp64 gradients of dt() for an upstream gradient ddt [B,Hkv,S]:
+    (dV through dt_proj [B,S,Hkv,d], dW [Hkv,Hkv*d], dbias [Hkv], dA [Hkv])."""
+    V, tv = _elem_array(V)
+    W, tw = _elem_array(W)
+    assert tv == tw
+    if bias is not None:
+        bias, tb = _elem_array(bias)
+        assert tb == tv
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    B, S, Hkv, d = V.shape
+    assert W.shape == (Hkv, Hkv * d) and A.shape == (Hkv,)
+    ddt = np.ascontiguousarray(ddt, dtype=np.float64)
+    assert ddt.shape == (B, Hkv, S)
+    dV = np.empty((B, S, Hkv, d))
+    dW = np.empty((Hkv, Hkv * d))
+    dbias = np.empty(Hkv)
+    dA = np.empty(Hkv)
+    _load().oracle_dt_bwd(_ptr(V), _ptr(W), _ptr(bias), _ptr(A), tv, B, S, Hkv, d, _ptr(ddt), _ptr(dV), _ptr(dW),
+                          _ptr(dbias), _ptr(dA))
+    return dV, dW, dbias, dA

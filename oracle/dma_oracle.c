@@ -373,3 +373,178 @@ void oracle_qk_norm_rope(const void *x, const void *w, int dtype, double eps, do
         }
     }
 }
+
+/*
+ * Gradients of the prefill attention (oracle_attn) with respect to Q, K, V and
+ * dt, for an upstream gradient dO of the output.  The kept sets are those of
+ * the forward (the top-w selection itself is piecewise constant in dt and has
+ * no gradient; every kept key's dt enters its score additively, Doge guide,
+ * DMA forward steps 3 and 4).  With s_k = c q.k_k + dt_k (c = d^-0.5) over the
+ * kept keys k of a query row, p = softmax(s), o = sum_k p_k v_k:
+ *   dp_k = dO . v_k,  ds_k = p_k (dp_k - dO . o)
+ *   dq  = c sum_k ds_k k_k
+ *   dk_k += c ds_k q,  dv_k += p_k dO,  ddt_k += ds_k
+ * summed over every query row and query head that keeps key k.  Padded rows
+ * contribute nothing.
+ *
+ *   dO [B][S][Hq][d] (dtype, like Q)
+ *   dQ [B][S][Hq][d], dK/dV [B][S][Hkv][d], ddt [B][Hkv][S]: double (out)
+ * Units (b, kv head) are independent and split over threads; within a unit
+ * the rows run in order.
+ */
+void oracle_attn_bwd(const void *Q, const void *K, const void *V, int dtype, const float *dt,
+                     const int32_t *seqlens, const void *dO, int B, int S, int Hq, int Hkv, int d, int w,
+                     double *dQ, double *dK, double *dV, double *ddt)
+{
+    const int G = Hq / Hkv;
+    const double c = 1.0 / sqrt((double)d);
+    const size_t kvs = (size_t)Hkv * d;
+#pragma omp parallel
+    {
+        key_t_ *buf = (key_t_ *)malloc(sizeof(key_t_) * (size_t)(S > 0 ? S : 1));
+        double *s = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+        double *dp = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+        double *o = (double *)malloc(sizeof(double) * (size_t)d);
+#pragma omp for collapse(2) schedule(dynamic, 1)
+        for (int b = 0; b < B; ++b)
+            for (int g = 0; g < Hkv; ++g) {
+                const int L = seqlens ? seqlens[b] : S;
+                const float *drow = dt + ((size_t)b * Hkv + g) * S;
+                double *ddt_row = ddt + ((size_t)b * Hkv + g) * S;
+                for (int j = 0; j < S; ++j) {
+                    ddt_row[j] = 0.0;
+                    for (int e = 0; e < d; ++e) {
+                        dK[((size_t)b * S + j) * kvs + (size_t)g * d + e] = 0.0;
+                        dV[((size_t)b * S + j) * kvs + (size_t)g * d + e] = 0.0;
+                    }
+                }
+                for (int i = 0; i < S; ++i)
+                    for (int hh = 0; hh < G; ++hh) {
+                        const int hq = g * G + hh;
+                        const size_t qo = (((size_t)b * S + i) * Hq + hq) * d;
+                        double *dq = dQ + qo;
+                        for (int e = 0; e < d; ++e)
+                            dq[e] = 0.0;
+                        if (i >= L)
+                            continue;
+                        const int nk = row_kept(drow, i, L, w, buf);
+                        /* forward: scores, softmax, output */
+                        double m = -INFINITY;
+                        for (int k = 0; k < nk; ++k) {
+                            const size_t kr = ((size_t)b * S + buf[k].idx) * kvs + (size_t)g * d;
+                            double dot = 0.0;
+                            for (int e = 0; e < d; ++e)
+                                dot += elem(Q, dtype, qo + e) * elem(K, dtype, kr + e);
+                            s[k] = c * dot + (double)drow[buf[k].idx];
+                            if (s[k] > m)
+                                m = s[k];
+                        }
+                        double l = 0.0;
+                        for (int k = 0; k < nk; ++k) {
+                            s[k] = exp(s[k] - m);
+                            l += s[k];
+                        }
+                        for (int e = 0; e < d; ++e)
+                            o[e] = 0.0;
+                        for (int k = 0; k < nk; ++k) {
+                            s[k] /= l; /* s now holds p */
+                            const size_t vr = ((size_t)b * S + buf[k].idx) * kvs + (size_t)g * d;
+                            for (int e = 0; e < d; ++e)
+                                o[e] += s[k] * elem(V, dtype, vr + e);
+                        }
+                        /* backward */
+                        double dod = 0.0;
+                        for (int e = 0; e < d; ++e)
+                            dod += elem(dO, dtype, qo + e) * o[e];
+                        for (int k = 0; k < nk; ++k) {
+                            const size_t vr = ((size_t)b * S + buf[k].idx) * kvs + (size_t)g * d;
+                            double t = 0.0;
+                            for (int e = 0; e < d; ++e)
+                                t += elem(dO, dtype, qo + e) * elem(V, dtype, vr + e);
+                            dp[k] = s[k] * (t - dod); /* ds_k */
+                        }
+                        for (int k = 0; k < nk; ++k) {
+                            const int j = buf[k].idx;
+                            const size_t kr = ((size_t)b * S + j) * kvs + (size_t)g * d;
+                            for (int e = 0; e < d; ++e) {
+                                dq[e] += c * dp[k] * elem(K, dtype, kr + e);
+                                dK[kr + e] += c * dp[k] * elem(Q, dtype, qo + e);
+                                dV[kr + e] += s[k] * elem(dO, dtype, qo + e);
+                            }
+                            ddt_row[j] += dp[k];
+                        }
+                    }
+            }
+        free(o);
+        free(dp);
+        free(s);
+        free(buf);
+    }
+}
+
+/*
+ * Gradients of dt (oracle_dt) for an upstream gradient ddt: with
+ * x = bias + W . concat_h V (per token and kv head), dt = exp(A softplus(x)),
+ *   ddt/dA = dt softplus(x),  ddt/dx = dt A sigmoid(x)
+ * so dx = ddt dt A sigmoid(x) and
+ *   dA[h] = sum ddt dt softplus(x),  dbias[h] = sum dx,
+ *   dW[h][c] = sum dx[h] V[c],       dV[c] += sum_h dx[h] W[h][c]
+ * (sums over batches and positions).  Doge guide, DMA forward step 3.
+ *
+ *   ddt [B][Hkv][S] double
+ *   dV [B][S][Hkv][d] double (out, the dt path's part only), dW [Hkv][Hkv*d],
+ *   dbias [Hkv], dA [Hkv] double (out)
+ */
+void oracle_dt_bwd(const void *V, const void *W, const void *bias, const float *A, int dtype,
+                   int B, int S, int Hkv, int d, const double *ddt,
+                   double *dV, double *dW, double *dbias, double *dA)
+{
+    const int width = Hkv * d;
+    double *dx = (double *)malloc(sizeof(double) * (size_t)B * S * Hkv);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int s = 0; s < S; ++s) {
+            const size_t vrow = ((size_t)b * S + s) * width;
+            for (int h = 0; h < Hkv; ++h) {
+                double x = bias ? elem(bias, dtype, h) : 0.0;
+                for (int c = 0; c < width; ++c)
+                    x += elem(W, dtype, (size_t)h * width + c) * elem(V, dtype, vrow + c);
+                const double a = (double)A[h];
+                const double dtv = exp(a * softplus(x));
+                const double sig = 1.0 / (1.0 + exp(-x));
+                const double g = ddt[((size_t)b * Hkv + h) * S + s];
+                dx[((size_t)b * S + s) * Hkv + h] = g * dtv * a * sig;
+            }
+            for (int c = 0; c < width; ++c) {
+                double acc = 0.0;
+                for (int h = 0; h < Hkv; ++h)
+                    acc += dx[((size_t)b * S + s) * Hkv + h] * elem(W, dtype, (size_t)h * width + c);
+                dV[vrow + c] = acc;
+            }
+        }
+    for (int h = 0; h < Hkv; ++h) {
+        double sa = 0.0, sb = 0.0;
+        for (int b = 0; b < B; ++b)
+            for (int s = 0; s < S; ++s) {
+                const size_t vrow = ((size_t)b * S + s) * width;
+                double x = bias ? elem(bias, dtype, h) : 0.0;
+                for (int c = 0; c < width; ++c)
+                    x += elem(W, dtype, (size_t)h * width + c) * elem(V, dtype, vrow + c);
+                const double sp = softplus(x);
+                sa += ddt[((size_t)b * Hkv + h) * S + s] * exp((double)A[h] * sp) * sp;
+                sb += dx[((size_t)b * S + s) * Hkv + h];
+            }
+        dA[h] = sa;
+        dbias[h] = sb;
+    }
+#pragma omp parallel for schedule(static)
+    for (int hc = 0; hc < Hkv * width; ++hc) {
+        const int h = hc / width, c = hc % width;
+        double acc = 0.0;
+        for (int b = 0; b < B; ++b)
+            for (int s = 0; s < S; ++s)
+                acc += dx[((size_t)b * S + s) * Hkv + h] * elem(V, dtype, ((size_t)b * S + s) * width + c);
+        dW[hc] = acc;
+    }
+    free(dx);
+}
