@@ -16,6 +16,9 @@ Functions mirror the C ABI in ``include/dma.h``:
     qk_norm_rope(Q, K, q_norm_w, k_norm_w, ...)         -> (Q', K')
     prologue(Q, K, V, q_norm_w, k_norm_w, W, A, ...)    -> (Q', K', dt)
     DecodeState, decode_state_init(...), decode_step(...)  incremental decode
+    attn_bwd(Q, K, V, dt, tau, tie, w, dO, seqlens=None) -> (dQ, dK, dV, ddt)
+    dt_bwd(V, W, A, ddt, bias=None, dV=None)            -> (dW, dbias, dA); adds into dV
+    prefill_bwd(Q, K, V, W, A, w, dO, ...)               -> dict of every gradient
 """
 from __future__ import annotations
 
@@ -38,7 +41,8 @@ _STATUS = {
 EXPORTS = ("dma_version", "dma_status_str", "dma_dt", "dma_select", "dma_attn_fwd",
            "dma_decode_workspace_bytes", "dma_decode", "dma_decode_state_bytes",
            "dma_decode_step_workspace_bytes", "dma_decode_state_init", "dma_decode_step",
-           "dma_decode_state_kept", "dma_qk_norm_rope", "dma_prologue")
+           "dma_decode_state_kept", "dma_qk_norm_rope", "dma_prologue",
+           "dma_attn_bwd_workspace_bytes", "dma_attn_bwd", "dma_dt_bwd_workspace_bytes", "dma_dt_bwd")
 
 
 class DmaError(RuntimeError):
@@ -85,6 +89,14 @@ def lib():
     L.dma_qk_norm_rope.restype = I
     L.dma_prologue.argtypes = [P, P, P, I, P, P, ctypes.c_float, D, P, P, P, P, I, I, I, I, I, P, P, P, P]
     L.dma_prologue.restype = I
+    L.dma_attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    L.dma_attn_bwd_workspace_bytes.restype = SZ
+    L.dma_attn_bwd.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, SZ, P]
+    L.dma_attn_bwd.restype = I
+    L.dma_dt_bwd_workspace_bytes.argtypes = [I, I, I, I]
+    L.dma_dt_bwd_workspace_bytes.restype = SZ
+    L.dma_dt_bwd.argtypes = [P, P, P, P, I, P, I, I, I, I, P, P, P, P, P, SZ, P]
+    L.dma_dt_bwd.restype = I
     _lib = L
     return L
 
@@ -343,3 +355,86 @@ def prologue(Q, K, V, q_norm_w, k_norm_w, W, A, bias=None, eps=1e-6, rope_theta=
                              float(rope_theta), _ptr(positions), _ptr(W), _ptr(bias), _ptr(A), B, S, Hq, Hkv, d,
                              _ptr(Q_out), _ptr(K_out), _ptr(dt_out), _stream(Q)), "dma_prologue")
     return Q_out, K_out, dt_out
+
+
+def attn_bwd_workspace_bytes(B, S, Hq, Hkv, d, w):
+    return int(lib().dma_attn_bwd_workspace_bytes(B, S, Hq, Hkv, d, w))
+
+
+def attn_bwd(Q, K, V, dt_, tau, tie, w, dO, seqlens=None, workspace=None, out=None):
+    """Gradients of attn_fwd for the upstream gradient dO: (dQ, dK, dV) in the dtype of Q and
+    ddt [B, Hkv, S] float32 (bf16 only)."""
+    _check(Q, "Q", torch.bfloat16, 4)
+    dev = Q.device
+    B, S, Hq, d = Q.shape
+    Hkv = K.shape[2]
+    for name, t in (("K", K), ("V", V)):
+        _check(t, name, Q.dtype, 4, dev)
+        if tuple(t.shape) != (B, S, Hkv, d):
+            raise ValueError(f"{name} must be [B, S, Hkv, d] matching Q")
+    _check(dO, "dO", Q.dtype, 4, dev)
+    if dO.shape != Q.shape:
+        raise ValueError("dO must have the shape of Q")
+    for name, t, dtp in (("dt", dt_, torch.float32), ("tau", tau, torch.float32), ("tie", tie, torch.int32)):
+        _check(t, name, dtp, 3, dev)
+        if tuple(t.shape) != (B, Hkv, S):
+            raise ValueError(f"{name} must be [B, Hkv, S]")
+    if seqlens is not None:
+        _check(seqlens, "seqlens", torch.int32, 1, dev)
+    nbytes = attn_bwd_workspace_bytes(B, S, Hq, Hkv, d, w)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V),
+               torch.empty((B, Hkv, S), dtype=torch.float32, device=dev))
+    dQ, dK, dV, ddt = out
+    _call(lib().dma_attn_bwd(_ptr(Q), _ptr(K), _ptr(V), BF16, _ptr(dt_), _ptr(tau), _ptr(tie), _ptr(seqlens),
+                             _ptr(dO), B, S, Hq, Hkv, d, int(w), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ddt),
+                             _ptr(workspace), workspace.numel(), _stream(Q)), "dma_attn_bwd")
+    return dQ, dK, dV, ddt
+
+
+def dt_bwd_workspace_bytes(B, S, Hkv, d):
+    return int(lib().dma_dt_bwd_workspace_bytes(B, S, Hkv, d))
+
+
+def dt_bwd(V, W, A, ddt, bias=None, dV=None, workspace=None):
+    """Gradients of dt() for the upstream gradient ddt [B, Hkv, S] float32: (dW, dbias, dA) float32.
+    If dV [B, S, Hkv, d] (dtype of V) is given, the dt path's part of the value gradient is added to it."""
+    _check(V, "V", ndim=4)
+    dev = V.device
+    _check(W, "W", V.dtype, 2, dev)
+    _check(A, "A", torch.float32, 1, dev)
+    _check(ddt, "ddt", torch.float32, 3, dev)
+    B, S, Hkv, d = V.shape
+    if tuple(ddt.shape) != (B, Hkv, S):
+        raise ValueError("ddt must be [B, Hkv, S]")
+    if bias is not None:
+        _check(bias, "bias", V.dtype, 1, dev)
+    if dV is not None:
+        _check(dV, "dV", V.dtype, 4, dev)
+        if dV.shape != V.shape:
+            raise ValueError("dV must have the shape of V")
+    nbytes = dt_bwd_workspace_bytes(B, S, Hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    dW = torch.empty((Hkv, Hkv * d), dtype=torch.float32, device=dev)
+    dbias = torch.empty(Hkv, dtype=torch.float32, device=dev)
+    dA = torch.empty(Hkv, dtype=torch.float32, device=dev)
+    _call(lib().dma_dt_bwd(_ptr(V), _ptr(W), _ptr(bias), _ptr(A), _dtype_code(V), _ptr(ddt), B, S, Hkv, d,
+                           _ptr(dV), _ptr(dW), _ptr(dbias), _ptr(dA), _ptr(workspace), workspace.numel(),
+                           _stream(V)), "dma_dt_bwd")
+    return dW, dbias, dA
+
+
+def prefill_bwd(Q, K, V, W, A, w, dO, bias=None, seqlens=None, fwd=None):
+    """Every gradient of prefill() for the upstream gradient dO: dQ, dK, dV (attention and dt path),
+    dW, dbias, dA and ddt.  fwd = (dt, tau, tie) of the forward, recomputed when None."""
+    if fwd is None:
+        d_ = dt(V, W, A, bias)
+        tau, tie = select(d_, w, seqlens)
+    else:
+        d_, tau, tie = fwd
+    dQ, dK, dV, ddt = attn_bwd(Q, K, V, d_, tau, tie, w, dO, seqlens)
+    dW, dbias, dA = dt_bwd(V, W, A, ddt, bias, dV=dV)
+    return {"dQ": dQ, "dK": dK, "dV": dV, "dW": dW, "dbias": dbias, "dA": dA, "ddt": ddt}

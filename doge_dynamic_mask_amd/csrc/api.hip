@@ -174,4 +174,44 @@ int dma_prologue(const void *Q, const void *K, const void *V, int dtype, const v
     return from_hip(dma::launch_dt(V, W, bias, A, dtype, B, S, Hkv, d, dt_out, S, nullptr, (hipStream_t)stream));
 }
 
+size_t dma_attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int d, int w) {
+    if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || w < 1 || Hq % Hkv != 0 || !head_dim_ok(d)) return 0;
+    return dma::attn_bwd_ws_bytes(B, S, Hq);
+}
+
+int dma_attn_bwd(const void *Q, const void *K, const void *V, int dtype, const float *dt, const float *tau,
+                 const int32_t *tie, const int32_t *seqlens, const void *dO, int B, int S, int Hq, int Hkv, int d,
+                 int w, void *dQ, void *dK, void *dV, float *ddt, void *ws, size_t ws_bytes, void *stream) {
+    if (!Q || !K || !V || !dt || !tau || !tie || !dO || !dQ || !dK || !dV || !ddt) return DMA_ERR_NULL;
+    if (!dtype_ok(dtype)) return DMA_ERR_DTYPE;
+    if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || d < 1 || w < 1 || Hq % Hkv != 0) return DMA_ERR_SHAPE;
+    const int G = Hq / Hkv;
+    if (dtype != DMA_BF16 || !head_dim_ok(d) || G > dma::kMaxGroupBwd || 64 % G != 0) return DMA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hkv * S > 0x7fffffff) return DMA_ERR_UNSUPPORTED;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(dQ) || !aligned16(dK) ||
+        !aligned16(dV))
+        return DMA_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < dma::attn_bwd_ws_bytes(B, S, Hq)) return DMA_ERR_WORKSPACE;
+    return from_hip(dma::launch_attn_bwd(Q, K, V, dt, tau, tie, seqlens, dO, B, S, Hq, Hkv, d, dQ, dK, dV, ddt, ws,
+                                         (hipStream_t)stream));
+}
+
+size_t dma_dt_bwd_workspace_bytes(int B, int S, int Hkv, int d) {
+    if (B < 1 || S < 1 || Hkv < 1 || !head_dim_ok(d)) return 0;
+    return dma::dt_bwd_ws_bytes(B, S, Hkv, d);
+}
+
+int dma_dt_bwd(const void *V, const void *W, const void *bias, const float *A, int dtype, const float *ddt, int B,
+               int S, int Hkv, int d, void *dV, float *dW, float *dbias, float *dA, void *ws, size_t ws_bytes,
+               void *stream) {
+    if (!V || !W || !A || !ddt || !dW || !dA) return DMA_ERR_NULL;
+    if (!dtype_ok(dtype)) return DMA_ERR_DTYPE;
+    if (B < 1 || S < 1 || Hkv < 1 || d < 1) return DMA_ERR_SHAPE;
+    if (!head_dim_ok(d) || Hkv > dma::kMaxHkvDt) return DMA_ERR_UNSUPPORTED;
+    if ((int64_t)B * S > 0x7fffffff || dma::dt_bwd_lds_bytes(Hkv, d) > 65536) return DMA_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < dma::dt_bwd_ws_bytes(B, S, Hkv, d)) return DMA_ERR_WORKSPACE;
+    return from_hip(dma::launch_dt_bwd(V, W, bias, A, dtype, ddt, B, S, Hkv, d, dV, dW, dbias, dA, ws,
+                                       (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -1,0 +1,522 @@
+// Backward of the prefill attention under the dynamic top-w mask.
+// Doge guide (gitcode), DMA section, forward steps 3 and 4: training runs the
+// same masked attention, s_ij = d^-0.5 q_i.k_j + dt_j over the kept keys j of
+// row i, p = softmax(s), o_i = sum_j p_ij v_j, and learns end to end through
+// dt what to mask.  The kept sets are the forward's (the top-w selection is
+// piecewise constant in dt); with dp_ij = dO_i.v_j and D_i = dO_i.o_i =
+// sum_j p_ij dp_ij:
+//   ds_ij = p_ij (dp_ij - D_i)
+//   dq_i = c sum_j ds_ij k_j,  dk_j = c sum_i ds_ij q_i,  dv_j = sum_i p_ij dO_i,
+//   ddt_j = sum_i ds_ij        (c = d^-0.5; sums over rows and query heads).
+//
+// Two kernels, neither with atomics, so every result is deterministic.
+//
+// Query side (attn_bwd_q_kernel): one workgroup per (batch, kv head, tile of
+// 64 / G query rows), its four waves holding 16 (row, head) pairs each, one
+// pair per lane column.  Key blocks of 64 from position 0 to the tile's last
+// row are staged in LDS; every kept test is evaluated (key j is kept by row i
+// when j <= i < L and selkey(dt_j, j) >= selkey(tau_i, tie_i)).  Pass 1 finds
+// each pair's log-sum-exp; pass 2 recomputes the scores and forms dS^T and
+// dQ^T += K^T dS^T.  D_i is accumulated in pass 1 as sum_j p_ij dp_ij (with
+// the same online rescaling as the softmax sum), in float32 from the very
+// weights the gradients use, rather than from a rounded output: the dt
+// gradient of a key kept with weight near 1 by many rows is a sum of nearly
+// cancelling terms, and an output rounded to bf16 would leave its rounding in
+// every one of them.  It also writes each pair's log-sum-exp and D_i for the
+// key side.
+//
+// Key side (attn_bwd_kv_kernel): one workgroup per (batch, kv head, tile of
+// 64 or 128 keys); every wave holds 16 or 32 keys, one key per lane column,
+// with their K and V rows as MFMA operands in registers for the whole
+// workgroup.  By nesting the rows that keep key j form a run [j, e_j), and the
+// thresholds grow with the row, so the workgroup walks row blocks of 64 pairs
+// from its first key on and stops at the first row whose threshold passes all
+// of its keys.  dV^T += dO^T P and dK^T += Q^T dS accumulate in registers;
+// ddt is the column sum of dS.
+//
+// Both kernels touch every (pair, key) of the causal range they walk, not only
+// the kept ones: work grows like the dense causal attention rather than like
+// the kept count.
+//
+// Layout facts of v_mfma_f32_16x16x32_bf16 (l = lane, q = l / 16):
+//   A[m = l%16][k = 8q + j], B[k = 8q + j][n = l%16], C[m = 4q + i][n = l%16].
+// A product over a 32-long k range whose operand comes from accumulators uses
+// the k-slot order (q, j) -> 16 (j / 4) + 4q + j % 4: then the B operand of
+// lane l is exactly the four values of each of two 16-row accumulator tiles
+// that lane l holds, and the A operand is two LDS transpose reads of four rows
+// each.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dma {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPairs = 64;   // (row, head) pairs per query tile and per row block
+constexpr int kBlk = 64;     // keys per block on the query side
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i16x4 lds_tr16(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS row pitch (bf16 elements) of every staged tile: a 16- or 48-word step
+// between rows, so that row reads and transpose reads spread over the banks.
+template <int D> constexpr int pitch() { return D + 32; }
+
+// A operand of a product over the 32 rows base .. base+31 of the row-major
+// LDS tile T (pitch P), column c0 + l%16, in the permuted k-slot order.
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
+// of the four 16-bit values at the addresses of lanes i/4 + 4s (s = 0..3);
+// with lane k of group q pointing at row r0 + k/4, column c0 + 4 (k%4), lane i
+// gets column c0 + i of rows r0 .. r0+3.
+template <int P>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t *T, int base, int c0, int lane) {
+    const int q = lane >> 4, k = lane & 15;
+    const uint16_t *p = T + (base + 4 * q + (k >> 2)) * P + c0 + 4 * (k & 3);
+    const i16x4 lo = lds_tr16(p);
+    const i16x4 hi = lds_tr16(p + 16 * P);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// B operand in the same permuted order from two accumulator tiles.
+__device__ __forceinline__ bf16x8 acc_operand(const f32x4 &lo, const f32x4 &hi) {
+    bf16x8 b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        b[i] = (__bf16)lo[i];
+        b[4 + i] = (__bf16)hi[i];
+    }
+    return b;
+}
+
+// eight bf16 at p (16-byte aligned), from global memory or LDS
+__device__ __forceinline__ bf16x8 ld8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+// ---------------------------------------------------------------- query side
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_bwd_q_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    const float *__restrict__ dt, const float *__restrict__ tau, const int32_t *__restrict__ tie,
+    const int32_t *__restrict__ seqlens, const uint16_t *__restrict__ dO, int S, int Hq, int Hkv, int G, int ntq,
+    float qscale, float c, uint16_t *__restrict__ dQ, float *__restrict__ lse_ws,
+    float *__restrict__ dd_ws) {
+    constexpr int P = pitch<D>();
+    constexpr int NS = D / 32;          // k-steps of 32 over head_dim
+    constexpr int NV = kBlk * D / 8 / kThreads;  // 16-byte vectors per thread per tile
+    __shared__ __align__(16) uint16_t Ks[kBlk * P];
+    __shared__ __align__(16) uint16_t Vs[kBlk * P];
+    __shared__ float dtl_s[kBlk];
+    __shared__ uint64_t skey_s[kBlk];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int q = lane >> 4, pq = lane & 15;
+    const int tq = blockIdx.x % ntq;
+    const int g = (blockIdx.x / ntq) % Hkv;
+    const int b = blockIdx.x / (ntq * Hkv);
+    const int L = seqlens ? seqlens[b] : S;
+    const int RB = kPairs / G;
+    const int i0 = tq * RB;
+    const int pr = 16 * wave + pq;      // this lane's pair
+    const int i = i0 + pr / G, hq = g * G + pr % G;
+    const bool live = i < L;
+    const int ic = min(i, S - 1);
+    const size_t qrow = (((size_t)b * S + ic) * Hq + hq) * D;
+    const size_t urow = ((size_t)b * Hkv + g) * S;
+
+    if (i0 >= L) {  // every row of the tile is padding (uniform)
+        if (i < S) {
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t)
+                *reinterpret_cast<uint2 *>(dQ + qrow + 16 * t + 4 * q) = make_uint2(0, 0);
+            if (q == 0) {
+                lse_ws[((size_t)b * Hq + hq) * S + i] = 0.f;
+                dd_ws[((size_t)b * Hq + hq) * S + i] = 0.f;
+            }
+        }
+        return;
+    }
+    const int kmax = min(i0 + RB, L) - 1;  // last key any row of the tile can keep
+    const uint64_t thr = live ? selkey(tau[urow + i], (uint32_t)tie[urow + i]) : ~0ull;
+
+    // Q and dO of this lane's pair (elements 32s + 8q .. +7)
+    bf16x8 qf[NS], of[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        qf[s] = ld8(Q + qrow + 32 * s + 8 * q);
+        of[s] = ld8(dO + qrow + 32 * s + 8 * q);
+    }
+
+    const uint32_t kvs = (uint32_t)(Hkv * D);
+    const uint16_t *Kb = K + (size_t)b * S * kvs + (size_t)g * D;
+    const uint16_t *Vb = V + (size_t)b * S * kvs + (size_t)g * D;
+    const float *drow = dt + urow;
+    // A key block's K and V rows and dt are requested into registers one
+    // block ahead and written to LDS after the barrier that ends the block
+    // before.  Keys past the tile's last row repeat it (never kept).
+    u32x4 rk[NV], rv[NV];
+    float rdt;
+    auto fetch = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int v = tid + u * kThreads;
+            const size_t off = (size_t)(uint32_t)min(k0 + v / (D / 8), kmax) * kvs + 8 * (v % (D / 8));
+            rk[u] = *reinterpret_cast<const u32x4 *>(Kb + off);
+            rv[u] = *reinterpret_cast<const u32x4 *>(Vb + off);
+        }
+        rdt = drow[min(k0 + (tid & (kBlk - 1)), kmax)];
+    };
+    auto put = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int v = tid + u * kThreads;
+            const int kk = v / (D / 8), cv = v % (D / 8);
+            *reinterpret_cast<u32x4 *>(&Ks[kk * P + 8 * cv]) = rk[u];
+            *reinterpret_cast<u32x4 *>(&Vs[kk * P + 8 * cv]) = rv[u];
+        }
+        if (tid < kBlk) {
+            dtl_s[tid] = rdt * kLog2e;
+            skey_s[tid] = selkey(rdt, (uint32_t)min(k0 + tid, kmax));
+        }
+    };
+    // base-2 scores of the block's 64 keys against this lane's pair and
+    // dp = dO . v: z[mt][r] and dp[mt][r] are key 16 mt + 4 q + r, z = -inf
+    // where not kept
+    auto scores = [&](int k0, float (&z)[4][4], f32x4 (&dp)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+            dp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                sacc = mfma16(ld8(&Ks[(16 * mt + pq) * P + 32 * s + 8 * q]), qf[s], sacc);
+                dp[mt] = mfma16(ld8(&Vs[(16 * mt + pq) * P + 32 * s + 8 * q]), of[s], dp[mt]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int kk = 16 * mt + 4 * q + r, j = k0 + kk;
+                const bool kept = live & (j <= i) & (skey_s[kk] >= thr);
+                const float zz = fmaf(sacc[r], qscale, dtl_s[kk]);
+                z[mt][r] = kept ? zz : -INFINITY;
+            }
+        }
+    };
+
+    // ---- pass 1: log-sum-exp (base 2) of each pair over its kept keys, and
+    // D = sum_j p_j dp_j, both with the online rescaling
+    float m = -INFINITY, l = 0.f, u = 0.f;
+    fetch(0);
+    for (int k0 = 0; k0 <= kmax; k0 += kBlk) {
+        put(k0);
+        __syncthreads();
+        fetch(k0 + kBlk <= kmax ? k0 + kBlk : 0);  // the next block, or pass 2's first
+        float z[4][4];
+        f32x4 dp[4];
+        scores(k0, z, dp);
+        float mb = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mb = fmaxf(mb, z[mt][r]);
+        if (mb > m) {
+            const float a = __builtin_amdgcn_exp2f(m - mb);  // 0 when m = -inf
+            l *= a;
+            u *= a;
+            m = mb;
+        }
+        if (m > -INFINITY) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float e = __builtin_amdgcn_exp2f(z[mt][r] - m);
+                    l += e;
+                    u = fmaf(e, dp[mt][r], u);
+                }
+        }
+        __syncthreads();
+    }
+    float dd;
+    {
+        float mo = fmaxf(m, __shfl_xor(m, 16, 64));
+        mo = fmaxf(mo, __shfl_xor(mo, 32, 64));
+        const float a = m > -INFINITY ? __builtin_amdgcn_exp2f(m - mo) : 0.f;
+        float lo = l * a, uo = u * a;
+        lo += __shfl_xor(lo, 16, 64);
+        lo += __shfl_xor(lo, 32, 64);
+        uo += __shfl_xor(uo, 16, 64);
+        uo += __shfl_xor(uo, 32, 64);
+        m = mo;
+        l = lo;
+        dd = live ? uo / lo : 0.f;
+    }
+    const float lse2 = live ? m + log2f(l) : 0.f;
+
+    // ---- pass 2: dS^T and dQ^T += K^T dS^T
+    f32x4 dq[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) dq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 <= kmax; k0 += kBlk) {
+        put(k0);
+        __syncthreads();
+        if (k0 + kBlk <= kmax) fetch(k0 + kBlk);
+        float z[4][4];
+        f32x4 dp[4], ds[4];
+        scores(k0, z, dp);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = __builtin_amdgcn_exp2f(z[mt][r] - lse2);  // 0 where not kept
+                ds[mt][r] = p * (dp[mt][r] - dd);
+            }
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const bf16x8 bop = acc_operand(ds[2 * s2], ds[2 * s2 + 1]);
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t) dq[t] = mfma16(tr_operand<P>(Ks, 32 * s2, 16 * t, lane), bop, dq[t]);
+        }
+        __syncthreads();
+    }
+
+    if (i < S) {
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+            const uint32_t w0 = (uint32_t)f32_to_bf16(dq[t][0] * c) | ((uint32_t)f32_to_bf16(dq[t][1] * c) << 16);
+            const uint32_t w1 = (uint32_t)f32_to_bf16(dq[t][2] * c) | ((uint32_t)f32_to_bf16(dq[t][3] * c) << 16);
+            *reinterpret_cast<uint2 *>(dQ + qrow + 16 * t + 4 * q) = make_uint2(w0, w1);
+        }
+        if (q == 0) {
+            lse_ws[((size_t)b * Hq + hq) * S + i] = lse2;
+            dd_ws[((size_t)b * Hq + hq) * S + i] = dd;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ key side
+// NKS: 16-key subtiles per wave (keys per workgroup = 64 NKS).
+template <int D, int NKS>
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    const float *__restrict__ dt, const float *__restrict__ tau, const int32_t *__restrict__ tie,
+    const int32_t *__restrict__ seqlens, const uint16_t *__restrict__ dO, const float *__restrict__ lse_ws,
+    const float *__restrict__ dd_ws, int S, int Hq, int Hkv, int G, int nkt, float qscale, float c,
+    uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, float *__restrict__ ddt) {
+    constexpr int P = pitch<D>();
+    constexpr int NS = D / 32;
+    constexpr int KT = 64 * NKS;                     // keys per workgroup
+    constexpr int NV = kPairs * D / 8 / kThreads;    // 16-byte vectors per thread per tile
+    __shared__ __align__(16) uint16_t Qs[kPairs * P];
+    __shared__ __align__(16) uint16_t Os[kPairs * P];  // dO of the row block
+    __shared__ float lse_s[kPairs], dd_s[kPairs];
+    __shared__ uint64_t thr_s[kPairs];
+    __shared__ uint64_t kmax_s[4];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int q = lane >> 4, kk = lane & 15;
+    // early key tiles (the longest row ranges) are dispatched first
+    const int nbg = gridDim.x / nkt;
+    const int kt = blockIdx.x / nbg, bg = blockIdx.x % nbg;
+    const int g = bg % Hkv, b = bg / Hkv;
+    const int L = seqlens ? seqlens[b] : S;
+    const int j0 = kt * KT;
+    const uint32_t kvs = (uint32_t)(Hkv * D);
+    const size_t urow = ((size_t)b * Hkv + g) * S;
+
+    int jk[NKS];
+    bool kvalid[NKS];
+    float dtl[NKS];
+    uint64_t skey[NKS];
+    bf16x8 kb[NKS][NS], vb[NKS][NS];
+    uint64_t kmax = 0;
+#pragma unroll
+    for (int ns = 0; ns < NKS; ++ns) {
+        jk[ns] = j0 + 16 * (NKS * wave + ns) + kk;
+        kvalid[ns] = jk[ns] < L;
+        const int jc = min(jk[ns], S - 1);
+        const float dv = dt[urow + jc];
+        dtl[ns] = dv * kLog2e;
+        skey[ns] = kvalid[ns] ? selkey(dv, (uint32_t)jc) : 0ull;
+        kmax = skey[ns] > kmax ? skey[ns] : kmax;
+        const uint16_t *kr = K + ((size_t)b * S + jc) * kvs + (size_t)g * D;
+        const uint16_t *vr = V + ((size_t)b * S + jc) * kvs + (size_t)g * D;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            kb[ns][s] = ld8(kr + 32 * s + 8 * q);
+            vb[ns][s] = ld8(vr + 32 * s + 8 * q);
+        }
+    }
+    // largest selection key of the workgroup's valid keys
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const uint64_t y = __shfl_xor(kmax, o, 64);
+        kmax = y > kmax ? y : kmax;
+    }
+    if (lane == 0) kmax_s[wave] = kmax;
+    __syncthreads();
+    kmax = kmax_s[0];
+#pragma unroll
+    for (int w2 = 1; w2 < 4; ++w2) kmax = kmax_s[w2] > kmax ? kmax_s[w2] : kmax;
+
+    f32x4 dka[NKS][D / 16], dva[NKS][D / 16];
+    float dsum[NKS];
+#pragma unroll
+    for (int ns = 0; ns < NKS; ++ns) {
+        dsum[ns] = 0.f;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+            dka[ns][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dva[ns][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    const int RB = kPairs / G;
+    // A row block (Q and dO of its 64 pairs, their log-sum-exp and D, the
+    // row thresholds) is requested into registers one block ahead and written
+    // to LDS after the barrier that ends the block before.  Rows past the end
+    // repeat the last one; rows past the valid length keep nothing.
+    u32x4 rq[NV], ro[NV];
+    float rlse, rdd;
+    uint64_t rthr;
+    auto fetch = [&](int r0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int v = tid + u * kThreads;
+            const int p = v / (D / 8), cv = v % (D / 8);
+            const int row = min(r0 + p / G, S - 1), hq = g * G + p % G;
+            const size_t off = (((size_t)b * S + row) * Hq + hq) * D + 8 * cv;
+            rq[u] = *reinterpret_cast<const u32x4 *>(Q + off);
+            ro[u] = *reinterpret_cast<const u32x4 *>(dO + off);
+        }
+        const int pp = tid & (kPairs - 1);
+        const int row = min(r0 + pp / G, S - 1), hq = g * G + pp % G;
+        rlse = lse_ws[((size_t)b * Hq + hq) * S + row];
+        rdd = dd_ws[((size_t)b * Hq + hq) * S + row];
+        const int rr = r0 + pp, rc = min(rr, S - 1);
+        const uint64_t t = selkey(tau[urow + rc], (uint32_t)tie[urow + rc]);
+        rthr = (pp < RB && rr < L) ? t : ~0ull;
+    };
+    auto put = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int v = tid + u * kThreads;
+            const int p = v / (D / 8), cv = v % (D / 8);
+            *reinterpret_cast<u32x4 *>(&Qs[p * P + 8 * cv]) = rq[u];
+            *reinterpret_cast<u32x4 *>(&Os[p * P + 8 * cv]) = ro[u];
+        }
+        if (tid < kPairs) {
+            lse_s[tid] = rlse;
+            dd_s[tid] = rdd;
+            thr_s[tid] = rthr;
+        }
+    };
+    if (j0 < L) fetch(j0);
+    for (int r0 = j0; r0 < L && j0 < L; r0 += RB) {
+        put();
+        __syncthreads();
+        if (thr_s[0] > kmax) break;  // this row and every later one keep none of the keys
+        if (r0 + RB < L) fetch(r0 + RB);
+
+#pragma unroll
+        for (int ns = 0; ns < NKS; ++ns) {
+            f32x4 pm[4], dsm[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    sacc = mfma16(ld8(&Qs[(16 * t + kk) * P + 32 * s + 8 * q]), kb[ns][s], sacc);
+                    dp = mfma16(ld8(&Os[(16 * t + kk) * P + 32 * s + 8 * q]), vb[ns][s], dp);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int p = 16 * t + 4 * q + r;  // pair of this accumulator entry
+                    const int row = r0 + p / G;
+                    const bool kept = kvalid[ns] & (jk[ns] <= row) & (row < L) & (skey[ns] >= thr_s[p / G]);
+                    const float arg = fmaf(sacc[r], qscale, dtl[ns]) - lse_s[p];
+                    const float pv = __builtin_amdgcn_exp2f(kept ? arg : -INFINITY);  // 0 where not kept
+                    pm[t][r] = pv;
+                    dsm[t][r] = pv * (dp[r] - dd_s[p]);
+                    dsum[ns] += dsm[t][r];
+                }
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const bf16x8 pb = acc_operand(pm[2 * s2], pm[2 * s2 + 1]);
+                const bf16x8 sb = acc_operand(dsm[2 * s2], dsm[2 * s2 + 1]);
+#pragma unroll
+                for (int t = 0; t < D / 16; ++t) {
+                    dva[ns][t] = mfma16(tr_operand<P>(Os, 32 * s2, 16 * t, lane), pb, dva[ns][t]);
+                    dka[ns][t] = mfma16(tr_operand<P>(Qs, 32 * s2, 16 * t, lane), sb, dka[ns][t]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int ns = 0; ns < NKS; ++ns) {
+        float sdt = dsum[ns];
+        sdt += __shfl_xor(sdt, 16, 64);
+        sdt += __shfl_xor(sdt, 32, 64);
+        const int j = jk[ns];
+        if (j < S) {
+            if (q == 0) ddt[urow + j] = sdt;
+            const size_t off = ((size_t)b * S + j) * kvs + (size_t)g * D;
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t) {
+                const uint32_t k0w = (uint32_t)f32_to_bf16(dka[ns][t][0] * c) |
+                                     ((uint32_t)f32_to_bf16(dka[ns][t][1] * c) << 16);
+                const uint32_t k1w = (uint32_t)f32_to_bf16(dka[ns][t][2] * c) |
+                                     ((uint32_t)f32_to_bf16(dka[ns][t][3] * c) << 16);
+                const uint32_t v0w = (uint32_t)f32_to_bf16(dva[ns][t][0]) | ((uint32_t)f32_to_bf16(dva[ns][t][1]) << 16);
+                const uint32_t v1w = (uint32_t)f32_to_bf16(dva[ns][t][2]) | ((uint32_t)f32_to_bf16(dva[ns][t][3]) << 16);
+                *reinterpret_cast<uint2 *>(dK + off + 16 * t + 4 * q) = make_uint2(k0w, k1w);
+                *reinterpret_cast<uint2 *>(dV + off + 16 * t + 4 * q) = make_uint2(v0w, v1w);
+            }
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_bwd_d(const void *Q, const void *K, const void *V, const float *dt, const float *tau,
+                        const int32_t *tie, const int32_t *seqlens, const void *dO, int B, int S,
+                        int Hq, int Hkv, void *dQ, void *dK, void *dV, float *ddt, void *ws, hipStream_t stream) {
+    const int G = Hq / Hkv;
+    const int RB = kPairs / G;
+    const int ntq = (S + RB - 1) / RB;
+    const float c = 1.0f / sqrtf((float)D);
+    const float qscale = c * kLog2e;
+    float *lse_ws = (float *)ws;
+    float *dd_ws = lse_ws + (size_t)B * Hq * S;
+    hipLaunchKernelGGL((attn_bwd_q_kernel<D>), dim3((unsigned)(B * Hkv * ntq)), dim3(kThreads), 0, stream,
+                       (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau, tie, seqlens,
+                       (const uint16_t *)dO, S, Hq, Hkv, G, ntq, qscale, c, (uint16_t *)dQ, lse_ws, dd_ws);
+    constexpr int NKS = 1;
+    const int nkt = (S + 64 * NKS - 1) / (64 * NKS);
+    hipLaunchKernelGGL((attn_bwd_kv_kernel<D, NKS>), dim3((unsigned)(B * Hkv * nkt)), dim3(kThreads), 0, stream,
+                       (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau, tie, seqlens,
+                       (const uint16_t *)dO, lse_ws, dd_ws, S, Hq, Hkv, G, nkt, qscale, c, (uint16_t *)dK,
+                       (uint16_t *)dV, ddt);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_bwd_ws_bytes(int B, int S, int Hq) { return (size_t)2 * B * Hq * S * sizeof(float); }
+
+hipError_t launch_attn_bwd(const void *Q, const void *K, const void *V, const float *dt, const float *tau,
+                           const int32_t *tie, const int32_t *seqlens, const void *dO, int B, int S, int Hq,
+                           int Hkv, int d, void *dQ, void *dK, void *dV, float *ddt, void *ws, hipStream_t stream) {
+    if (d == 128)
+        return launch_bwd_d<128>(Q, K, V, dt, tau, tie, seqlens, dO, B, S, Hq, Hkv, dQ, dK, dV, ddt, ws, stream);
+    return launch_bwd_d<64>(Q, K, V, dt, tau, tie, seqlens, dO, B, S, Hq, Hkv, dQ, dK, dV, ddt, ws, stream);
+}
+
+}  // namespace dma

@@ -47,11 +47,25 @@ hipError_t launch_qk_norm_rope(const void *Q, const void *K, int dtype, const vo
                                double rope_theta, const int32_t *positions, int B, int S, int Hq, int Hkv, int d,
                                void *Qo, void *Ko, hipStream_t stream);
 
+// Backward of the prefill attention (bwd.hip), bf16.
+size_t attn_bwd_ws_bytes(int B, int S, int Hq);
+hipError_t launch_attn_bwd(const void *Q, const void *K, const void *V, const float *dt, const float *tau,
+                           const int32_t *tie, const int32_t *seqlens, const void *dO, int B, int S, int Hq,
+                           int Hkv, int d, void *dQ, void *dK, void *dV, float *ddt, void *ws, hipStream_t stream);
+
+// Backward of dt (dt_bwd.hip).
+size_t dt_bwd_ws_bytes(int B, int S, int Hkv, int d);
+size_t dt_bwd_lds_bytes(int Hkv, int d);
+hipError_t launch_dt_bwd(const void *V, const void *W, const void *bias, const float *A, int dtype, const float *ddt,
+                         int B, int S, int Hkv, int d, void *dV, float *dW, float *dbias, float *dA, void *ws,
+                         hipStream_t stream);
+
 // Limits the launchers rely on (checked by the ABI layer).
 constexpr int kMaxHkvDt = 16;          // dt kernel: heads accumulated in registers
 constexpr int kMaxGroupAttn = 128;     // prefill: query heads per kv head
 constexpr int kMaxGroupDecode = 16;    // decode: query heads per kv head
 constexpr int kMaxKeptDecode = 131072; // decode: kept positions per (batch, kv head)
 constexpr size_t kDtLdsBytes = 65536;  // dt kernel: W staged in LDS
+constexpr int kMaxGroupBwd = 8;        // backward: query heads per kv head (a divisor of 64)
 
 }  // namespace dma

@@ -247,6 +247,66 @@ int dma_prologue(const void *Q, const void *K, const void *V, int dtype, const v
                  const float *A, int B, int S, int Hq, int Hkv, int d, void *Q_out, void *K_out, float *dt_out,
                  void *stream);
 
+/*
+ * dma_attn_bwd_workspace_bytes -- device workspace of dma_attn_bwd (0 on
+ * invalid sizes): two float32 values per (batch, query head, row).
+ */
+size_t dma_attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int d, int w);
+
+/*
+ * dma_attn_bwd -- gradients of dma_attn_fwd.  Doge guide, DMA section: the
+ * same masked attention runs in training, and dt is learnt end to end through
+ * it (forward step 3's remark on learning what to mask).  The kept sets are
+ * those of (tau, tie); the selection itself has no gradient.  With
+ * p = softmax over the kept keys of s = d**-0.5 q.k + dt, dp_j = dO.v_j and
+ * D = sum_j p_j dp_j (= dO.o):  ds_j = p_j (dp_j - D),
+ * dq = d**-0.5 sum_j ds_j k_j,  dk_j = d**-0.5 sum ds_j q,  dv_j = sum p_j dO,
+ * ddt_j = sum ds_j, the last three summed over every row and query head that
+ * keeps key j.  D is recomputed in float32 from the kept keys, so the forward
+ * output is not an argument.
+ *
+ *   Q, K, V, dt, tau, tie, seqlens, w: as given to dma_attn_fwd
+ *   dO  [B][S][Hq][d]  upstream gradient of the output
+ *   dQ [B][S][Hq][d], dK/dV [B][S][Hkv][d] (dtype, out); ddt [B][Hkv][S]
+ *   float32 (out).  Padded rows and keys get zeros.
+ *   ws, ws_bytes: device workspace of at least dma_attn_bwd_workspace_bytes()
+ * bf16 only; d in {64, 128}; Hq/Hkv in {1, 2, 4, 8}.  Products on matrix
+ * cores with float32 accumulation (p and ds rounded to bf16 as operands);
+ * deterministic (no atomics).  Work grows with the causal range of each row,
+ * not with w.
+ */
+int dma_attn_bwd(const void *Q, const void *K, const void *V, int dtype, const float *dt, const float *tau,
+                 const int32_t *tie, const int32_t *seqlens, const void *dO, int B, int S, int Hq, int Hkv, int d,
+                 int w, void *dQ, void *dK, void *dV, float *ddt, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * dma_dt_bwd_workspace_bytes -- device workspace of dma_dt_bwd (0 on invalid
+ * sizes): one partial sum of dW, dbias and dA per 64 tokens.
+ */
+size_t dma_dt_bwd_workspace_bytes(int B, int S, int Hkv, int d);
+
+/*
+ * dma_dt_bwd -- gradients of dma_dt for an upstream gradient ddt (Doge guide,
+ * DMA forward step 3: dt_proj and the learnt per-head A).  With x the
+ * projection of a token for kv head h and dt = exp(A softplus(x)):
+ *   dx = ddt dt A sigmoid(x);  dA[h] = sum ddt dt softplus(x);
+ *   dbias[h] = sum dx;  dW[h][c] = sum dx V[c];  dV[c] += sum_h dx W[h][c]
+ * (sums over every batch and position).
+ *
+ *   V, W, bias (nullable), A, dtype: as given to dma_dt
+ *   ddt  [B][Hkv][S] float32, e.g. dma_attn_bwd's
+ *   dV   [B][S][Hkv][d] dtype, or NULL: the dt path's part of the value
+ *        gradient is ADDED in place (pass dma_attn_bwd's dV to get the total)
+ *   dW [Hkv][Hkv*d], dbias [Hkv] (nullable), dA [Hkv]: float32 (out)
+ *   ws, ws_bytes: device workspace of at least dma_dt_bwd_workspace_bytes()
+ * float32 arithmetic; dW, dbias and dA are summed in a fixed order
+ * (deterministic).  Supports d in {64, 128}, Hkv <= 16, Hkv*Hkv*d <= 16384 -
+ * 128*Hkv.
+ */
+int dma_dt_bwd(const void *V, const void *W, const void *bias, const float *A, int dtype, const float *ddt, int B,
+               int S, int Hkv, int d, void *dV, float *dW, float *dbias, float *dA, void *ws, size_t ws_bytes,
+               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

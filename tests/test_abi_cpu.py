@@ -158,3 +158,32 @@ def test_qk_norm_rope_validation(dma):
     assert pro(Q=None) == -1
     assert pro(Hkv=17) == -4
     assert pro(W=ctypes.c_void_p(0x1004)) == -4
+
+
+def test_bwd_validation(dma):
+    need = dma.dma_attn_bwd_workspace_bytes(2, 64, 8, 2, 64, 16)
+    assert need > 0 and dma.dma_attn_bwd_workspace_bytes(2, 64, 7, 2, 64, 16) == 0
+
+    def call(Q=FAKE, dtype=1, Hq=8, Hkv=2, d=64, ws=FAKE2, nb=need, dO=FAKE):
+        return dma.dma_attn_bwd(Q, FAKE, FAKE, dtype, FAKE, FAKE, FAKE, None, dO, 2, 64, Hq, Hkv, d, 16,
+                                FAKE2, FAKE2, FAKE2, FAKE2, ws, nb, None)
+    assert call(Q=None) == -1
+    assert call(dO=None) == -1
+    assert call(dtype=4) == -3
+    assert call(dtype=0) == -4        # float32: the backward is bf16 only
+    assert call(Hq=7) == -2
+    assert call(Hq=6, Hkv=2) == -4    # G = 3 does not divide the 64-pair tiles
+    assert call(Hq=32, Hkv=2) == -4   # G = 16
+    assert call(d=96) == -4
+    assert call(ws=None) == -5
+    assert call(nb=need - 1) == -5
+    nd = dma.dma_dt_bwd_workspace_bytes(2, 64, 4, 64)
+    assert nd > 0
+
+    def dcall(V=FAKE, dW=FAKE2, Hkv=4, d=64, ws=FAKE2, nb=nd):
+        return dma.dma_dt_bwd(V, FAKE, None, FAKE, 1, FAKE, 2, 64, Hkv, d, None, dW, None, FAKE2, ws, nb, None)
+    assert dcall(V=None) == -1
+    assert dcall(dW=None) == -1
+    assert dcall(Hkv=17) == -4
+    assert dcall(Hkv=16, d=128) == -4  # W would not fit the workgroup's LDS
+    assert dcall(ws=None) == -5
