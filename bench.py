@@ -365,6 +365,22 @@ def main():
         q_, k_, v_, d, _, _ = nxt(pre_sets)
         dma.prologue(q_, k_, v_, wq, wk, W, A, bias, Q_out=q_, K_out=k_, dt_out=d)
 
+    # The backward of the prefill (attention gradients, then the dt chain's),
+    # on the rotating input sets with one upstream gradient dO.
+    dO = torch.randn_like(Q)
+    ws_b = torch.empty(dma.attn_bwd_workspace_bytes(wl_p.B, wl_p.S, wl_p.Hq, wl_p.Hkv, wl_p.d, wl_p.w),
+                       dtype=torch.uint8, device=dev)
+    ws_db = torch.empty(dma.dt_bwd_workspace_bytes(wl_p.B, wl_p.S, wl_p.Hkv, wl_p.d), dtype=torch.uint8, device=dev)
+    g_out = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V), torch.empty_like(dt))
+
+    def c_attn_bwd():
+        q_, k_, v_, d, ta, ti = nxt(pre_sets)
+        dma.attn_bwd(q_, k_, v_, d, ta, ti, wl_p.w, dO, workspace=ws_b, out=g_out)
+
+    def c_dt_bwd():
+        _, _, v_, _, _, _ = nxt(pre_sets)
+        dma.dt_bwd(v_, W, A, g_out[3], bias, dV=g_out[2], workspace=ws_db)
+
     def c_decode():
         kc, vc, dc = nxt(dec_sets)
         dma.decode(q, kc, vc, dc, lens, wl_d.w, out=out, workspace=ws)
@@ -387,6 +403,7 @@ def main():
 
     calls = (("dt", c_dt), ("select", c_select), ("attn_fwd", c_attn),
              ("dt_append", c_dt_append), ("decode", c_decode), ("decode_step", c_decode_step),
+             ("attn_bwd", c_attn_bwd), ("dt_bwd", c_dt_bwd),
              ("qk_norm_rope", c_qk_norm_rope), ("prologue", c_prologue))
     avg, host_launch_ms = {}, {}
     for n, f in calls:
@@ -433,6 +450,8 @@ def main():
     step_gbs = sbytes / (avg["decode_step"] * 1e-3) / 1e9
     pbytes = prologue_bytes(wl_p.B, wl_p.S, wl_p.Hq, wl_p.Hkv, wl_p.d)
     pro_gbs = pbytes / (avg["prologue"] * 1e-3) / 1e9
+    ms_bwd = avg["attn_bwd"] + avg["dt_bwd"]
+    bwd_tflops = 2.5 * flops / (ms_bwd * 1e-3) / 1e12
 
     line = {
         "metric": "DMA prefill kept-key TFLOP/s + decode GB/s, % of MI355X roofline",
@@ -475,6 +494,12 @@ def main():
             "value": round(pro_gbs, 2), "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS,
             "frac": round(pro_gbs / PEAK_HBM_GBS, 5), "bytes": pbytes, "ms": round(avg["prologue"], 5),
             "note": "dma_prologue on the prefill workload, in place: Q/K RMSNorm + rotary, then dt",
+        },
+        "backward": {
+            "value": round(bwd_tflops, 3), "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
+            "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 5), "flops": 2.5 * flops, "ms": round(ms_bwd, 5),
+            "note": "dma_attn_bwd + dma_dt_bwd on the prefill workload; kept-key flops of the five products "
+                    "(scores, dp, dq, dk, dv) = 2.5x the forward's",
         },
         "ms_prefill": round(ms_pre, 5),
         "ms_decode_step": round(ms_dec, 5),

@@ -209,6 +209,7 @@ int dma_dt_bwd(const void *V, const void *W, const void *bias, const float *A, i
     if (B < 1 || S < 1 || Hkv < 1 || d < 1) return DMA_ERR_SHAPE;
     if (!head_dim_ok(d) || Hkv > dma::kMaxHkvDt) return DMA_ERR_UNSUPPORTED;
     if ((int64_t)B * S > 0x7fffffff || dma::dt_bwd_lds_bytes(Hkv, d) > 65536) return DMA_ERR_UNSUPPORTED;
+    if (!aligned16(V) || !aligned16(dV)) return DMA_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < dma::dt_bwd_ws_bytes(B, S, Hkv, d)) return DMA_ERR_WORKSPACE;
     return from_hip(dma::launch_dt_bwd(V, W, bias, A, dtype, ddt, B, S, Hkv, d, dV, dW, dbias, dA, ws,
                                        (hipStream_t)stream));

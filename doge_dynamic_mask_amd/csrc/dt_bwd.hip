@@ -5,14 +5,16 @@
 //   dx = ddt dt A sigmoid(x),   dA[h] += ddt dt softplus(x),   dbias[h] += dx,
 //   dW[h][c] += dx V[t][c],     dV[t][c] += sum_h dx W[h][c].
 //
-// dt_bwd_token_kernel: one workgroup per run of kTok tokens.  W is staged in
-// LDS; each wave takes a token at a time, its lanes splitting the Hkv*d
-// channels: x by a wave reduction per head, then dx and the dA term, and the
-// token's dV contribution added in place.  Then the workgroup's partial sums
-// of dW (each thread a (head, channel) entry at a time, channel fastest, so
-// the V reads are coalesced), dbias and dA go to the workspace.
-// dt_bwd_reduce_kernel sums the partials of every workgroup in a fixed order:
-// the result does not depend on scheduling.
+// dt_bwd_token_kernel: one workgroup per run of 16 tokens.  W is staged in
+// LDS; each 16-lane group takes one token, its lanes splitting the token's
+// Hkv*d channels in 16-byte vectors: x by a group reduction per head, then dx
+// and the dA term, and the token's dV contribution added in place.  Then the workgroup's partial sums
+// of dW (each thread a channel and every head, the loads of all the
+// workgroup's tokens for that channel issued together and coalesced across
+// threads), dbias and dA go to the workspace.
+// The partials are summed in two fixed-order levels (dt_bwd_sum_kernel):
+// slices of at most kSlice partials, all of a slice's loads in flight at
+// once, then the slice sums; the result does not depend on scheduling.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -20,10 +22,36 @@ namespace dma {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTok = 64;  // tokens per workgroup
+constexpr int kTok = 16;  // tokens per workgroup
 
 __device__ __forceinline__ float softplus_acc(float x) {
     return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x));
+}
+
+template <typename T> __device__ __forceinline__ void unpack_vec(const u32x4 &u, float *v);
+template <> __device__ __forceinline__ void unpack_vec<uint16_t>(const u32x4 &u, float *v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(u[i] << 16);
+        v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+}
+template <> __device__ __forceinline__ void unpack_vec<float>(const u32x4 &u, float *v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(u[i]);
+}
+template <typename T> __device__ __forceinline__ u32x4 pack_vec(const float *v);
+template <> __device__ __forceinline__ u32x4 pack_vec<uint16_t>(const float *v) {
+    u32x4 u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+    return u;
+}
+template <> __device__ __forceinline__ u32x4 pack_vec<float>(const float *v) {
+    u32x4 u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = __float_as_uint(v[i]);
+    return u;
 }
 
 template <typename T>
@@ -34,54 +62,73 @@ __global__ __launch_bounds__(kThreads) void dt_bwd_token_kernel(
     float *Ws = smem;                          // [Hkv][width] as float
     float *dxs = Ws + (size_t)Hkv * width;     // [kTok][Hkv]
     float *gas = dxs + kTok * Hkv;             // [kTok][Hkv]
+    static_assert(kTok == 4 * (kThreads / 64), "one token per 16-lane group");
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int t0 = blockIdx.x * kTok;
     const int nt = min(kTok, ntok - t0);
     for (int e = tid; e < Hkv * width; e += kThreads) Ws[e] = Elem<T>::load(W, e);
     __syncthreads();
 
-    const int nc = width / 64;  // channels per lane (width is a multiple of 64)
-    for (int tt = wave; tt < nt; tt += kThreads / 64) {
-        const int t = t0 + tt;
-        const int b = t / S, s = t - b * S;
-        const T *vrow = V + (size_t)t * width;
-        float xs[kMaxHkvDt];
+    // Every 16-lane group of a wave takes one token (so a workgroup's 16
+    // tokens are all in flight at once); its lanes split the token's 16-byte
+    // vectors of Hkv*d channels.
+    constexpr int EV = 16 / (int)sizeof(T);
+    const int nvec = width / EV;
+    const int grp = lane >> 4, l16 = lane & 15;
+    const int tt = 4 * wave + grp;
+    const bool tok_ok = tt < nt;
+    const int t = t0 + (tok_ok ? tt : nt - 1);
+    const int b = t / S, s = t - b * S;
+    const T *vrow = V + (size_t)t * width;
+    float xs[kMaxHkvDt];
 #pragma unroll
-        for (int h = 0; h < kMaxHkvDt; ++h) xs[h] = 0.f;
-        for (int k = 0; k < nc; ++k) {
-            const int c = lane + 64 * k;
-            const float v = Elem<T>::load(vrow, c);
-#pragma unroll
-            for (int h = 0; h < kMaxHkvDt; ++h)
-                if (h < Hkv) xs[h] = fmaf(Ws[h * width + c], v, xs[h]);
-        }
-        float dx[kMaxHkvDt];
+    for (int h = 0; h < kMaxHkvDt; ++h) xs[h] = 0.f;
+    for (int j = l16; j < nvec; j += 16) {
+        float v[EV];
+        unpack_vec<T>(*reinterpret_cast<const u32x4 *>(vrow + EV * j), v);
 #pragma unroll
         for (int h = 0; h < kMaxHkvDt; ++h) {
-            dx[h] = 0.f;
             if (h < Hkv) {
-                const float x = wave_sum(xs[h]) + (bias ? Elem<T>::load(bias, h) : 0.f);
-                const float a = A[h];
-                const float sp = softplus_acc(x);
-                const float dtv = expf(a * sp);
-                const float g = ddt[((size_t)b * Hkv + h) * S + s];
-                dx[h] = g * dtv * a / (1.f + expf(-x));
-                if (lane == 0) {
-                    dxs[tt * Hkv + h] = dx[h];
-                    gas[tt * Hkv + h] = g * dtv * sp;
-                }
+                const float *wr = Ws + h * width + EV * j;
+#pragma unroll
+                for (int e = 0; e < EV; ++e) xs[h] = fmaf(wr[e], v[e], xs[h]);
             }
         }
-        if (dV) {
-            T *drow = dV + (size_t)t * width;
-            for (int k = 0; k < nc; ++k) {
-                const int c = lane + 64 * k;
-                float acc = Elem<T>::load(drow, c);
+    }
+    float dx[kMaxHkvDt];
 #pragma unroll
-                for (int h = 0; h < kMaxHkvDt; ++h)
-                    if (h < Hkv) acc = fmaf(dx[h], Ws[h * width + c], acc);
-                Elem<T>::store(drow, c, acc);
+    for (int h = 0; h < kMaxHkvDt; ++h) {
+        dx[h] = 0.f;
+        if (h < Hkv) {
+            float xh = xs[h];
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) xh += __shfl_xor(xh, o, 64);
+            const float x = xh + (bias ? Elem<T>::load(bias, h) : 0.f);
+            const float a = A[h];
+            const float sp = softplus_acc(x);
+            const float dtv = expf(a * sp);
+            const float g = ddt[((size_t)b * Hkv + h) * S + s];
+            dx[h] = g * dtv * a / (1.f + expf(-x));
+            if (l16 == 0 && tok_ok) {
+                dxs[tt * Hkv + h] = dx[h];
+                gas[tt * Hkv + h] = g * dtv * sp;
             }
+        }
+    }
+    if (dV && tok_ok) {
+        T *drow = dV + (size_t)t * width;
+        for (int j = l16; j < nvec; j += 16) {
+            float v[EV];
+            unpack_vec<T>(*reinterpret_cast<const u32x4 *>(drow + EV * j), v);
+#pragma unroll
+            for (int h = 0; h < kMaxHkvDt; ++h) {
+                if (h < Hkv) {
+                    const float *wr = Ws + h * width + EV * j;
+#pragma unroll
+                    for (int e = 0; e < EV; ++e) v[e] = fmaf(dx[h], wr[e], v[e]);
+                }
+            }
+            *reinterpret_cast<u32x4 *>(drow + EV * j) = pack_vec<T>(v);
         }
     }
     __syncthreads();
@@ -89,11 +136,24 @@ __global__ __launch_bounds__(kThreads) void dt_bwd_token_kernel(
     // partial sums of this workgroup's tokens
     const size_t stride = (size_t)Hkv * width + 2 * Hkv;
     float *out = part + (size_t)blockIdx.x * stride;
-    for (int e = tid; e < Hkv * width; e += kThreads) {
-        const int h = e / width, c = e - h * width;
-        float acc = 0.f;
-        for (int tt = 0; tt < nt; ++tt) acc = fmaf(dxs[tt * Hkv + h], Elem<T>::load(V, (size_t)(t0 + tt) * width + c), acc);
-        out[e] = acc;
+    for (int c = tid; c < width; c += kThreads) {
+        float v[kTok];
+#pragma unroll
+        for (int tt = 0; tt < kTok; ++tt) v[tt] = Elem<T>::load(V, (size_t)(t0 + min(tt, nt - 1)) * width + c);
+        float acc[kMaxHkvDt];
+#pragma unroll
+        for (int h = 0; h < kMaxHkvDt; ++h) acc[h] = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < kTok; ++tt) {
+            if (tt < nt) {
+#pragma unroll
+                for (int h = 0; h < kMaxHkvDt; ++h)
+                    if (h < Hkv) acc[h] = fmaf(dxs[tt * Hkv + h], v[tt], acc[h]);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < kMaxHkvDt; ++h)
+            if (h < Hkv) out[(size_t)h * width + c] = acc[h];
     }
     if (tid < Hkv) {
         float sb = 0.f, sa = 0.f;
@@ -106,15 +166,27 @@ __global__ __launch_bounds__(kThreads) void dt_bwd_token_kernel(
     }
 }
 
-__global__ __launch_bounds__(kThreads) void dt_bwd_reduce_kernel(const float *__restrict__ part, int nparts, int Hkv,
-                                                                 int width, float *__restrict__ dW,
-                                                                 float *__restrict__ dbias, float *__restrict__ dA) {
-    const size_t stride = (size_t)Hkv * width + 2 * Hkv;
+constexpr int kSlice = 16;  // partials summed per thread and level
+
+// out[y][e] = sum of in[p][e] over the y-th slice of kSlice rows p (rows of
+// nout floats).  With dW != nullptr (the last level, one slice) the sums go to
+// dW, dbias and dA instead.
+__global__ __launch_bounds__(kThreads) void dt_bwd_sum_kernel(const float *__restrict__ in, int nrows, int nout, int Hkv,
+                                                              int width, float *__restrict__ out,
+                                                              float *__restrict__ dW, float *__restrict__ dbias,
+                                                              float *__restrict__ dA) {
     const int e = blockIdx.x * kThreads + threadIdx.x;
-    if (e >= (int)stride) return;
+    if (e >= nout) return;
+    const int p0 = blockIdx.y * kSlice;
+    float v[kSlice];
+#pragma unroll
+    for (int k = 0; k < kSlice; ++k) v[k] = p0 + k < nrows ? in[(size_t)(p0 + k) * nout + e] : 0.f;
     float acc = 0.f;
-    for (int p = 0; p < nparts; ++p) acc += part[(size_t)p * stride + e];
-    if (e < Hkv * width) {
+#pragma unroll
+    for (int k = 0; k < kSlice; ++k) acc += v[k];
+    if (!dW) {
+        out[(size_t)blockIdx.y * nout + e] = acc;
+    } else if (e < Hkv * width) {
         dW[e] = acc;
     } else if (e < Hkv * width + Hkv) {
         if (dbias) dbias[e - Hkv * width] = acc;
@@ -125,10 +197,17 @@ __global__ __launch_bounds__(kThreads) void dt_bwd_reduce_kernel(const float *__
 
 }  // namespace
 
+// rows of partial sums left after each level: ceil(n / kSlice) until one
+static size_t sum_levels_rows(size_t nparts) {
+    size_t tot = 0;
+    for (size_t n = (nparts + kSlice - 1) / kSlice; n > 1; n = (n + kSlice - 1) / kSlice) tot += n;
+    return tot;
+}
+
 size_t dt_bwd_ws_bytes(int B, int S, int Hkv, int d) {
     const size_t ntok = (size_t)B * S;
     const size_t nparts = (ntok + kTok - 1) / kTok;
-    return nparts * ((size_t)Hkv * Hkv * d + 2 * Hkv) * sizeof(float);
+    return (nparts + sum_levels_rows(nparts)) * ((size_t)Hkv * Hkv * d + 2 * Hkv) * sizeof(float);
 }
 
 size_t dt_bwd_lds_bytes(int Hkv, int d) { return ((size_t)Hkv * Hkv * d + 2 * kTok * Hkv) * sizeof(float); }
@@ -148,8 +227,20 @@ hipError_t launch_dt_bwd(const void *V, const void *W, const void *bias, const f
         hipLaunchKernelGGL(dt_bwd_token_kernel<float>, dim3(nparts), dim3(kThreads), lds, stream, (const float *)V,
                            (const float *)W, (const float *)bias, A, ddt, S, Hkv, width, ntok, (float *)dV, part);
     const int nout = width * Hkv + 2 * Hkv;
-    hipLaunchKernelGGL(dt_bwd_reduce_kernel, dim3((nout + kThreads - 1) / kThreads), dim3(kThreads), 0, stream,
-                       (const float *)part, nparts, Hkv, width, dW, dbias, dA);
+    const unsigned gx = (unsigned)((nout + kThreads - 1) / kThreads);
+    const float *in = part;
+    float *next = part + (size_t)nparts * nout;
+    int n = nparts;
+    while (n > kSlice) {
+        const int m = (n + kSlice - 1) / kSlice;
+        hipLaunchKernelGGL(dt_bwd_sum_kernel, dim3(gx, (unsigned)m), dim3(kThreads), 0, stream, in, n, nout, Hkv,
+                           width, next, (float *)nullptr, (float *)nullptr, (float *)nullptr);
+        in = next;
+        next += (size_t)m * nout;
+        n = m;
+    }
+    hipLaunchKernelGGL(dt_bwd_sum_kernel, dim3(gx, 1u), dim3(kThreads), 0, stream, in, n, nout, Hkv, width,
+                       (float *)nullptr, dW, dbias, dA);
     return hipGetLastError();
 }
 

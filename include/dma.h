@@ -281,7 +281,7 @@ int dma_attn_bwd(const void *Q, const void *K, const void *V, int dtype, const f
 
 /*
  * dma_dt_bwd_workspace_bytes -- device workspace of dma_dt_bwd (0 on invalid
- * sizes): one partial sum of dW, dbias and dA per 64 tokens.
+ * sizes): one partial sum of dW, dbias and dA per 16 tokens.
  */
 size_t dma_dt_bwd_workspace_bytes(int B, int S, int Hkv, int d);
 

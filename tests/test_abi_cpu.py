@@ -187,3 +187,4 @@ def test_bwd_validation(dma):
     assert dcall(Hkv=17) == -4
     assert dcall(Hkv=16, d=128) == -4  # W would not fit the workgroup's LDS
     assert dcall(ws=None) == -5
+    assert dcall(V=ctypes.c_void_p(0x1002)) == -4  # misaligned
