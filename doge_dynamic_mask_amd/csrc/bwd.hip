@@ -116,9 +116,16 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_q_kernel(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int q = lane >> 4, pq = lane & 15;
-    const int tq = blockIdx.x % ntq;
-    const int g = (blockIdx.x / ntq) % Hkv;
-    const int b = blockIdx.x / (ntq * Hkv);
+    // Work item = (batch, kv head, query tile).  Workgroup ids go round-robin
+    // over the 8 XCDs: hand each XCD a contiguous run of items, so that the
+    // tiles of one (batch, kv head), which all read the same K and V rows,
+    // share that XCD's L2; within a run the tiles with the most keys first.
+    const int nwg = gridDim.x, per_xcd = nwg >> 3;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int item = (slot < per_xcd && (nwg & 7) == 0) ? xcd * per_xcd + slot : blockIdx.x;
+    const int tq = ntq - 1 - item % ntq;
+    const int g = (item / ntq) % Hkv;
+    const int b = item / (ntq * Hkv);
     const int L = seqlens ? seqlens[b] : S;
     const int RB = kPairs / G;
     const int i0 = tq * RB;
@@ -320,7 +327,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int q = lane >> 4, kk = lane & 15;
-    // early key tiles (the longest row ranges) are dispatched first
+    // Early key tiles (the longest row ranges) are dispatched first.  Ids go
+    // round-robin over the 8 XCDs, so with a multiple of 8 (batch, kv head)
+    // units each unit stays on one XCD, whose L2 then holds its Q and dO rows.
     const int nbg = gridDim.x / nkt;
     const int kt = blockIdx.x / nbg, bg = blockIdx.x % nbg;
     const int g = bg % Hkv, b = bg / Hkv;
