@@ -50,11 +50,11 @@ def _load():
         P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
         lib.oracle_dt.argtypes = [P, P, P, P, I, I, I, I, I, P]
         lib.oracle_dt.restype = None
-        lib.oracle_select.argtypes = [P, P, I, I, I, I, P, I64, P, P]
+        lib.oracle_select.argtypes = [P, P, I, I, I, I, I, P, I64, P, P]
         lib.oracle_select.restype = None
-        lib.oracle_kept_row.argtypes = [P, P, I, I, I, I, I, I, P]
+        lib.oracle_kept_row.argtypes = [P, P, I, I, I, I, I, I, I, P]
         lib.oracle_kept_row.restype = ctypes.c_int
-        lib.oracle_attn.argtypes = [P, P, P, I, P, P, I, I, I, I, I, I, P, I64, P]
+        lib.oracle_attn.argtypes = [P, P, P, I, P, P, I, I, I, I, I, I, I, P, I64, P]
         lib.oracle_attn.restype = None
         lib.oracle_decode.argtypes = [P, P, P, I, P, P, I, I, I, I, I, I, P, P]
         lib.oracle_decode.restype = None
@@ -109,8 +109,9 @@ def dt(V, W, bias, A):
     return out
 
 
-def select(dt32, w, seqlens=None, rows=None):
-    """(tau, tie) per row.  dt32 is float32 [B,Hkv,S]; rows is an optional (n,3) list of (b,g,i)."""
+def select(dt32, w, seqlens=None, rows=None, win=None):
+    """(tau, tie) per row.  dt32 is float32 [B,Hkv,S]; rows is an optional (n,3) list of (b,g,i);
+    win: sliding window of win positions (None: full causal)."""
     dt32 = np.ascontiguousarray(dt32, dtype=np.float32)
     B, Hkv, S = dt32.shape
     r, n = _rows_array(rows)
@@ -118,22 +119,24 @@ def select(dt32, w, seqlens=None, rows=None):
     tau = np.empty(shape, dtype=np.float32)
     tie = np.empty(shape, dtype=np.int32)
     seq = _seq(seqlens)
-    _load().oracle_select(_ptr(dt32), _ptr(seq), B, Hkv, S, int(w), _ptr(r), n, _ptr(tau), _ptr(tie))
+    _load().oracle_select(_ptr(dt32), _ptr(seq), B, Hkv, S, int(w), int(win or 0), _ptr(r), n, _ptr(tau), _ptr(tie))
     return tau, tie
 
 
-def kept_row(dt32, w, b, g, i, seqlens=None):
-    """Kept key indices of one row, ascending."""
+def kept_row(dt32, w, b, g, i, seqlens=None, win=None):
+    """Kept key indices of one row, ascending (win: sliding window, None for full causal)."""
     dt32 = np.ascontiguousarray(dt32, dtype=np.float32)
     B, Hkv, S = dt32.shape
     out = np.empty(max(int(w), 1), dtype=np.int32)
     seq = _seq(seqlens)
-    n = _load().oracle_kept_row(_ptr(dt32), _ptr(seq), Hkv, S, int(w), int(b), int(g), int(i), _ptr(out))
+    n = _load().oracle_kept_row(_ptr(dt32), _ptr(seq), Hkv, S, int(w), int(win or 0), int(b), int(g), int(i),
+                                _ptr(out))
     return out[:n].copy()
 
 
-def attn(Q, K, V, dt32, w, seqlens=None, rows=None):
-    """fp64 attention.  Full [B,S,Hq,d] output, or [n, G, d] for a (b,g,i) row list."""
+def attn(Q, K, V, dt32, w, seqlens=None, rows=None, win=None):
+    """fp64 attention.  Full [B,S,Hq,d] output, or [n, G, d] for a (b,g,i) row list.
+    win: sliding window of win positions (None: full causal)."""
     Q, tq = _elem_array(Q)
     K, tk = _elem_array(K)
     V, tv = _elem_array(V)
@@ -148,7 +151,7 @@ def attn(Q, K, V, dt32, w, seqlens=None, rows=None):
     out = np.empty((n, G, d) if r is not None else (B, S, Hq, d), dtype=np.float64)
     seq = _seq(seqlens)
     _load().oracle_attn(_ptr(Q), _ptr(K), _ptr(V), tq, _ptr(dt32), _ptr(seq), B, S, Hq, Hkv, d,
-                        int(w), _ptr(r), n, _ptr(out))
+                        int(w), int(win or 0), _ptr(r), n, _ptr(out))
     return out
 
 

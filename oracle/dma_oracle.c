@@ -103,18 +103,35 @@ static int better_first(const void *pa, const void *pb)
 }
 
 /*
- * Keys of query row i, in selection order, into buf (capacity >= i + 1).
- * Valid keys are j <= i (causal mask) and j < L (right padding).  Returns how
- * many of them the row keeps: all valid keys if there are at most w of them,
- * else the first w in the order above (Doge guide, DMA forward step 3: the
- * top-k branch keeps keep_window_size positions and masks the rest).
+ * First key visible to row i: 0 for the full causal mask, i - win + 1 (at
+ * least 0) under a sliding window of win positions (DogeConfig's
+ * sliding_window: with a value, the attention mask is the sliding-window
+ * causal mask, under which row i sees the keys i - win < j <= i).
  */
-static int row_kept(const float *dt_row, int i, int L, int w, key_t_ *buf)
+static int first_visible(int i, int win)
 {
-    int n = (i + 1 < L) ? i + 1 : L;
-    for (int j = 0; j < n; ++j) {
-        buf[j].dt = dt_row[j];
-        buf[j].idx = j;
+    return (win > 0 && i - win + 1 > 0) ? i - win + 1 : 0;
+}
+
+/*
+ * Keys of query row i, in selection order, into buf (capacity >= i + 1).
+ * Valid keys are first_visible(i, win) <= j <= i (causal mask, and the
+ * sliding window when win > 0) and j < L (right padding).  Returns how many
+ * of them the row keeps: all valid keys if there are at most w of them, else
+ * the first w in the order above (Doge guide, DMA forward step 3: the
+ * masked positions hold min_dtype before the top-k, so a masked key never
+ * outranks a valid one; the top-k branch keeps keep_window_size positions
+ * and masks the rest).
+ */
+static int row_kept(const float *dt_row, int i, int L, int w, int win, key_t_ *buf)
+{
+    const int lo = first_visible(i, win);
+    const int hi = (i + 1 < L) ? i + 1 : L;
+    int n = 0;
+    for (int j = lo; j < hi; ++j) {
+        buf[n].dt = dt_row[j];
+        buf[n].idx = j;
+        ++n;
     }
     qsort(buf, (size_t)n, sizeof *buf, better_first);
     return n < w ? n : w;
@@ -125,14 +142,15 @@ static int row_kept(const float *dt_row, int i, int L, int w, key_t_ *buf)
  * last (w-th) kept key.  A key j of row i is kept exactly when it is valid and
  * (dt_j > tau_i, or dt_j == tau_i and j <= t_i).  Canonical forms: a row with
  * at most w valid keys keeps them all and gets (-inf, -1); a padded row
- * (i >= L) keeps nothing and gets (+inf, -1).
+ * (i >= L) keeps nothing and gets (+inf, -1).  win > 0: sliding window of win
+ * positions (win <= 0: full causal).
  *
  *   dt      [B][Hkv][S] float32
  *   seqlens [B] int32 or NULL (then every batch has length S)
  *   rows    list of nrows (b, g, i) triples, or NULL for every row
  *   tau/tie one entry per requested row ([B][Hkv][S] when rows == NULL)
  */
-void oracle_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w,
+void oracle_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w, int win,
                    const int32_t *rows, int64_t nrows, float *tau, int32_t *tie)
 {
     const int64_t total = rows ? nrows : (int64_t)B * Hkv * S;
@@ -157,12 +175,12 @@ void oracle_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int 
                 tie[r] = -1;
                 continue;
             }
-            if (i + 1 <= w) {
+            if (i + 1 - first_visible(i, win) <= w) {
                 tau[r] = -INFINITY;
                 tie[r] = -1;
                 continue;
             }
-            int nk = row_kept(dt + ((size_t)b * Hkv + g) * S, i, L, w, buf);
+            int nk = row_kept(dt + ((size_t)b * Hkv + g) * S, i, L, w, win, buf);
             tau[r] = buf[nk - 1].dt;
             tie[r] = buf[nk - 1].idx;
         }
@@ -174,14 +192,14 @@ void oracle_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int 
  * Kept key indices of one query row, ascending, into out (capacity >= w).
  * Returns their count.  Used by the tests to materialise kept sets.
  */
-int oracle_kept_row(const float *dt, const int32_t *seqlens, int Hkv, int S, int w,
+int oracle_kept_row(const float *dt, const int32_t *seqlens, int Hkv, int S, int w, int win,
                     int b, int g, int i, int32_t *out)
 {
     const int L = seqlens ? seqlens[b] : S;
     if (i >= L)
         return 0;
     key_t_ *buf = (key_t_ *)malloc(sizeof(key_t_) * (size_t)(i + 1));
-    int nk = row_kept(dt + ((size_t)b * Hkv + g) * S, i, L, w, buf);
+    int nk = row_kept(dt + ((size_t)b * Hkv + g) * S, i, L, w, win, buf);
     /* report in index order */
     int n = 0;
     char *mark = (char *)calloc((size_t)i + 1, 1);
@@ -238,13 +256,13 @@ static void attend(const void *q, size_t qoff, const void *K, const void *Vv, in
  * Prefill attention with the dynamic mask, for all rows or for a list of
  * (b, g, i) rows (each list entry produces the G query heads of kv head g).
  * Query head hq uses kv head hq / G (contiguous groups, G = Hq / Hkv).  Padded
- * rows (i >= L) produce zeros.
+ * rows (i >= L) produce zeros.  win > 0: sliding window of win positions.
  *
  *   Q [B][S][Hq][d], K/V [B][S][Hkv][d] (dtype); dt [B][Hkv][S] float32
  *   out: [B][S][Hq][d] double when rows == NULL, else [nrows][G][d]
  */
 void oracle_attn(const void *Q, const void *K, const void *V, int dtype, const float *dt,
-                 const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d, int w,
+                 const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d, int w, int win,
                  const int32_t *rows, int64_t nrows, double *out)
 {
     const int G = Hq / Hkv;
@@ -275,7 +293,7 @@ void oracle_attn(const void *Q, const void *K, const void *V, int dtype, const f
                         o[e] = 0.0;
                     continue;
                 }
-                int nk = row_kept(dt + ((size_t)b * Hkv + g) * S, i, L, w, buf);
+                int nk = row_kept(dt + ((size_t)b * Hkv + g) * S, i, L, w, win, buf);
                 attend(Q, (((size_t)b * S + i) * Hq + hq) * d, K, V, dtype,
                        ((size_t)b * S * Hkv + g) * d, (size_t)Hkv * d, d,
                        dt + ((size_t)b * Hkv + g) * S, buf, nk, s_buf, o);
@@ -313,10 +331,10 @@ void oracle_decode(const void *q, const void *Kc, const void *Vc, int dtype,
             for (int g = 0; g < Hkv; ++g) {
                 const int L = cache_lens[b];
                 const float *drow = dt_cache + ((size_t)b * Hkv + g) * Lmax;
-                int nk = row_kept(drow, L - 1, L, w, buf);
+                int nk = row_kept(drow, L - 1, L, w, 0, buf);
                 if (kept_idx) {
                     int32_t *ki = kept_idx + ((size_t)b * Hkv + g) * w;
-                    char *mark = (char *)calloc((size_t)L, 1);
+                    char *mark = (char *)calloc((size_t)(L > 0 ? L : 1), 1);
                     for (int k = 0; k < nk; ++k)
                         mark[buf[k].idx] = 1;
                     int n = 0;
@@ -427,7 +445,7 @@ void oracle_attn_bwd(const void *Q, const void *K, const void *V, int dtype, con
                             dq[e] = 0.0;
                         if (i >= L)
                             continue;
-                        const int nk = row_kept(drow, i, L, w, buf);
+                        const int nk = row_kept(drow, i, L, w, 0, buf);
                         /* forward: scores, softmax, output */
                         double m = -INFINITY;
                         for (int k = 0; k < nk; ++k) {

@@ -17,14 +17,17 @@ import numpy as np
 MIN_DTYPE = float(np.finfo(np.float32).min)
 
 
-def mask(dt32, w, seqlens=None):
-    """Materialised additive mask M[b, g, i, j] (float64)."""
+def mask(dt32, w, seqlens=None, win=None):
+    """Materialised additive mask M[b, g, i, j] (float64).  win: the sliding-window
+    causal mask of DogeConfig's sliding_window (row i sees i - win < j <= i)."""
     dt32 = np.asarray(dt32, dtype=np.float32)
     B, Hkv, S = dt32.shape
     M = np.broadcast_to(dt32[:, :, None, :].astype(np.float64), (B, Hkv, S, S)).copy()
     i = np.arange(S)[:, None]
     j = np.arange(S)[None, :]
     M[:, :, j > i] = MIN_DTYPE
+    if win is not None:
+        M[:, :, j <= i - win] = MIN_DTYPE
     if seqlens is not None:
         for b in range(B):
             M[b, :, :, int(seqlens[b]):] = MIN_DTYPE
@@ -36,12 +39,12 @@ def mask(dt32, w, seqlens=None):
     return M
 
 
-def kept_sets(dt32, w, seqlens=None):
+def kept_sets(dt32, w, seqlens=None, win=None):
     """Boolean [B,Hkv,S,S]: key j takes part in row i's softmax."""
-    return mask(dt32, w, seqlens) > MIN_DTYPE
+    return mask(dt32, w, seqlens, win) > MIN_DTYPE
 
 
-def attention(Q, K, V, dt32, w, seqlens=None):
+def attention(Q, K, V, dt32, w, seqlens=None, win=None):
     """fp64 output [B,S,Hq,d] of the masked softmax; Q/K/V given as float arrays."""
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -49,7 +52,7 @@ def attention(Q, K, V, dt32, w, seqlens=None):
     B, S, Hq, d = Q.shape
     Hkv = K.shape[2]
     G = Hq // Hkv
-    M = mask(dt32, w, seqlens)
+    M = mask(dt32, w, seqlens, win)
     out = np.zeros((B, S, Hq, d))
     for b in range(B):
         for hq in range(Hq):
