@@ -19,6 +19,8 @@ Functions mirror the C ABI in ``include/dma.h``:
     attn_bwd(Q, K, V, dt, tau, tie, w, dO, seqlens=None) -> (dQ, dK, dV, ddt)
     dt_bwd(V, W, A, ddt, bias=None, dV=None)            -> (dW, dbias, dA); adds into dV
     prefill_bwd(Q, K, V, W, A, w, dO, ...)               -> dict of every gradient
+    select_window(dt, w, win, seqlens=None)             -> (tau, tie) under a sliding window
+    attn_window_fwd(Q, K, V, dt, tau, tie, w, win, seqlens=None) -> O
 """
 from __future__ import annotations
 
@@ -42,7 +44,8 @@ EXPORTS = ("dma_version", "dma_status_str", "dma_dt", "dma_select", "dma_attn_fw
            "dma_decode_workspace_bytes", "dma_decode", "dma_decode_state_bytes",
            "dma_decode_step_workspace_bytes", "dma_decode_state_init", "dma_decode_step",
            "dma_decode_state_kept", "dma_qk_norm_rope", "dma_prologue",
-           "dma_attn_bwd_workspace_bytes", "dma_attn_bwd", "dma_dt_bwd_workspace_bytes", "dma_dt_bwd")
+           "dma_attn_bwd_workspace_bytes", "dma_attn_bwd", "dma_dt_bwd_workspace_bytes", "dma_dt_bwd",
+           "dma_select_window", "dma_attn_window_fwd")
 
 
 class DmaError(RuntimeError):
@@ -97,6 +100,10 @@ def lib():
     L.dma_dt_bwd_workspace_bytes.restype = SZ
     L.dma_dt_bwd.argtypes = [P, P, P, P, I, P, I, I, I, I, P, P, P, P, P, SZ, P]
     L.dma_dt_bwd.restype = I
+    L.dma_select_window.argtypes = [P, P, I, I, I, I, I, P, P, P]
+    L.dma_select_window.restype = I
+    L.dma_attn_window_fwd.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, I, I, I, P, P]
+    L.dma_attn_window_fwd.restype = I
     _lib = L
     return L
 
@@ -438,3 +445,41 @@ def prefill_bwd(Q, K, V, W, A, w, dO, bias=None, seqlens=None, fwd=None):
     dQ, dK, dV, ddt = attn_bwd(Q, K, V, d_, tau, tie, w, dO, seqlens)
     dW, dbias, dA = dt_bwd(V, W, A, ddt, bias, dV=dV)
     return {"dQ": dQ, "dK": dK, "dV": dV, "dW": dW, "dbias": dbias, "dA": dA, "ddt": ddt}
+
+
+def select_window(dt_, w, win, seqlens=None, tau=None, tie=None):
+    """Per-row threshold pairs under a sliding window of win positions: (tau, tie), each [B, Hkv, S]."""
+    _check(dt_, "dt", torch.float32, 3)
+    B, Hkv, S = dt_.shape
+    if seqlens is not None:
+        _check(seqlens, "seqlens", torch.int32, 1, dt_.device)
+    if tau is None:
+        tau = torch.empty_like(dt_)
+    if tie is None:
+        tie = torch.empty((B, Hkv, S), dtype=torch.int32, device=dt_.device)
+    _call(lib().dma_select_window(_ptr(dt_), _ptr(seqlens), B, Hkv, S, int(w), int(win), _ptr(tau), _ptr(tie),
+                                  _stream(dt_)), "dma_select_window")
+    return tau, tie
+
+
+def attn_window_fwd(Q, K, V, dt_, tau, tie, w, win, seqlens=None, out=None):
+    """Masked attention under a sliding window of win positions: O [B, S, Hq, d] (bf16)."""
+    _check(Q, "Q", torch.bfloat16, 4)
+    dev = Q.device
+    B, S, Hq, d = Q.shape
+    Hkv = K.shape[2]
+    for name, t in (("K", K), ("V", V)):
+        _check(t, name, Q.dtype, 4, dev)
+        if tuple(t.shape) != (B, S, Hkv, d):
+            raise ValueError(f"{name} must be [B, S, Hkv, d] matching Q")
+    for name, t, dtp in (("dt", dt_, torch.float32), ("tau", tau, torch.float32), ("tie", tie, torch.int32)):
+        _check(t, name, dtp, 3, dev)
+        if tuple(t.shape) != (B, Hkv, S):
+            raise ValueError(f"{name} must be [B, Hkv, S]")
+    if seqlens is not None:
+        _check(seqlens, "seqlens", torch.int32, 1, dev)
+    if out is None:
+        out = torch.empty_like(Q)
+    _call(lib().dma_attn_window_fwd(_ptr(Q), _ptr(K), _ptr(V), BF16, _ptr(dt_), _ptr(tau), _ptr(tie), _ptr(seqlens),
+                                    B, S, Hq, Hkv, d, int(w), int(win), _ptr(out), _stream(Q)), "dma_attn_window_fwd")
+    return out

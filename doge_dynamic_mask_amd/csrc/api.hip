@@ -215,4 +215,26 @@ int dma_dt_bwd(const void *V, const void *W, const void *bias, const float *A, i
                                        (hipStream_t)stream));
 }
 
+int dma_select_window(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w, int win, float *tau,
+                      int32_t *tie, void *stream) {
+    if (!dt || !tau || !tie) return DMA_ERR_NULL;
+    if (B < 1 || Hkv < 1 || S < 1 || w < 1 || win < 1) return DMA_ERR_SHAPE;
+    if ((int64_t)B * Hkv * S > ((int64_t)1 << 40)) return DMA_ERR_UNSUPPORTED;
+    return from_hip(dma::launch_select_window(dt, seqlens, B, Hkv, S, w, win, tau, tie, (hipStream_t)stream));
+}
+
+int dma_attn_window_fwd(const void *Q, const void *K, const void *V, int dtype, const float *dt, const float *tau,
+                        const int32_t *tie, const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d, int w,
+                        int win, void *O, void *stream) {
+    if (!Q || !K || !V || !dt || !tau || !tie || !O) return DMA_ERR_NULL;
+    if (!dtype_ok(dtype)) return DMA_ERR_DTYPE;
+    if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || d < 1 || w < 1 || win < 1 || Hq % Hkv != 0) return DMA_ERR_SHAPE;
+    const int G = Hq / Hkv;
+    if (dtype != DMA_BF16 || !head_dim_ok(d) || G > dma::kMaxGroupBwd || 64 % G != 0) return DMA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hkv * S > 0x7fffffff) return DMA_ERR_UNSUPPORTED;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return DMA_ERR_UNSUPPORTED;
+    return from_hip(dma::launch_attn_window(Q, K, V, dt, tau, tie, seqlens, B, S, Hq, Hkv, d, win, O,
+                                            (hipStream_t)stream));
+}
+
 }  // extern "C"

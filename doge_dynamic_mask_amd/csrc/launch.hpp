@@ -60,6 +60,13 @@ hipError_t launch_dt_bwd(const void *V, const void *W, const void *bias, const f
                          int B, int S, int Hkv, int d, void *dV, float *dW, float *dbias, float *dA, void *ws,
                          hipStream_t stream);
 
+// Sliding-window variant (window.hip).
+hipError_t launch_select_window(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w, int win,
+                                float *tau, int32_t *tie, hipStream_t stream);
+hipError_t launch_attn_window(const void *Q, const void *K, const void *V, const float *dt, const float *tau,
+                              const int32_t *tie, const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d,
+                              int win, void *O, hipStream_t stream);
+
 // Limits the launchers rely on (checked by the ABI layer).
 constexpr int kMaxHkvDt = 16;          // dt kernel: heads accumulated in registers
 constexpr int kMaxGroupAttn = 128;     // prefill: query heads per kv head

@@ -307,6 +307,34 @@ int dma_dt_bwd(const void *V, const void *W, const void *bias, const float *A, i
                int S, int Hkv, int d, void *dV, float *dW, float *dbias, float *dA, void *ws, size_t ws_bytes,
                void *stream);
 
+/*
+ * Sliding-window variant -- Doge guide, DogeConfig table (sliding_window: with
+ * a value, the attention mask is the sliding-window causal mask) and DMA
+ * forward step 3 (the dynamic mask keeps the top keep_window_size of the
+ * visible keys; masked keys hold min_dtype and never outrank valid ones).
+ * Row i sees the keys i - win < j <= i with j < L_b.  The kept sets no longer
+ * nest from row to row, so these entry points select and attend per row.
+ *
+ * dma_select_window -- the threshold pair of every row over its window, with
+ * the conventions of dma_select: (tau, tie) is the w-th kept key under (dt
+ * desc, index asc); (-inf, -1) when the row sees at most w keys; (+inf, -1)
+ * for a padded row.  Exact (comparisons only).  win >= 1.
+ */
+int dma_select_window(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w, int win, float *tau,
+                      int32_t *tie, void *stream);
+
+/*
+ * dma_attn_window_fwd -- dma_attn_fwd's computation over the kept keys of
+ * each row's window, (tau, tie) from dma_select_window with the same w and
+ * win.  Every key of the window is tested; work grows with win, not w.
+ * bf16 only; d in {64, 128}; Hq/Hkv in {1, 2, 4, 8}.  P is rounded once to
+ * bf16 for the product with V and the softmax sum is taken over the rounded
+ * weights; float32 accumulation; output rounded to nearest even.
+ */
+int dma_attn_window_fwd(const void *Q, const void *K, const void *V, int dtype, const float *dt, const float *tau,
+                        const int32_t *tie, const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d, int w,
+                        int win, void *O, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

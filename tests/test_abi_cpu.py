@@ -188,3 +188,20 @@ def test_bwd_validation(dma):
     assert dcall(Hkv=16, d=128) == -4  # W would not fit the workgroup's LDS
     assert dcall(ws=None) == -5
     assert dcall(V=ctypes.c_void_p(0x1002)) == -4  # misaligned
+
+
+def test_window_validation(dma):
+    assert dma.dma_select_window(None, None, 1, 1, 8, 2, 4, FAKE, FAKE, None) == -1
+    assert dma.dma_select_window(FAKE, None, 1, 1, 8, 2, 0, FAKE, FAKE, None) == -2
+    assert dma.dma_select_window(FAKE, None, 1, 1, 8, 0, 4, FAKE, FAKE, None) == -2
+
+    def call(Q=FAKE, dtype=1, Hq=4, Hkv=2, d=64, win=16, O=FAKE2):
+        return dma.dma_attn_window_fwd(Q, FAKE, FAKE, dtype, FAKE, FAKE, FAKE, None, 1, 64, Hq, Hkv, d, 8, win, O,
+                                       None)
+    assert call(Q=None) == -1
+    assert call(O=None) == -1
+    assert call(dtype=2) == -3
+    assert call(dtype=0) == -4
+    assert call(win=0) == -2
+    assert call(Hq=6, Hkv=2) == -4
+    assert call(d=80) == -4
