@@ -74,13 +74,15 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_each": COPY_CAL_BYTES, "copies": 5}), flush=True)
 
 
-def kept_flops(B, Hq, S, d, w, seqlens=None):
-    """Sum over query heads and valid rows of 4*d*min(valid keys, w)."""
+def kept_flops(B, Hq, S, d, w, seqlens=None, win=None):
+    """Sum over query heads and valid rows of 4*d*min(valid keys, w); with a
+    sliding window of win positions a row has at most win valid keys."""
     total = 0
     for b in range(B):
         L = S if seqlens is None else int(seqlens[b])
         i = np.arange(L, dtype=np.int64)
-        total += int(np.minimum(i + 1, w).sum()) * Hq
+        vis = i + 1 if win is None else np.minimum(i + 1, win)
+        total += int(np.minimum(vis, w).sum()) * Hq
     return total * 4 * d
 
 
@@ -195,6 +197,61 @@ def prefill_breakdown(dma, name, dev, evict, R=8, rounds=4):
             "tflops_prefill": round(flops / (tot * 1e-3) / 1e12, 2),
             "tflops_attn": round(flops / (res["attn_fwd"] * 1e-3) / 1e12, 2),
             "attn_frac_of_peak": round(flops / (res["attn_fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def window_breakdown(dma, dev, evict, win=4096, R=6, rounds=3):
+    """The sliding-window variant on the long workload (B1 Hq16 Hkv8 S8192
+    d128 w2048) with a window of `win` positions: per-call GPU time of
+    dma_select_window and dma_attn_window_fwd, timed like the other calls
+    (after an eviction, R launches each on its own copy of the inputs)."""
+    wl = si.WORKLOADS["long"]
+    inp = si.make_inputs(wl)
+    Q, K, V = to_dev(inp["Q"], dev), to_dev(inp["K"], dev), to_dev(inp["V"], dev)
+    dt = dma.dt(V, to_dev(inp["W"], dev), to_dev(inp["A"], dev), to_dev(inp["bias"], dev))
+    tau, tie = dma.select_window(dt, wl.w, win)
+    O = torch.empty_like(Q)
+    first = (Q, K, V, dt, tau, tie)
+    set_bytes = sum(t.numel() * t.element_size() for t in first)
+    nsets = 1 + -(-300 * 2**20 // set_bytes)
+    sets = [first] + [tuple(t.clone() for t in first) for _ in range(nsets - 1)]
+    rot = [0]
+
+    def nxt():
+        rot[0] += 1
+        return sets[rot[0] % nsets]
+
+    def c_sel():
+        s_ = nxt()
+        dma.select_window(s_[3], wl.w, win, tau=s_[4], tie=s_[5])
+
+    def c_attn():
+        s_ = nxt()
+        dma.attn_window_fwd(*s_, wl.w, win, out=O)
+
+    res = {}
+    for n, f in (("select_window", c_sel), ("attn_window_fwd", c_attn)):
+        f()
+        torch.cuda.synchronize()
+        pairs = []
+        for _ in range(rounds):
+            evict()
+            evict()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(R):
+                f()
+            b.record()
+            pairs.append((a, b))
+        torch.cuda.synchronize()
+        res[n] = float(np.mean([a.elapsed_time(b) for a, b in pairs])) / R
+    del sets
+    flops = kept_flops(wl.B, wl.Hq, wl.S, wl.d, wl.w, win=win)
+    tot = sum(res.values())
+    return {"workload": f"long (B1 Hq16 Hkv8 S8192 d128 w2048) with sliding_window {win}",
+            "ms": {k: round(v, 5) for k, v in res.items()}, "kept_flops": flops,
+            "tflops": round(flops / (tot * 1e-3) / 1e12, 2),
+            "tflops_attn": round(flops / (res["attn_window_fwd"] * 1e-3) / 1e12, 2),
+            "attn_frac_of_peak": round(flops / (res["attn_window_fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def main():
@@ -509,6 +566,7 @@ def main():
         "host_ms_per_launch": {n: round(v, 5) for n, v in host_launch_ms.items()},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
     }
+    line["window_variant"] = window_breakdown(dma, dev, evict)
     if args.other_configs:
         line["other_configs"] = {n: prefill_breakdown(dma, n, dev, evict) for n in ("long", "padded")}
     if not args.no_cpu_baseline:
