@@ -64,6 +64,10 @@ def _load():
         lib.oracle_attn_bwd.restype = None
         lib.oracle_dt_bwd.argtypes = [P, P, P, P, I, I, I, I, I, P, P, P, P, P]
         lib.oracle_dt_bwd.restype = None
+        lib.oracle_cdmoe.argtypes = [P, P, P, P, I, I, I, I, I, P, P, P]
+        lib.oracle_cdmoe.restype = None
+        lib.oracle_cdmoe_route.argtypes = [P, I, I, I, P, P]
+        lib.oracle_cdmoe_route.restype = None
         _lib = lib
     return _lib
 
@@ -235,3 +239,34 @@ def dt_bwd(V, W, bias, A, ddt):
     _load().oracle_dt_bwd(_ptr(V), _ptr(W), _ptr(bias), _ptr(A), tv, B, S, Hkv, d, _ptr(ddt), _ptr(dV), _ptr(dW),
                           _ptr(dbias), _ptr(dA))
     return dV, dW, dbias, dA
+
+
+def cdmoe(h, router, down, up, k):
+    """CDMoE routed experts, fp64: (idx [T,k] int32 in selection order, weights [T,k], out [T,H]).
+    h [T,H], router [2*nk,H], down/up [nk*nk,H], all float32 or all bf16 bits."""
+    h, th = _elem_array(h)
+    router, tr = _elem_array(router)
+    down, td = _elem_array(down)
+    up, tu = _elem_array(up)
+    assert th == tr == td == tu
+    T, H = h.shape
+    nk = router.shape[0] // 2
+    assert router.shape == (2 * nk, H) and down.shape == (nk * nk, H) and up.shape == down.shape and k <= nk
+    idx = np.empty((T, k), np.int32)
+    wts = np.empty((T, k))
+    out = np.empty((T, H))
+    _load().oracle_cdmoe(_ptr(h), _ptr(router), _ptr(down), _ptr(up), th, T, H, nk, int(k), _ptr(idx), _ptr(wts),
+                         _ptr(out))
+    return idx, wts, out
+
+
+def cdmoe_route(logits, k):
+    """Routing from float32 logits [T, 2*nk]: (idx [T,k] int32 in selection order, weights [T,k])."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, n2 = logits.shape
+    nk = n2 // 2
+    assert k <= nk
+    idx = np.empty((T, k), np.int32)
+    wts = np.empty((T, k))
+    _load().oracle_cdmoe_route(_ptr(logits), T, nk, int(k), _ptr(idx), _ptr(wts))
+    return idx, wts

@@ -566,3 +566,128 @@ void oracle_dt_bwd(const void *V, const void *W, const void *bias, const float *
     }
     free(dx);
 }
+
+/*
+ * Cross Domain MoE (CDMoE) routed experts -- Doge guide, section on CDMoE and
+ * the DogeConfig table (num_experts, num_experts_per_tok, hidden_act).  Per
+ * token with hidden state h (length H):
+ *   logits = router_gate h, 2*nk values: the first nk are the x domain, the
+ *            last nk the y domain (nk = floor(sqrt(num_experts)));
+ *   the top k of each domain (larger first, lower index first among equal);
+ *   every pair (a, b) of the two lists scores sx_a + sy_b and names expert
+ *            ix_a * nk + iy_b; the token keeps the top k pairs (larger score
+ *            first, lower expert index first among equal);
+ *   weights = softmax over the k kept scores;
+ *   out = sum over kept experts e of weight_e * silu(down_e . h) * up_e.
+ * Plain loops and qsort, fp64 on the stored values.
+ *
+ *   h [T][H], router [2*nk][H], down/up [nk*nk][H] (dtype)
+ *   idx [T][k] int32 (out, in selection order), wts [T][k] double (out),
+ *   out [T][H] double (out)
+ */
+typedef struct {
+    double v;
+    int32_t idx;
+} score_t_;
+
+static int score_first(const void *pa, const void *pb)
+{
+    const score_t_ *a = (const score_t_ *)pa, *b = (const score_t_ *)pb;
+    if (a->v > b->v)
+        return -1;
+    if (a->v < b->v)
+        return 1;
+    return (a->idx > b->idx) - (a->idx < b->idx);
+}
+
+void oracle_cdmoe(const void *h, const void *router, const void *down, const void *up, int dtype, int T, int H,
+                  int nk, int k, int32_t *idx, double *wts, double *out)
+{
+#pragma omp parallel
+    {
+        score_t_ *sx = (score_t_ *)malloc(sizeof(score_t_) * (size_t)nk);
+        score_t_ *sy = (score_t_ *)malloc(sizeof(score_t_) * (size_t)nk);
+        score_t_ *pairs = (score_t_ *)malloc(sizeof(score_t_) * (size_t)k * k);
+#pragma omp for schedule(dynamic, 4)
+        for (int t = 0; t < T; ++t) {
+            const size_t hr = (size_t)t * H;
+            for (int n = 0; n < 2 * nk; ++n) {
+                double acc = 0.0;
+                for (int c = 0; c < H; ++c)
+                    acc += elem(router, dtype, (size_t)n * H + c) * elem(h, dtype, hr + c);
+                score_t_ *dst = n < nk ? &sx[n] : &sy[n - nk];
+                dst->v = acc;
+                dst->idx = n < nk ? n : n - nk;
+            }
+            qsort(sx, (size_t)nk, sizeof *sx, score_first);
+            qsort(sy, (size_t)nk, sizeof *sy, score_first);
+            for (int a = 0; a < k; ++a)
+                for (int b = 0; b < k; ++b) {
+                    pairs[a * k + b].v = sx[a].v + sy[b].v;
+                    pairs[a * k + b].idx = sx[a].idx * nk + sy[b].idx;
+                }
+            qsort(pairs, (size_t)k * k, sizeof *pairs, score_first);
+            double m = pairs[0].v, l = 0.0;
+            for (int e = 0; e < k; ++e)
+                l += exp(pairs[e].v - m);
+            for (int c = 0; c < H; ++c)
+                out[hr + c] = 0.0;
+            for (int e = 0; e < k; ++e) {
+                const int x = pairs[e].idx;
+                const double wgt = exp(pairs[e].v - m) / l;
+                idx[(size_t)t * k + e] = x;
+                wts[(size_t)t * k + e] = wgt;
+                double z = 0.0;
+                for (int c = 0; c < H; ++c)
+                    z += elem(down, dtype, (size_t)x * H + c) * elem(h, dtype, hr + c);
+                const double act = z / (1.0 + exp(-z));
+                for (int c = 0; c < H; ++c)
+                    out[hr + c] += wgt * act * elem(up, dtype, (size_t)x * H + c);
+            }
+        }
+        free(pairs);
+        free(sy);
+        free(sx);
+    }
+}
+
+/*
+ * The routing step alone, from given router logits (float32 [T][2*nk]): the
+ * kept experts in selection order and their weights, as oracle_cdmoe.
+ */
+void oracle_cdmoe_route(const float *logits, int T, int nk, int k, int32_t *idx, double *wts)
+{
+#pragma omp parallel
+    {
+        score_t_ *sx = (score_t_ *)malloc(sizeof(score_t_) * (size_t)nk);
+        score_t_ *sy = (score_t_ *)malloc(sizeof(score_t_) * (size_t)nk);
+        score_t_ *pairs = (score_t_ *)malloc(sizeof(score_t_) * (size_t)k * k);
+#pragma omp for schedule(static)
+        for (int t = 0; t < T; ++t) {
+            for (int n = 0; n < nk; ++n) {
+                sx[n].v = logits[(size_t)t * 2 * nk + n];
+                sx[n].idx = n;
+                sy[n].v = logits[(size_t)t * 2 * nk + nk + n];
+                sy[n].idx = n;
+            }
+            qsort(sx, (size_t)nk, sizeof *sx, score_first);
+            qsort(sy, (size_t)nk, sizeof *sy, score_first);
+            for (int a = 0; a < k; ++a)
+                for (int b = 0; b < k; ++b) {
+                    pairs[a * k + b].v = sx[a].v + sy[b].v;
+                    pairs[a * k + b].idx = sx[a].idx * nk + sy[b].idx;
+                }
+            qsort(pairs, (size_t)k * k, sizeof *pairs, score_first);
+            double m = pairs[0].v, l = 0.0;
+            for (int e = 0; e < k; ++e)
+                l += exp(pairs[e].v - m);
+            for (int e = 0; e < k; ++e) {
+                idx[(size_t)t * k + e] = pairs[e].idx;
+                wts[(size_t)t * k + e] = exp(pairs[e].v - m) / l;
+            }
+        }
+        free(pairs);
+        free(sy);
+        free(sx);
+    }
+}

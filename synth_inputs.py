@@ -185,3 +185,15 @@ def make_positions(B, S, kind, seed) -> np.ndarray:
     else:
         raise ValueError(kind)
     return np.ascontiguousarray(p, dtype=np.int32)
+
+
+def make_cdmoe(T, H, nk, dtype, seed):
+    """CDMoE inputs: hidden states h [T, H] ~ N(0, 1), router_gate [2*nk, H],
+    down_embed and up_embed [nk*nk, H] ~ N(0, 0.02^2) (the DogeConfig
+    initializer_range), stored as float32 or bf16 bits."""
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((T, H), dtype=np.float32)
+    router = rng.normal(0.0, 0.02, size=(2 * nk, H)).astype(np.float32)
+    down = rng.normal(0.0, 0.02, size=(nk * nk, H)).astype(np.float32)
+    up = rng.normal(0.0, 0.02, size=(nk * nk, H)).astype(np.float32)
+    return _store(h, dtype), _store(router, dtype), _store(down, dtype), _store(up, dtype)

@@ -1,0 +1,81 @@
+"""Pins of the oracle's CDMoE routed experts (CPU).
+
+The two-stage product-key routing (top k per domain, then the top k of the
+k*k pairs) is checked against a brute force that scores every one of the
+nk*nk experts directly (score = x logit + y logit, expert ax*nk + ay) and
+sorts them all; the weights against the softmax closed form; the logits
+against a library matmul; the expert output against a dense formulation
+that weights every expert (zero for the ones not kept).
+"""
+import numpy as np
+import pytest
+
+import synth_inputs as si
+
+
+def _brute_route(logits, k):
+    T, n2 = logits.shape
+    nk = n2 // 2
+    lx, ly = logits[:, :nk].astype(np.float64), logits[:, nk:].astype(np.float64)
+    idx = np.empty((T, k), np.int64)
+    sc = np.empty((T, k))
+    for t in range(T):
+        s = (lx[t][:, None] + ly[t][None, :]).reshape(-1)   # expert a*nk + b
+        order = np.lexsort((np.arange(nk * nk), -s))         # score desc, index asc
+        idx[t] = order[:k]
+        sc[t] = s[order[:k]]
+    return idx, sc
+
+
+@pytest.mark.parametrize("nk,k,kind", [(8, 3, "normal"), (16, 16, "normal"), (12, 5, "few"), (11, 1, "few"),
+                                       (128, 64, "normal")])
+def test_route_equals_global_topk_over_all_experts(oracle_mod, nk, k, kind):
+    rng = np.random.default_rng(nk * 100 + k)
+    T = 7
+    if kind == "few":     # many exact ties, resolved by the lower expert index
+        logits = rng.choice(np.array([-1.0, 0.0, 0.5, 2.0], np.float32), size=(T, 2 * nk))
+    else:
+        logits = rng.standard_normal((T, 2 * nk)).astype(np.float32)
+    idx, wts = oracle_mod.cdmoe_route(logits, k)
+    bidx, bsc = _brute_route(logits, k)
+    assert np.array_equal(idx, bidx)
+    ref_w = np.exp(bsc - bsc.max(axis=1, keepdims=True))
+    ref_w /= ref_w.sum(axis=1, keepdims=True)
+    assert np.allclose(wts, ref_w, rtol=1e-14, atol=0)
+    assert np.allclose(wts.sum(axis=1), 1.0, rtol=1e-14)
+
+
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_cdmoe_output_against_dense_formulation(oracle_mod, dtype):
+    T, H, nk, k = 6, 48, 9, 4
+    h, router, down, up = si.make_cdmoe(T, H, nk, dtype, seed=3)
+    idx, wts, out = oracle_mod.cdmoe(h, router, down, up, k)
+    f = (lambda x: si.bf16_bits_to_f32(x).astype(np.float64)) if dtype == "bf16" else (lambda x: x.astype(np.float64))
+    hf, rf, df, uf = f(h), f(router), f(down), f(up)
+    logits = hf @ rf.T                                    # library matmul
+    # the kept experts are the global top k of all nk*nk scores (fp64 logits)
+    for t in range(T):
+        s = (logits[t, :nk][:, None] + logits[t, nk:][None, :]).reshape(-1)
+        order = np.lexsort((np.arange(nk * nk), -s))[:k]
+        assert idx[t].tolist() == order.tolist()
+        wdense = np.zeros(nk * nk)
+        e = np.exp(s[order] - s[order].max())
+        wdense[order] = e / e.sum()
+        ref = (wdense * _silu(df @ hf[t])) @ uf            # every expert, zero weight unless kept
+        assert np.allclose(out[t], ref, rtol=1e-10, atol=1e-12)
+        assert np.allclose(wts[t], wdense[order], rtol=1e-12)
+
+
+def test_single_expert_gets_weight_one(oracle_mod):
+    T, H, nk = 3, 16, 5
+    h, router, down, up = si.make_cdmoe(T, H, nk, "f32", seed=4)
+    idx, wts, out = oracle_mod.cdmoe(h, router, down, up, 1)
+    assert np.array_equal(wts, np.ones((T, 1)))
+    for t in range(T):
+        e = idx[t, 0]
+        z = float(down[e].astype(np.float64) @ h[t].astype(np.float64))
+        assert np.allclose(out[t], _silu(z) * up[e].astype(np.float64), rtol=1e-12, atol=1e-14)
