@@ -573,10 +573,12 @@ void oracle_dt_bwd(const void *V, const void *W, const void *bias, const float *
  * token with hidden state h (length H):
  *   logits = router_gate h, 2*nk values: the first nk are the x domain, the
  *            last nk the y domain (nk = floor(sqrt(num_experts)));
- *   the top k of each domain (larger first, lower index first among equal);
+ *   the top k of each domain (larger first, lower index first among equal),
+ *            a and b being the ranks in the two lists;
  *   every pair (a, b) of the two lists scores sx_a + sy_b and names expert
  *            ix_a * nk + iy_b; the token keeps the top k pairs (larger score
- *            first, lower expert index first among equal);
+ *            first; among equal scores the lower a, then the lower b: the
+ *            order of the two domains' own rankings);
  *   weights = softmax over the k kept scores;
  *   out = sum over kept experts e of weight_e * silu(down_e . h) * up_e.
  * Plain loops and qsort, fp64 on the stored values.
@@ -587,6 +589,7 @@ void oracle_dt_bwd(const void *V, const void *W, const void *bias, const float *
  */
 typedef struct {
     double v;
+    int32_t tb;  /* tie order: lower first */
     int32_t idx;
 } score_t_;
 
@@ -597,7 +600,7 @@ static int score_first(const void *pa, const void *pb)
         return -1;
     if (a->v < b->v)
         return 1;
-    return (a->idx > b->idx) - (a->idx < b->idx);
+    return (a->tb > b->tb) - (a->tb < b->tb);
 }
 
 void oracle_cdmoe(const void *h, const void *router, const void *down, const void *up, int dtype, int T, int H,
@@ -617,13 +620,14 @@ void oracle_cdmoe(const void *h, const void *router, const void *down, const voi
                     acc += elem(router, dtype, (size_t)n * H + c) * elem(h, dtype, hr + c);
                 score_t_ *dst = n < nk ? &sx[n] : &sy[n - nk];
                 dst->v = acc;
-                dst->idx = n < nk ? n : n - nk;
+                dst->idx = dst->tb = n < nk ? n : n - nk;
             }
             qsort(sx, (size_t)nk, sizeof *sx, score_first);
             qsort(sy, (size_t)nk, sizeof *sy, score_first);
             for (int a = 0; a < k; ++a)
                 for (int b = 0; b < k; ++b) {
                     pairs[a * k + b].v = sx[a].v + sy[b].v;
+                    pairs[a * k + b].tb = a * k + b;
                     pairs[a * k + b].idx = sx[a].idx * nk + sy[b].idx;
                 }
             qsort(pairs, (size_t)k * k, sizeof *pairs, score_first);
@@ -653,7 +657,10 @@ void oracle_cdmoe(const void *h, const void *router, const void *down, const voi
 
 /*
  * The routing step alone, from given router logits (float32 [T][2*nk]): the
- * kept experts in selection order and their weights, as oracle_cdmoe.
+ * kept experts in selection order and their weights, as oracle_cdmoe, except
+ * that a pair's score is the float32 sum of its two float32 logits (the pages
+ * fix no precision; the HIP kernel ranks pairs on that float32 sum, and a
+ * ranking decided by floating point is taken in the kernel's precision).
  */
 void oracle_cdmoe_route(const float *logits, int T, int nk, int k, int32_t *idx, double *wts)
 {
@@ -666,15 +673,16 @@ void oracle_cdmoe_route(const float *logits, int T, int nk, int k, int32_t *idx,
         for (int t = 0; t < T; ++t) {
             for (int n = 0; n < nk; ++n) {
                 sx[n].v = logits[(size_t)t * 2 * nk + n];
-                sx[n].idx = n;
+                sx[n].idx = sx[n].tb = n;
                 sy[n].v = logits[(size_t)t * 2 * nk + nk + n];
-                sy[n].idx = n;
+                sy[n].idx = sy[n].tb = n;
             }
             qsort(sx, (size_t)nk, sizeof *sx, score_first);
             qsort(sy, (size_t)nk, sizeof *sy, score_first);
             for (int a = 0; a < k; ++a)
                 for (int b = 0; b < k; ++b) {
-                    pairs[a * k + b].v = sx[a].v + sy[b].v;
+                    pairs[a * k + b].v = (double)((float)sx[a].v + (float)sy[b].v);
+                    pairs[a * k + b].tb = a * k + b;
                     pairs[a * k + b].idx = sx[a].idx * nk + sy[b].idx;
                 }
             qsort(pairs, (size_t)k * k, sizeof *pairs, score_first);

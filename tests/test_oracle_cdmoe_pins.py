@@ -1,9 +1,14 @@
 """Pins of the oracle's CDMoE routed experts (CPU).
 
+(The routing from given float32 logits ranks a pair on the float32 sum of its
+two logits, the precision the GPU kernel decides in; the brute force below
+does the same.)
+
 The two-stage product-key routing (top k per domain, then the top k of the
 k*k pairs) is checked against a brute force that scores every one of the
-nk*nk experts directly (score = x logit + y logit, expert ax*nk + ay) and
-sorts them all; the weights against the softmax closed form; the logits
+nk*nk experts directly (score = x logit + y logit) and sorts them all, equal
+scores in the order of the two domains' own rankings (the x key's rank, then
+the y key's); the weights against the softmax closed form; the logits
 against a library matmul; the expert output against a dense formulation
 that weights every expert (zero for the ones not kept).
 """
@@ -13,15 +18,25 @@ import pytest
 import synth_inputs as si
 
 
+def _domain_rank(v):
+    """rank of each key in its domain: larger first, lower index first among equal"""
+    order = np.lexsort((np.arange(v.size), -v))
+    r = np.empty(v.size, np.int64)
+    r[order] = np.arange(v.size)
+    return r
+
+
 def _brute_route(logits, k):
     T, n2 = logits.shape
     nk = n2 // 2
-    lx, ly = logits[:, :nk].astype(np.float64), logits[:, nk:].astype(np.float64)
+    lx, ly = logits[:, :nk].astype(np.float32), logits[:, nk:].astype(np.float32)
     idx = np.empty((T, k), np.int64)
     sc = np.empty((T, k))
     for t in range(T):
-        s = (lx[t][:, None] + ly[t][None, :]).reshape(-1)   # expert a*nk + b
-        order = np.lexsort((np.arange(nk * nk), -s))         # score desc, index asc
+        # expert a*nk + b scores the float32 sum of its two logits
+        s = (lx[t][:, None] + ly[t][None, :]).reshape(-1).astype(np.float64)
+        tie = (_domain_rank(lx[t])[:, None] * nk + _domain_rank(ly[t])[None, :]).reshape(-1)
+        order = np.lexsort((tie, -s))                        # score desc, then the domain ranks
         idx[t] = order[:k]
         sc[t] = s[order[:k]]
     return idx, sc
@@ -60,7 +75,8 @@ def test_cdmoe_output_against_dense_formulation(oracle_mod, dtype):
     # the kept experts are the global top k of all nk*nk scores (fp64 logits)
     for t in range(T):
         s = (logits[t, :nk][:, None] + logits[t, nk:][None, :]).reshape(-1)
-        order = np.lexsort((np.arange(nk * nk), -s))[:k]
+        tie = (_domain_rank(logits[t, :nk])[:, None] * nk + _domain_rank(logits[t, nk:])[None, :]).reshape(-1)
+        order = np.lexsort((tie, -s))[:k]
         assert idx[t].tolist() == order.tolist()
         wdense = np.zeros(nk * nk)
         e = np.exp(s[order] - s[order].max())
