@@ -21,6 +21,7 @@ Functions mirror the C ABI in ``include/dma.h``:
     prefill_bwd(Q, K, V, W, A, w, dO, ...)               -> dict of every gradient
     select_window(dt, w, win, seqlens=None)             -> (tau, tie) under a sliding window
     attn_window_fwd(Q, K, V, dt, tau, tie, w, win, seqlens=None) -> O
+    cdmoe_logits(h, router), cdmoe_route(logits, k), cdmoe_experts(h, down, up, idx, weights)
 """
 from __future__ import annotations
 
@@ -45,7 +46,8 @@ EXPORTS = ("dma_version", "dma_status_str", "dma_dt", "dma_select", "dma_attn_fw
            "dma_decode_step_workspace_bytes", "dma_decode_state_init", "dma_decode_step",
            "dma_decode_state_kept", "dma_qk_norm_rope", "dma_prologue",
            "dma_attn_bwd_workspace_bytes", "dma_attn_bwd", "dma_dt_bwd_workspace_bytes", "dma_dt_bwd",
-           "dma_select_window", "dma_attn_window_fwd")
+           "dma_select_window", "dma_attn_window_fwd", "dma_cdmoe_logits", "dma_cdmoe_route",
+           "dma_cdmoe_experts")
 
 
 class DmaError(RuntimeError):
@@ -104,6 +106,12 @@ def lib():
     L.dma_select_window.restype = I
     L.dma_attn_window_fwd.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, I, I, I, P, P]
     L.dma_attn_window_fwd.restype = I
+    L.dma_cdmoe_logits.argtypes = [P, P, I, I, I, I, P, P]
+    L.dma_cdmoe_logits.restype = I
+    L.dma_cdmoe_route.argtypes = [P, I, I, I, P, P, P]
+    L.dma_cdmoe_route.restype = I
+    L.dma_cdmoe_experts.argtypes = [P, P, P, I, P, P, I, I, I, I, P, P]
+    L.dma_cdmoe_experts.restype = I
     _lib = L
     return L
 
@@ -482,4 +490,54 @@ def attn_window_fwd(Q, K, V, dt_, tau, tie, w, win, seqlens=None, out=None):
         out = torch.empty_like(Q)
     _call(lib().dma_attn_window_fwd(_ptr(Q), _ptr(K), _ptr(V), BF16, _ptr(dt_), _ptr(tau), _ptr(tie), _ptr(seqlens),
                                     B, S, Hq, Hkv, d, int(w), int(win), _ptr(out), _stream(Q)), "dma_attn_window_fwd")
+    return out
+
+
+def cdmoe_logits(h, router, out=None):
+    """Router logits [T, 2*nk] float32 of hidden states h [T, H] (bf16) for router [2*nk, H]."""
+    _check(h, "h", torch.bfloat16, 2)
+    _check(router, "router", torch.bfloat16, 2, h.device)
+    T, H = h.shape
+    n2 = router.shape[0]
+    if router.shape[1] != H or n2 % 2:
+        raise ValueError("router must be [2*nk, H]")
+    if out is None:
+        out = torch.empty((T, n2), dtype=torch.float32, device=h.device)
+    _call(lib().dma_cdmoe_logits(_ptr(h), _ptr(router), BF16, T, H, n2 // 2, _ptr(out), _stream(h)),
+          "dma_cdmoe_logits")
+    return out
+
+
+def cdmoe_route(logits, k, idx=None, weights=None):
+    """Product-key routing: (expert indices [T, k] int32 best first, weights [T, k] float32)."""
+    _check(logits, "logits", torch.float32, 2)
+    T, n2 = logits.shape
+    if idx is None:
+        idx = torch.empty((T, int(k)), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((T, int(k)), dtype=torch.float32, device=logits.device)
+    _call(lib().dma_cdmoe_route(_ptr(logits), T, n2 // 2, int(k), _ptr(idx), _ptr(weights), _stream(logits)),
+          "dma_cdmoe_route")
+    return idx, weights
+
+
+def cdmoe_experts(h, down, up, idx, weights, out=None):
+    """sum_e weights * silu(down[idx] . h) * up[idx] per token: [T, H] bf16."""
+    _check(h, "h", torch.bfloat16, 2)
+    dev = h.device
+    _check(down, "down", torch.bfloat16, 2, dev)
+    _check(up, "up", torch.bfloat16, 2, dev)
+    _check(idx, "idx", torch.int32, 2, dev)
+    _check(weights, "weights", torch.float32, 2, dev)
+    T, H = h.shape
+    E = down.shape[0]
+    nk = int(round(E ** 0.5))
+    if nk * nk != E or tuple(up.shape) != (E, H) or down.shape[1] != H:
+        raise ValueError("down/up must be [nk*nk, H]")
+    if idx.shape[0] != T or weights.shape != idx.shape:
+        raise ValueError("idx/weights must be [T, k]")
+    if out is None:
+        out = torch.empty_like(h)
+    _call(lib().dma_cdmoe_experts(_ptr(h), _ptr(down), _ptr(up), BF16, _ptr(idx), _ptr(weights), T, H, nk,
+                                  idx.shape[1], _ptr(out), _stream(h)), "dma_cdmoe_experts")
     return out

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdma.so")
-SOURCES = ["api.hip", "dt.hip", "select.hip", "attn.hip", "decode.hip", "decode_state.hip", "prologue.hip", "bwd.hip", "dt_bwd.hip", "window.hip"]
+SOURCES = ["api.hip", "dt.hip", "select.hip", "attn.hip", "decode.hip", "decode_state.hip", "prologue.hip", "bwd.hip", "dt_bwd.hip", "window.hip", "cdmoe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -237,4 +237,31 @@ int dma_attn_window_fwd(const void *Q, const void *K, const void *V, int dtype, 
                                             (hipStream_t)stream));
 }
 
+int dma_cdmoe_logits(const void *h, const void *router, int dtype, int T, int H, int nk, float *logits,
+                     void *stream) {
+    if (!h || !router || !logits) return DMA_ERR_NULL;
+    if (!dtype_ok(dtype)) return DMA_ERR_DTYPE;
+    if (T < 1 || H < 1 || nk < 1) return DMA_ERR_SHAPE;
+    if (dtype != DMA_BF16 || H % 32 != 0 || nk > dma::kMaxCdmoeKeys) return DMA_ERR_UNSUPPORTED;
+    if (!aligned16(h) || !aligned16(router)) return DMA_ERR_UNSUPPORTED;
+    return from_hip(dma::launch_cdmoe_logits(h, router, T, H, nk, logits, (hipStream_t)stream));
+}
+
+int dma_cdmoe_route(const float *logits, int T, int nk, int k, int32_t *idx, float *weights, void *stream) {
+    if (!logits || !idx || !weights) return DMA_ERR_NULL;
+    if (T < 1 || nk < 1 || k < 1 || k > nk) return DMA_ERR_SHAPE;
+    if (nk > dma::kMaxCdmoeKeys || k > dma::kMaxCdmoeTopk) return DMA_ERR_UNSUPPORTED;
+    return from_hip(dma::launch_cdmoe_route(logits, T, nk, k, idx, weights, (hipStream_t)stream));
+}
+
+int dma_cdmoe_experts(const void *h, const void *down, const void *up, int dtype, const int32_t *idx,
+                      const float *weights, int T, int H, int nk, int k, void *out, void *stream) {
+    if (!h || !down || !up || !idx || !weights || !out) return DMA_ERR_NULL;
+    if (!dtype_ok(dtype)) return DMA_ERR_DTYPE;
+    if (T < 1 || H < 1 || nk < 1 || k < 1 || k > nk * nk) return DMA_ERR_SHAPE;
+    if (dtype != DMA_BF16 || H % 512 != 0 || k > dma::kMaxCdmoeTopk || T > 0x7fffffff) return DMA_ERR_UNSUPPORTED;
+    if (!aligned16(h) || !aligned16(down) || !aligned16(up) || !aligned16(out)) return DMA_ERR_UNSUPPORTED;
+    return from_hip(dma::launch_cdmoe_experts(h, down, up, idx, weights, T, H, k, out, (hipStream_t)stream));
+}
+
 }  // extern "C"

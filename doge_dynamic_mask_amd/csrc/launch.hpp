@@ -67,6 +67,14 @@ hipError_t launch_attn_window(const void *Q, const void *K, const void *V, const
                               const int32_t *tie, const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d,
                               int win, void *O, hipStream_t stream);
 
+// CDMoE routed experts (cdmoe.hip), bf16.
+hipError_t launch_cdmoe_logits(const void *h, const void *router, int T, int H, int nk, float *logits,
+                               hipStream_t stream);
+hipError_t launch_cdmoe_route(const float *logits, int T, int nk, int k, int32_t *idx, float *wts,
+                              hipStream_t stream);
+hipError_t launch_cdmoe_experts(const void *h, const void *down, const void *up, const int32_t *idx, const float *wts,
+                                int T, int H, int k, void *out, hipStream_t stream);
+
 // Limits the launchers rely on (checked by the ABI layer).
 constexpr int kMaxHkvDt = 16;          // dt kernel: heads accumulated in registers
 constexpr int kMaxGroupAttn = 128;     // prefill: query heads per kv head
@@ -74,5 +82,7 @@ constexpr int kMaxGroupDecode = 16;    // decode: query heads per kv head
 constexpr int kMaxKeptDecode = 131072; // decode: kept positions per (batch, kv head)
 constexpr size_t kDtLdsBytes = 65536;  // dt kernel: W staged in LDS
 constexpr int kMaxGroupBwd = 8;        // backward: query heads per kv head (a divisor of 64)
+constexpr int kMaxCdmoeKeys = 256;     // CDMoE routing: keys per domain
+constexpr int kMaxCdmoeTopk = 128;     // CDMoE routing: experts kept per token
 
 }  // namespace dma

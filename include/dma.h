@@ -335,6 +335,41 @@ int dma_attn_window_fwd(const void *Q, const void *K, const void *V, int dtype, 
                         const int32_t *tie, const int32_t *seqlens, int B, int S, int Hq, int Hkv, int d, int w,
                         int win, void *O, void *stream);
 
+/*
+ * CDMoE routed experts -- Doge guide, section on Cross Domain MoE, and the
+ * DogeConfig table (num_experts = nk*nk, num_experts_per_tok = k,
+ * hidden_act = silu).  Tokens are rows of hidden states h [T][H].
+ *
+ * dma_cdmoe_logits -- router_gate: logits[t][n] = sum_c router[n][c] h[t][c]
+ * for the 2*nk outputs (the first nk are the x domain, the last nk the y
+ * domain).  h [T][H], router [2*nk][H] bf16; logits [T][2*nk] float32 (out).
+ * Matrix cores, float32 accumulation.  H a multiple of 32, nk <= 256.
+ */
+int dma_cdmoe_logits(const void *h, const void *router, int dtype, int T, int H, int nk, float *logits,
+                     void *stream);
+
+/*
+ * dma_cdmoe_route -- product-key routing: the top k of each domain (larger
+ * first, lower index first among equal), the k best of the pairs of the two
+ * lists by score x logit + y logit (a float32 sum; equal scores in the order
+ * of the two domains' own rankings, x first), each naming expert
+ * x index * nk + y index, and the softmax of the k best scores.
+ *   logits [T][2*nk] float32; idx [T][k] int32 (out, best first);
+ *   weights [T][k] float32 (out).  Exact selection.  k <= min(nk, 128),
+ *   nk <= 256.
+ */
+int dma_cdmoe_route(const float *logits, int T, int nk, int k, int32_t *idx, float *weights, void *stream);
+
+/*
+ * dma_cdmoe_experts -- the kept experts of each token as embedding rows:
+ *   out[t] = sum_e weights[t][e] * silu(down[idx[t][e]] . h[t]) * up[idx[t][e]]
+ *   h [T][H], down/up [nk*nk][H] bf16; idx, weights as from dma_cdmoe_route;
+ *   out [T][H] bf16 (out).  float32 arithmetic, one rounding at the end.
+ *   H a multiple of 512, k <= 128.  The expert indices must be below nk*nk.
+ */
+int dma_cdmoe_experts(const void *h, const void *down, const void *up, int dtype, const int32_t *idx,
+                      const float *weights, int T, int H, int nk, int k, void *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,6 +68,10 @@ def _load():
         lib.oracle_cdmoe.restype = None
         lib.oracle_cdmoe_route.argtypes = [P, I, I, I, P, P]
         lib.oracle_cdmoe_route.restype = None
+        lib.oracle_cdmoe_logits.argtypes = [P, P, I, I, I, I, P]
+        lib.oracle_cdmoe_logits.restype = None
+        lib.oracle_cdmoe_experts.argtypes = [P, P, P, I, P, P, I, I, I, P]
+        lib.oracle_cdmoe_experts.restype = None
         _lib = lib
     return _lib
 
@@ -270,3 +274,30 @@ def cdmoe_route(logits, k):
     wts = np.empty((T, k))
     _load().oracle_cdmoe_route(_ptr(logits), T, nk, int(k), _ptr(idx), _ptr(wts))
     return idx, wts
+
+
+def cdmoe_logits(h, router):
+    """Router logits [T, 2*nk] in fp64."""
+    h, th = _elem_array(h)
+    router, tr = _elem_array(router)
+    assert th == tr
+    T, H = h.shape
+    nk = router.shape[0] // 2
+    out = np.empty((T, 2 * nk))
+    _load().oracle_cdmoe_logits(_ptr(h), _ptr(router), th, T, H, nk, _ptr(out))
+    return out
+
+
+def cdmoe_experts(h, down, up, idx, wts):
+    """Expert output [T, H] in fp64 for given kept experts idx [T, k] and weights [T, k]."""
+    h, th = _elem_array(h)
+    down, td = _elem_array(down)
+    up, tu = _elem_array(up)
+    assert th == td == tu
+    T, H = h.shape
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    wts = np.ascontiguousarray(wts, dtype=np.float64)
+    k = idx.shape[1]
+    out = np.empty((T, H))
+    _load().oracle_cdmoe_experts(_ptr(h), _ptr(down), _ptr(up), th, _ptr(idx), _ptr(wts), T, H, k, _ptr(out))
+    return out

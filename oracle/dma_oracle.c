@@ -699,3 +699,40 @@ void oracle_cdmoe_route(const float *logits, int T, int nk, int k, int32_t *idx,
         free(sx);
     }
 }
+
+/* The router logits alone (as in oracle_cdmoe): logits [T][2*nk] double. */
+void oracle_cdmoe_logits(const void *h, const void *router, int dtype, int T, int H, int nk, double *logits)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t)
+        for (int n = 0; n < 2 * nk; ++n) {
+            double acc = 0.0;
+            for (int c = 0; c < H; ++c)
+                acc += elem(router, dtype, (size_t)n * H + c) * elem(h, dtype, (size_t)t * H + c);
+            logits[(size_t)t * 2 * nk + n] = acc;
+        }
+}
+
+/*
+ * The experts alone, for given kept experts and weights (as in oracle_cdmoe):
+ * out[t] = sum_e wts[t][e] * silu(down[idx[t][e]] . h[t]) * up[idx[t][e]].
+ */
+void oracle_cdmoe_experts(const void *h, const void *down, const void *up, int dtype, const int32_t *idx,
+                          const double *wts, int T, int H, int k, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        const size_t hr = (size_t)t * H;
+        for (int c = 0; c < H; ++c)
+            out[hr + c] = 0.0;
+        for (int e = 0; e < k; ++e) {
+            const size_t er = (size_t)idx[(size_t)t * k + e] * H;
+            double z = 0.0;
+            for (int c = 0; c < H; ++c)
+                z += elem(down, dtype, er + c) * elem(h, dtype, hr + c);
+            const double a = wts[(size_t)t * k + e] * z / (1.0 + exp(-z));
+            for (int c = 0; c < H; ++c)
+                out[hr + c] += a * elem(up, dtype, er + c);
+        }
+    }
+}

@@ -205,3 +205,16 @@ def test_window_validation(dma):
     assert call(win=0) == -2
     assert call(Hq=6, Hkv=2) == -4
     assert call(d=80) == -4
+
+
+def test_cdmoe_validation(dma):
+    assert dma.dma_cdmoe_logits(None, FAKE, 1, 4, 64, 8, FAKE2, None) == -1
+    assert dma.dma_cdmoe_logits(FAKE, FAKE, 0, 4, 64, 8, FAKE2, None) == -4    # bf16 only
+    assert dma.dma_cdmoe_logits(FAKE, FAKE, 1, 4, 60, 8, FAKE2, None) == -4    # H % 32
+    assert dma.dma_cdmoe_logits(FAKE, FAKE, 1, 4, 64, 300, FAKE2, None) == -4  # nk > 256
+    assert dma.dma_cdmoe_route(None, 4, 16, 4, FAKE, FAKE2, None) == -1
+    assert dma.dma_cdmoe_route(FAKE, 4, 16, 17, FAKE, FAKE2, None) == -2       # k > nk
+    assert dma.dma_cdmoe_route(FAKE, 4, 256, 129, FAKE, FAKE2, None) == -4     # k > 128
+    assert dma.dma_cdmoe_experts(FAKE, FAKE, FAKE, 1, FAKE, None, 4, 512, 8, 4, FAKE2, None) == -1
+    assert dma.dma_cdmoe_experts(FAKE, FAKE, FAKE, 1, FAKE, FAKE, 4, 500, 8, 4, FAKE2, None) == -4
+    assert dma.dma_cdmoe_experts(FAKE, FAKE, FAKE, 1, FAKE, FAKE, 4, 512, 16, 129, FAKE2, None) == -4

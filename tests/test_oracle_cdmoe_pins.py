@@ -95,3 +95,25 @@ def test_single_expert_gets_weight_one(oracle_mod):
         e = idx[t, 0]
         z = float(down[e].astype(np.float64) @ h[t].astype(np.float64))
         assert np.allclose(out[t], _silu(z) * up[e].astype(np.float64), rtol=1e-12, atol=1e-14)
+
+
+def test_logits_and_experts_alone(oracle_mod):
+    """The two halves exported on their own: logits against a library matmul,
+    experts against the dense all-expert formulation for arbitrary (also
+    repeated) expert lists and weights, and both against the whole oracle."""
+    T, H, nk, k = 5, 32, 6, 3
+    h, router, down, up = si.make_cdmoe(T, H, nk, "bf16", seed=8)
+    f = lambda x: si.bf16_bits_to_f32(x).astype(np.float64)
+    lg = oracle_mod.cdmoe_logits(h, router)
+    assert np.allclose(lg, f(h) @ f(router).T, rtol=1e-12, atol=1e-15)
+    rng = np.random.default_rng(9)
+    idx = rng.integers(0, nk * nk, size=(T, k)).astype(np.int32)
+    idx[0, 1] = idx[0, 0]                                   # a repeated expert adds twice
+    w = rng.random((T, k))
+    got = oracle_mod.cdmoe_experts(h, down, up, idx, w)
+    for t in range(T):
+        wd = np.zeros(nk * nk)
+        np.add.at(wd, idx[t], w[t])
+        assert np.allclose(got[t], (wd * _silu(f(down) @ f(h)[t])) @ f(up), rtol=1e-10, atol=1e-14)
+    i2, w2, o2 = oracle_mod.cdmoe(h, router, down, up, k)
+    assert np.allclose(oracle_mod.cdmoe_experts(h, down, up, i2, w2), o2, rtol=1e-12, atol=1e-15)
