@@ -18,9 +18,10 @@
 // every (a', b') with a' <= a and b' <= b (their scores are at least as large,
 // and equal scores go in the order of the domain ranks), so only the pairs
 // with (a + 1)(b + 1) <= k can be among the k best: about k (1 + ln k) of them
-// instead of k^2.  These are ranked among themselves the same way; the
-// softmax of the k best scores gives the weights.  Pair scores are float32
-// sums of the two logits.
+// instead of k^2.  For k <= 64 the k-th best of them is found one bit of its
+// 64-bit key at a time and the k winners are sorted across the lanes; larger
+// k ranks every candidate against every other.  The softmax of the k best
+// scores gives the weights.  Pair scores are float32 sums of the two logits.
 //
 // cdmoe_experts_kernel: one workgroup per token.  Its waves take the kept
 // experts in turn for z = down_e . h (lanes split the hidden size), each
@@ -98,36 +99,53 @@ __global__ __launch_bounds__(kThreads) void cdmoe_logits_kernel(const uint16_t *
 // ---------------------------------------------------------------- routing
 constexpr int kMaxNk = 256;
 constexpr int kMaxK = 128;
-constexpr int kMaxCand = 768;  // sum over a < k of floor(k / (a + 1)) for k <= 128 is 695
+// candidates for k <= 64 (sum over a < k of floor(k / (a + 1)) is at most
+// 303) and for k <= 128 (695); SMALL kernels hold the smaller LDS layout, so
+// that more of them are resident
+constexpr int kMaxCandSmall = 320;
+constexpr int kMaxCandLarge = 768;
 
+template <int MAXC, int MAXK>
 struct RouteLds {
-    float lv[2][kMaxNk];   // logits of the two domains
-    float sv[2][kMaxK];    // top-k values in rank order
-    int si[2][kMaxK];      // and their indices
-    int pref[kMaxK + 1];   // first candidate of each x rank
-    float cs[kMaxCand];    // candidate scores
-    int ct[kMaxCand];      // candidate tie order a * k + b
-    int ce[kMaxCand];      // candidate expert index
+    __align__(16) float cs[MAXC];        // candidate scores
+    __align__(16) int ct[MAXC];          // candidate tie order a * k + b
+    __align__(16) int ce[MAXC];          // candidate expert index
+    __align__(16) float lv[2][kMaxNk];   // logits of the two domains
+    __align__(16) float sv[2][MAXK];     // top-k values in rank order
+    __align__(16) int si[2][MAXK];       // and their indices
+    __align__(16) int pref[MAXK + 4];    // first candidate of each x rank
 };
 
+template <bool SMALL>
 __global__ __launch_bounds__(kThreads) void cdmoe_route_kernel(const float *__restrict__ logits, int T, int nk, int k,
                                                                int32_t *__restrict__ idx, float *__restrict__ wts) {
-    __shared__ RouteLds lds[kWaves];
+    constexpr int kMaxCand = SMALL ? kMaxCandSmall : kMaxCandLarge;
+    using Lds = RouteLds<kMaxCand, SMALL ? 64 : kMaxK>;
+    __shared__ Lds lds[kWaves];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * kWaves + wave;
     if (t >= T) return;  // uniform per wave; no block barrier below
-    RouteLds &L = lds[wave];
+    Lds &L = lds[wave];
     const float *lrow = logits + (size_t)t * 2 * nk;
-    for (int n = lane; n < 2 * nk; n += 64) L.lv[n >= nk][n >= nk ? n - nk : n] = lrow[n];
+    const int nk4 = (nk + 3) & ~3;  // domains padded to 4 with -inf (never better)
+    for (int n = lane; n < 2 * nk4; n += 64) {
+        const int d = n >= nk4, m2 = n - d * nk4;
+        L.lv[d][m2] = m2 < nk ? lrow[d * nk + m2] : -INFINITY;
+    }
     wave_lds_sync();
-    // rank of each key in its domain; the k best go to (sv, si) in rank order
+    // rank of each key in its domain (4 keys per LDS read); the k best go to
+    // (sv, si) in rank order
     for (int d = 0; d < 2; ++d) {
         for (int n = lane; n < nk; n += 64) {
             const float v = L.lv[d][n];
             int rank = 0;
-            for (int m2 = 0; m2 < nk; ++m2) {
-                const float u = L.lv[d][m2];
-                rank += (u > v) | ((u == v) & (m2 < n));
+#pragma unroll 8
+            for (int m2 = 0; m2 < nk4; m2 += 4) {
+                const float4 u = *reinterpret_cast<const float4 *>(&L.lv[d][m2]);
+                rank += (u.x > v) | ((u.x == v) & (m2 < n));
+                rank += (u.y > v) | ((u.y == v) & (m2 + 1 < n));
+                rank += (u.z > v) | ((u.z == v) & (m2 + 2 < n));
+                rank += (u.w > v) | ((u.w == v) & (m2 + 3 < n));
             }
             if (rank < k) {
                 L.sv[d][rank] = v;
@@ -157,20 +175,108 @@ __global__ __launch_bounds__(kThreads) void cdmoe_route_kernel(const float *__re
     }
     wave_lds_sync();
     const int ncand = L.pref[k];
-    for (int c = lane; c < ncand; c += 64) {
-        int lo = 0, hi = k - 1;  // the last a with pref[a] <= c
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (L.pref[mid] <= c) lo = mid; else hi = mid - 1;
+    const int ncand4 = (ncand + 3) & ~3;  // padded with candidates that lose to all
+    for (int c = ncand + lane; c < ncand4; c += 64) {
+        L.cs[c] = -INFINITY;
+        L.ct[c] = 0x7fffffff;
+    }
+    {
+        // x rank a pairs with y ranks b < k / (a + 1): lane b writes (a, b)
+        const int b = lane;
+        const float yv = b < k ? L.sv[1][b] : 0.f;
+        const int yi = b < k ? L.si[1][b] : 0;
+        for (int a = 0; a < k; ++a) {
+            if (b < min(k, k / (a + 1))) {
+                const int c = L.pref[a] + b;
+                L.cs[c] = L.sv[0][a] + yv;
+                L.ct[c] = a * k + b;
+                L.ce[c] = L.si[0][a] * nk + yi;
+            }
         }
-        const int a = lo, b = c - L.pref[a];
-        L.cs[c] = L.sv[0][a] + L.sv[1][b];
-        L.ct[c] = a * k + b;
-        L.ce[c] = L.si[0][a] * nk + L.si[1][b];
+        // y ranks 64 .. k-1 (k > 64) pair only with x rank 0
+        for (int b2 = 64 + lane; b2 < k; b2 += 64) {
+            L.cs[b2] = L.sv[0][0] + L.sv[1][b2];
+            L.ct[b2] = b2;
+            L.ce[b2] = L.si[0][0] * nk + L.si[1][b2];
+        }
     }
     wave_lds_sync();
-    // rank the candidates; the best score is the softmax's offset
+    // the best score is the softmax's offset
     const float top = L.sv[0][0] + L.sv[1][0];
+    if constexpr (SMALL) {
+        // A candidate's 44-bit selection key: its score's order bits, then the
+        // lower tie order first; keys are unique.  The k-th largest key by one
+        // bit at a time (a count over all candidates per bit), the k winners
+        // compacted one per lane, then sorted across the lanes.
+        constexpr int NC = 5;  // for k <= 64 there are at most 303 candidates
+        uint64_t key[NC];
+        int cid[NC];
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+            const int c = lane + 64 * u;
+            cid[u] = c;
+            // tie orders a * k + b are below 64 * 64 = 2^12
+            key[u] = c < ncand ? ((uint64_t)ordkey(L.cs[c]) << 12) | (uint64_t)(4095u - (uint32_t)L.ct[c]) : 0ull;
+        }
+        // the wave's count of keys >= probe: each lane counts at most NC < 8,
+        // summed over the lanes bit by bit with ballots (no lane shuffles)
+        uint64_t thr = 0;
+        for (int bit = 43; bit >= 0; --bit) {
+            const uint64_t probe = thr | (1ull << bit);
+            int c1 = 0;
+#pragma unroll
+            for (int u = 0; u < NC; ++u) c1 += key[u] >= probe;
+            const int cnt = __popcll(__ballot(c1 & 1)) + 2 * __popcll(__ballot(c1 & 2)) +
+                            4 * __popcll(__ballot(c1 & 4));
+            if (cnt >= k) thr = probe;
+        }
+        // winners (exactly k keys are >= thr) to LDS, one slot each
+        uint64_t *wk = reinterpret_cast<uint64_t *>(&L.lv[0][0]);  // the logits are no longer needed
+        int *we = reinterpret_cast<int *>(&L.lv[1][0]);
+        int base = 0;
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+            const bool win = key[u] >= thr && key[u] != 0ull;
+            const uint64_t m = __ballot(win);
+            if (win) {
+                const int pos = base + __popcll(m & ((1ull << lane) - 1));
+                wk[pos] = key[u];
+                we[pos] = L.ce[cid[u]];
+            }
+            base += __popcll(m);
+        }
+        wave_lds_sync();
+        uint64_t kk = lane < k ? wk[lane] : 0ull;
+        int ee = lane < k ? we[lane] : 0;
+        // bitonic sort across the 64 lanes, largest key first
+        for (int size = 2; size <= 64; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                const uint32_t lo32 = (uint32_t)__shfl_xor((int)(uint32_t)kk, stride, 64);
+                const uint32_t hi32 = (uint32_t)__shfl_xor((int)(uint32_t)(kk >> 32), stride, 64);
+                const uint64_t pk = ((uint64_t)hi32 << 32) | lo32;
+                const int pe = __shfl_xor(ee, stride, 64);
+                const bool up = (lane & size) == 0, lower = (lane & stride) == 0;
+                const bool take_max = up == lower;
+                const bool mine = take_max ? kk >= pk : kk <= pk;
+                if (!mine) {
+                    kk = pk;
+                    ee = pe;
+                }
+            }
+        }
+        // the winner's score from its order bits (ordkey is invertible up to
+        // the sign of zero)
+        const uint32_t ob = (uint32_t)(kk >> 12);
+        const float sc = __uint_as_float((ob & 0x80000000u) ? (ob & 0x7fffffffu) : ~ob);
+        const float e = lane < k ? __expf(sc - top) : 0.f;
+        const float den = wave_sum(e);
+        if (lane < k) {
+            idx[(size_t)t * k + lane] = ee;
+            wts[(size_t)t * k + lane] = e / den;
+        }
+        return;
+    } else {
+    // k > 64: every candidate ranked against every other
     float mysum = 0.f;
     int myrank[kMaxCand / 64];
     float myscore[kMaxCand / 64];
@@ -182,9 +288,14 @@ __global__ __launch_bounds__(kThreads) void cdmoe_route_kernel(const float *__re
             const float v = L.cs[c];
             const int tb = L.ct[c];
             int rank = 0;
-            for (int c2 = 0; c2 < ncand; ++c2) {
-                const float v2 = L.cs[c2];
-                rank += (v2 > v) | ((v2 == v) & (L.ct[c2] < tb));
+#pragma unroll 8
+            for (int c2 = 0; c2 < ncand4; c2 += 4) {
+                const float4 v2 = *reinterpret_cast<const float4 *>(&L.cs[c2]);
+                const int4 t2 = *reinterpret_cast<const int4 *>(&L.ct[c2]);
+                rank += (v2.x > v) | ((v2.x == v) & (t2.x < tb));
+                rank += (v2.y > v) | ((v2.y == v) & (t2.y < tb));
+                rank += (v2.z > v) | ((v2.z == v) & (t2.z < tb));
+                rank += (v2.w > v) | ((v2.w == v) & (t2.w < tb));
             }
             myrank[u] = rank;
             myscore[u] = v;
@@ -198,6 +309,7 @@ __global__ __launch_bounds__(kThreads) void cdmoe_route_kernel(const float *__re
             idx[(size_t)t * k + myrank[u]] = L.ce[c];
             wts[(size_t)t * k + myrank[u]] = __expf(myscore[u] - top) / denom;
         }
+    }
     }
 }
 
@@ -272,8 +384,11 @@ hipError_t launch_cdmoe_logits(const void *h, const void *router, int T, int H, 
 
 hipError_t launch_cdmoe_route(const float *logits, int T, int nk, int k, int32_t *idx, float *wts,
                               hipStream_t stream) {
-    hipLaunchKernelGGL(cdmoe_route_kernel, dim3((unsigned)((T + kWaves - 1) / kWaves)), dim3(kThreads), 0, stream,
-                       logits, T, nk, k, idx, wts);
+    const dim3 grid((unsigned)((T + kWaves - 1) / kWaves));
+    if (k <= 64)
+        hipLaunchKernelGGL(cdmoe_route_kernel<true>, grid, dim3(kThreads), 0, stream, logits, T, nk, k, idx, wts);
+    else
+        hipLaunchKernelGGL(cdmoe_route_kernel<false>, grid, dim3(kThreads), 0, stream, logits, T, nk, k, idx, wts);
     return hipGetLastError();
 }
 
