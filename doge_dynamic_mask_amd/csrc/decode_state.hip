@@ -23,10 +23,12 @@
 //     if any) and attends over its slots with the new row in place of the
 //     slot it takes: K straight into the score MFMA's operand registers, V
 //     through LDS, 32-slot blocks per wave with the next in flight, as the
-//     cache-scanning decode; one partial (max, sum, output) per query head.
+//     cache-scanning decode; one partial (max, sum, output) per query head,
+//     and the smallest key of its range after the step.
 //  2. combine: merges the partials of each (batch, query head) into the
 //     output; the workgroup of the first query head of each kv head then
-//     writes the admitted key into its slot and finds the new worst key.
+//     writes the admitted key into its slot and takes the new worst key
+//     from the range minima.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -67,7 +69,7 @@ inline StateLayout state_layout(int B, int Hkv, int d, int w) {
 inline int max_parts(int w) { return (w + 63) / 64; }
 
 struct StepWs {
-    size_t pm, pl, po, total;
+    size_t pm, pl, po, pk, ps, total;
 };
 
 inline StepWs step_ws_layout(int B, int Hq, int Hkv, int d, int w) {
@@ -77,7 +79,9 @@ inline StepWs step_ws_layout(int B, int Hq, int Hkv, int d, int w) {
     l.pm = 0;
     l.pl = up(l.pm + sizeof(float) * B * Hq * np);
     l.po = up(l.pl + sizeof(float) * B * Hq * np);
-    l.total = up(l.po + sizeof(float) * B * Hq * np * d);
+    l.pk = up(l.po + sizeof(float) * B * Hq * np * d);
+    l.ps = up(l.pk + sizeof(uint64_t) * B * Hkv * np);
+    l.total = up(l.ps + sizeof(int32_t) * B * Hkv * np);
     // state initialisation borrows the start of the workspace for thresholds
     if (l.total < up(sizeof(uint64_t) * B * Hkv)) l.total = up(sizeof(uint64_t) * B * Hkv);
     return l;
@@ -271,7 +275,8 @@ __global__ __launch_bounds__(kThreads, 2) void state_attend_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
     const float *__restrict__ dt_new, int Hq, int Hkv, int w, const BgHdr *__restrict__ hdr,
     const uint64_t *__restrict__ keys, const uint16_t *__restrict__ Ks, const uint16_t *__restrict__ Vs,
-    float *__restrict__ pm, float *__restrict__ pl, float *__restrict__ po, float qscale) {
+    float *__restrict__ pm, float *__restrict__ pl, float *__restrict__ po, uint64_t *__restrict__ pk,
+    int32_t *__restrict__ ps, float qscale) {
     constexpr int NW = kThreads / 64;
     constexpr int KB = 32;          // slots per wave block
     constexpr int NS = D / 32;      // 32-wide head_dim slices
@@ -284,6 +289,8 @@ __global__ __launch_bounds__(kThreads, 2) void state_attend_kernel(
     __shared__ float l_dtl[kMaxSlotsPerWG];
     __shared__ __align__(16) uint16_t Vw[NW][KB * KP];
     __shared__ float mw[NW][16], lw[NW][16];
+    __shared__ uint64_t red_k[NW];
+    __shared__ int red_s[NW];
 
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int nsplit = gridDim.x;
@@ -405,11 +412,46 @@ __global__ __launch_bounds__(kThreads, 2) void state_attend_kernel(
     // both depend only on the header
     int kb = wave * KB;
     if (kb < cnt) load_rows(kr, vr, kb);
+    // the same pass finds the smallest key of the range after the step (the
+    // admitted slot holding the new key), the candidate for the next eviction
+    uint64_t mk = ~0ull;
+    int ms = -1;
     for (int x = tid; x < cnt; x += kThreads) {
         const int s = s0 + x;
-        l_dtl[x] = (s == adm ? dtn : key_dt(kb_keys[s])) * kLog2e;
+        const uint64_t ku = s == adm ? key_new : kb_keys[s];
+        l_dtl[x] = (s == adm ? dtn : key_dt(ku)) * kLog2e;
+        if (ku < mk) {
+            mk = ku;
+            ms = s;
+        }
     }
-    __syncthreads();  // l_dtl visible
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)mk, o, 64);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(mk >> 32), o, 64);
+        const int os = __shfl_xor(ms, o, 64);
+        const uint64_t ok = ((uint64_t)hi << 32) | lo;
+        if (ok < mk) {
+            mk = ok;
+            ms = os;
+        }
+    }
+    if (lane == 0) {
+        red_k[wave] = mk;
+        red_s[wave] = ms;
+    }
+    __syncthreads();  // l_dtl and the per-wave minima visible
+    if (tid == 0) {
+#pragma unroll
+        for (int w2 = 1; w2 < NW; ++w2) {
+            if (red_k[w2] < mk) {
+                mk = red_k[w2];
+                ms = red_s[w2];
+            }
+        }
+        pk[bg * nsplit + split] = mk;
+        ps[bg * nsplit + split] = ms;
+    }
 
     // this wave's blocks: kb = (wave + NW*k) * KB, two register sets in turn;
     // the next block is requested unconditionally (offsets clamp to the last
@@ -465,18 +507,40 @@ __global__ __launch_bounds__(kThreads, 2) void state_attend_kernel(
 // One workgroup (d threads) per (batch, query head): merges the partials into
 // the output.  The workgroup of the first query head of each kv head then
 // applies the step to the state: the admitted key into its slot, the worst
-// kept key found again, the length advanced.
+// kept key taken from the attend workgroups' range minima, the length
+// advanced.
 __global__ __launch_bounds__(128) void state_combine_kernel(
-    const float *__restrict__ pm, const float *__restrict__ pl, const float *__restrict__ po, int nchunk, int d,
-    int Hq, int Hkv, int w, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
-    const float *__restrict__ dt_new, BgHdr *__restrict__ hdr, uint64_t *__restrict__ keys,
-    int32_t *__restrict__ pos, uint16_t *__restrict__ Ks, uint16_t *__restrict__ Vs, uint16_t *__restrict__ out) {
+    const float *__restrict__ pm, const float *__restrict__ pl, const float *__restrict__ po,
+    const uint64_t *__restrict__ pk, const int32_t *__restrict__ ps, int nchunk, int d, int Hq, int Hkv, int w,
+    const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new, const float *__restrict__ dt_new,
+    BgHdr *__restrict__ hdr, uint64_t *__restrict__ keys, int32_t *__restrict__ pos, uint16_t *__restrict__ Ks,
+    uint16_t *__restrict__ Vs, uint16_t *__restrict__ out) {
     constexpr int kGroup = 8;
     __shared__ uint64_t red_k[2];
     __shared__ int red_s[2];
     const int bh = blockIdx.x;  // b * Hq + hq
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int e = min(tid, d - 1);
+    const int G = Hq / Hkv;
+    const int b = bh / Hq, hq = bh - b * Hq;
+    const int g = hq / G;
+    const size_t bg = (size_t)b * Hkv + g;
+    // the step's own inputs depend on nothing the merge computes: requested
+    // together with the partials
+    const BgHdr h = hdr[bg];
+    const float dtn = dt_new[bg];
+    const uint16_t kn = k_new[bg * d + e], vn = v_new[bg * d + e];
+    uint64_t mk = ~0ull;
+    int ms = -1;
+    for (int x = tid; x < nchunk; x += blockDim.x) {
+        const uint64_t k = pk[bg * nchunk + x];
+        const int sl = ps[bg * nchunk + x];
+        if (k < mk) {
+            mk = k;
+            ms = sl;
+        }
+    }
+
     const float *m = pm + (size_t)bh * nchunk;
     const float *l = pl + (size_t)bh * nchunk;
     const float *o = po + (size_t)bh * nchunk * d + e;
@@ -510,37 +574,50 @@ __global__ __launch_bounds__(128) void state_combine_kernel(
     }
     if (tid < d) out[(size_t)bh * d + tid] = f32_to_bf16(den > 0.f ? num / den : 0.f);
 
-    const int G = Hq / Hkv;
-    const int b = bh / Hq, hq = bh - b * Hq;
-    if (hq % G != 0) return;  // uniform
-    const int g = hq / G;
-    const size_t bg = (size_t)b * Hkv + g;
-    const BgHdr h = hdr[bg];
-    const uint64_t key_new = selkey(dt_new[bg], (uint32_t)h.len);
+    if (hq != g * G) return;  // uniform
+    const uint64_t key_new = selkey(dtn, (uint32_t)h.len);
     int n;
     const int adm = admit(h, key_new, w, n);
-    uint64_t *kb = keys + bg * w;
     if (adm >= 0) {
         const size_t dst = (bg * w + adm) * d;
-        for (int x = tid; x < d; x += blockDim.x) {
-            Ks[dst + x] = k_new[bg * d + x];
-            Vs[dst + x] = v_new[bg * d + x];
+        if (tid < d) {
+            Ks[dst + tid] = kn;
+            Vs[dst + tid] = vn;
         }
         if (tid == 0) {
-            kb[adm] = key_new;
+            keys[bg * w + adm] = key_new;
             pos[bg * w + adm] = h.len;
         }
     }
-    uint64_t kmin;
-    int smin;
-    worst_key(kb, n, adm, key_new, (int)blockDim.x, kmin, smin, red_k, red_s);
+#pragma unroll
+    for (int o2 = 32; o2 >= 1; o2 >>= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)mk, o2, 64);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(mk >> 32), o2, 64);
+        const int os = __shfl_xor(ms, o2, 64);
+        const uint64_t ok = ((uint64_t)hi << 32) | lo;
+        if (ok < mk) {
+            mk = ok;
+            ms = os;
+        }
+    }
+    if (lane == 0) {
+        red_k[wave] = mk;
+        red_s[wave] = ms;
+    }
+    __syncthreads();
     if (tid == 0) {
+        for (int q = 1; q < (int)(blockDim.x + 63) / 64; ++q) {
+            if (red_k[q] < mk) {
+                mk = red_k[q];
+                ms = red_s[q];
+            }
+        }
         BgHdr nh;
         nh.n = n;
         nh.len = h.len + 1;
-        nh.min_slot = smin;
+        nh.min_slot = ms;
         nh.pad = 0;
-        nh.min_key = kmin;
+        nh.min_key = mk;
         hdr[bg] = nh;
     }
 }
@@ -592,21 +669,23 @@ hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_ne
     uint16_t *Ks = (uint16_t *)(st + sl.K);
     uint16_t *Vs = (uint16_t *)(st + sl.V);
     float *pm = (float *)(wsb + wl.pm), *pl = (float *)(wsb + wl.pl), *po = (float *)(wsb + wl.po);
+    uint64_t *pk = (uint64_t *)(wsb + wl.pk);
+    int32_t *ps = (int32_t *)(wsb + wl.ps);
     const float qscale = (float)(1.0 / __builtin_sqrt((double)d) * 1.4426950408889634);
     const int nparts = parts_for(B, Hkv, w);
     const dim3 grid(nparts, Hkv, B);
     if (d == 128)
         hipLaunchKernelGGL(state_attend_kernel<128>, grid, dim3(kThreads), 0, stream, (const uint16_t *)q,
                            (const uint16_t *)k_new, (const uint16_t *)v_new, dt_new, Hq, Hkv, w, hdr, keys, Ks, Vs,
-                           pm, pl, po, qscale);
+                           pm, pl, po, pk, ps, qscale);
     else
         hipLaunchKernelGGL(state_attend_kernel<64>, grid, dim3(kThreads), 0, stream, (const uint16_t *)q,
                            (const uint16_t *)k_new, (const uint16_t *)v_new, dt_new, Hq, Hkv, w, hdr, keys, Ks, Vs,
-                           pm, pl, po, qscale);
+                           pm, pl, po, pk, ps, qscale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(state_combine_kernel, dim3(B * Hq), dim3(d), 0, stream, pm, pl, po, nparts, d, Hq, Hkv, w,
-                       (const uint16_t *)k_new, (const uint16_t *)v_new, dt_new, hdr, keys, pos, Ks, Vs,
+    hipLaunchKernelGGL(state_combine_kernel, dim3(B * Hq), dim3(d), 0, stream, pm, pl, po, pk, ps, nparts, d, Hq,
+                       Hkv, w, (const uint16_t *)k_new, (const uint16_t *)v_new, dt_new, hdr, keys, pos, Ks, Vs,
                        (uint16_t *)out);
     return hipGetLastError();
 }
