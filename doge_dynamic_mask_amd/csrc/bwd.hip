@@ -13,9 +13,12 @@
 //
 // Query side (attn_bwd_q_kernel): one workgroup per (batch, kv head, tile of
 // 64 / G query rows), its four waves holding 16 (row, head) pairs each, one
-// pair per lane column.  Key blocks of 64 from position 0 to the tile's last
-// row are staged in LDS; every kept test is evaluated (key j is kept by row i
-// when j <= i < L and selkey(dt_j, j) >= selkey(tau_i, tie_i)).  Pass 1 finds
+// pair per lane column.  Only candidate keys are walked: by nesting, those
+// kept by row i0 (the tile's first row) and the tile's own keys, about
+// w + 64/G of them, compacted into an LDS list (the causal range when they
+// overflow it).  Key blocks of 64 candidates are gathered into LDS and every
+// kept test is evaluated (key j is kept by row i when j <= i < L and
+// selkey(dt_j, j) >= selkey(tau_i, tie_i)).  Pass 1 finds
 // each pair's log-sum-exp; pass 2 recomputes the scores and forms dS^T and
 // dQ^T += K^T dS^T.  D_i is accumulated in pass 1 as sum_j p_ij dp_ij (with
 // the same online rescaling as the softmax sum), in float32 from the very
@@ -34,9 +37,9 @@
 // of its keys.  dV^T += dO^T P and dK^T += Q^T dS accumulate in registers;
 // ddt is the column sum of dS.
 //
-// Both kernels touch every (pair, key) of the causal range they walk, not only
-// the kept ones: work grows like the dense causal attention rather than like
-// the kept count.
+// The key side touches every (pair, key) of the row range it walks, not only
+// the kept ones: its work grows like the dense causal attention rather than
+// like the kept count.
 //
 // Layout facts of v_mfma_f32_16x16x32_bf16 (l = lane, q = l / 16):
 //   A[m = l%16][k = 8q + j], B[k = 8q + j][n = l%16], C[m = 4q + i][n = l%16].
@@ -54,6 +57,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPairs = 64;   // (row, head) pairs per query tile and per row block
 constexpr int kBlk = 64;     // keys per block on the query side
+constexpr int kCandCap = 3072;  // candidate keys of a query tile held in LDS
+constexpr int kScanKeys = 4 * kThreads;  // prefix keys classified per scan step
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -100,7 +105,7 @@ __device__ __forceinline__ bf16x8 ld8(const uint16_t *p) { return *reinterpret_c
 
 // ---------------------------------------------------------------- query side
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_bwd_q_kernel(
+__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const float *__restrict__ dt, const float *__restrict__ tau, const int32_t *__restrict__ tie,
     const int32_t *__restrict__ seqlens, const uint16_t *__restrict__ dO, int S, int Hq, int Hkv, int G, int ntq,
@@ -113,6 +118,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_q_kernel(
     __shared__ __align__(16) uint16_t Vs[kBlk * P];
     __shared__ float dtl_s[kBlk];
     __shared__ uint64_t skey_s[kBlk];
+    __shared__ int jk_s[kBlk];
+    __shared__ int c_idx[kCandCap];
+    __shared__ uint32_t wcnt[kThreads / 64];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int q = lane >> 4, pq = lane & 15;
@@ -163,22 +171,78 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_q_kernel(
     const uint16_t *Kb = K + (size_t)b * S * kvs + (size_t)g * D;
     const uint16_t *Vb = V + (size_t)b * S * kvs + (size_t)g * D;
     const float *drow = dt + urow;
+
+    // ---- candidate keys.  By nesting, a key j <= i0 that some row of the
+    // tile keeps is kept by row i0, and the keys (i0, kmax] are the tile's
+    // own: only those are walked, about w + 64/G keys instead of the causal
+    // range.  They are compacted into LDS (in index order within each scan
+    // step's wave and register; the order changes only the summation order);
+    // past kCandCap candidates the whole causal range is walked instead.
+    int n;
+    {
+        const uint64_t thr0 = selkey(tau[urow + i0], (uint32_t)tie[urow + i0]);
+        const uint64_t lt_mask = (1ull << lane) - 1ull;
+        int base = 0;
+        for (int c0 = 0; c0 <= i0; c0 += kScanKeys) {
+            float dv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dv[e] = drow[min(c0 + tid + kThreads * e, i0)];
+            bool pr[4];
+            uint32_t nw = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = c0 + tid + kThreads * e;
+                pr[e] = j <= i0 && selkey(dv[e], (uint32_t)j) >= thr0;
+                nw += (uint32_t)__popcll(__ballot(pr[e]));
+            }
+            if (lane == 0) wcnt[wave] = nw;
+            __syncthreads();
+            int off = base, tot = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < kThreads / 64; ++w2) {
+                const int cw = (int)wcnt[w2];
+                off += w2 < wave ? cw : 0;
+                tot += cw;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint64_t bl = __ballot(pr[e]);
+                const int pos = off + (int)__popcll(bl & lt_mask);
+                if (pr[e] && pos < kCandCap) c_idx[pos] = c0 + tid + kThreads * e;
+                off += (int)__popcll(bl);
+            }
+            base += tot;
+            __syncthreads();  // wcnt is rewritten by the next step
+        }
+        for (int x = tid; x < kmax - i0; x += kThreads)
+            if (base + x < kCandCap) c_idx[base + x] = i0 + 1 + x;
+        n = base + (kmax - i0);
+    }
+    const bool gathered = n <= kCandCap;
+    if (!gathered) n = kmax + 1;
+    __syncthreads();  // c_idx visible
+
+    // key at list position x (x < n)
+    auto key_at = [&](int x) __attribute__((always_inline)) { return gathered ? c_idx[x] : x; };
     // A key block's K and V rows and dt are requested into registers one
     // block ahead and written to LDS after the barrier that ends the block
-    // before.  Keys past the tile's last row repeat it (never kept).
+    // before.  Positions past the list's end repeat its last key and are
+    // marked never kept.
     u32x4 rk[NV], rv[NV];
     float rdt;
-    auto fetch = [&](int k0) __attribute__((always_inline)) {
+    int rj;
+    auto fetch = [&](int x0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int v = tid + u * kThreads;
-            const size_t off = (size_t)(uint32_t)min(k0 + v / (D / 8), kmax) * kvs + 8 * (v % (D / 8));
+            const size_t off = (size_t)(uint32_t)key_at(min(x0 + v / (D / 8), n - 1)) * kvs + 8 * (v % (D / 8));
             rk[u] = *reinterpret_cast<const u32x4 *>(Kb + off);
             rv[u] = *reinterpret_cast<const u32x4 *>(Vb + off);
         }
-        rdt = drow[min(k0 + (tid & (kBlk - 1)), kmax)];
+        rj = key_at(min(x0 + (tid & (kBlk - 1)), n - 1));
+        rdt = drow[rj];
     };
-    auto put = [&](int k0) __attribute__((always_inline)) {
+    auto put = [&](int x0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int v = tid + u * kThreads;
@@ -188,13 +252,14 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_q_kernel(
         }
         if (tid < kBlk) {
             dtl_s[tid] = rdt * kLog2e;
-            skey_s[tid] = selkey(rdt, (uint32_t)min(k0 + tid, kmax));
+            skey_s[tid] = selkey(rdt, (uint32_t)rj);
+            jk_s[tid] = x0 + tid < n ? rj : 0x7fffffff;
         }
     };
     // base-2 scores of the block's 64 keys against this lane's pair and
     // dp = dO . v: z[mt][r] and dp[mt][r] are key 16 mt + 4 q + r, z = -inf
     // where not kept
-    auto scores = [&](int k0, float (&z)[4][4], f32x4 (&dp)[4]) __attribute__((always_inline)) {
+    auto scores = [&](float (&z)[4][4], f32x4 (&dp)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -206,8 +271,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_q_kernel(
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int kk = 16 * mt + 4 * q + r, j = k0 + kk;
-                const bool kept = live & (j <= i) & (skey_s[kk] >= thr);
+                const int kk = 16 * mt + 4 * q + r;
+                const bool kept = live & (jk_s[kk] <= i) & (skey_s[kk] >= thr);
                 const float zz = fmaf(sacc[r], qscale, dtl_s[kk]);
                 z[mt][r] = kept ? zz : -INFINITY;
             }
@@ -218,13 +283,13 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_q_kernel(
     // D = sum_j p_j dp_j, both with the online rescaling
     float m = -INFINITY, l = 0.f, u = 0.f;
     fetch(0);
-    for (int k0 = 0; k0 <= kmax; k0 += kBlk) {
-        put(k0);
+    for (int x0 = 0; x0 < n; x0 += kBlk) {
+        put(x0);
         __syncthreads();
-        fetch(k0 + kBlk <= kmax ? k0 + kBlk : 0);  // the next block, or pass 2's first
+        fetch(x0 + kBlk < n ? x0 + kBlk : 0);  // the next block, or pass 2's first
         float z[4][4];
         f32x4 dp[4];
-        scores(k0, z, dp);
+        scores(z, dp);
         float mb = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -268,13 +333,13 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_q_kernel(
     f32x4 dq[D / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) dq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 <= kmax; k0 += kBlk) {
-        put(k0);
+    for (int x0 = 0; x0 < n; x0 += kBlk) {
+        put(x0);
         __syncthreads();
-        if (k0 + kBlk <= kmax) fetch(k0 + kBlk);
+        if (x0 + kBlk < n) fetch(x0 + kBlk);
         float z[4][4];
         f32x4 dp[4], ds[4];
-        scores(k0, z, dp);
+        scores(z, dp);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll

@@ -44,6 +44,10 @@ BWD_CASES = [
     (1, 300, 2, 2, 64, 1, None, "few"),              # w = 1
     (1, 190, 1, 1, 64, 64, None, "const"),           # G = 1, all dt equal
     (2, 97, 16, 2, 128, 33, (97, 1), "lognormal"),   # G = 8, a batch of length 1
+    (1, 2600, 4, 2, 64, 300, None, "lognormal"),     # query tiles past 1024 keys: several scan steps
+    # late query tiles have more candidate keys than the query kernel's LDS
+    # list holds and walk the causal range instead
+    (1, 3300, 2, 1, 64, 3100, None, "lognormal"),
 ]
 
 
