@@ -29,13 +29,17 @@
 // key side.
 //
 // Key side (attn_bwd_kv_kernel): one workgroup per (batch, kv head, tile of
-// 64 or 128 keys); every wave holds 16 or 32 keys, one key per lane column,
-// with their K and V rows as MFMA operands in registers for the whole
-// workgroup.  By nesting the rows that keep key j form a run [j, e_j), and the
-// thresholds grow with the row, so the workgroup walks row blocks of 64 pairs
-// from its first key on and stops at the first row whose threshold passes all
-// of its keys.  dV^T += dO^T P and dK^T += Q^T dS accumulate in registers;
-// ddt is the column sum of dS.
+// 64 keys), two row groups of four waves; every wave holds 16 keys, one key
+// per lane column, with their K and V rows as MFMA operands in registers.  By
+// nesting the rows that keep key j form a run [j, e_j), and the thresholds
+// grow with the row, so the workgroup walks row blocks of 64 pairs from its
+// first key on (the two groups take alternate blocks, which halves the
+// longest tile's chain) and stops at the first row whose threshold passes
+// all of its keys.  Per block each lane finds its key's run of rows (two
+// threshold compares, a binary search in the block where the key drops out),
+// so the element test is one unsigned compare.  dV^T += dO^T P and
+// dK^T += Q^T dS accumulate in registers, ddt is the column sum of dS; the
+// second group hands its sums to the first through LDS (fixed order).
 //
 // The key side touches every (pair, key) of the row range it walks, not only
 // the kept ones: its work grows like the dense causal attention rather than
@@ -372,9 +376,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
 }
 
 // ------------------------------------------------------------------ key side
-// NKS: 16-key subtiles per wave (keys per workgroup = 64 NKS).
-template <int D, int NKS>
-__global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
+constexpr int kKvThreads = 512;  // two row groups of four waves
+
+template <int D>
+__global__ __launch_bounds__(kKvThreads) void attn_bwd_kv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const float *__restrict__ dt, const float *__restrict__ tau, const int32_t *__restrict__ tie,
     const int32_t *__restrict__ seqlens, const uint16_t *__restrict__ dO, const float *__restrict__ lse_ws,
@@ -382,15 +387,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
     uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, float *__restrict__ ddt) {
     constexpr int P = pitch<D>();
     constexpr int NS = D / 32;
-    constexpr int KT = 64 * NKS;                     // keys per workgroup
-    constexpr int NV = kPairs * D / 8 / kThreads;    // 16-byte vectors per thread per tile
-    __shared__ __align__(16) uint16_t Qs[kPairs * P];
-    __shared__ __align__(16) uint16_t Os[kPairs * P];  // dO of the row block
-    __shared__ float lse_s[kPairs], dd_s[kPairs];
-    __shared__ uint64_t thr_s[kPairs];
+    constexpr int NT = D / 16;
+    constexpr int NV = kPairs * D / 8 / kThreads;  // 16-byte vectors per group thread per tile
+    static_assert(4 * kPairs * P * 2 >= 4 * (2 * NT + 1) * 4 * 64 * 4, "the exchange fits in the row tiles");
+    // Q of each group's row block, then dO of each ([2 + h])
+    __shared__ __align__(16) uint16_t tiles[4][kPairs * P];
+    __shared__ __align__(16) float lse_s[2][kPairs], dd_s[2][kPairs];
+    __shared__ uint64_t thr_s[2][kPairs];
     __shared__ uint64_t kmax_s[4];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int hg = wave >> 2, kw = wave & 3;  // row group; key wave within it
+    const int gt = tid & (kThreads - 1);      // thread index within the row group
     const int q = lane >> 4, kk = lane & 15;
     // Early key tiles (the longest row ranges) are dispatched first.  Ids go
     // round-robin over the 8 XCDs, so with a multiple of 8 (batch, kv head)
@@ -399,58 +407,54 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
     const int kt = blockIdx.x / nbg, bg = blockIdx.x % nbg;
     const int g = bg % Hkv, b = bg / Hkv;
     const int L = seqlens ? seqlens[b] : S;
-    const int j0 = kt * KT;
+    const int j0 = kt * 64;
     const uint32_t kvs = (uint32_t)(Hkv * D);
     const size_t urow = ((size_t)b * Hkv + g) * S;
 
-    int jk[NKS];
-    bool kvalid[NKS];
-    float dtl[NKS];
-    uint64_t skey[NKS];
-    bf16x8 kb[NKS][NS], vb[NKS][NS];
-    uint64_t kmax = 0;
-#pragma unroll
-    for (int ns = 0; ns < NKS; ++ns) {
-        jk[ns] = j0 + 16 * (NKS * wave + ns) + kk;
-        kvalid[ns] = jk[ns] < L;
-        const int jc = min(jk[ns], S - 1);
+    // this lane's key (both row groups hold the same 64 keys)
+    const int jk = j0 + 16 * kw + kk;
+    const bool kvalid = jk < L;
+    const int jc = min(jk, S - 1);
+    bf16x8 kb[NS], vb[NS];
+    float dtl;
+    uint64_t skey;
+    {
         const float dv = dt[urow + jc];
-        dtl[ns] = dv * kLog2e;
-        skey[ns] = kvalid[ns] ? selkey(dv, (uint32_t)jc) : 0ull;
-        kmax = skey[ns] > kmax ? skey[ns] : kmax;
+        dtl = dv * kLog2e;
+        skey = kvalid ? selkey(dv, (uint32_t)jc) : 0ull;
         const uint16_t *kr = K + ((size_t)b * S + jc) * kvs + (size_t)g * D;
         const uint16_t *vr = V + ((size_t)b * S + jc) * kvs + (size_t)g * D;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            kb[ns][s] = ld8(kr + 32 * s + 8 * q);
-            vb[ns][s] = ld8(vr + 32 * s + 8 * q);
+            kb[s] = ld8(kr + 32 * s + 8 * q);
+            vb[s] = ld8(vr + 32 * s + 8 * q);
         }
     }
     // largest selection key of the workgroup's valid keys
+    uint64_t kmax = skey;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
         const uint64_t y = __shfl_xor(kmax, o, 64);
         kmax = y > kmax ? y : kmax;
     }
-    if (lane == 0) kmax_s[wave] = kmax;
+    if (lane == 0 && hg == 0) kmax_s[kw] = kmax;
     __syncthreads();
     kmax = kmax_s[0];
 #pragma unroll
     for (int w2 = 1; w2 < 4; ++w2) kmax = kmax_s[w2] > kmax ? kmax_s[w2] : kmax;
 
-    f32x4 dka[NKS][D / 16], dva[NKS][D / 16];
-    float dsum[NKS];
+    f32x4 dka[NT], dva[NT];
+    float dsum = 0.f;
 #pragma unroll
-    for (int ns = 0; ns < NKS; ++ns) {
-        dsum[ns] = 0.f;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-            dka[ns][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            dva[ns][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+    for (int t = 0; t < NT; ++t) {
+        dka[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dva[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     const int RB = kPairs / G;
+    uint16_t *Qg = tiles[hg], *Og = tiles[2 + hg];
+    float *lse_g = lse_s[hg], *dd_g = dd_s[hg];
+    uint64_t *thr_g = thr_s[hg];
     // A row block (Q and dO of its 64 pairs, their log-sum-exp and D, the
     // row thresholds) is requested into registers one block ahead and written
     // to LDS after the barrier that ends the block before.  Rows past the end
@@ -461,14 +465,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
     auto fetch = [&](int r0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int v = tid + u * kThreads;
+            const int v = gt + u * kThreads;
             const int p = v / (D / 8), cv = v % (D / 8);
             const int row = min(r0 + p / G, S - 1), hq = g * G + p % G;
             const size_t off = (((size_t)b * S + row) * Hq + hq) * D + 8 * cv;
             rq[u] = *reinterpret_cast<const u32x4 *>(Q + off);
             ro[u] = *reinterpret_cast<const u32x4 *>(dO + off);
         }
-        const int pp = tid & (kPairs - 1);
+        const int pp = gt & (kPairs - 1);
         const int row = min(r0 + pp / G, S - 1), hq = g * G + pp % G;
         rlse = lse_ws[((size_t)b * Hq + hq) * S + row];
         rdd = dd_ws[((size_t)b * Hq + hq) * S + row];
@@ -479,81 +483,139 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_kv_kernel(
     auto put = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int v = tid + u * kThreads;
+            const int v = gt + u * kThreads;
             const int p = v / (D / 8), cv = v % (D / 8);
-            *reinterpret_cast<u32x4 *>(&Qs[p * P + 8 * cv]) = rq[u];
-            *reinterpret_cast<u32x4 *>(&Os[p * P + 8 * cv]) = ro[u];
+            *reinterpret_cast<u32x4 *>(&Qg[p * P + 8 * cv]) = rq[u];
+            *reinterpret_cast<u32x4 *>(&Og[p * P + 8 * cv]) = ro[u];
         }
-        if (tid < kPairs) {
-            lse_s[tid] = rlse;
-            dd_s[tid] = rdd;
-            thr_s[tid] = rthr;
+        if (gt < kPairs) {
+            lse_g[gt] = rlse;
+            dd_g[gt] = rdd;
+            thr_g[gt] = rthr;
         }
     };
-    if (j0 < L) fetch(j0);
-    for (int r0 = j0; r0 < L && j0 < L; r0 += RB) {
-        put();
-        __syncthreads();
-        if (thr_s[0] > kmax) break;  // this row and every later one keep none of the keys
-        if (r0 + RB < L) fetch(r0 + RB);
-
+    // This lane's key against the group's row block: S and dP on the matrix
+    // cores, P and dS in registers, dV^T += dO^T P and dK^T += Q^T dS.  The
+    // pairs keeping the key form the run [plo, phi) of the block (the rows
+    // keeping a key are a run, and pair p holds row p / G); elsewhere the
+    // bias is -inf.
+    auto subtile = [&](int plo, int phi) __attribute__((always_inline)) {
+        const uint32_t span = (uint32_t)(phi - plo);
+        const int pb = 4 * q - plo;
+        f32x4 pm[4], dsm[4];
 #pragma unroll
-        for (int ns = 0; ns < NKS; ++ns) {
-            f32x4 pm[4], dsm[4];
+        for (int t = 0; t < 4; ++t) {
+            f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    sacc = mfma16(ld8(&Qs[(16 * t + kk) * P + 32 * s + 8 * q]), kb[ns][s], sacc);
-                    dp = mfma16(ld8(&Os[(16 * t + kk) * P + 32 * s + 8 * q]), vb[ns][s], dp);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int p = 16 * t + 4 * q + r;  // pair of this accumulator entry
-                    const int row = r0 + p / G;
-                    const bool kept = kvalid[ns] & (jk[ns] <= row) & (row < L) & (skey[ns] >= thr_s[p / G]);
-                    const float arg = fmaf(sacc[r], qscale, dtl[ns]) - lse_s[p];
-                    const float pv = __builtin_amdgcn_exp2f(kept ? arg : -INFINITY);  // 0 where not kept
-                    pm[t][r] = pv;
-                    dsm[t][r] = pv * (dp[r] - dd_s[p]);
-                    dsum[ns] += dsm[t][r];
-                }
+            for (int s = 0; s < NS; ++s) {
+                sacc = mfma16(ld8(&Qg[(16 * t + kk) * P + 32 * s + 8 * q]), kb[s], sacc);
+                dp = mfma16(ld8(&Og[(16 * t + kk) * P + 32 * s + 8 * q]), vb[s], dp);
             }
+            const float4 l4 = *reinterpret_cast<const float4 *>(&lse_g[16 * t + 4 * q]);
+            const float4 d4 = *reinterpret_cast<const float4 *>(&dd_g[16 * t + 4 * q]);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const bf16x8 pb = acc_operand(pm[2 * s2], pm[2 * s2 + 1]);
-                const bf16x8 sb = acc_operand(dsm[2 * s2], dsm[2 * s2 + 1]);
-#pragma unroll
-                for (int t = 0; t < D / 16; ++t) {
-                    dva[ns][t] = mfma16(tr_operand<P>(Os, 32 * s2, 16 * t, lane), pb, dva[ns][t]);
-                    dka[ns][t] = mfma16(tr_operand<P>(Qs, 32 * s2, 16 * t, lane), sb, dka[ns][t]);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const float bb = (uint32_t)(pb + 16 * t + r) < span ? dtl : -INFINITY;
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], qscale, bb) - lv[r]);  // 0 where not kept
+                pm[t][r] = pv;
+                dsm[t][r] = pv * (dp[r] - dv[r]);
+                dsum += dsm[t][r];
             }
         }
-        __syncthreads();
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const bf16x8 pbf = acc_operand(pm[2 * s2], pm[2 * s2 + 1]);
+            const bf16x8 sbf = acc_operand(dsm[2 * s2], dsm[2 * s2 + 1]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                dva[t] = mfma16(tr_operand<P>(Og, 32 * s2, 16 * t, lane), pbf, dva[t]);
+                dka[t] = mfma16(tr_operand<P>(Qg, 32 * s2, 16 * t, lane), sbf, dka[t]);
+            }
+        }
+    };
+
+    // The two row groups take alternate row blocks: group h the blocks
+    // base + h RB for base = j0, j0 + 2 RB, ...
+    if (j0 < L) {
+        if (j0 + hg * RB < L) fetch(j0 + hg * RB);
+        for (int base = j0; base < L; base += 2 * RB) {
+            const int r0 = base + hg * RB;
+            const bool act = r0 < L;
+            if (act) put();
+            __syncthreads();
+            // the first row of group 0's block and every later row keep none
+            // of the keys (thresholds grow with the row): done
+            if (thr_s[0][0] > kmax) break;
+            if (r0 + 2 * RB < L) fetch(r0 + 2 * RB);
+            if (act && thr_g[0] <= kmax) {
+                const int rl = min(RB, L - r0);  // rows of the block inside the sequence
+                // the block rows keeping key jk: from row jk on (j <= i), while
+                // the row's threshold is at most its key (a key once dropped
+                // stays dropped)
+                const int lo = min(max(jk - r0, 0), RB);
+                int hi = 0;
+                if (kvalid && thr_g[0] <= skey) {
+                    if (thr_g[rl - 1] <= skey) {
+                        hi = rl;
+                    } else {  // first row in (0, rl - 1] whose threshold passes the key
+                        int a = 1, e = rl - 1;
+                        while (a < e) {
+                            const int mid = (a + e) >> 1;
+                            if (thr_g[mid] > skey) e = mid; else a = mid + 1;
+                        }
+                        hi = a;
+                    }
+                }
+                const int plo = lo * G, phi = max(hi, lo) * G;
+                if (__any(phi > plo)) subtile(plo, phi);
+            }
+            __syncthreads();
+        }
     }
 
+    // group 1 hands its sums to group 0 through LDS (the row tiles are free
+    // now), which adds them in a fixed order and writes the key's gradients
+    __syncthreads();
+    float *xb = reinterpret_cast<float *>(&tiles[0][0]);  // [4 waves][2 NT + 1][4][64 lanes]
+    float *xw = xb + kw * (2 * NT + 1) * 4 * 64;
+    if (hg == 1) {
 #pragma unroll
-    for (int ns = 0; ns < NKS; ++ns) {
-        float sdt = dsum[ns];
-        sdt += __shfl_xor(sdt, 16, 64);
-        sdt += __shfl_xor(sdt, 32, 64);
-        const int j = jk[ns];
-        if (j < S) {
-            if (q == 0) ddt[urow + j] = sdt;
-            const size_t off = ((size_t)b * S + j) * kvs + (size_t)g * D;
+        for (int t = 0; t < NT; ++t) {
 #pragma unroll
-            for (int t = 0; t < D / 16; ++t) {
-                const uint32_t k0w = (uint32_t)f32_to_bf16(dka[ns][t][0] * c) |
-                                     ((uint32_t)f32_to_bf16(dka[ns][t][1] * c) << 16);
-                const uint32_t k1w = (uint32_t)f32_to_bf16(dka[ns][t][2] * c) |
-                                     ((uint32_t)f32_to_bf16(dka[ns][t][3] * c) << 16);
-                const uint32_t v0w = (uint32_t)f32_to_bf16(dva[ns][t][0]) | ((uint32_t)f32_to_bf16(dva[ns][t][1]) << 16);
-                const uint32_t v1w = (uint32_t)f32_to_bf16(dva[ns][t][2]) | ((uint32_t)f32_to_bf16(dva[ns][t][3]) << 16);
-                *reinterpret_cast<uint2 *>(dK + off + 16 * t + 4 * q) = make_uint2(k0w, k1w);
-                *reinterpret_cast<uint2 *>(dV + off + 16 * t + 4 * q) = make_uint2(v0w, v1w);
+            for (int i = 0; i < 4; ++i) {
+                xw[((2 * t) * 4 + i) * 64 + lane] = dka[t][i];
+                xw[((2 * t + 1) * 4 + i) * 64 + lane] = dva[t][i];
             }
+        }
+        xw[(2 * NT * 4) * 64 + lane] = dsum;
+    }
+    __syncthreads();
+    if (hg == 1) return;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dka[t][i] += xw[((2 * t) * 4 + i) * 64 + lane];
+            dva[t][i] += xw[((2 * t + 1) * 4 + i) * 64 + lane];
+        }
+    }
+    dsum += xw[(2 * NT * 4) * 64 + lane];
+
+    float sdt = dsum;
+    sdt += __shfl_xor(sdt, 16, 64);
+    sdt += __shfl_xor(sdt, 32, 64);
+    if (jk < S) {
+        if (q == 0) ddt[urow + jk] = sdt;
+        const size_t off = ((size_t)b * S + jk) * kvs + (size_t)g * D;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t k0w = (uint32_t)f32_to_bf16(dka[t][0] * c) | ((uint32_t)f32_to_bf16(dka[t][1] * c) << 16);
+            const uint32_t k1w = (uint32_t)f32_to_bf16(dka[t][2] * c) | ((uint32_t)f32_to_bf16(dka[t][3] * c) << 16);
+            const uint32_t v0w = (uint32_t)f32_to_bf16(dva[t][0]) | ((uint32_t)f32_to_bf16(dva[t][1]) << 16);
+            const uint32_t v1w = (uint32_t)f32_to_bf16(dva[t][2]) | ((uint32_t)f32_to_bf16(dva[t][3]) << 16);
+            *reinterpret_cast<uint2 *>(dK + off + 16 * t + 4 * q) = make_uint2(k0w, k1w);
+            *reinterpret_cast<uint2 *>(dV + off + 16 * t + 4 * q) = make_uint2(v0w, v1w);
         }
     }
 }
@@ -572,9 +634,8 @@ hipError_t launch_bwd_d(const void *Q, const void *K, const void *V, const float
     hipLaunchKernelGGL((attn_bwd_q_kernel<D>), dim3((unsigned)(B * Hkv * ntq)), dim3(kThreads), 0, stream,
                        (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau, tie, seqlens,
                        (const uint16_t *)dO, S, Hq, Hkv, G, ntq, qscale, c, (uint16_t *)dQ, lse_ws, dd_ws);
-    constexpr int NKS = 1;
-    const int nkt = (S + 64 * NKS - 1) / (64 * NKS);
-    hipLaunchKernelGGL((attn_bwd_kv_kernel<D, NKS>), dim3((unsigned)(B * Hkv * nkt)), dim3(kThreads), 0, stream,
+    const int nkt = (S + 63) / 64;
+    hipLaunchKernelGGL((attn_bwd_kv_kernel<D>), dim3((unsigned)(B * Hkv * nkt)), dim3(kKvThreads), 0, stream,
                        (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau, tie, seqlens,
                        (const uint16_t *)dO, lse_ws, dd_ws, S, Hq, Hkv, G, nkt, qscale, c, (uint16_t *)dK,
                        (uint16_t *)dV, ddt);
