@@ -179,55 +179,77 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
     // ---- candidate keys.  By nesting, a key j <= i0 that some row of the
     // tile keeps is kept by row i0, and the keys (i0, kmax] are the tile's
     // own: only those are walked, about w + 64/G keys instead of the causal
-    // range.  They are compacted into LDS (in index order within each scan
-    // step's wave and register; the order changes only the summation order);
-    // past kCandCap candidates the whole causal range is walked instead.
-    int n;
+    // range.  They are compacted into LDS in two classes: "full" keys, kept
+    // by every row of the tile (a key j <= i0 kept by the last row kmax, as
+    // thresholds grow with the row), from the front, and the rest from the
+    // back (each class in index order within a scan step's wave and register;
+    // the order changes only the summation order).  Blocks of full keys need
+    // no kept test.  Past kCandCap candidates the whole causal range is
+    // walked instead.
+    int n, nF;
     {
         const uint64_t thr0 = selkey(tau[urow + i0], (uint32_t)tie[urow + i0]);
+        const uint64_t thrl = selkey(tau[urow + kmax], (uint32_t)tie[urow + kmax]);
         const uint64_t lt_mask = (1ull << lane) - 1ull;
-        int base = 0;
+        int baseF = 0, baseP = 0;
         for (int c0 = 0; c0 <= i0; c0 += kScanKeys) {
             float dv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) dv[e] = drow[min(c0 + tid + kThreads * e, i0)];
-            bool pr[4];
-            uint32_t nw = 0;
+            bool pf[4], pp[4];
+            uint32_t nfw = 0, npw = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = c0 + tid + kThreads * e;
-                pr[e] = j <= i0 && selkey(dv[e], (uint32_t)j) >= thr0;
-                nw += (uint32_t)__popcll(__ballot(pr[e]));
+                const uint64_t sk = selkey(dv[e], (uint32_t)j);
+                const bool cand = j <= i0 && sk >= thr0;
+                pf[e] = cand && sk >= thrl;
+                pp[e] = cand && !pf[e];
+                nfw += (uint32_t)__popcll(__ballot(pf[e]));
+                npw += (uint32_t)__popcll(__ballot(pp[e]));
             }
-            if (lane == 0) wcnt[wave] = nw;
+            if (lane == 0) wcnt[wave] = nfw | (npw << 16);  // at most 1024 each
             __syncthreads();
-            int off = base, tot = 0;
+            int offF = baseF, offP = baseP, totF = 0, totP = 0;
 #pragma unroll
             for (int w2 = 0; w2 < kThreads / 64; ++w2) {
-                const int cw = (int)wcnt[w2];
-                off += w2 < wave ? cw : 0;
-                tot += cw;
+                const int cf = (int)(wcnt[w2] & 0xffffu), cp = (int)(wcnt[w2] >> 16);
+                offF += w2 < wave ? cf : 0;
+                offP += w2 < wave ? cp : 0;
+                totF += cf;
+                totP += cp;
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint64_t bl = __ballot(pr[e]);
-                const int pos = off + (int)__popcll(bl & lt_mask);
-                if (pr[e] && pos < kCandCap) c_idx[pos] = c0 + tid + kThreads * e;
-                off += (int)__popcll(bl);
+                const int j = c0 + tid + kThreads * e;
+                const uint64_t bf = __ballot(pf[e]), bp = __ballot(pp[e]);
+                const int posF = offF + (int)__popcll(bf & lt_mask);
+                const int posP = offP + (int)__popcll(bp & lt_mask);
+                if (pf[e] && posF < kCandCap) c_idx[posF] = j;
+                if (pp[e] && posP < kCandCap) c_idx[kCandCap - 1 - posP] = j;
+                offF += (int)__popcll(bf);
+                offP += (int)__popcll(bp);
             }
-            base += tot;
+            baseF += totF;
+            baseP += totP;
             __syncthreads();  // wcnt is rewritten by the next step
         }
         for (int x = tid; x < kmax - i0; x += kThreads)
-            if (base + x < kCandCap) c_idx[base + x] = i0 + 1 + x;
-        n = base + (kmax - i0);
+            if (baseP + x < kCandCap) c_idx[kCandCap - 1 - (baseP + x)] = i0 + 1 + x;
+        nF = baseF;
+        n = baseF + baseP + (kmax - i0);
     }
-    const bool gathered = n <= kCandCap;
-    if (!gathered) n = kmax + 1;
+    const bool gathered = n <= kCandCap;  // then the two classes do not overlap
+    if (!gathered) {
+        n = kmax + 1;
+        nF = 0;
+    }
     __syncthreads();  // c_idx visible
 
     // key at list position x (x < n)
-    auto key_at = [&](int x) __attribute__((always_inline)) { return gathered ? c_idx[x] : x; };
+    auto key_at = [&](int x) __attribute__((always_inline)) {
+        return gathered ? c_idx[x < nF ? x : kCandCap - 1 - (x - nF)] : x;
+    };
     // A key block's K and V rows and dt are requested into registers one
     // block ahead and written to LDS after the barrier that ends the block
     // before.  Positions past the list's end repeat its last key and are
@@ -262,8 +284,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
     };
     // base-2 scores of the block's 64 keys against this lane's pair and
     // dp = dO . v: z[mt][r] and dp[mt][r] are key 16 mt + 4 q + r, z = -inf
-    // where not kept
-    auto scores = [&](float (&z)[4][4], f32x4 (&dp)[4]) __attribute__((always_inline)) {
+    // where not kept; a block of full keys (full) is kept by every row of
+    // the tile, so only the rows past the length need masking, which the
+    // caller does
+    auto scores = [&](bool full, float (&z)[4][4], f32x4 (&dp)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -273,12 +297,20 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
                 sacc = mfma16(ld8(&Ks[(16 * mt + pq) * P + 32 * s + 8 * q]), qf[s], sacc);
                 dp[mt] = mfma16(ld8(&Vs[(16 * mt + pq) * P + 32 * s + 8 * q]), of[s], dp[mt]);
             }
+            const float4 d4 = *reinterpret_cast<const float4 *>(&dtl_s[16 * mt + 4 * q]);
+            const float dls[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int kk = 16 * mt + 4 * q + r;
-                const bool kept = live & (jk_s[kk] <= i) & (skey_s[kk] >= thr);
-                const float zz = fmaf(sacc[r], qscale, dtl_s[kk]);
-                z[mt][r] = kept ? zz : -INFINITY;
+            for (int r = 0; r < 4; ++r) z[mt][r] = fmaf(sacc[r], qscale, dls[r]);
+        }
+        if (!full) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int kk = 16 * mt + 4 * q + r;
+                    const bool kept = live & (jk_s[kk] <= i) & (skey_s[kk] >= thr);
+                    z[mt][r] = kept ? z[mt][r] : -INFINITY;
+                }
             }
         }
     };
@@ -293,7 +325,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
         fetch(x0 + kBlk < n ? x0 + kBlk : 0);  // the next block, or pass 2's first
         float z[4][4];
         f32x4 dp[4];
-        scores(z, dp);
+        scores(x0 + kBlk <= nF, z, dp);  // rows past the length: results unused
         float mb = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -332,6 +364,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
         dd = live ? uo / lo : 0.f;
     }
     const float lse2 = live ? m + log2f(l) : 0.f;
+    const float lse_p = live ? lse2 : INFINITY;  // p = 0 for rows past the length
 
     // ---- pass 2: dS^T and dQ^T += K^T dS^T
     f32x4 dq[D / 16];
@@ -343,12 +376,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
         if (x0 + kBlk < n) fetch(x0 + kBlk);
         float z[4][4];
         f32x4 dp[4], ds[4];
-        scores(z, dp);
+        scores(x0 + kBlk <= nF, z, dp);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float p = __builtin_amdgcn_exp2f(z[mt][r] - lse2);  // 0 where not kept
+                const float p = __builtin_amdgcn_exp2f(z[mt][r] - lse_p);  // 0 where not kept
                 ds[mt][r] = p * (dp[mt][r] - dd);
             }
         }
