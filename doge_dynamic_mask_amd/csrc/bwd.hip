@@ -29,17 +29,17 @@
 // key side.
 //
 // Key side (attn_bwd_kv_kernel): one workgroup per (batch, kv head, tile of
-// 64 keys), two row groups of four waves; every wave holds 16 keys, one key
-// per lane column, with their K and V rows as MFMA operands in registers.  By
-// nesting the rows that keep key j form a run [j, e_j), and the thresholds
-// grow with the row, so the workgroup walks row blocks of 64 pairs from its
-// first key on (the two groups take alternate blocks, which halves the
-// longest tile's chain) and stops at the first row whose threshold passes
-// all of its keys.  Per block each lane finds its key's run of rows (two
+// 64 keys), row groups of four waves (three at d = 64, two at d = 128, as
+// registers and LDS allow); every wave holds 16 keys, one key per lane
+// column, with their K and V rows as MFMA operands in registers.  By nesting
+// the rows that keep key j form a run [j, e_j), and the thresholds grow with
+// the row, so the workgroup walks row blocks of 64 pairs from its first key
+// on (the groups take the blocks in turn, which shortens the longest tile's
+// chain) and stops at the first row whose threshold passes all of its keys.  Per block each lane finds its key's run of rows (two
 // threshold compares, a binary search in the block where the key drops out),
 // so the element test is one unsigned compare.  dV^T += dO^T P and
 // dK^T += Q^T dS accumulate in registers, ddt is the column sum of dS; the
-// second group hands its sums to the first through LDS (fixed order).
+// other groups hand their sums to the first through LDS, in group order.
 //
 // The key side touches every (pair, key) of the row range it walks, not only
 // the kept ones: its work grows like the dense causal attention rather than
@@ -409,10 +409,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
 }
 
 // ------------------------------------------------------------------ key side
-constexpr int kKvThreads = 512;  // two row groups of four waves
-
-template <int D>
-__global__ __launch_bounds__(kKvThreads) void attn_bwd_kv_kernel(
+// NG row groups of four waves (kThreads threads each)
+template <int D, int NG>
+__global__ __launch_bounds__(NG * kThreads) void attn_bwd_kv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const float *__restrict__ dt, const float *__restrict__ tau, const int32_t *__restrict__ tie,
     const int32_t *__restrict__ seqlens, const uint16_t *__restrict__ dO, const float *__restrict__ lse_ws,
@@ -422,11 +421,11 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_kv_kernel(
     constexpr int NS = D / 32;
     constexpr int NT = D / 16;
     constexpr int NV = kPairs * D / 8 / kThreads;  // 16-byte vectors per group thread per tile
-    static_assert(4 * kPairs * P * 2 >= 4 * (2 * NT + 1) * 4 * 64 * 4, "the exchange fits in the row tiles");
-    // Q of each group's row block, then dO of each ([2 + h])
-    __shared__ __align__(16) uint16_t tiles[4][kPairs * P];
-    __shared__ __align__(16) float lse_s[2][kPairs], dd_s[2][kPairs];
-    __shared__ uint64_t thr_s[2][kPairs];
+    static_assert(2 * NG * kPairs * P * 2 >= 4 * (2 * NT + 1) * 4 * 64 * 4, "the exchange fits in the row tiles");
+    // Q of each group's row block, then dO of each ([NG + h])
+    __shared__ __align__(16) uint16_t tiles[2 * NG][kPairs * P];
+    __shared__ __align__(16) float lse_s[NG][kPairs], dd_s[NG][kPairs];
+    __shared__ uint64_t thr_s[NG][kPairs];
     __shared__ uint64_t kmax_s[4];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -485,7 +484,7 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_kv_kernel(
     }
 
     const int RB = kPairs / G;
-    uint16_t *Qg = tiles[hg], *Og = tiles[2 + hg];
+    uint16_t *Qg = tiles[hg], *Og = tiles[NG + hg];
     float *lse_g = lse_s[hg], *dd_g = dd_s[hg];
     uint64_t *thr_g = thr_s[hg];
     // A row block (Q and dO of its 64 pairs, their log-sum-exp and D, the
@@ -535,31 +534,34 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_kv_kernel(
     auto subtile = [&](int plo, int phi) __attribute__((always_inline)) {
         const uint32_t span = (uint32_t)(phi - plo);
         const int pb = 4 * q - plo;
-        f32x4 pm[4], dsm[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                sacc = mfma16(ld8(&Qg[(16 * t + kk) * P + 32 * s + 8 * q]), kb[s], sacc);
-                dp = mfma16(ld8(&Og[(16 * t + kk) * P + 32 * s + 8 * q]), vb[s], dp);
-            }
-            const float4 l4 = *reinterpret_cast<const float4 *>(&lse_g[16 * t + 4 * q]);
-            const float4 d4 = *reinterpret_cast<const float4 *>(&dd_g[16 * t + 4 * q]);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float bb = (uint32_t)(pb + 16 * t + r) < span ? dtl : -INFINITY;
-                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], qscale, bb) - lv[r]);  // 0 where not kept
-                pm[t][r] = pv;
-                dsm[t][r] = pv * (dp[r] - dv[r]);
-                dsum += dsm[t][r];
-            }
-        }
+        // two halves of 32 pairs: the second half's scores are formed while
+        // the first half's products run
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            const bf16x8 pbf = acc_operand(pm[2 * s2], pm[2 * s2 + 1]);
-            const bf16x8 sbf = acc_operand(dsm[2 * s2], dsm[2 * s2 + 1]);
+            f32x4 pm[2], dsm[2];
+#pragma unroll
+            for (int th = 0; th < 2; ++th) {
+                const int t = 2 * s2 + th;
+                f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    sacc = mfma16(ld8(&Qg[(16 * t + kk) * P + 32 * s + 8 * q]), kb[s], sacc);
+                    dp = mfma16(ld8(&Og[(16 * t + kk) * P + 32 * s + 8 * q]), vb[s], dp);
+                }
+                const float4 l4 = *reinterpret_cast<const float4 *>(&lse_g[16 * t + 4 * q]);
+                const float4 d4 = *reinterpret_cast<const float4 *>(&dd_g[16 * t + 4 * q]);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float bb = (uint32_t)(pb + 16 * t + r) < span ? dtl : -INFINITY;
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], qscale, bb) - lv[r]);  // 0 where not kept
+                    pm[th][r] = pv;
+                    dsm[th][r] = pv * (dp[r] - dv[r]);
+                    dsum += dsm[th][r];
+                }
+            }
+            const bf16x8 pbf = acc_operand(pm[0], pm[1]);
+            const bf16x8 sbf = acc_operand(dsm[0], dsm[1]);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 dva[t] = mfma16(tr_operand<P>(Og, 32 * s2, 16 * t, lane), pbf, dva[t]);
@@ -568,11 +570,11 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_kv_kernel(
         }
     };
 
-    // The two row groups take alternate row blocks: group h the blocks
-    // base + h RB for base = j0, j0 + 2 RB, ...
+    // The row groups take turns over the row blocks: group h the blocks
+    // base + h RB for base = j0, j0 + NG RB, ...
     if (j0 < L) {
         if (j0 + hg * RB < L) fetch(j0 + hg * RB);
-        for (int base = j0; base < L; base += 2 * RB) {
+        for (int base = j0; base < L; base += NG * RB) {
             const int r0 = base + hg * RB;
             const bool act = r0 < L;
             if (act) put();
@@ -580,7 +582,7 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_kv_kernel(
             // the first row of group 0's block and every later row keep none
             // of the keys (thresholds grow with the row): done
             if (thr_s[0][0] > kmax) break;
-            if (r0 + 2 * RB < L) fetch(r0 + 2 * RB);
+            if (r0 + NG * RB < L) fetch(r0 + NG * RB);
             if (act && thr_g[0] <= kmax) {
                 const int rl = min(RB, L - r0);  // rows of the block inside the sequence
                 // the block rows keeping key jk: from row jk on (j <= i), while
@@ -607,33 +609,38 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_kv_kernel(
         }
     }
 
-    // group 1 hands its sums to group 0 through LDS (the row tiles are free
-    // now), which adds them in a fixed order and writes the key's gradients
-    __syncthreads();
-    float *xb = reinterpret_cast<float *>(&tiles[0][0]);  // [4 waves][2 NT + 1][4][64 lanes]
-    float *xw = xb + kw * (2 * NT + 1) * 4 * 64;
-    if (hg == 1) {
+    // the other groups hand their sums to group 0 through LDS (the row tiles
+    // are free now), one group at a time in group order, and group 0 writes
+    // the key's gradients
+    float *xw = reinterpret_cast<float *>(&tiles[0][0]) + kw * (2 * NT + 1) * 4 * 64;  // [4 waves][2 NT + 1][4][64]
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
+    for (int h2 = 1; h2 < NG; ++h2) {
+        __syncthreads();
+        if (hg == h2) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                xw[((2 * t) * 4 + i) * 64 + lane] = dka[t][i];
-                xw[((2 * t + 1) * 4 + i) * 64 + lane] = dva[t][i];
+            for (int t = 0; t < NT; ++t) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xw[((2 * t) * 4 + i) * 64 + lane] = dka[t][i];
+                    xw[((2 * t + 1) * 4 + i) * 64 + lane] = dva[t][i];
+                }
             }
+            xw[(2 * NT * 4) * 64 + lane] = dsum;
         }
-        xw[(2 * NT * 4) * 64 + lane] = dsum;
-    }
-    __syncthreads();
-    if (hg == 1) return;
+        __syncthreads();
+        if (hg == 0) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+            for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            dka[t][i] += xw[((2 * t) * 4 + i) * 64 + lane];
-            dva[t][i] += xw[((2 * t + 1) * 4 + i) * 64 + lane];
+                for (int i = 0; i < 4; ++i) {
+                    dka[t][i] += xw[((2 * t) * 4 + i) * 64 + lane];
+                    dva[t][i] += xw[((2 * t + 1) * 4 + i) * 64 + lane];
+                }
+            }
+            dsum += xw[(2 * NT * 4) * 64 + lane];
         }
     }
-    dsum += xw[(2 * NT * 4) * 64 + lane];
+    if (hg > 0) return;
 
     float sdt = dsum;
     sdt += __shfl_xor(sdt, 16, 64);
@@ -668,7 +675,8 @@ hipError_t launch_bwd_d(const void *Q, const void *K, const void *V, const float
                        (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau, tie, seqlens,
                        (const uint16_t *)dO, S, Hq, Hkv, G, ntq, qscale, c, (uint16_t *)dQ, lse_ws, dd_ws);
     const int nkt = (S + 63) / 64;
-    hipLaunchKernelGGL((attn_bwd_kv_kernel<D>), dim3((unsigned)(B * Hkv * nkt)), dim3(kKvThreads), 0, stream,
+    constexpr int NG = D == 64 ? 3 : 2;  // row groups the registers and LDS allow
+    hipLaunchKernelGGL((attn_bwd_kv_kernel<D, NG>), dim3((unsigned)(B * Hkv * nkt)), dim3(NG * kThreads), 0, stream,
                        (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau, tie, seqlens,
                        (const uint16_t *)dO, lse_ws, dd_ws, S, Hq, Hkv, G, nkt, qscale, c, (uint16_t *)dK,
                        (uint16_t *)dV, ddt);
