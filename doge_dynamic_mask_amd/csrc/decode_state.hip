@@ -298,14 +298,11 @@ __global__ __launch_bounds__(kThreads, 2) void state_attend_kernel(
     const int G = Hq / Hkv;
     const int col = lane & 15, grp = lane >> 4;
     const size_t bg = (size_t)b * Hkv + g;
-    const BgHdr h = hdr[bg];
-    const float dtn = dt_new[bg];
-    const uint64_t key_new = selkey(dtn, (uint32_t)h.len);
-    int n;
-    const int adm = admit(h, key_new, w, n);
-    const int per = (n + nsplit - 1) / nsplit;
-    const int s0 = min(split * per, n), s1 = min(s0 + per, n);
-    const int cnt = s1 - s0;
+    // the workgroup's range of slots does not depend on the header (only
+    // its first n slots are kept), so its first requests need not wait for it
+    const int per = (w + nsplit - 1) / nsplit;
+    const int s0 = min(split * per, w);
+    const int cnt_all = min(per, w - s0);
     const uint64_t *kb_keys = keys + bg * w;
     const uint16_t *Kb = Ks + bg * w * D;
     const uint16_t *Vb = Vs + bg * w * D;
@@ -333,23 +330,47 @@ __global__ __launch_bounds__(kThreads, 2) void state_attend_kernel(
     // as whole rows for LDS (vector v = lane + 64u: row v / RV, column v % RV);
     // the admitted slot reads the new token's row
     u32x4 kr[NK], vr[NU], kn[NK], vn[NU];
-    auto row_of = [&](const uint16_t *base, const uint16_t *nrow, int x) __attribute__((always_inline)) {
-        const int s = s0 + min(x, cnt - 1);
-        return s == adm ? nrow : base + (size_t)s * D;
+    // slot offset x of a range of c slots, slot a holding the new token
+    auto row_of = [&](const uint16_t *base, const uint16_t *nrow, int x, int c, int a) __attribute__((always_inline)) {
+        const int s = s0 + min(x, c - 1);
+        return s == a ? nrow : base + (size_t)s * D;
     };
-    auto load_rows = [&](u32x4 (&kx)[NK], u32x4 (&vx)[NU], int kb) __attribute__((always_inline)) {
+    auto load_rows_of = [&](u32x4 (&kx)[NK], u32x4 (&vx)[NU], int kb, int c, int a) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const uint16_t *kp = row_of(Kb, kn_row, kb + 16 * c + col);
+        for (int cc = 0; cc < 2; ++cc) {
+            const uint16_t *kp = row_of(Kb, kn_row, kb + 16 * cc + col, c, a);
 #pragma unroll
-            for (int s2 = 0; s2 < NS; ++s2) kx[c * NS + s2] = *reinterpret_cast<const u32x4 *>(kp + 32 * s2 + 8 * grp);
+            for (int s2 = 0; s2 < NS; ++s2) kx[cc * NS + s2] = *reinterpret_cast<const u32x4 *>(kp + 32 * s2 + 8 * grp);
         }
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            const uint16_t *vp = row_of(Vb, vn_row, kb + (lane + 64 * u) / RV);
+            const uint16_t *vp = row_of(Vb, vn_row, kb + (lane + 64 * u) / RV, c, a);
             vx[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + ((lane + 64 * u) % RV) * 8));
         }
     };
+    // requested before the header: this wave's first block as if every slot
+    // of the range were kept and none admitted, and the range's keys
+    constexpr int KPT = kMaxSlotsPerWG / kThreads;
+    int kb = wave * KB;
+    if (kb < cnt_all) load_rows_of(kr, vr, kb, cnt_all, -1);
+    uint64_t kv[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+        if (i * kThreads < cnt_all) kv[i] = kb_keys[s0 + min(tid + i * kThreads, cnt_all - 1)];
+
+    const BgHdr h = hdr[bg];
+    const float dtn = dt_new[bg];
+    const uint64_t key_new = selkey(dtn, (uint32_t)h.len);
+    int n;
+    const int adm = admit(h, key_new, w, n);
+    const int cnt = max(0, min(n - s0, cnt_all));  // kept slots of the range after the step
+    auto load_rows = [&](u32x4 (&kx)[NK], u32x4 (&vx)[NU], int kb) __attribute__((always_inline)) {
+        load_rows_of(kx, vx, kb, cnt, adm);
+    };
+    // the first block again where the guess was wrong: it holds the admitted
+    // slot, or slots past the kept ones (whose rows are not defined)
+    if (kb < cnt && ((cnt != cnt_all && kb + KB > cnt) || (unsigned)(adm - (s0 + kb)) < (unsigned)KB))
+        load_rows(kr, vr, kb);
     auto block = [&](const u32x4 (&kx)[NK], const u32x4 (&vx)[NU], int kb) __attribute__((always_inline)) {
         const int nb = min(KB, cnt - kb);
 #pragma unroll
@@ -408,21 +429,22 @@ __global__ __launch_bounds__(kThreads, 2) void state_attend_kernel(
             oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, oacc[t], 0, 0, 0);
         }
     };
-    // this wave's first block is requested before the keys of the dt bias:
-    // both depend only on the header
-    int kb = wave * KB;
-    if (kb < cnt) load_rows(kr, vr, kb);
-    // the same pass finds the smallest key of the range after the step (the
-    // admitted slot holding the new key), the candidate for the next eviction
+    // the dt bias of the range's kept slots; the same pass finds the
+    // smallest key of the range after the step (the admitted slot holding the
+    // new key), the candidate for the next eviction
     uint64_t mk = ~0ull;
     int ms = -1;
-    for (int x = tid; x < cnt; x += kThreads) {
-        const int s = s0 + x;
-        const uint64_t ku = s == adm ? key_new : kb_keys[s];
-        l_dtl[x] = (s == adm ? dtn : key_dt(ku)) * kLog2e;
-        if (ku < mk) {
-            mk = ku;
-            ms = s;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int x = tid + i * kThreads;
+        if (x < cnt) {
+            const int s = s0 + x;
+            const uint64_t ku = s == adm ? key_new : kv[i];
+            l_dtl[x] = (s == adm ? dtn : key_dt(ku)) * kLog2e;
+            if (ku < mk) {
+                mk = ku;
+                ms = s;
+            }
         }
     }
 #pragma unroll
