@@ -526,77 +526,77 @@ __global__ __launch_bounds__(kThreads, 2) void state_attend_kernel(
 }
 
 // ------------------------------------------------------ combine + update --
-// One workgroup (d threads) per (batch, query head): merges the partials into
-// the output.  The workgroup of the first query head of each kv head then
-// applies the step to the state: the admitted key into its slot, the worst
-// kept key taken from the attend workgroups' range minima, the length
-// advanced.
-__global__ __launch_bounds__(128) void state_combine_kernel(
+// One workgroup per (batch, kv head), min(G * d, 1024) threads, a thread per
+// (query head, output element) in turn: merges the partials into the output.  Then the
+// step is applied to the state: the admitted key into its slot, the worst
+// kept key taken from the attend workgroups' range minima (wave 0), the
+// length advanced.
+__global__ __launch_bounds__(1024) void state_combine_kernel(
     const float *__restrict__ pm, const float *__restrict__ pl, const float *__restrict__ po,
     const uint64_t *__restrict__ pk, const int32_t *__restrict__ ps, int nchunk, int d, int Hq, int Hkv, int w,
     const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new, const float *__restrict__ dt_new,
     BgHdr *__restrict__ hdr, uint64_t *__restrict__ keys, int32_t *__restrict__ pos, uint16_t *__restrict__ Ks,
     uint16_t *__restrict__ Vs, uint16_t *__restrict__ out) {
     constexpr int kGroup = 8;
-    __shared__ uint64_t red_k[2];
-    __shared__ int red_s[2];
-    const int bh = blockIdx.x;  // b * Hq + hq
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int e = min(tid, d - 1);
+    const size_t bg = blockIdx.x;  // b * Hkv + g
+    const int tid = threadIdx.x, lane = tid & 63;
     const int G = Hq / Hkv;
-    const int b = bh / Hq, hq = bh - b * Hq;
-    const int g = hq / G;
-    const size_t bg = (size_t)b * Hkv + g;
     // the step's own inputs depend on nothing the merge computes: requested
     // together with the partials
     const BgHdr h = hdr[bg];
     const float dtn = dt_new[bg];
-    const uint16_t kn = k_new[bg * d + e], vn = v_new[bg * d + e];
+    const int ec = min(tid, d - 1);
+    const uint16_t kn = k_new[bg * d + ec], vn = v_new[bg * d + ec];
     uint64_t mk = ~0ull;
     int ms = -1;
-    for (int x = tid; x < nchunk; x += blockDim.x) {
-        const uint64_t k = pk[bg * nchunk + x];
-        const int sl = ps[bg * nchunk + x];
-        if (k < mk) {
-            mk = k;
-            ms = sl;
+    if (tid < 64) {
+        for (int x = lane; x < nchunk; x += 64) {
+            const uint64_t k = pk[bg * nchunk + x];
+            const int sl = ps[bg * nchunk + x];
+            if (k < mk) {
+                mk = k;
+                ms = sl;
+            }
         }
     }
 
-    const float *m = pm + (size_t)bh * nchunk;
-    const float *l = pl + (size_t)bh * nchunk;
-    const float *o = po + (size_t)bh * nchunk * d + e;
-    float M = -INFINITY, den = 0.f, num = 0.f;
-    for (int s0 = 0; s0 < nchunk; s0 += kGroup) {
-        float mv[kGroup], lv[kGroup], ov[kGroup];
+    for (int x = tid; x < G * d; x += blockDim.x) {
+        const int hh = x / d, e = x - hh * d;
+        const size_t bh = bg * G + hh;  // b * Hq + g * G + hh
+        const float *m = pm + bh * nchunk;
+        const float *l = pl + bh * nchunk;
+        const float *o = po + bh * nchunk * d + e;
+        float M = -INFINITY, den = 0.f, num = 0.f;
+        for (int s0 = 0; s0 < nchunk; s0 += kGroup) {
+            float mv[kGroup], lv[kGroup], ov[kGroup];
 #pragma unroll
-        for (int u = 0; u < kGroup; ++u) {
-            const int s = min(s0 + u, nchunk - 1);
-            mv[u] = m[s];
-            lv[u] = l[s];
-            ov[u] = o[(size_t)s * d];
+            for (int u = 0; u < kGroup; ++u) {
+                const int s = min(s0 + u, nchunk - 1);
+                mv[u] = m[s];
+                lv[u] = l[s];
+                ov[u] = o[(size_t)s * d];
+            }
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u)
+                if (s0 + u >= nchunk) mv[u] = -INFINITY;
+            float Mn = M;
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) Mn = fmaxf(Mn, mv[u]);
+            if (Mn == -INFINITY) continue;
+            const float c = M == -INFINITY ? 0.f : exp2f(M - Mn);
+            den *= c;
+            num *= c;
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) {
+                const float f = mv[u] == -INFINITY ? 0.f : exp2f(mv[u] - Mn);
+                den = fmaf(lv[u], f, den);
+                num = fmaf(ov[u], f, num);
+            }
+            M = Mn;
         }
-#pragma unroll
-        for (int u = 0; u < kGroup; ++u)
-            if (s0 + u >= nchunk) mv[u] = -INFINITY;
-        float Mn = M;
-#pragma unroll
-        for (int u = 0; u < kGroup; ++u) Mn = fmaxf(Mn, mv[u]);
-        if (Mn == -INFINITY) continue;
-        const float c = M == -INFINITY ? 0.f : exp2f(M - Mn);
-        den *= c;
-        num *= c;
-#pragma unroll
-        for (int u = 0; u < kGroup; ++u) {
-            const float f = mv[u] == -INFINITY ? 0.f : exp2f(mv[u] - Mn);
-            den = fmaf(lv[u], f, den);
-            num = fmaf(ov[u], f, num);
-        }
-        M = Mn;
+        out[bh * d + e] = f32_to_bf16(den > 0.f ? num / den : 0.f);
     }
-    if (tid < d) out[(size_t)bh * d + tid] = f32_to_bf16(den > 0.f ? num / den : 0.f);
 
-    if (hq != g * G) return;  // uniform
     const uint64_t key_new = selkey(dtn, (uint32_t)h.len);
     int n;
     const int adm = admit(h, key_new, w, n);
@@ -611,36 +611,27 @@ __global__ __launch_bounds__(128) void state_combine_kernel(
             pos[bg * w + adm] = h.len;
         }
     }
+    if (tid < 64) {
 #pragma unroll
-    for (int o2 = 32; o2 >= 1; o2 >>= 1) {
-        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)mk, o2, 64);
-        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(mk >> 32), o2, 64);
-        const int os = __shfl_xor(ms, o2, 64);
-        const uint64_t ok = ((uint64_t)hi << 32) | lo;
-        if (ok < mk) {
-            mk = ok;
-            ms = os;
-        }
-    }
-    if (lane == 0) {
-        red_k[wave] = mk;
-        red_s[wave] = ms;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        for (int q = 1; q < (int)(blockDim.x + 63) / 64; ++q) {
-            if (red_k[q] < mk) {
-                mk = red_k[q];
-                ms = red_s[q];
+        for (int o2 = 32; o2 >= 1; o2 >>= 1) {
+            const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)mk, o2, 64);
+            const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(mk >> 32), o2, 64);
+            const int os = __shfl_xor(ms, o2, 64);
+            const uint64_t ok = ((uint64_t)hi << 32) | lo;
+            if (ok < mk) {
+                mk = ok;
+                ms = os;
             }
         }
-        BgHdr nh;
-        nh.n = n;
-        nh.len = h.len + 1;
-        nh.min_slot = ms;
-        nh.pad = 0;
-        nh.min_key = mk;
-        hdr[bg] = nh;
+        if (tid == 0) {
+            BgHdr nh;
+            nh.n = n;
+            nh.len = h.len + 1;
+            nh.min_slot = ms;
+            nh.pad = 0;
+            nh.min_key = mk;
+            hdr[bg] = nh;
+        }
     }
 }
 
@@ -706,8 +697,8 @@ hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_ne
                            pm, pl, po, pk, ps, qscale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(state_combine_kernel, dim3(B * Hq), dim3(d), 0, stream, pm, pl, po, pk, ps, nparts, d, Hq,
-                       Hkv, w, (const uint16_t *)k_new, (const uint16_t *)v_new, dt_new, hdr, keys, pos, Ks, Vs,
+    hipLaunchKernelGGL(state_combine_kernel, dim3(B * Hkv), dim3(min(Hq / Hkv * d, 1024)), 0, stream, pm, pl, po, pk,
+                       ps, nparts, d, Hq, Hkv, w, (const uint16_t *)k_new, (const uint16_t *)v_new, dt_new, hdr, keys, pos, Ks, Vs,
                        (uint16_t *)out);
     return hipGetLastError();
 }

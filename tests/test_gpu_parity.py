@@ -355,6 +355,7 @@ def _state_kept_sorted(st):
     (1, 16, 1, 64, 600, [250], "dyadic"),          # every position kept throughout
     (2, 8, 2, 64, 64, [3000, 64], "const"),        # all dt equal: the first w positions stay
     (1, 4, 1, 128, 3000, [5000], "lognormal"),     # w above one workgroup's 2048 slots
+    (2, 32, 2, 128, 300, [700, 40], "lognormal"),  # G = 16 at d = 128: more outputs per kv head than threads
 ])
 def test_decode_state_steps(dma, oracle_mod, B, Hq, Hkv, d, w, lens, kind):
     """Steps of the incremental decode against the oracle's decode of the
