@@ -443,8 +443,32 @@ __global__ __launch_bounds__(NG * kThreads) void attn_bwd_kv_kernel(
     const uint32_t kvs = (uint32_t)(Hkv * D);
     const size_t urow = ((size_t)b * Hkv + g) * S;
 
-    // this lane's key (both row groups hold the same 64 keys)
-    const int jk = j0 + 16 * kw + kk;
+    // The tile's keys ordered by selection key, best first, in four rank
+    // blocks of 16: the waves holding the lower keys, which leave the rows'
+    // kept sets first, stop working early (a wave skips the blocks where none
+    // of its keys is kept).  Every row group holds the same 64 keys, group h
+    // key wave kw the rank block (kw + h) mod 4, so that the long-lived blocks
+    // of the groups sit on different SIMDs (wave i of a workgroup runs on
+    // SIMD i mod 4).
+    __shared__ uint64_t tsk[64];
+    __shared__ int perm[64];
+    if (tid < 64) {
+        const int j = j0 + tid;
+        tsk[tid] = j < L ? selkey(dt[urow + min(j, S - 1)], (uint32_t)j) : 0ull;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        const uint64_t mine = tsk[tid];
+        int r = 0;
+        for (int u = 0; u < 64; ++u) {
+            const uint64_t o = tsk[u];
+            r += (int)((o > mine) | ((o == mine) & (u < tid)));
+        }
+        perm[r] = tid;
+    }
+    __syncthreads();
+    const int rb = (kw + hg) & 3;  // rank block of this wave's keys
+    const int jk = j0 + perm[16 * rb + kk];
     const bool kvalid = jk < L;
     const int jc = min(jk, S - 1);
     bf16x8 kb[NS], vb[NS];
@@ -612,7 +636,7 @@ __global__ __launch_bounds__(NG * kThreads) void attn_bwd_kv_kernel(
     // the other groups hand their sums to group 0 through LDS (the row tiles
     // are free now), one group at a time in group order, and group 0 writes
     // the key's gradients
-    float *xw = reinterpret_cast<float *>(&tiles[0][0]) + kw * (2 * NT + 1) * 4 * 64;  // [4 waves][2 NT + 1][4][64]
+    float *xw = reinterpret_cast<float *>(&tiles[0][0]) + rb * (2 * NT + 1) * 4 * 64;  // [4 rank blocks][2 NT + 1][4][64]
 #pragma unroll
     for (int h2 = 1; h2 < NG; ++h2) {
         __syncthreads();
