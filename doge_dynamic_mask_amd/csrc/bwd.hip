@@ -34,12 +34,16 @@
 // column, with their K and V rows as MFMA operands in registers.  By nesting
 // the rows that keep key j form a run [j, e_j), and the thresholds grow with
 // the row, so the workgroup walks row blocks of 64 pairs from its first key
-// on (the groups take the blocks in turn, which shortens the longest tile's
-// chain) and stops at the first row whose threshold passes all of its keys.  Per block each lane finds its key's run of rows (two
-// threshold compares, a binary search in the block where the key drops out),
-// so the element test is one unsigned compare.  dV^T += dO^T P and
-// dK^T += Q^T dS accumulate in registers, ddt is the column sum of dS; the
-// other groups hand their sums to the first through LDS, in group order.
+// on (the groups take the blocks in turn) and stops at the first row whose
+// threshold passes all of its keys.  The tile's keys are ordered by selection
+// key into rank blocks of 16 (a wave whose keys have all dropped out skips
+// the block), each row group holding the blocks on rotated waves so that the
+// long-lived ones run on different SIMDs.  Per block each lane finds its
+// key's run of rows (two threshold compares, a binary search in the block
+// where the key drops out), so the element test is one unsigned compare.
+// dV^T += dO^T P and dK^T += Q^T dS accumulate in registers, ddt is the
+// column sum of dS; the other groups hand their sums to the first through
+// LDS, in group order.
 //
 // The key side touches every (pair, key) of the row range it walks, not only
 // the kept ones: its work grows like the dense causal attention rather than
