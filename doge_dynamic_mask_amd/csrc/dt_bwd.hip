@@ -12,9 +12,11 @@
 // of dW (each thread a channel and every head, the loads of all the
 // workgroup's tokens for that channel issued together and coalesced across
 // threads), dbias and dA go to the workspace.
-// The partials are summed in two fixed-order levels (dt_bwd_sum_kernel):
-// slices of at most kSlice partials, all of a slice's loads in flight at
-// once, then the slice sums; the result does not depend on scheduling.
+// The partials are summed in fixed-order levels (dt_bwd_sum_kernel): slices
+// of kSlice partials, all of a slice's loads in flight at once, until at
+// most kFinalRows are left, which dt_bwd_final_kernel sums (four waves take
+// a quarter of the rows each, then add their sums in wave order); the
+// result does not depend on scheduling.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -169,12 +171,9 @@ __global__ __launch_bounds__(kThreads) void dt_bwd_token_kernel(
 constexpr int kSlice = 16;  // partials summed per thread and level
 
 // out[y][e] = sum of in[p][e] over the y-th slice of kSlice rows p (rows of
-// nout floats).  With dW != nullptr (the last level, one slice) the sums go to
-// dW, dbias and dA instead.
-__global__ __launch_bounds__(kThreads) void dt_bwd_sum_kernel(const float *__restrict__ in, int nrows, int nout, int Hkv,
-                                                              int width, float *__restrict__ out,
-                                                              float *__restrict__ dW, float *__restrict__ dbias,
-                                                              float *__restrict__ dA) {
+// nout floats).
+__global__ __launch_bounds__(kThreads) void dt_bwd_sum_kernel(const float *__restrict__ in, int nrows, int nout,
+                                                              float *__restrict__ out) {
     const int e = blockIdx.x * kThreads + threadIdx.x;
     if (e >= nout) return;
     const int p0 = blockIdx.y * kSlice;
@@ -184,9 +183,37 @@ __global__ __launch_bounds__(kThreads) void dt_bwd_sum_kernel(const float *__res
     float acc = 0.f;
 #pragma unroll
     for (int k = 0; k < kSlice; ++k) acc += v[k];
-    if (!dW) {
-        out[(size_t)blockIdx.y * nout + e] = acc;
-    } else if (e < Hkv * width) {
+    out[(size_t)blockIdx.y * nout + e] = acc;
+}
+
+constexpr int kFinalRows = 4 * kSlice;  // rows the last level sums
+
+// The last level: column e = 64 blockIdx.x + lane of the n <= kFinalRows
+// rows of in, summed into dW, dbias and dA.
+__global__ __launch_bounds__(kThreads) void dt_bwd_final_kernel(const float *__restrict__ in, int nrows, int nout,
+                                                                int Hkv, int width, float *__restrict__ dW,
+                                                                float *__restrict__ dbias, float *__restrict__ dA) {
+    __shared__ float part[kThreads / 64][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = blockIdx.x * 64 + lane;
+    const int ec = min(e, nout - 1);
+    const int per = (nrows + 3) / 4;
+    const int p0 = wave * per;
+    float v[kSlice];
+#pragma unroll
+    for (int k = 0; k < kSlice; ++k) {
+        const int p = min(p0 + k, nrows - 1);  // past the wave's rows: a repeat, not added
+        v[k] = in[(size_t)p * nout + ec];
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kSlice; ++k)
+        if (k < per && p0 + k < nrows) acc += v[k];
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0 || e >= nout) return;
+    acc = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    if (e < Hkv * width) {
         dW[e] = acc;
     } else if (e < Hkv * width + Hkv) {
         if (dbias) dbias[e - Hkv * width] = acc;
@@ -197,10 +224,14 @@ __global__ __launch_bounds__(kThreads) void dt_bwd_sum_kernel(const float *__res
 
 }  // namespace
 
-// rows of partial sums left after each level: ceil(n / kSlice) until one
+// rows of partial sums left after each level: ceil(n / kSlice) until at most
+// kFinalRows
 static size_t sum_levels_rows(size_t nparts) {
     size_t tot = 0;
-    for (size_t n = (nparts + kSlice - 1) / kSlice; n > 1; n = (n + kSlice - 1) / kSlice) tot += n;
+    for (size_t n = nparts; n > (size_t)kFinalRows;) {
+        n = (n + kSlice - 1) / kSlice;
+        tot += n;
+    }
     return tot;
 }
 
@@ -231,16 +262,15 @@ hipError_t launch_dt_bwd(const void *V, const void *W, const void *bias, const f
     const float *in = part;
     float *next = part + (size_t)nparts * nout;
     int n = nparts;
-    while (n > kSlice) {
+    while (n > kFinalRows) {
         const int m = (n + kSlice - 1) / kSlice;
-        hipLaunchKernelGGL(dt_bwd_sum_kernel, dim3(gx, (unsigned)m), dim3(kThreads), 0, stream, in, n, nout, Hkv,
-                           width, next, (float *)nullptr, (float *)nullptr, (float *)nullptr);
+        hipLaunchKernelGGL(dt_bwd_sum_kernel, dim3(gx, (unsigned)m), dim3(kThreads), 0, stream, in, n, nout, next);
         in = next;
         next += (size_t)m * nout;
         n = m;
     }
-    hipLaunchKernelGGL(dt_bwd_sum_kernel, dim3(gx, 1u), dim3(kThreads), 0, stream, in, n, nout, Hkv, width,
-                       (float *)nullptr, dW, dbias, dA);
+    hipLaunchKernelGGL(dt_bwd_final_kernel, dim3((unsigned)((nout + 63) / 64)), dim3(kThreads), 0, stream, in, n, nout,
+                       Hkv, width, dW, dbias, dA);
     return hipGetLastError();
 }
 

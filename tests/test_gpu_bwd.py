@@ -109,7 +109,9 @@ def test_attn_bwd_full_size_c2(dma, oracle_mod):
 
 
 DT_CASES = [(2, 100, 4, 64, "bf16", True), (1, 67, 1, 64, "f32", False), (1, 130, 8, 128, "bf16", False),
-            (3, 64, 2, 128, "f32", True)]
+            (3, 64, 2, 128, "f32", True),
+            # more per-workgroup partial sums than the last level takes: one and two slice levels first
+            (2, 1100, 2, 64, "bf16", True), (1, 17000, 1, 64, "f32", False)]
 
 
 @pytest.mark.parametrize("B,S,Hkv,d,dtype,with_bias", DT_CASES)
