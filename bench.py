@@ -135,9 +135,16 @@ def cpu_baseline(pre_inp, wl_p, min_seconds=10.0):
         if time.perf_counter() - t0 >= min_seconds:
             break
     el = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": flops * reps / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"full prefill of the same batch (dt + select + attention, every row), "
-                      f"{reps} repetitions in {el:.1f} s, fp64"}
+                      f"{reps} repetitions in {el:.1f} s, fp64",
+            "host": {"cpu_model": model, "visible_cpus": os.cpu_count()}}
 
 
 def prefill_breakdown(dma, name, dev, evict, R=8, rounds=4):
@@ -305,7 +312,7 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the DMA hot path has no cross-GPU step in this build "
+        print("bench.py measures one GPU: the DMA hot path here has no cross-GPU step "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
@@ -410,8 +417,10 @@ def main():
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_pre = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    ms_dec = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    pre_each = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_each = [e[2].elapsed_time(e[3]) for e in evs]
+    ms_pre = float(np.mean(pre_each))
+    ms_dec = float(np.mean(dec_each))
 
     # Average launch duration per call: after an eviction, R back-to-back
     # launches of one call between two events, ROUNDS times.  Each launch
@@ -596,6 +605,9 @@ def main():
         },
         "ms_prefill": round(ms_pre, 5),
         "ms_decode_step": round(ms_dec, 5),
+        "step_ms_percentiles": {
+            n: {q: round(float(np.percentile(v, int(q[1:]))), 5) for q in ("p10", "p50", "p90")}
+            for n, v in (("prefill", pre_each), ("decode", dec_each))},
         "kernel_ms_avg": {n: round(v, 5) for n, v in avg.items()},
         "ms_prefill_as_one_graph": round(ms_pre_graph, 5),
         "host_enqueue_ms_per_step": round(float(np.mean(host_ms)), 4),
