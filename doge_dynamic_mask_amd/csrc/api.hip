@@ -55,7 +55,7 @@ int dma_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, i
     if (!dt || !tau || !tie) return DMA_ERR_NULL;
     if (B < 1 || Hkv < 1 || S < 1 || w < 1) return DMA_ERR_SHAPE;
     if (B > 65535 || Hkv > 65535) return DMA_ERR_UNSUPPORTED;
-    return from_hip(dma::launch_select(dt, seqlens, B, Hkv, S, w, tau, tie, (hipStream_t)stream));
+    return from_hip(dma::launch_select(dt, seqlens, B, Hkv, S, w, 0, tau, tie, (hipStream_t)stream));
 }
 
 int dma_attn_fwd(const void *Q, const void *K, const void *V, int dtype, const float *dt,

@@ -12,7 +12,8 @@ hipError_t launch_dt(const void *V, const void *W, const void *bias, const float
                      int B, int S, int Hkv, int d, float *dt_out, int64_t ld_out,
                      const int32_t *out_pos, hipStream_t stream);
 
-hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w,
+// win = 0: the full causal range; win >= 64: a sliding window of win positions
+hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w, int win,
                          float *tau, int32_t *tie, hipStream_t stream);
 
 hipError_t launch_attn(const void *Q, const void *K, const void *V, int dtype, const float *dt,

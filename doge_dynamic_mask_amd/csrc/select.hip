@@ -26,6 +26,15 @@
 //      that row already sees (band keys always; new key j from row j on).
 // Output per row: (tau, tie) = (dt, index) of the w-th kept key, or the
 // canonical (-inf, -1) / (+inf, -1).  Only comparisons touch dt.
+//
+// Sliding window of win >= C positions (row i sees [i - win + 1, i]): the
+// keys every valid row of the chunk sees form the "prefix" [pl, r0) with
+// pl = hi - win (hi: end of the chunk's valid rows), and row i sees besides
+// them the chunk's keys up to i and the "leaving" keys [i - win + 1, pl),
+// at most C keys in all, so the same band argument holds; the leaving keys
+// join the candidates (at most C - 1 more), and a candidate counts the
+// leaving keys a row still sees with a ballot and a shifted bit count.
+// Without a window the kernel is the full causal one (WIN = false).
 #include "common.hpp"
 #include "launch.hpp"
 #include "radix_select.hpp"
@@ -38,12 +47,12 @@ constexpr int kCollectCap = 512;    // boundary-bin keys ranked exactly in LDS
 constexpr int kUnroll = 16;         // prefix keys per thread per pass step (loads in flight)
 constexpr int kStage = 8192;        // prefixes up to this many keys are kept in LDS
 
-template <int C, int NB>
+template <int C, int NB, bool WIN>
 struct SelectShared {
     RadixShared<kThreads> rs;       // fallback radix select
     uint32_t hist[NB];
     uint64_t col[kCollectCap];
-    uint64_t cand[2 * C + 1];       // band (by rank) then the chunk's own keys
+    uint64_t cand[(WIN ? 3 : 2) * C + 1];  // band (by rank), the chunk's own keys, the keys leaving its windows
     uint32_t red[2][kThreads / 64];
     uint32_t ncol, nfound;
     uint32_t binA, binB, aboveA;
@@ -81,15 +90,17 @@ __device__ __forceinline__ void for_staged(const uint32_t *keys, int P, F f) {
     for (int j = threadIdx.x; j < P; j += kThreads) f(j, keys[j]);
 }
 
-// C: rows per chunk (the band holds C+1 prefix keys); NB: histogram bins
-template <int C, int NB>
+// C: rows per chunk (the band holds C+1 prefix keys); NB: histogram bins;
+// WIN: rows see a sliding window of win >= C positions (else the full causal
+// range, win unused)
+template <int C, int NB, bool WIN>
 __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restrict__ dt,
                                                           const int32_t *__restrict__ seqlens,
-                                                          int Hkv, int S, int w,
+                                                          int Hkv, int S, int w, int win,
                                                           float *__restrict__ tau,
                                                           int32_t *__restrict__ tie) {
     constexpr int kChunk = C;
-    __shared__ SelectShared<C, NB> sh;
+    __shared__ SelectShared<C, NB, WIN> sh;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = blockIdx.y, b = blockIdx.z;
     const int r0 = blockIdx.x * kChunk;
@@ -97,25 +108,38 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
     const size_t base = ((size_t)b * Hkv + g) * S;
     const float *row = dt + base;
     const int rend = min(r0 + kChunk, S);
+    const bool all_kept = WIN && win <= w;  // every window holds at most w keys
     const int lo = max(r0, w);    // first row holding more than w valid keys
     const int hi = min(rend, L);  // end of the valid rows of this chunk
-    // this thread's key of the chunk (C <= kThreads), requested before the
-    // prefix work so that its latency is hidden there
+    // With a sliding window (win >= C) the keys every valid row of the chunk
+    // sees are [pl, r0); row i also sees the chunk's keys up to i and the
+    // "leaving" keys [max(0, i - win + 1), pl), together at most C keys.
+    const int pl = WIN ? min(r0, max(0, hi - win)) : 0;
+    const int jl0 = WIN ? min(pl, max(0, lo - win + 1)) : 0;  // first leaving key
+    // this thread's key of the chunk (C <= kThreads) and leaving key,
+    // requested before the prefix work so that their latency is hidden there
     const float own = row[min(r0 + tid, S - 1)];
+    const float lvk = WIN ? row[min(jl0 + tid, S - 1)] : 0.f;
 
     for (int t = tid; t < rend - r0; t += kThreads) {
         const int i = r0 + t;
         if (i >= L) {
             tau[base + i] = INFINITY;
             tie[base + i] = -1;
-        } else if (i < w) {
+        } else if (i < w || all_kept) {
             tau[base + i] = -INFINITY;
             tie[base + i] = -1;
         }
     }
-    if (lo >= hi) return;  // uniform across the workgroup
+    if (lo >= hi || all_kept) return;  // uniform across the workgroup
 
-    const int P = r0;  // prefix [0, r0): all valid, as r0 < hi <= L
+    const int P = r0 - pl;  // prefix [pl, r0): all valid, as r0 < hi <= L
+    row += pl;              // prefix positions below are relative to pl
+    // a selection key with a prefix-relative index, made absolute (the order
+    // of equal values is kept: both indices count from the same end)
+    auto absolute = [&](uint64_t k) {
+        return (k & 0xffffffff00000000ull) | (uint64_t)(~(uint32_t)(pl + (int)~(uint32_t)k));
+    };
     const int A0 = max(0, min(P, w - kChunk - 1));
     const int nb = min(P, w) - A0;  // band size, 0 when the prefix is empty
     if (nb > 0) {
@@ -212,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
                 const uint64_t me = sh.col[x];
                 uint32_t r = aboveA;
                 for (uint32_t u = 0; u < m; ++u) r += sh.col[u] > me ? 1u : 0u;
-                if (r >= rankA && r <= rankB) sh.cand[r - rankA] = me;
+                if (r >= rankA && r <= rankB) sh.cand[r - rankA] = absolute(me);
             }
         } else {
             // fallback: exact two-target radix select, then the keys between
@@ -235,13 +259,16 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
                 const uint64_t me = sh.col[x];
                 uint32_t r = 0;
                 for (uint32_t u = 0; u < f; ++u) r += sh.col[u] > me ? 1u : 0u;
-                if (r < (uint32_t)nb) sh.cand[r] = me;
+                if (r < (uint32_t)nb) sh.cand[r] = absolute(me);
             }
         }
     }
-    // the chunk's own keys after the band
+    row -= pl;
+    // the chunk's own keys after the band, then the leaving keys
     const int nnew = hi - r0;
+    const int nleave = pl - jl0;  // < C
     if (tid < nnew) sh.cand[nb + tid] = selkey(own, (uint32_t)(r0 + tid));
+    if (WIN && tid < nleave) sh.cand[nb + nnew + tid] = selkey(lvk, (uint32_t)(jl0 + tid));
     __syncthreads();
 
     // ---- b: each candidate finds the rows it is the threshold of.  The
@@ -256,9 +283,13 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
     constexpr int kWaves = kThreads / 64;
     constexpr int kUnrollB = 4;
     const int need = w - A0 - 1;  // better candidates a row's w-th key has
-    const int ncand = nb + nnew;
+    const int ncand = nb + nnew + nleave;
     const uint64_t nk0 = lane < nnew ? sh.cand[nb + lane] : 0ull;  // 0: below every key
     const uint64_t nk1 = (C > 64 && lane + 64 < nnew) ? sh.cand[nb + 64 + lane] : 0ull;
+    // leaving key jl0 + x in lane x (of two registers); row i sees those from
+    // position i - win + 1 on, i.e. from lane s = i - win + 1 - jl0
+    const uint64_t lk0 = WIN && lane < nleave ? sh.cand[nb + nnew + lane] : 0ull;
+    const uint64_t lk1 = (WIN && C > 64 && lane + 64 < nleave) ? sh.cand[nb + nnew + 64 + lane] : 0ull;
     uint64_t bk[(C + 1 + 63) / 64];  // the band holds at most C + 1 keys
 #pragma unroll
     for (int q = 0; q < (int)(sizeof(bk) / sizeof(bk[0])); ++q)
@@ -266,6 +297,14 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
     const int t0 = lane, t1 = lane + 64;  // this lane's rows (chunk offsets)
     const bool v0 = r0 + t0 >= lo && r0 + t0 < hi;
     const bool v1 = C > 64 && r0 + t1 >= lo && r0 + t1 < hi;
+    // first position each row sees (0 without a window), and its first
+    // leaving lane
+    const int f0 = WIN ? max(0, r0 + t0 - win + 1) : 0, f1 = WIN ? max(0, r0 + t1 - win + 1) : 0;
+    const int s0 = max(0, f0 - jl0), s1 = max(0, f1 - jl0);
+    // set bits of the 128-bit mask (hi:lo) at positions >= s
+    auto count_from = [](uint64_t lo64, uint64_t hi64, int s) {
+        return s >= 128 ? 0 : s >= 64 ? __popcll(hi64 >> (s - 64)) : __popcll(lo64 >> s) + __popcll(hi64);
+    };
     int h0 = -1, h1 = -1;  // threshold position of rows t0, t1 if this wave has it
     uint32_t o0 = 0, o1 = 0;  // and its dt order bits
     const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -290,16 +329,24 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
             // plus bit 0
             const int c0 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m0 >> 33),
                                  __builtin_amdgcn_mbcnt_lo((uint32_t)(m0 >> 1), 0u)) + (int)(m0 & 1);
-            const int c1 = C > 64 ? __popcll(m0) + (int)(m1 & 1) +
-                                        (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m1 >> 33),
-                                             __builtin_amdgcn_mbcnt_lo((uint32_t)(m1 >> 1), 0u))
-                                  : 0;
+            int c1 = C > 64 ? __popcll(m0) + (int)(m1 & 1) +
+                                  (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m1 >> 33),
+                                       __builtin_amdgcn_mbcnt_lo((uint32_t)(m1 >> 1), 0u))
+                            : 0;
+            int cl0 = 0;
+            if (WIN && nleave > 0) {  // uniform
+                const uint64_t l0 = __ballot(lk0 > kx[u]);
+                const uint64_t l1 = C > 64 ? __ballot(lk1 > kx[u]) : 0ull;
+                cl0 = count_from(l0, l1, s0);
+                if (C > 64) c1 += count_from(l0, l1, s1);
+            }
             // the candidate is visible to rows at or after its own position
-            const bool g0 = v0 & (c0 == need_x) & (r0 + t0 >= jx);
+            // (and, with a window, to those whose window still holds it)
+            const bool g0 = v0 & (c0 + cl0 == need_x) & (r0 + t0 >= jx) & (jx >= f0);
             h0 = g0 ? jx : h0;
             o0 = g0 ? (uint32_t)(kx[u] >> 32) : o0;
             if (C > 64) {
-                const bool g1 = v1 & (c1 == need_x) & (r0 + t1 >= jx);
+                const bool g1 = v1 & (c1 == need_x) & (r0 + t1 >= jx) & (jx >= f1);
                 h1 = g1 ? jx : h1;
                 o1 = g1 ? (uint32_t)(kx[u] >> 32) : o1;
             }
@@ -320,18 +367,23 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
 
 }  // namespace
 
-hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w,
+hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w, int win,
                          float *tau, int32_t *tie, hipStream_t stream) {
     // short rows: more, smaller chunks; long rows: half the prefix passes
-    if (S <= 4096) {
-        const dim3 grid((S + 63) / 64, Hkv, B);
-        hipLaunchKernelGGL((select_kernel<64, 1024>), grid, dim3(kThreads), 0, stream, dt, seqlens, Hkv, S, w,
-                           tau, tie);
+    // (a window needs win >= C)
+    const bool small = S <= 4096 || (win > 0 && win < 128);
+    const dim3 grid(small ? (S + 63) / 64 : (S + 127) / 128, Hkv, B);
+#define DMA_SEL(C, NB, WIN)                                                                                   \
+    hipLaunchKernelGGL((select_kernel<C, NB, WIN>), grid, dim3(kThreads), 0, stream, dt, seqlens, Hkv, S, w, win, \
+                       tau, tie)
+    if (win > 0) {
+        if (small) DMA_SEL(64, 1024, true);
+        else DMA_SEL(128, 4096, true);
     } else {
-        const dim3 grid((S + 127) / 128, Hkv, B);
-        hipLaunchKernelGGL((select_kernel<128, 4096>), grid, dim3(kThreads), 0, stream, dt, seqlens, Hkv, S, w,
-                           tau, tie);
+        if (small) DMA_SEL(64, 1024, false);
+        else DMA_SEL(128, 4096, false);
     }
+#undef DMA_SEL
     return hipGetLastError();
 }
 

@@ -339,6 +339,9 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
 
 hipError_t launch_select_window(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w, int win,
                                 float *tau, int32_t *tie, hipStream_t stream) {
+    // windows of at least one selector chunk: the chunked band selector
+    if (win >= 64 && B <= 65535 && Hkv <= 65535)
+        return launch_select(dt, seqlens, B, Hkv, S, w, win, tau, tie, stream);
     const int64_t nrows = (int64_t)B * Hkv * S;
     const unsigned grid = (unsigned)((nrows + kWaves - 1) / kWaves);
     hipLaunchKernelGGL(select_window_kernel, dim3(grid), dim3(kThreads), 0, stream, dt, seqlens, Hkv, S, w, win,

@@ -29,6 +29,12 @@ SEL_CASES = [
     (2, 1, 3000, 300, 1000, "wide", True),
     (1, 2, 3000, 300, 3003, "const", False),    # window wider than the sequence
     (1, 1, 5000, 2048, 4096, "lognormal", False),
+    # windows of at least 64 go through the chunked band selector: windows
+    # just above a chunk, w close to the window, ties, padding, both chunk sizes
+    (1, 1, 4500, 30, 100, "lognormal", True),
+    (1, 2, 900, 120, 130, "dyadic", True),
+    (2, 2, 5000, 500, 700, "few", True),
+    (1, 1, 4200, 127, 128, "const", False),
 ]
 
 
