@@ -4,8 +4,8 @@
 // i - win < j <= i (and j < L); DMA forward step 3 then keeps the top
 // keep_window_size (= w) of them by dt, masked keys (min_dtype) never
 // outranking valid ones.  The kept sets no longer nest from row to row (keys
-// leave the window), so neither the prefix-threshold selector nor the
-// gathered-candidate attention applies.
+// leave the window).  Windows of at least 64 are selected by the chunked band
+// selector (select_kernel with a window); shorter ones here:
 //
 // select_window_kernel: one wave per row.  The w-th key of the row's window
 // under (dt desc, index asc) by a range-adapted radix select on the
@@ -16,9 +16,11 @@
 // Exact: comparisons and integer arithmetic only.
 //
 // attn_window_kernel: one workgroup per (batch, kv head, tile of 64 / G rows),
-// 16 (row, head) pairs per wave in lane columns; key blocks of 64 over the
-// tile's window range [i0 - win + 1, last row] staged in LDS, every (pair, key)
-// tested (j in the row's window, selkey(dt_j, j) >= selkey(tau_i, tie_i)),
+// 16 (row, head) pairs per wave in lane columns.  The candidate keys of the
+// tile's window range [i0 - win + 1, last row] (those at or above the
+// smallest threshold of its rows; no other key is kept by any of them) are
+// compacted into an LDS list, and blocks of 64 candidates are gathered into
+// LDS, every (pair, key) tested (j in the row's window, selkey(dt_j, j) >= selkey(tau_i, tie_i)),
 // S^T = K Q^T and O^T += V^T P^T on 16x16x32 bf16 MFMA with an online softmax
 // in base 2 (the running max shared by the four lanes of a pair; P rounded
 // once to bf16 and the softmax sum taken over the same rounded weights).
@@ -33,6 +35,8 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 256;
 constexpr int kPairs = 64;
 constexpr int kBlk = 64;
+constexpr int kWinCap = 4224;            // candidate keys of a query tile held in LDS
+constexpr int kScanKeys = 4 * kThreads;  // keys classified per scan step
 
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -198,6 +202,10 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
     __shared__ __align__(16) uint16_t Vs[kBlk * P];
     __shared__ float dtl_s[kBlk];
     __shared__ uint64_t skey_s[kBlk];
+    __shared__ int jk_s[kBlk];
+    __shared__ int c_idx[kWinCap];
+    __shared__ uint32_t wcnt[kThreads / 64];
+    __shared__ uint64_t tmin[kThreads / 64];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int q = lane >> 4, pq = lane & 15;
@@ -235,19 +243,89 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
     const uint16_t *Kb = K + (size_t)b * S * kvs + (size_t)g * D;
     const uint16_t *Vb = V + (size_t)b * S * kvs + (size_t)g * D;
     const float *drow = dt + urow;
+
+    // ---- candidate keys: a key of the tile's window range that no row of
+    // the tile keeps lies below every row's threshold, so only the keys at or
+    // above the smallest threshold of the tile's valid rows are walked
+    // (about w / win of the range), compacted into LDS in index order within
+    // each scan step's wave and register; past kWinCap candidates the whole
+    // range is walked instead
+    int n;
+    {
+        uint64_t tm = ~0ull;
+        for (int r = tid; r < kmax - i0 + 1; r += kThreads) {
+            const uint64_t t = selkey(tau[urow + i0 + r], (uint32_t)tie[urow + i0 + r]);
+            tm = t < tm ? t : tm;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const uint64_t y = __shfl_xor(tm, o, 64);
+            tm = y < tm ? y : tm;
+        }
+        if (lane == 0) tmin[wave] = tm;
+        __syncthreads();
+        tm = tmin[0];
+#pragma unroll
+        for (int w2 = 1; w2 < kThreads / 64; ++w2) tm = tmin[w2] < tm ? tmin[w2] : tm;
+        const uint64_t lt_mask = (1ull << lane) - 1ull;
+        int base = 0;
+        for (int c0 = kmin; c0 <= kmax; c0 += kScanKeys) {
+            float dv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dv[e] = drow[min(c0 + tid + kThreads * e, kmax)];
+            bool pr[4];
+            uint32_t nw = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = c0 + tid + kThreads * e;
+                pr[e] = j <= kmax && selkey(dv[e], (uint32_t)j) >= tm;
+                nw += (uint32_t)__popcll(__ballot(pr[e]));
+            }
+            if (lane == 0) wcnt[wave] = nw;
+            __syncthreads();
+            int off = base, tot = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < kThreads / 64; ++w2) {
+                const int cw = (int)wcnt[w2];
+                off += w2 < wave ? cw : 0;
+                tot += cw;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint64_t bl = __ballot(pr[e]);
+                const int pos = off + (int)__popcll(bl & lt_mask);
+                if (pr[e] && pos < kWinCap) c_idx[pos] = c0 + tid + kThreads * e;
+                off += (int)__popcll(bl);
+            }
+            base += tot;
+            __syncthreads();  // wcnt is rewritten by the next step
+        }
+        n = base;
+    }
+    const bool gathered = n <= kWinCap;
+    if (!gathered) n = kmax - kmin + 1;
+    // key at list position x (x < n)
+    auto key_at = [&](int x) __attribute__((always_inline)) { return gathered ? c_idx[x] : kmin + x; };
+
+    // A key block's K and V rows and dt are requested into registers one
+    // block ahead and written to LDS after the barrier that ends the block
+    // before.  Positions past the list's end repeat its last key and are
+    // marked never kept.
     u32x4 rk[NV], rv[NV];
     float rdt;
-    auto fetch = [&](int k0) __attribute__((always_inline)) {
+    int rj;
+    auto fetch = [&](int x0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int v = tid + u * kThreads;
-            const size_t off = (size_t)(uint32_t)min(k0 + v / (D / 8), kmax) * kvs + 8 * (v % (D / 8));
+            const size_t off = (size_t)(uint32_t)key_at(min(x0 + v / (D / 8), n - 1)) * kvs + 8 * (v % (D / 8));
             rk[u] = *reinterpret_cast<const u32x4 *>(Kb + off);
             rv[u] = *reinterpret_cast<const u32x4 *>(Vb + off);
         }
-        rdt = drow[min(k0 + (tid & (kBlk - 1)), kmax)];
+        rj = key_at(min(x0 + (tid & (kBlk - 1)), n - 1));
+        rdt = drow[rj];
     };
-    auto put = [&](int k0) __attribute__((always_inline)) {
+    auto put = [&](int x0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int v = tid + u * kThreads;
@@ -257,7 +335,8 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
         }
         if (tid < kBlk) {
             dtl_s[tid] = rdt * kLog2e;
-            skey_s[tid] = selkey(rdt, (uint32_t)min(k0 + tid, kmax));
+            skey_s[tid] = selkey(rdt, (uint32_t)rj);
+            jk_s[tid] = x0 + tid < n ? rj : 0x7fffffff;
         }
     };
 
@@ -266,11 +345,11 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-    fetch(kmin);
-    for (int k0 = kmin; k0 <= kmax; k0 += kBlk) {
-        put(k0);
+    if (n > 0) fetch(0);
+    for (int x0 = 0; x0 < n; x0 += kBlk) {
+        put(x0);
         __syncthreads();
-        if (k0 + kBlk <= kmax) fetch(k0 + kBlk);
+        if (x0 + kBlk < n) fetch(x0 + kBlk);
         float z[4][4];
         float mb = -INFINITY;
 #pragma unroll
@@ -280,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
             for (int s = 0; s < NS; ++s) sacc = mfma16(ld8(&Ks[(16 * mt + pq) * P + 32 * s + 8 * q]), qf[s], sacc);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int kk = 16 * mt + 4 * q + r, j = k0 + kk;
+                const int kk = 16 * mt + 4 * q + r, j = jk_s[kk];
                 const bool kept = live & (j >= lo_i) & (j <= i) & (skey_s[kk] >= thr);
                 const float zz = fmaf(sacc[r], qscale, dtl_s[kk]);
                 z[mt][r] = kept ? zz : -INFINITY;

@@ -55,6 +55,9 @@ ATTN_CASES = [
     (2, 257, 2, 2, 64, 33, 100, "few", None),
     (1, 190, 1, 1, 64, 7, 190, "const", None),
     (2, 97, 16, 2, 128, 10, 40, "lognormal", (97, 1)),
+    (1, 2600, 4, 2, 64, 300, 1500, "lognormal", None),   # candidate lists over several scan steps
+    # wider windows than the attention kernel's LDS list holds: the window range is walked
+    (1, 4700, 2, 1, 64, 4000, 4500, "wide", None),
 ]
 
 
