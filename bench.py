@@ -47,8 +47,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 # profiles/dma_kernels_prefill_b4s2048_decode_b64l16384_hbm_counters.md.  The
 # figure holds only for the attention source it was measured on: when the
 # hash of those files differs, traffic is reported as null.
-ATTN_TRAFFIC = {"bytes": 26087219,
-                "sources_sha256": "67094476a521c0cd3024667874538c3c0b0c52b21a0f0eac6393f9336675e7a1"}
+ATTN_TRAFFIC = {"bytes": 26108416,
+                "sources_sha256": "dc85285bef52cf9b22312007b0b58318a801c0dbbb285bed3505c75e498a07df"}
 ATTN_SOURCES = ("doge_dynamic_mask_amd/csrc/attn.hip", "doge_dynamic_mask_amd/csrc/common.hpp")
 COPY_CAL_BYTES = 256 * 1024 * 1024
 

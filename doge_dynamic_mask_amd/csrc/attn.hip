@@ -19,9 +19,8 @@
 // key, plus the tile's own keys), each with the run of tile rows that keeps
 // it.  It then walks the candidates in blocks of 64 keys: gather the K and V
 // rows (row-major, plain 16-byte copies) into LDS, S^T = K Q^T on 32x32x16
-// bf16 MFMA with the accumulators starting at the keys' dt bias (in units of
-// the score scale, so the matrix cores add it), in blocks holding partial
-// keys the row-run test, an online softmax in base 2, and O^T += V^T P^T
+// bf16 MFMA, the dt bias (plus, in blocks holding partial keys only, the
+// row-run test) in registers, an online softmax in base 2, and O^T += V^T P^T
 // on MFMA with P rounded once to bf16.  The V^T operand is read straight from the row-major
 // V tile with the gfx950 LDS transpose read (ds_read_b64_tr_b16).  Only
 // ~w + Bq keys are touched per tile instead of the dense causal prefix.
@@ -97,7 +96,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     static_assert(kBK * RV % kThreads == 0, "block staging split");
     static_assert(4 * (kCarrySlots + 1) <= 64 && 4 * (kCarrySlots + 1) <= 4 * kMaxSteps, "carry scan");
     __shared__ __align__(16) int c_idx[kCap];
-    __shared__ __align__(16) float c_dtl[kCap];     // dt * log2(e) / qscale: the score accumulators' start
+    __shared__ __align__(16) float c_dtl[kCap];     // dt * log2(e)
     __shared__ __align__(16) int c_lo[kPartCap];    // masked region: first tile row keeping the key
     __shared__ __align__(16) int c_span[kPartCap];  // masked region: rows keeping it
     __shared__ uint64_t thr[kRowsPerWG];            // threshold key of each tile row
@@ -108,10 +107,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int h = lane >> 5, ql = lane & 31;
-    // The score accumulators start at the key's dt bias in units of the
-    // score scale, so that the matrix cores add the bias: the base-2 score is
-    // qscale * acc, and the softmax takes qscale * acc - max in one fma.
-    const float bscale = kLog2e / qscale;
     // Work item = (batch, kv head, group of tpw consecutive query tiles).
     // XCD-aware order: workgroup ids go round-robin over the 8 XCDs, so hand
     // each XCD a contiguous run of work items; nearby tiles of one kv head
@@ -276,10 +271,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                     const int op = nF + (int)(base >> 16) + (int)__popcll(__ballot(cc[q] == 2) & lt_mask);
                     if (cc[q] == 1) {
                         c_idx[of] = jc[q];
-                        c_dtl[of] = dc[q] * bscale;
+                        c_dtl[of] = dc[q] * kLog2e;
                     } else if (cc[q] == 2) {
                         c_idx[op] = jc[q];
-                        c_dtl[op] = dc[q] * bscale;
+                        c_dtl[op] = dc[q] * kLog2e;
                     }
                 }
                 scan = i_last + 1;
@@ -355,11 +350,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                         const int j = jb + e;
                         if (c[e] == 1) {
                             c_idx[of] = j;
-                            c_dtl[of] = dv[bb][e] * bscale;
+                            c_dtl[of] = dv[bb][e] * kLog2e;
                             ++of;
                         } else if (c[e] == 2) {
                             c_idx[op] = j;
-                            c_dtl[op] = dv[bb][e] * bscale;
+                            c_dtl[op] = dv[bb][e] * kLog2e;
                             ++op;
                         }
                     }
@@ -409,21 +404,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 __syncthreads();
                 if (blk + kBK < n) load_block(blk + kBK, n);  // in flight during the math below
 
-                // S^T = K Q^T + bias for two 32-key halves of the block (the
-                // accumulators start at the keys' dt / qscale); the K fragments
+                // S^T = K Q^T for two 32-key halves of the block; the K fragments
                 // of step ks+1 are read while step ks multiplies
-                f32x16 sacc[2];
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const float4 dl4 = *reinterpret_cast<const float4 *>(&c_dtl[blk + 32 * kt + 8 * r4 + 4 * h]);
-                        sacc[kt][4 * r4 + 0] = dl4.x;
-                        sacc[kt][4 * r4 + 1] = dl4.y;
-                        sacc[kt][4 * r4 + 2] = dl4.z;
-                        sacc[kt][4 * r4 + 3] = dl4.w;
-                    }
-                }
+                f32x16 sacc[2] = {f32x16{}, f32x16{}};
                 const uint16_t *kp0 = &Ks[ql * T::KP + 8 * h];
                 const uint16_t *kp1 = &Ks[(32 + ql) * T::KP + 8 * h];
                 bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kp0);
@@ -441,11 +424,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                     a1 = n1;
                 }
 
-                // where partial keys are, the row-run test; then the online
-                // softmax in base 2 (scores in accumulator units: the block max
-                // is scaled once)
+                // dt bias (and, where partial keys are, the row-run test), then
+                // the online softmax in base 2
+                float z[2][16];
                 float mloc = -INFINITY;
-                if (blk >= pbase) {
+                if (blk < pbase) {
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const int pos = blk + 32 * kt + 8 * r4 + 4 * h;
+                            const float4 dl4 = *reinterpret_cast<const float4 *>(&c_dtl[pos]);
+                            const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float zz = fmaf(sacc[kt][4 * r4 + e], qscale, dls[e]);
+                                z[kt][4 * r4 + e] = zz;
+                                mloc = fmaxf(mloc, zz);
+                            }
+                        }
+                    }
+                } else {
 #pragma unroll
                     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -453,26 +452,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                             const int pos = blk + 32 * kt + 8 * r4 + 4 * h;
                             const int4 lo4 = *reinterpret_cast<const int4 *>(&c_lo[pos - pbase]);
                             const int4 sp4 = *reinterpret_cast<const int4 *>(&c_span[pos - pbase]);
+                            const float4 dl4 = *reinterpret_cast<const float4 *>(&c_dtl[pos]);
                             const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
                             const int sps[4] = {sp4.x, sp4.y, sp4.z, sp4.w};
+                            const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const bool ok = (unsigned)(r - los[e]) < (unsigned)sps[e];
-                                sacc[kt][4 * r4 + e] = ok ? sacc[kt][4 * r4 + e] : -INFINITY;
+                                const float zz = fmaf(sacc[kt][4 * r4 + e], qscale, ok ? dls[e] : -INFINITY);
+                                z[kt][4 * r4 + e] = zz;
+                                mloc = fmaxf(mloc, zz);
                             }
                         }
                     }
-                }
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[kt][e]);
                 }
                 // Lazy rescale: the running max only moves when a block raises it
                 // by more than 8 (base 2), so p stays <= 256 and most blocks skip
                 // the O rescale.  The final normalisation uses the same max, so
                 // the result is the softmax whatever max was used.
-                const float mblk = half_swap_max(mloc) * qscale;  // qscale > 0
+                const float mblk = half_swap_max(mloc);
                 const bool upd = mblk > mrow + 8.f;
                 if (__any(upd)) {
                     const float mnew = upd ? mblk : mrow;
@@ -483,11 +481,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                     for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
                 }
                 const float msub = (mrow == -INFINITY) ? 0.f : mrow;
-                float z[2][16];
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) z[kt][e] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][e], qscale, -msub));
+                    for (int e = 0; e < 16; ++e) z[kt][e] = __builtin_amdgcn_exp2f(z[kt][e] - msub);
                 }
 
                 // O^T += V^T P^T.  PV call c covers keys 16c..16c+15; lane half h
