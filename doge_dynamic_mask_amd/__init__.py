@@ -41,7 +41,7 @@ _STATUS = {
     -4: "DMA_ERR_UNSUPPORTED", -5: "DMA_ERR_WORKSPACE", -6: "DMA_ERR_HIP",
 }
 
-EXPORTS = ("dma_version", "dma_status_str", "dma_dt", "dma_select", "dma_attn_fwd",
+EXPORTS = ("dma_version", "dma_status_str", "dma_workspace_bytes", "dma_dt", "dma_select", "dma_attn_fwd",
            "dma_decode_workspace_bytes", "dma_decode", "dma_decode_state_bytes",
            "dma_decode_step_workspace_bytes", "dma_decode_state_init", "dma_decode_step",
            "dma_decode_state_kept", "dma_qk_norm_rope", "dma_prologue",
@@ -70,6 +70,7 @@ def lib():
     P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     L.dma_version.argtypes, L.dma_version.restype = [], I
     L.dma_status_str.argtypes, L.dma_status_str.restype = [I], ctypes.c_char_p
+    L.dma_workspace_bytes.argtypes, L.dma_workspace_bytes.restype = [I, I, I, I, I, I, I], SZ
     L.dma_dt.argtypes = [P, P, P, P, I, I, I, I, I, P, I64, P, P]
     L.dma_dt.restype = I
     L.dma_select.argtypes = [P, P, I, I, I, I, P, P, P]
@@ -147,6 +148,21 @@ def _check(t, name, dtype=None, ndim=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _shape(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _workspace(ws, nbytes, dev, name="workspace"):
+    """A caller's workspace (uint8, on dev, at least nbytes) or a new one."""
+    if ws is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(ws, name, torch.uint8, 1, dev)
+    if ws.numel() < nbytes:
+        raise ValueError(f"{name} holds {ws.numel()} bytes, {nbytes} needed")
+    return ws
+
+
 def _call(status, what):
     if status != 0:
         raise DmaError(status, what)
@@ -161,27 +177,47 @@ def dt(V, W, A, bias=None, out=None, out_pos=None):
     if bias is not None:
         _check(bias, "bias", V.dtype, 1, dev)
     B, S, Hkv, d = V.shape
-    if out is None:
-        out = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
-    _check(out, "out", torch.float32, 3, dev)
+    _shape(W, "W", (Hkv, Hkv * d))
+    _shape(A, "A", (Hkv,))
+    if bias is not None:
+        _shape(bias, "bias", (Hkv,))
     if out_pos is not None:
         _check(out_pos, "out_pos", torch.int32, 1, dev)
+        _shape(out_pos, "out_pos", (B,))
+    if out is not None:
+        _check(out, "out", torch.float32, 3, dev)
+        if out.shape[0] != B or out.shape[1] != Hkv or out.shape[2] < S:
+            raise ValueError(f"out must be [B={B}, Hkv={Hkv}, >= S={S}], got {tuple(out.shape)}")
+    else:
+        out = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
     ld = out.shape[2]
     _call(lib().dma_dt(_ptr(V), _ptr(W), _ptr(bias), _ptr(A), _dtype_code(V), B, S, Hkv, d,
                        _ptr(out), ld, _ptr(out_pos), _stream(V)), "dma_dt")
     return out
 
 
+def _select_args(dt_, seqlens, tau, tie):
+    B, Hkv, S = dt_.shape
+    dev = dt_.device
+    if seqlens is not None:
+        _check(seqlens, "seqlens", torch.int32, 1, dev)
+        _shape(seqlens, "seqlens", (B,))
+    for name, t, dtp in (("tau", tau, torch.float32), ("tie", tie, torch.int32)):
+        if t is not None:
+            _check(t, name, dtp, 3, dev)
+            _shape(t, name, (B, Hkv, S))
+    if tau is None:
+        tau = torch.empty_like(dt_)
+    if tie is None:
+        tie = torch.empty((B, Hkv, S), dtype=torch.int32, device=dev)
+    return tau, tie
+
+
 def select(dt_, w, seqlens=None, tau=None, tie=None):
     """Per-row threshold pairs (tau float32, tie int32), each [B, Hkv, S]."""
     _check(dt_, "dt", torch.float32, 3)
     B, Hkv, S = dt_.shape
-    if seqlens is not None:
-        _check(seqlens, "seqlens", torch.int32, 1, dt_.device)
-    if tau is None:
-        tau = torch.empty_like(dt_)
-    if tie is None:
-        tie = torch.empty((B, Hkv, S), dtype=torch.int32, device=dt_.device)
+    tau, tie = _select_args(dt_, seqlens, tau, tie)
     _call(lib().dma_select(_ptr(dt_), _ptr(seqlens), B, Hkv, S, int(w), _ptr(tau), _ptr(tie),
                            _stream(dt_)), "dma_select")
     return tau, tie
@@ -203,13 +239,27 @@ def attn_fwd(Q, K, V, dt_, tau, tie, w, seqlens=None, out=None):
             raise ValueError(f"{name} must be [B, Hkv, S]")
     if seqlens is not None:
         _check(seqlens, "seqlens", torch.int32, 1, dev)
+        _shape(seqlens, "seqlens", (B,))
     if out is None:
         out = torch.empty_like(Q)
     _check(out, "out", Q.dtype, 4, dev)
+    _shape(out, "out", Q.shape)
     _call(lib().dma_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q), _ptr(dt_), _ptr(tau), _ptr(tie),
                              _ptr(seqlens), B, S, Hq, Hkv, d, int(w), _ptr(out), _stream(Q)),
           "dma_attn_fwd")
     return out
+
+
+OP_DT, OP_SELECT, OP_ATTN_FWD, OP_DECODE, OP_DECODE_STEP, OP_ATTN_BWD, OP_DT_BWD = range(7)
+
+
+def workspace_bytes(op, B, S, Hq, Hkv, d, w):
+    """Device workspace of operation `op` (OP_*) in bytes; 0 when it takes none.
+    Raises ValueError for an unknown op or sizes the operation rejects."""
+    n = int(lib().dma_workspace_bytes(int(op), B, S, Hq, Hkv, d, int(w)))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError(f"dma_workspace_bytes: op {op} rejects sizes B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} w={w}")
+    return n
 
 
 def decode_workspace_bytes(B, Lmax, Hq, Hkv, d, w):
@@ -226,9 +276,15 @@ def decode(q, Kc, Vc, dt_cache, cache_lens, w, kept=False, out=None, workspace=N
     _check(cache_lens, "cache_lens", torch.int32, 1, dev)
     B, Hq, d = q.shape
     Lmax, Hkv = Kc.shape[1], Kc.shape[2]
+    _shape(Kc, "Kc", (B, Lmax, Hkv, d))
+    _shape(Vc, "Vc", Kc.shape)
+    _shape(dt_cache, "dt_cache", (B, Hkv, Lmax))
+    _shape(cache_lens, "cache_lens", (B,))
+    if out is not None:
+        _check(out, "out", q.dtype, 3, dev)
+        _shape(out, "out", q.shape)
     nbytes = decode_workspace_bytes(B, Lmax, Hq, Hkv, d, w)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, nbytes, dev)
     if out is None:
         out = torch.empty_like(q)
     kept_idx = torch.empty((B, Hkv, int(w)), dtype=torch.int32, device=dev) if kept else None
@@ -281,11 +337,15 @@ def decode_state_init(Kc, Vc, dt_cache, cache_lens, w, state=None, workspace=Non
     _check(dt_cache, "dt_cache", torch.float32, 3, dev)
     _check(cache_lens, "cache_lens", torch.int32, 1, dev)
     B, Lmax, Hkv, d = Kc.shape
+    _shape(Vc, "Vc", Kc.shape)
+    _shape(dt_cache, "dt_cache", (B, Hkv, Lmax))
+    _shape(cache_lens, "cache_lens", (B,))
+    if state is not None and (state.B, state.Hkv, state.d, state.w) != (B, Hkv, d, int(w)):
+        raise ValueError("the decode state was made for other sizes")
+    nbytes = decode_step_workspace_bytes(B, Hkv, Hkv, d, w)
+    workspace = _workspace(workspace, nbytes, dev)
     if state is None:
         state = DecodeState(B, Hkv, d, w, dev)
-    nbytes = decode_step_workspace_bytes(B, Hkv, Hkv, d, w)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     _call(lib().dma_decode_state_init(_ptr(Kc), _ptr(Vc), BF16, _ptr(dt_cache), _ptr(cache_lens), B, Lmax, Hkv, d,
                                       int(w), _ptr(state.buf), state.buf.numel(), _ptr(workspace),
                                       workspace.numel(), _stream(Kc)), "dma_decode_state_init")
@@ -300,14 +360,21 @@ def decode_step(q, k_new, v_new, dt_new, state, out=None, workspace=None):
     _check(v_new, "v_new", torch.bfloat16, 3, dev)
     _check(dt_new, "dt_new", torch.float32, 2, dev)
     B, Hq, d = q.shape
-    Hkv = k_new.shape[1]
-    if (B, Hkv, d) != (state.B, state.Hkv, state.d):
-        raise ValueError("q / k_new do not match the decode state")
+    Hkv = state.Hkv
+    if (B, d) != (state.B, state.d):
+        raise ValueError("q does not match the decode state")
+    _shape(k_new, "k_new", (B, Hkv, d))
+    _shape(v_new, "v_new", (B, Hkv, d))
+    _shape(dt_new, "dt_new", (B, Hkv))
+    if state.buf.device != dev:
+        raise ValueError(f"the decode state is on {state.buf.device}, expected {dev}")
+    if out is not None:
+        _check(out, "out", q.dtype, 3, dev)
+        _shape(out, "out", q.shape)
+    nbytes = decode_step_workspace_bytes(B, Hq, Hkv, d, state.w)
+    workspace = _workspace(workspace, nbytes, dev)
     if out is None:
         out = torch.empty_like(q)
-    nbytes = decode_step_workspace_bytes(B, Hq, Hkv, d, state.w)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     _call(lib().dma_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), BF16, _ptr(dt_new), B, Hq, Hkv, d, state.w,
                                 _ptr(state.buf), state.buf.numel(), _ptr(out), _ptr(workspace), workspace.numel(),
                                 _stream(q)), "dma_decode_step")
@@ -359,8 +426,11 @@ def prologue(Q, K, V, q_norm_w, k_norm_w, W, A, bias=None, eps=1e-6, rope_theta=
         raise ValueError("V must be [B, S, Hkv, d] matching K")
     _check(W, "W", Q.dtype, 2, dev)
     _check(A, "A", torch.float32, 1, dev)
+    _shape(W, "W", (Hkv, Hkv * d))
+    _shape(A, "A", (Hkv,))
     if bias is not None:
         _check(bias, "bias", Q.dtype, 1, dev)
+        _shape(bias, "bias", (Hkv,))
     if dt_out is None:
         dt_out = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
     _check(dt_out, "dt_out", torch.float32, 3, dev)
@@ -396,9 +466,16 @@ def attn_bwd(Q, K, V, dt_, tau, tie, w, dO, seqlens=None, workspace=None, out=No
             raise ValueError(f"{name} must be [B, Hkv, S]")
     if seqlens is not None:
         _check(seqlens, "seqlens", torch.int32, 1, dev)
+        _shape(seqlens, "seqlens", (B,))
+    if out is not None:
+        dQ, dK, dV, ddt = out
+        for name, t, ref in (("dQ", dQ, Q), ("dK", dK, K), ("dV", dV, V)):
+            _check(t, name, Q.dtype, 4, dev)
+            _shape(t, name, ref.shape)
+        _check(ddt, "ddt", torch.float32, 3, dev)
+        _shape(ddt, "ddt", (B, Hkv, S))
     nbytes = attn_bwd_workspace_bytes(B, S, Hq, Hkv, d, w)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, nbytes, dev)
     if out is None:
         out = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V),
                torch.empty((B, Hkv, S), dtype=torch.float32, device=dev))
@@ -424,15 +501,17 @@ def dt_bwd(V, W, A, ddt, bias=None, dV=None, workspace=None):
     B, S, Hkv, d = V.shape
     if tuple(ddt.shape) != (B, Hkv, S):
         raise ValueError("ddt must be [B, Hkv, S]")
+    _shape(W, "W", (Hkv, Hkv * d))
+    _shape(A, "A", (Hkv,))
     if bias is not None:
         _check(bias, "bias", V.dtype, 1, dev)
+        _shape(bias, "bias", (Hkv,))
     if dV is not None:
         _check(dV, "dV", V.dtype, 4, dev)
         if dV.shape != V.shape:
             raise ValueError("dV must have the shape of V")
     nbytes = dt_bwd_workspace_bytes(B, S, Hkv, d)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, nbytes, dev)
     dW = torch.empty((Hkv, Hkv * d), dtype=torch.float32, device=dev)
     dbias = torch.empty(Hkv, dtype=torch.float32, device=dev)
     dA = torch.empty(Hkv, dtype=torch.float32, device=dev)
@@ -459,12 +538,7 @@ def select_window(dt_, w, win, seqlens=None, tau=None, tie=None):
     """Per-row threshold pairs under a sliding window of win positions: (tau, tie), each [B, Hkv, S]."""
     _check(dt_, "dt", torch.float32, 3)
     B, Hkv, S = dt_.shape
-    if seqlens is not None:
-        _check(seqlens, "seqlens", torch.int32, 1, dt_.device)
-    if tau is None:
-        tau = torch.empty_like(dt_)
-    if tie is None:
-        tie = torch.empty((B, Hkv, S), dtype=torch.int32, device=dt_.device)
+    tau, tie = _select_args(dt_, seqlens, tau, tie)
     _call(lib().dma_select_window(_ptr(dt_), _ptr(seqlens), B, Hkv, S, int(w), int(win), _ptr(tau), _ptr(tie),
                                   _stream(dt_)), "dma_select_window")
     return tau, tie
@@ -486,8 +560,11 @@ def attn_window_fwd(Q, K, V, dt_, tau, tie, w, win, seqlens=None, out=None):
             raise ValueError(f"{name} must be [B, Hkv, S]")
     if seqlens is not None:
         _check(seqlens, "seqlens", torch.int32, 1, dev)
+        _shape(seqlens, "seqlens", (B,))
     if out is None:
         out = torch.empty_like(Q)
+    _check(out, "out", Q.dtype, 4, dev)
+    _shape(out, "out", Q.shape)
     _call(lib().dma_attn_window_fwd(_ptr(Q), _ptr(K), _ptr(V), BF16, _ptr(dt_), _ptr(tau), _ptr(tie), _ptr(seqlens),
                                     B, S, Hq, Hkv, d, int(w), int(win), _ptr(out), _stream(Q)), "dma_attn_window_fwd")
     return out
@@ -503,6 +580,8 @@ def cdmoe_logits(h, router, out=None):
         raise ValueError("router must be [2*nk, H]")
     if out is None:
         out = torch.empty((T, n2), dtype=torch.float32, device=h.device)
+    _check(out, "out", torch.float32, 2, h.device)
+    _shape(out, "out", (T, n2))
     _call(lib().dma_cdmoe_logits(_ptr(h), _ptr(router), BF16, T, H, n2 // 2, _ptr(out), _stream(h)),
           "dma_cdmoe_logits")
     return out
@@ -512,6 +591,12 @@ def cdmoe_route(logits, k, idx=None, weights=None):
     """Product-key routing: (expert indices [T, k] int32 best first, weights [T, k] float32)."""
     _check(logits, "logits", torch.float32, 2)
     T, n2 = logits.shape
+    if n2 % 2:
+        raise ValueError("logits must be [T, 2*nk]")
+    for name, t, dtp in (("idx", idx, torch.int32), ("weights", weights, torch.float32)):
+        if t is not None:
+            _check(t, name, dtp, 2, logits.device)
+            _shape(t, name, (T, int(k)))
     if idx is None:
         idx = torch.empty((T, int(k)), dtype=torch.int32, device=logits.device)
     if weights is None:
@@ -538,6 +623,8 @@ def cdmoe_experts(h, down, up, idx, weights, out=None):
         raise ValueError("idx/weights must be [T, k]")
     if out is None:
         out = torch.empty_like(h)
+    _check(out, "out", torch.bfloat16, 2, dev)
+    _shape(out, "out", h.shape)
     _call(lib().dma_cdmoe_experts(_ptr(h), _ptr(down), _ptr(up), BF16, _ptr(idx), _ptr(weights), T, H, nk,
                                   idx.shape[1], _ptr(out), _stream(h)), "dma_cdmoe_experts")
     return out

@@ -71,6 +71,24 @@ int dma_attn_fwd(const void *Q, const void *K, const void *V, int dtype, const f
                                      (hipStream_t)stream));
 }
 
+size_t dma_workspace_bytes(int op, int B, int S, int Hq, int Hkv, int d, int w) {
+    const size_t bad = (size_t)-1;
+    if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || d < 1 || w < 1 || Hq % Hkv != 0) return bad;
+    size_t n = 0;
+    switch (op) {
+        case DMA_OP_DT:
+        case DMA_OP_SELECT:
+        case DMA_OP_ATTN_FWD:
+            return 0;
+        case DMA_OP_DECODE: n = dma_decode_workspace_bytes(B, S, Hq, Hkv, d, w); break;
+        case DMA_OP_DECODE_STEP: n = dma_decode_step_workspace_bytes(B, Hq, Hkv, d, w); break;
+        case DMA_OP_ATTN_BWD: n = dma_attn_bwd_workspace_bytes(B, S, Hq, Hkv, d, w); break;
+        case DMA_OP_DT_BWD: n = dma_dt_bwd_workspace_bytes(B, S, Hkv, d); break;
+        default: return bad;
+    }
+    return n == 0 ? bad : n;
+}
+
 size_t dma_decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d, int w) {
     if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || d < 1 || w < 1 || Hq % Hkv != 0) return 0;
     return dma::decode_ws_bytes(B, Lmax, Hq, Hkv, d, w);
@@ -258,10 +276,10 @@ int dma_cdmoe_experts(const void *h, const void *down, const void *up, int dtype
                       const float *weights, int T, int H, int nk, int k, void *out, void *stream) {
     if (!h || !down || !up || !idx || !weights || !out) return DMA_ERR_NULL;
     if (!dtype_ok(dtype)) return DMA_ERR_DTYPE;
-    if (T < 1 || H < 1 || nk < 1 || k < 1 || k > nk * nk) return DMA_ERR_SHAPE;
+    if (T < 1 || H < 1 || nk < 1 || nk > 46340 || k < 1 || k > nk * nk) return DMA_ERR_SHAPE;
     if (dtype != DMA_BF16 || H % 512 != 0 || k > dma::kMaxCdmoeTopk || T > 0x7fffffff) return DMA_ERR_UNSUPPORTED;
     if (!aligned16(h) || !aligned16(down) || !aligned16(up) || !aligned16(out)) return DMA_ERR_UNSUPPORTED;
-    return from_hip(dma::launch_cdmoe_experts(h, down, up, idx, weights, T, H, k, out, (hipStream_t)stream));
+    return from_hip(dma::launch_cdmoe_experts(h, down, up, idx, weights, T, H, nk, k, out, (hipStream_t)stream));
 }
 
 }  // extern "C"

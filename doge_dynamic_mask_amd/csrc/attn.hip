@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const int grp = item % ngroups;
     const int g = (item / ngroups) % Hkv;
     const int b = item / (ngroups * Hkv);
-    const int L = seqlens ? seqlens[b] : S;
+    const int L = clamp_len(seqlens, b, S);
 
     const int m = wave * 32 + ql;  // stacked (row, head) pair of this lane
     const int r = m / G, hh = m - r * G;
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void attn_rowwise_kernel(
     const int hq = (int)((wid / S) % Hq);
     const int b = (int)(wid / ((int64_t)S * Hq));
     const int G = Hq / Hkv, g = hq / G;
-    const int L = seqlens ? seqlens[b] : S;
+    const int L = clamp_len(seqlens, b, S);
     const size_t obase = (((size_t)b * S + i) * Hq + hq) * d;
     constexpr int kMaxPer = 4;  // d <= 256
     if (i >= L) {

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
     const int tq = ntq - 1 - item % ntq;
     const int g = (item / ntq) % Hkv;
     const int b = item / (ntq * Hkv);
-    const int L = seqlens ? seqlens[b] : S;
+    const int L = clamp_len(seqlens, b, S);
     const int RB = kPairs / G;
     const int i0 = tq * RB;
     const int pr = 16 * wave + pq;      // this lane's pair
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(NG * kThreads) void attn_bwd_kv_kernel(
     const int nbg = gridDim.x / nkt;
     const int kt = blockIdx.x / nbg, bg = blockIdx.x % nbg;
     const int g = bg % Hkv, b = bg / Hkv;
-    const int L = seqlens ? seqlens[b] : S;
+    const int L = clamp_len(seqlens, b, S);
     const int j0 = kt * 64;
     const uint32_t kvs = (uint32_t)(Hkv * D);
     const size_t urow = ((size_t)b * Hkv + g) * S;

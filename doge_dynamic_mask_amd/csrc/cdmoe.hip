@@ -321,19 +321,25 @@ __global__ __launch_bounds__(kThreads) void cdmoe_experts_kernel(const uint16_t 
                                                                  const uint16_t *__restrict__ up,
                                                                  const int32_t *__restrict__ idx,
                                                                  const float *__restrict__ wts, int H, int k,
-                                                                 uint16_t *__restrict__ out) {
+                                                                 int E, uint16_t *__restrict__ out) {
     __shared__ float act[kMaxExperts];
     __shared__ int eid[kMaxExperts];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int t = blockIdx.x;
     const uint16_t *hrow = h + (size_t)t * H;
-    if (tid < k) eid[tid] = idx[(size_t)t * k + tid];
+    // an index outside [0, E) is outside the contract; it reads row 0 and
+    // gets weight zero rather than a row past the tables
+    if (tid < k) {
+        const int v = idx[(size_t)t * k + tid];
+        eid[tid] = (unsigned)v < (unsigned)E ? v : -1;
+    }
     __syncthreads();
     // z_e = down_e . h: wave w takes experts w, w + 4, ...; lanes split H in
     // 16-byte vectors (H is a multiple of 512)
     const int nv = H / 512;
     for (int e = wave; e < k; e += kWaves) {
-        const uint16_t *drow = down + (size_t)eid[e] * H;
+        const int ee = eid[e];
+        const uint16_t *drow = down + (size_t)max(ee, 0) * H;
         float z = 0.f;
         for (int v = 0; v < nv; ++v) {
             const int c = 8 * (lane + 64 * v);
@@ -342,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void cdmoe_experts_kernel(const uint16_t 
             for (int j = 0; j < 8; ++j) z = fmaf((float)dv[j], (float)hv[j], z);
         }
         z = wave_sum(z);
-        if (lane == 0) act[e] = z / (1.f + __expf(-z)) * wts[(size_t)t * k + e];
+        if (lane == 0) act[e] = ee < 0 ? 0.f : z / (1.f + __expf(-z)) * wts[(size_t)t * k + e];
     }
     __syncthreads();
     // out[c] = sum_e act_e up_e[c]: each thread a run of 4 channels per 1024
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void cdmoe_experts_kernel(const uint16_t 
             uint2 u[kEB];
 #pragma unroll
             for (int j = 0; j < kEB; ++j)
-                u[j] = *reinterpret_cast<const uint2 *>(up + (size_t)eid[min(e0 + j, k - 1)] * H + c0);
+                u[j] = *reinterpret_cast<const uint2 *>(up + (size_t)max(eid[min(e0 + j, k - 1)], 0) * H + c0);
 #pragma unroll
             for (int j = 0; j < kEB; ++j) {
                 if (e0 + j < k) {
@@ -393,9 +399,9 @@ hipError_t launch_cdmoe_route(const float *logits, int T, int nk, int k, int32_t
 }
 
 hipError_t launch_cdmoe_experts(const void *h, const void *down, const void *up, const int32_t *idx, const float *wts,
-                                int T, int H, int k, void *out, hipStream_t stream) {
+                                int T, int H, int nk, int k, void *out, hipStream_t stream) {
     hipLaunchKernelGGL(cdmoe_experts_kernel, dim3((unsigned)T), dim3(kThreads), 0, stream, (const uint16_t *)h,
-                       (const uint16_t *)down, (const uint16_t *)up, idx, wts, H, k, (uint16_t *)out);
+                       (const uint16_t *)down, (const uint16_t *)up, idx, wts, H, k, nk * nk, (uint16_t *)out);
     return hipGetLastError();
 }
 

@@ -57,6 +57,13 @@ __device__ __forceinline__ bool kept_test(float dtv, int j, float tau, int tie) 
     return (dtv > tau) || (dtv == tau && j <= tie);
 }
 
+// Valid length of batch b from a caller's lengths array (NULL: n), clamped
+// to [0, n]: the documented range is [1, n], and a value outside it must not
+// index past the rows it bounds.
+__device__ __forceinline__ int clamp_len(const int32_t *lens, int b, int n) {
+    return lens ? min(max(lens[b], 0), n) : n;
+}
+
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
 // Sum / max across the two 32-lane halves of a wave (lanes l and l^32).

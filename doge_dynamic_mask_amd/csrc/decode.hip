@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(
     static_assert(ITEMS % 4 == 0, "float4 loads");
     __shared__ SelShared sh;
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int L = cache_lens[b];
+    const int L = clamp_len(cache_lens, b, Lmax);
     const float *row = dt_cache + ((size_t)b * Hkv + g) * Lmax;
     const int j0 = tid * ITEMS;  // this thread owns positions j0 .. j0 + ITEMS - 1
 
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void decode_select_long_kernel(
     __shared__ RadixShared<kThreads> rs;
     __shared__ int wsum[kThreads / 64];
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int L = cache_lens[b];
+    const int L = clamp_len(cache_lens, b, Lmax);
     const float *row = dt_cache + ((size_t)b * Hkv + g) * Lmax;
     float t_tau = -INFINITY;
     int t_tie = -1;
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void decode_attend_kernel(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int G = Hq / Hkv;
     const int nchunk = gridDim.x;
-    const int L = cache_lens[b];
+    const int L = clamp_len(cache_lens, b, Lmax);
     const int c0 = chunk * BK;
     const int n = max(0, min(min(L, w) - c0, BK));  // kept positions of this chunk
     const size_t lbase = ((size_t)b * Hkv + g) * w + c0;
@@ -604,7 +604,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_wave_kernel(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int G = Hq / Hkv;
     const int col = lane & 15, grp = lane >> 4;
-    const int L = cache_lens[b];
+    const int L = clamp_len(cache_lens, b, Lmax);
     const int len = (L + nsplit - 1) / nsplit;
     const int jbeg = min(split * len, L), jend = min(jbeg + len, L);
     const uint64_t thr = thr_ws[(size_t)b * Hkv + g];

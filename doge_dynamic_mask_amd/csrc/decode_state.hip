@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kInitThreads) void state_init_kernel(
     __shared__ int red_s[kInitThreads / 64];
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const size_t bg = (size_t)b * Hkv + g;
-    const int L = cache_lens[b];
+    const int L = clamp_len(cache_lens, b, Lmax);
     const uint64_t thr = thr_ws[bg];
     const float *row = dt_cache + bg * Lmax;
     uint64_t *kb = keys + bg * w;

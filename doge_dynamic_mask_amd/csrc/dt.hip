@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void dt_kernel(const T *__restrict__ V, c
         }
 #pragma unroll
         for (int h = 0; h < kMaxHkvDt; ++h) {
-            if (h < Hkv && (h % kLanesPerToken) == q) {
+            if (h < Hkv && (h % kLanesPerToken) == q && (uint64_t)col < (uint64_t)ld) {
                 const float x = acc[h] + bs[h];
                 out[((int64_t)b * Hkv + h) * ld + col] = expf(As[h] * softplus_f32(x));
             }
@@ -205,7 +205,8 @@ __global__ __launch_bounds__(kMfmaThreads) void dt_mfma_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t tok = tile * 16 + 4 * kg + i;
-                if (tok < ntok)
+                // a column outside [0, ld) (an out_pos past the row) is not written
+                if (tok < ntok && (uint64_t)(ocol[i] + os[i]) < (uint64_t)ld)
                     out[((int64_t)ob[i] * Hkv + mr) * ld + ocol[i] + os[i]] = dt_from_x(a_h, acc[i] + b_h);
             }
         }

@@ -74,7 +74,7 @@ hipError_t launch_cdmoe_logits(const void *h, const void *router, int T, int H, 
 hipError_t launch_cdmoe_route(const float *logits, int T, int nk, int k, int32_t *idx, float *wts,
                               hipStream_t stream);
 hipError_t launch_cdmoe_experts(const void *h, const void *down, const void *up, const int32_t *idx, const float *wts,
-                                int T, int H, int k, void *out, hipStream_t stream);
+                                int T, int H, int nk, int k, void *out, hipStream_t stream);
 
 // Limits the launchers rely on (checked by the ABI layer).
 constexpr int kMaxHkvDt = 16;          // dt kernel: heads accumulated in registers

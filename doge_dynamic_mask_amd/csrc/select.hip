@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = blockIdx.y, b = blockIdx.z;
     const int r0 = blockIdx.x * kChunk;
-    const int L = seqlens ? seqlens[b] : S;
+    const int L = clamp_len(seqlens, b, S);
     const size_t base = ((size_t)b * Hkv + g) * S;
     const float *row = dt + base;
     const int rend = min(r0 + kChunk, S);

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void select_window_kernel(const float *__
     const int i = (int)(r % S);
     const int64_t bg = r / S;
     const int b = (int)(bg / Hkv);
-    const int L = seqlens ? seqlens[b] : S;
+    const int L = clamp_len(seqlens, b, S);
     if (i >= L) {
         if (lane == 0) {
             tau[r] = INFINITY;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
     const int tq = item % ntq;
     const int g = (item / ntq) % Hkv;
     const int b = item / (ntq * Hkv);
-    const int L = seqlens ? seqlens[b] : S;
+    const int L = clamp_len(seqlens, b, S);
     const int RB = kPairs / G;
     const int i0 = tq * RB;
     const int pr = 16 * wave + pq;

@@ -23,7 +23,10 @@
  *  - Causal: query row i sees keys j <= i.  Right padding: with a lengths
  *    array, batch b has L_b valid positions (1 <= L_b <= S); keys j >= L_b are
  *    masked and query rows i >= L_b produce zeros.  A NULL lengths array
- *    means L_b = S for every batch.
+ *    means L_b = S for every batch.  A length outside [0, S] breaks this
+ *    contract; the kernels clamp it into [0, S], so it never makes them read
+ *    or write past the rows it bounds (the same holds for cache lengths
+ *    against Lmax).
  *  - Top-w selection order: larger dt first; among equal dt the lower key
  *    index first.  dt values of valid keys must not be NaN (the method's
  *    exp(.) never produces one); -0.0 and +0.0 compare equal.
@@ -56,11 +59,33 @@ typedef enum dma_status {
 
 typedef enum dma_dtype { DMA_F32 = 0, DMA_BF16 = 1 } dma_dtype;
 
+/* Operations, for dma_workspace_bytes. */
+typedef enum dma_op {
+    DMA_OP_DT = 0,          /* dma_dt: no workspace */
+    DMA_OP_SELECT = 1,      /* dma_select: no workspace */
+    DMA_OP_ATTN_FWD = 2,    /* dma_attn_fwd: no workspace */
+    DMA_OP_DECODE = 3,      /* dma_decode (S is the cache length Lmax) */
+    DMA_OP_DECODE_STEP = 4, /* dma_decode_step and dma_decode_state_init (S unused) */
+    DMA_OP_ATTN_BWD = 5,    /* dma_attn_bwd */
+    DMA_OP_DT_BWD = 6       /* dma_dt_bwd (Hq and w unused) */
+} dma_op;
+
 /* Version of this ABI (major * 100 + minor). */
 int dma_version(void);
 
 /* Static text for a status code. */
 const char *dma_status_str(int status);
+
+/*
+ * dma_workspace_bytes -- bytes of caller-provided device workspace that
+ * operation `op` (a dma_op) needs for these sizes: 0 for the operations that
+ * need none (dma_dt, dma_select, dma_attn_fwd, which therefore take no
+ * workspace argument), the figure of the per-operation query otherwise
+ * (dma_decode_workspace_bytes, dma_decode_step_workspace_bytes,
+ * dma_attn_bwd_workspace_bytes, dma_dt_bwd_workspace_bytes).  Returns
+ * (size_t)-1 for an unknown op or sizes the operation rejects.
+ */
+size_t dma_workspace_bytes(int op, int B, int S, int Hq, int Hkv, int d, int w);
 
 /*
  * dma_dt -- Doge guide, DMA forward step 3, first two bullets: dt_proj maps
@@ -272,8 +297,11 @@ size_t dma_attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int d, int w)
  *   ws, ws_bytes: device workspace of at least dma_attn_bwd_workspace_bytes()
  * bf16 only; d in {64, 128}; Hq/Hkv in {1, 2, 4, 8}.  Products on matrix
  * cores with float32 accumulation (p and ds rounded to bf16 as operands);
- * deterministic (no atomics).  Work grows with the causal range of each row,
- * not with w.
+ * deterministic (no atomics).  The query side walks about w + 64/(Hq/Hkv)
+ * candidate keys per tile of rows; the key side walks, for each tile of 64
+ * keys, the rows from its first key to the last row that keeps any of them
+ * (with dt drawn independently per key that is often most of the causal
+ * range).
  */
 int dma_attn_bwd(const void *Q, const void *K, const void *V, int dtype, const float *dt, const float *tau,
                  const int32_t *tie, const int32_t *seqlens, const void *dO, int B, int S, int Hq, int Hkv, int d,

@@ -218,3 +218,29 @@ def test_cdmoe_validation(dma):
     assert dma.dma_cdmoe_experts(FAKE, FAKE, FAKE, 1, FAKE, None, 4, 512, 8, 4, FAKE2, None) == -1
     assert dma.dma_cdmoe_experts(FAKE, FAKE, FAKE, 1, FAKE, FAKE, 4, 500, 8, 4, FAKE2, None) == -4
     assert dma.dma_cdmoe_experts(FAKE, FAKE, FAKE, 1, FAKE, FAKE, 4, 512, 16, 129, FAKE2, None) == -4
+
+
+def test_generic_workspace_query(dma):
+    """dma_workspace_bytes(op, ...) dispatches to the per-operation queries;
+    the operations without scratch report 0; unknown ops and bad sizes give
+    (size_t)-1."""
+    bad = ctypes.c_size_t(-1).value
+    dma.dma_workspace_bytes.restype = ctypes.c_size_t
+    B, S, Hq, Hkv, d, w = 4, 2048, 8, 2, 128, 256
+    for op in (0, 1, 2):
+        assert dma.dma_workspace_bytes(op, B, S, Hq, Hkv, d, w) == 0
+    assert dma.dma_workspace_bytes(3, B, S, Hq, Hkv, d, w) == dma.dma_decode_workspace_bytes(B, S, Hq, Hkv, d, w)
+    assert dma.dma_workspace_bytes(4, B, S, Hq, Hkv, d, w) == dma.dma_decode_step_workspace_bytes(B, Hq, Hkv, d, w)
+    assert dma.dma_workspace_bytes(5, B, S, Hq, Hkv, 64, w) == dma.dma_attn_bwd_workspace_bytes(B, S, Hq, Hkv, 64, w)
+    assert dma.dma_workspace_bytes(6, B, S, Hq, Hkv, 64, w) == dma.dma_dt_bwd_workspace_bytes(B, S, Hkv, 64)
+    for op in (3, 4, 5, 6):
+        assert dma.dma_workspace_bytes(op, B, S, Hq, Hkv, d, w) > 0
+    assert dma.dma_workspace_bytes(7, B, S, Hq, Hkv, d, w) == bad
+    assert dma.dma_workspace_bytes(-1, B, S, Hq, Hkv, d, w) == bad
+    assert dma.dma_workspace_bytes(3, 0, S, Hq, Hkv, d, w) == bad
+    assert dma.dma_workspace_bytes(0, B, S, 7, Hkv, d, w) == bad       # Hq % Hkv != 0
+    assert dma.dma_workspace_bytes(5, B, S, Hq, Hkv, 96, w) == bad     # head_dim the backward rejects
+    import doge_dynamic_mask_amd as m
+    assert m.workspace_bytes(m.OP_DECODE, B, S, Hq, Hkv, d, w) == dma.dma_decode_workspace_bytes(B, S, Hq, Hkv, d, w)
+    with pytest.raises(ValueError):
+        m.workspace_bytes(9, B, S, Hq, Hkv, d, w)
