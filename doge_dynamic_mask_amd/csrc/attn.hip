@@ -50,7 +50,8 @@ constexpr int kMaxSteps = 32;    // fill steps counted per round (32768 keys)
 constexpr int kBatchSteps = 8;   // fill steps whose loads are issued together
 constexpr int kPartCap = 2 * kRowsPerWG + 2 * kBK;  // slots of the masked region
 constexpr int kCarrySlots = kCap / kThreads;         // carried candidates per thread
-constexpr int kTargetItems = 1024;                   // workgroups a launch aims for
+constexpr int kTargetItems = 4096;                   // work items a launch aims for
+constexpr int kChunk = 8;                            // consecutive groups of one unit per XCD chunk
 
 template <int D>
 struct Tiles {
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const float *__restrict__ dt, const float *__restrict__ tau, const int32_t *__restrict__ tie,
     const int32_t *__restrict__ seqlens, int S, int Hq, int Hkv, int G, int Bq, int ntiles, int tpw,
-    uint16_t *__restrict__ O, float qscale) {
+    int nunits, uint16_t *__restrict__ O, float qscale) {
     using T = Tiles<D>;
     constexpr int RV = D / 8;                    // 16-byte vectors per K/V row
     constexpr int NL = kBK * RV / kThreads;      // K (and V) vectors per thread per block
@@ -107,18 +108,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int h = lane >> 5, ql = lane & 31;
-    // Work item = (batch, kv head, group of tpw consecutive query tiles).
-    // XCD-aware order: workgroup ids go round-robin over the 8 XCDs, so hand
-    // each XCD a contiguous run of work items; nearby tiles of one kv head
-    // share most candidate K/V rows in that XCD's L2.
+    // Work item = (unit (batch, kv head), group of tpw consecutive query
+    // tiles).  Each unit's groups are cut into chunks of kChunk consecutive
+    // groups, and workgroup ids go round-robin over the 8 XCDs, so the k-th
+    // workgroup of XCD x takes group k % kChunk of the chunk with rank
+    // 8 * (k / kChunk) + x.  Chunk ranks run over row position first and
+    // rotate the unit with it, so every XCD gets an equal share of every
+    // unit's rows (padded units, whose later groups are empty, do not load
+    // one XCD more than another), the groups of a chunk share their
+    // candidate K/V rows in one XCD's L2, and items are many more than the
+    // XCD's workgroup slots, so the last round of slow items stays short.
     const int ngroups = (ntiles + tpw - 1) / tpw;
-    const int nwg = gridDim.x;
-    const int per_xcd = nwg >> 3;
+    const int nchunk_u = (ngroups + kChunk - 1) / kChunk;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int item = (slot < per_xcd && (nwg & 7) == 0) ? xcd * per_xcd + slot : blockIdx.x;
-    const int grp = item % ngroups;
-    const int g = (item / ngroups) % Hkv;
-    const int b = item / (ngroups * Hkv);
+    const int qch = (slot / kChunk) * 8 + xcd;  // chunk rank
+    if (qch >= nunits * nchunk_u) return;
+    const int cch = qch / nunits;               // chunk position in its unit
+    const int unit = (qch - cch * nunits + cch) % nunits;
+    const int grp = cch * kChunk + slot % kChunk;
+    if (grp >= ngroups) return;
+    const int g = unit % Hkv;
+    const int b = unit / Hkv;
     const int L = clamp_len(seqlens, b, S);
 
     const int m = wave * 32 + ql;  // stacked (row, head) pair of this lane
@@ -617,22 +627,26 @@ hipError_t launch_attn(const void *Q, const void *K, const void *V, int dtype, c
         const int G = Hq / Hkv;
         const int Bq = kRowsPerWG / G;
         const int ntiles = (S + Bq - 1) / Bq;
-        // consecutive tiles per workgroup: enough work items to fill the chip
-        // about four times over, and the prefix scan of a tile's first
-        // candidate list amortised over the rest of its group
+        // consecutive tiles per workgroup: enough work items to fill the
+        // chip's workgroup slots several times over (a short last round),
+        // and the prefix scan of a group's first candidate list amortised
+        // over the rest of its group
         const int64_t total = (int64_t)ntiles * Hkv * B;
         const int tpw = (int)std::max<int64_t>(1, std::min<int64_t>(total / kTargetItems, ntiles));
-        const int64_t items = (int64_t)((ntiles + tpw - 1) / tpw) * Hkv * B;
+        const int64_t ngroups = (ntiles + tpw - 1) / tpw;
+        const int64_t nchunks = (int64_t)B * Hkv * ((ngroups + kChunk - 1) / kChunk);
+        const int64_t items = 8 * (int64_t)kChunk * ((nchunks + 7) / 8);
         if (items > 0x7fffffff) return hipErrorInvalidValue;
         const dim3 grid((unsigned)items);
+        const int nunits = B * Hkv;
         if (d == 128)
             hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(kThreads), 0, stream,
                                (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau,
-                               tie, seqlens, S, Hq, Hkv, G, Bq, ntiles, tpw, (uint16_t *)O, qscale);
+                               tie, seqlens, S, Hq, Hkv, G, Bq, ntiles, tpw, nunits, (uint16_t *)O, qscale);
         else
             hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(kThreads), 0, stream,
                                (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau,
-                               tie, seqlens, S, Hq, Hkv, G, Bq, ntiles, tpw, (uint16_t *)O, qscale);
+                               tie, seqlens, S, Hq, Hkv, G, Bq, ntiles, tpw, nunits, (uint16_t *)O, qscale);
     } else {
         const int64_t waves = (int64_t)B * Hq * S;
         const int64_t blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);
