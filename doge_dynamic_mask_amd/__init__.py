@@ -42,7 +42,7 @@ _STATUS = {
 }
 
 EXPORTS = ("dma_version", "dma_status_str", "dma_workspace_bytes", "dma_dt", "dma_select", "dma_attn_fwd",
-           "dma_decode_workspace_bytes", "dma_decode", "dma_decode_state_bytes",
+           "dma_decode_workspace_bytes", "dma_decode", "dma_decode_noalloc", "dma_decode_state_bytes",
            "dma_decode_step_workspace_bytes", "dma_decode_state_init", "dma_decode_step",
            "dma_decode_state_kept", "dma_qk_norm_rope", "dma_prologue",
            "dma_attn_bwd_workspace_bytes", "dma_attn_bwd", "dma_dt_bwd_workspace_bytes", "dma_dt_bwd",
@@ -81,6 +81,8 @@ def lib():
     L.dma_decode_workspace_bytes.restype = SZ
     L.dma_decode.argtypes = [P, P, P, I, P, P, I, I, I, I, I, I, P, P, P, SZ, P]
     L.dma_decode.restype = I
+    L.dma_decode_noalloc.argtypes = [P, P, P, I, P, P, I, I, I, I, I, I, P, P, P]
+    L.dma_decode_noalloc.restype = I
     L.dma_decode_state_bytes.argtypes, L.dma_decode_state_bytes.restype = [I, I, I, I], SZ
     L.dma_decode_step_workspace_bytes.argtypes = [I, I, I, I, I]
     L.dma_decode_step_workspace_bytes.restype = SZ
@@ -291,6 +293,37 @@ def decode(q, Kc, Vc, dt_cache, cache_lens, w, kept=False, out=None, workspace=N
     _call(lib().dma_decode(_ptr(q), _ptr(Kc), _ptr(Vc), _dtype_code(q), _ptr(dt_cache), _ptr(cache_lens),
                            B, Lmax, Hq, Hkv, d, int(w), _ptr(out), _ptr(kept_idx), _ptr(workspace),
                            workspace.numel(), _stream(q)), "dma_decode")
+    return (out, kept_idx) if kept else out
+
+
+DECODE_NOALLOC_MAX_WORKSPACE = 16 << 20
+
+
+def decode_noalloc(q, Kc, Vc, dt_cache, cache_lens, w, kept=False, out=None):
+    """decode() through dma_decode_noalloc: no workspace is allocated (the library's static device
+    array serves instead; sizes needing more than 16 MiB of workspace are rejected).  Outputs are
+    allocated here unless given; calls that overlap in time on one device race."""
+    _check(q, "q", ndim=3)
+    dev = q.device
+    _check(Kc, "Kc", q.dtype, 4, dev)
+    _check(Vc, "Vc", q.dtype, 4, dev)
+    _check(dt_cache, "dt_cache", torch.float32, 3, dev)
+    _check(cache_lens, "cache_lens", torch.int32, 1, dev)
+    B, Hq, d = q.shape
+    Lmax, Hkv = Kc.shape[1], Kc.shape[2]
+    _shape(Kc, "Kc", (B, Lmax, Hkv, d))
+    _shape(Vc, "Vc", Kc.shape)
+    _shape(dt_cache, "dt_cache", (B, Hkv, Lmax))
+    _shape(cache_lens, "cache_lens", (B,))
+    if out is not None:
+        _check(out, "out", q.dtype, 3, dev)
+        _shape(out, "out", q.shape)
+    else:
+        out = torch.empty_like(q)
+    kept_idx = torch.empty((B, Hkv, int(w)), dtype=torch.int32, device=dev) if kept else None
+    _call(lib().dma_decode_noalloc(_ptr(q), _ptr(Kc), _ptr(Vc), _dtype_code(q), _ptr(dt_cache), _ptr(cache_lens),
+                                   B, Lmax, Hq, Hkv, d, int(w), _ptr(out), _ptr(kept_idx), _stream(q)),
+          "dma_decode_noalloc")
     return (out, kept_idx) if kept else out
 
 

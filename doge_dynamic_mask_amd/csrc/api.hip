@@ -110,6 +110,21 @@ int dma_decode(const void *q, const void *Kc, const void *Vc, int dtype, const f
                                        out, kept_idx, ws, (hipStream_t)stream));
 }
 
+int dma_decode_noalloc(const void *q, const void *Kc, const void *Vc, int dtype, const float *dt_cache,
+                       const int32_t *cache_lens, int B, int Lmax, int Hq, int Hkv, int d, int w, void *out,
+                       int32_t *kept_idx, void *stream) {
+    if (!q || !Kc || !Vc || !dt_cache || !cache_lens || !out) return DMA_ERR_NULL;
+    if (!dtype_ok(dtype)) return DMA_ERR_DTYPE;
+    if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || d < 1 || w < 1 || Hq % Hkv != 0) return DMA_ERR_SHAPE;
+    if (!head_dim_ok(d) || Hq / Hkv > dma::kMaxGroupDecode) return DMA_ERR_UNSUPPORTED;
+    if (B > 65535 || Hkv > 65535) return DMA_ERR_UNSUPPORTED;
+    if ((Lmax < w ? Lmax : w) > dma::kMaxKeptDecode) return DMA_ERR_UNSUPPORTED;
+    if (!aligned16(Kc) || !aligned16(Vc)) return DMA_ERR_UNSUPPORTED;
+    if (dma::decode_ws_bytes(B, Lmax, Hq, Hkv, d, w) > dma::kDecodeNoAllocScratchBytes) return DMA_ERR_WORKSPACE;
+    return from_hip(dma::launch_decode_noalloc(q, Kc, Vc, dtype, dt_cache, cache_lens, B, Lmax, Hq, Hkv, d, w, out,
+                                               kept_idx, (hipStream_t)stream));
+}
+
 size_t dma_decode_state_bytes(int B, int Hkv, int d, int w) {
     if (B < 1 || Hkv < 1 || w < 1 || !head_dim_ok(d)) return 0;
     return dma::decode_state_bytes(B, Hkv, d, w);

@@ -29,6 +29,8 @@
 #include "launch.hpp"
 #include "radix_select.hpp"
 
+#include <mutex>
+
 namespace dma {
 namespace {
 
@@ -956,6 +958,41 @@ hipError_t launch_decode_thresholds(const float *dt_cache, const int32_t *cache_
 
 size_t decode_ws_bytes(int B, int Lmax, int Hq, int Hkv, int d, int w) {
     return ws_layout(B, Lmax, Hq, Hkv, d, w).total;
+}
+
+// ---------------------------------------------------- allocation-free decode --
+// dma_decode_noalloc's workspace: a file-scope device array, one copy per
+// device the library runs on, held until the process ends.  Host code never
+// passes `scratch` itself to a kernel (in host code the name is a host-side
+// stand-in, not a device address): the device address of each device's copy
+// is looked up once, with that device current, and kept per device.
+namespace {
+static __device__ __align__(256) unsigned char scratch[kDecodeNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void *g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+}  // namespace
+
+hipError_t launch_decode_noalloc(const void *q, const void *Kc, const void *Vc, int dtype, const float *dt_cache,
+                                 const int32_t *cache_lens, int B, int Lmax, int Hq, int Hkv, int d, int w,
+                                 void *out, int32_t *kept_idx, hipStream_t stream) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    // every part of the workspace that the kernels read is written first by
+    // the same call (thresholds by the select, one partial per attend
+    // workgroup), so nothing needs clearing between calls
+    return launch_decode(q, Kc, Vc, dtype, dt_cache, cache_lens, B, Lmax, Hq, Hkv, d, w, out, kept_idx,
+                         g_scratch_ptr[dev], stream);
 }
 
 hipError_t launch_decode(const void *q, const void *Kc, const void *Vc, int dtype,

@@ -27,6 +27,13 @@ hipError_t launch_decode(const void *q, const void *Kc, const void *Vc, int dtyp
                          int Hq, int Hkv, int d, int w, void *out, int32_t *kept_idx, void *ws,
                          hipStream_t stream);
 
+// dma_decode with its workspace in a static device array of
+// kDecodeNoAllocScratchBytes per device (no allocation).
+constexpr size_t kDecodeNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t launch_decode_noalloc(const void *q, const void *Kc, const void *Vc, int dtype, const float *dt_cache,
+                                 const int32_t *cache_lens, int B, int Lmax, int Hq, int Hkv, int d, int w,
+                                 void *out, int32_t *kept_idx, hipStream_t stream);
+
 // The selection key of the w-th kept position of each (batch, kv head) of a
 // decode cache (0 when every position is kept), as dma_decode's first step.
 hipError_t launch_decode_thresholds(const float *dt_cache, const int32_t *cache_lens, int B, int Lmax, int Hkv,

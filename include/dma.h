@@ -181,6 +181,26 @@ int dma_decode(const void *q, const void *Kc, const void *Vc, int dtype,
                size_t ws_bytes, void *stream);
 
 /*
+ * dma_decode_noalloc -- dma_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments without ws / ws_bytes, the same
+ * kernels and results.  Its workspace is a static device array of 16 MiB
+ * per device, part of the library's code object and held until the process
+ * ends; sizes whose dma_decode_workspace_bytes() exceeds 16 MiB are rejected
+ * with DMA_ERR_WORKSPACE before anything is enqueued (the decode workload
+ * of B = 64, Lmax = 16384, Hq = 8, Hkv = 2, d = 128, w = 2048 needs about
+ * 10 MiB).  The call itself allocates nothing: its first call on a device
+ * looks up that device's copy of the array.  All calls on one device share
+ * the array, so calls that overlap in time on one device (on different
+ * streams, or from different threads without ordering) race and must not
+ * be issued; calls ordered on one stream are safe, and each call writes
+ * every part of the array it reads.
+ */
+int dma_decode_noalloc(const void *q, const void *Kc, const void *Vc, int dtype,
+                       const float *dt_cache, const int32_t *cache_lens, int B, int Lmax, int Hq,
+                       int Hkv, int d, int w, void *out, int32_t *kept_idx, void *stream);
+
+/*
  * Incremental decode -- Doge guide, DMA section, forward steps 3 and 4 at
  * inference, one token at a time.  The kept sets nest (under dt desc, index
  * asc, the kept set of position p is a subset of that of p-1 plus {p}), so

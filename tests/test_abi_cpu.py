@@ -244,3 +244,23 @@ def test_generic_workspace_query(dma):
     assert m.workspace_bytes(m.OP_DECODE, B, S, Hq, Hkv, d, w) == dma.dma_decode_workspace_bytes(B, S, Hq, Hkv, d, w)
     with pytest.raises(ValueError):
         m.workspace_bytes(9, B, S, Hq, Hkv, d, w)
+
+
+def test_decode_noalloc_validation(dma):
+    """The allocation-free decode rejects bad arguments, and sizes whose
+    workspace exceeds its 16 MiB static array, before any HIP call."""
+    def call(q=FAKE, cache_lens=FAKE, dtype=1, B=4, Lmax=2048, Hq=8, Hkv=2, d=128, w=256, out=FAKE2):
+        return dma.dma_decode_noalloc(q, FAKE, FAKE, dtype, FAKE, cache_lens, B, Lmax, Hq, Hkv, d, w, out, None,
+                                      None)
+    assert call(q=None) == -1
+    assert call(cache_lens=None) == -1
+    assert call(out=None) == -1
+    assert call(dtype=9) == -3
+    assert call(Hq=7) == -2
+    assert call(w=0) == -2
+    assert call(d=80) == -4
+    assert call(Hq=64, Hkv=2) == -4
+    # the decode workload's workspace fits; a 64k-position cache with w = 8192 does not
+    assert dma.dma_decode_workspace_bytes(64, 16384, 8, 2, 128, 2048) <= 16 << 20
+    assert dma.dma_decode_workspace_bytes(64, 65536, 16, 2, 128, 8192) > 16 << 20
+    assert call(B=64, Lmax=65536, Hq=16, Hkv=2, d=128, w=8192) == -5
