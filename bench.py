@@ -1,25 +1,27 @@
-"""Benchmark of the DMA forward hot path on one MI355X.
+"""Benchmark of the DMA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--other-configs]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-variants]
     python bench.py --copy-calibration     (a plain 256 MiB copy, for counter scaling)
+    python bench.py --attn-only NAME       (a few attention launches of one prefill workload)
 
 One step = the whole hot path over one batch of synthetic input:
-  prefill  B=4 Hq=8 Hkv=4 S=2048 d=64 w=512 bf16  (dma_dt -> dma_select -> dma_attn_fwd)
+  prefill  B=2 Hq=16 Hkv=4 S=32768 d=128 w=2048 bf16, right-padded lengths
+           ~ U[16384, 32768] (dma_dt -> dma_select -> dma_attn_fwd)
   decode   B=64 Hq=8 Hkv=2 d=128 w=2048, 16384 cached positions
            (dma_dt appends the new token's dt, then dma_decode)
-A 512 MiB read before each decode evicts the kept K/V rows from the caches
-(with clean lines, so no write-back traffic lands on the decode), so decode
-moves its bytes from HBM; a 512 MiB read before the prefill does the same
-for the prefill inputs.  The evictions are outside the timed kernels.
+A 512 MiB read before each half evicts the inputs from the caches (with
+clean lines, so no write-back traffic lands on the timed calls); the
+evictions are outside the timed kernels.
 
-Printed: ONE JSON line.  value = prefill kept-key TFLOP/s (kept (query, key)
-pairs x 4*d flop over the GPU time of the three prefill calls, launched back
-to back); the decode GB/s (algorithmic bytes over dma_decode's GPU time)
-rides along under "decode".  ms_per_step = prefill + decode GPU time of one
-step (the cache evictions are excluded); the wall-clock time per step
-including them is reported too.  Times come from HIP events recorded between
-the calls on the stream the kernels run on; the prefill replayed as one HIP
-graph is timed as well.
+Printed: ONE JSON line.  value = prefill kept-key TFLOP/s of the padded
+workload (kept (query, key) pairs x 4*d flop over the GPU time of the three
+prefill calls, launched back to back); the decode GB/s (algorithmic bytes
+over dma_decode's GPU time) rides along under "decode".  The long
+(B1 Hq16 Hkv8 S8192 d128 w2048) and c2 (B4 Hq8 Hkv4 S2048 d64 w512) prefill
+workloads are timed per call under "prefill_configs".  ms_per_step = prefill
++ decode GPU time of one step.  Times come from HIP events recorded between
+the calls on the stream the kernels run on (torch's current stream, which
+the binding launches on).
 """
 from __future__ import annotations
 
@@ -40,15 +42,13 @@ import synth_inputs as si  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 
-# HBM bytes per launch of the prefill attention kernel on this workload, from
-# two rocprofv3 counter runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB
-# per dispatch), each scaled by copy_bytes / counter reading of a plain copy of
+# HBM bytes per launch of the padded workload's attention kernel, from two
+# rocprofv3 counter runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch), each scaled by copy_bytes / counter reading of a plain copy of
 # known size (--copy-calibration); the runs and their readings are in
-# profiles/dma_kernels_prefill_b4s2048_decode_b64l16384_hbm_counters.md.  The
-# figure holds only for the attention source it was measured on: when the
-# hash of those files differs, traffic is reported as null.
-ATTN_TRAFFIC = {"bytes": 26108416,
-                "sources_sha256": "dc85285bef52cf9b22312007b0b58318a801c0dbbb285bed3505c75e498a07df"}
+# profiles/.  The figure holds only for the attention source it was measured
+# on: when the hash of those files differs, traffic is reported as null.
+ATTN_TRAFFIC = {"bytes": None, "sources_sha256": ""}
 ATTN_SOURCES = ("doge_dynamic_mask_amd/csrc/attn.hip", "doge_dynamic_mask_amd/csrc/common.hpp")
 COPY_CAL_BYTES = 256 * 1024 * 1024
 
@@ -117,93 +117,187 @@ def to_dev(x, dev):
     return (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
 
 
-def cpu_baseline(pre_inp, wl_p, min_seconds=10.0):
-    """The oracle (plain C, fp64, OpenMP) timed on the host: full prefill of
-    the same batch (dt, select, attention over every row), repeated until
-    min_seconds have passed.  Reported in the metric's unit (kept-key TFLOP/s)."""
-    import oracle
-    oracle.build(force=False)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    flops = kept_flops(wl_p.B, wl_p.Hq, wl_p.S, wl_p.d, wl_p.w)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        dt = oracle.dt(pre_inp["V"], pre_inp["W"], pre_inp["bias"], pre_inp["A"])
-        dt32 = dt.astype(np.float32)
-        oracle.select(dt32, wl_p.w)
-        oracle.attn(pre_inp["Q"], pre_inp["K"], pre_inp["V"], dt32, wl_p.w)
-        reps += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    el = time.perf_counter() - t0
-    model = ""
+
+def host_cpu_info():
+    """CPU model, sockets and core counts of this host."""
+    model, phys = "", set()
     try:
         with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+            for ln in f:
+                if ln.startswith("model name") and not model:
+                    model = ln.split(":", 1)[1].strip()
+                elif ln.startswith("physical id"):
+                    phys.add(ln.split(":", 1)[1].strip())
     except OSError:
         pass
-    return {"value": flops * reps / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"full prefill of the same batch (dt + select + attention, every row), "
-                      f"{reps} repetitions in {el:.1f} s, fp64",
-            "host": {"cpu_model": model, "visible_cpus": os.cpu_count()}}
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "sockets": max(1, len(phys)), "nproc": os.cpu_count(), "usable_cpus": usable}
 
 
-def prefill_breakdown(dma, name, dev, evict, R=8, rounds=4):
-    """Per-call GPU time of one prefill workload, timed like the main
-    workload's calls: after an eviction, R back-to-back launches between two
-    events, each on its own copy of the inputs (enough copies that every
-    launch reads from HBM)."""
-    wl = si.WORKLOADS[name]
-    inp = si.make_inputs(wl)
-    Q, K, V = to_dev(inp["Q"], dev), to_dev(inp["K"], dev), to_dev(inp["V"], dev)
-    W, A, bias = to_dev(inp["W"], dev), to_dev(inp["A"], dev), to_dev(inp["bias"], dev)
-    seq = None if inp["seqlens"] is None else to_dev(inp["seqlens"], dev)
-    dt = torch.empty((wl.B, wl.Hkv, wl.S), dtype=torch.float32, device=dev)
-    tau, tie = torch.empty_like(dt), torch.empty(dt.shape, dtype=torch.int32, device=dev)
-    O = torch.empty_like(Q)
-    dma.dt(V, W, A, bias, out=dt)
-    dma.select(dt, wl.w, seq, tau=tau, tie=tie)
-    first = (Q, K, V, dt, tau, tie)
-    set_bytes = sum(t.numel() * t.element_size() for t in first)
-    nsets = 1 + -(-300 * 2**20 // set_bytes)
-    sets = [first] + [tuple(t.clone() for t in first) for _ in range(nsets - 1)]
-    rot = [0]
+def cpu_baseline(inp, wl, rows_per_unit=768, reps=3):
+    """The oracle (plain C, fp64, OpenMP over rows) timed on the host on a
+    stratified sample of the prefill workload: dt over every token, then the
+    selection and the attention of rows_per_unit rows per (batch, kv head),
+    evenly spaced over [0, L_b) (so the rows before and after the first w
+    keys are represented as in the full workload).  Each stage runs once to
+    warm up, then reps times; the median is taken.  value = kept-key flops of
+    the sampled rows / (select + attention time of the sample + the dt time
+    prorated to the sampled share of the rows)."""
+    import oracle
+    oracle.build(force=False)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    L = inp["seqlens"] if inp["seqlens"] is not None else np.full(wl.B, wl.S, np.int32)
+    rows = sorted({(b, g, int(i)) for b in range(wl.B) for g in range(wl.Hkv)
+                   for i in np.linspace(0, int(L[b]) - 1, rows_per_unit).round()})
+    rows = np.array(rows, dtype=np.int32)
+    G = wl.Hq // wl.Hkv
+    sample_flops = int(sum(4 * wl.d * G * min(int(i) + 1, wl.w) for _, _, i in rows))
+    total_rows = int(sum(int(x) for x in L)) * wl.Hkv
+    total_flops = kept_flops(wl.B, wl.Hq, wl.S, wl.d, wl.w, inp["seqlens"])
 
-    def nxt():
-        rot[0] += 1
-        return sets[rot[0] % nsets]
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            r = fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts)), r
 
-    def c_dt():
-        s_ = nxt()
-        dma.dt(s_[2], W, A, bias, out=s_[3])
+    t_dt, dt64 = timed(lambda: oracle.dt(inp["V"], inp["W"], inp["bias"], inp["A"]))
+    dt32 = dt64.astype(np.float32)
+    t_sel, _ = timed(lambda: oracle.select(dt32, wl.w, inp["seqlens"], rows=rows))
+    t_attn, _ = timed(lambda: oracle.attn(inp["Q"], inp["K"], inp["V"], dt32, wl.w, inp["seqlens"], rows=rows))
+    share = len(rows) / total_rows
+    t_sample = t_sel + t_attn + t_dt * share
+    return {"value": sample_flops / t_sample / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {total_rows} (batch, kv head, row) rows of the padded prefill, "
+                      f"{rows_per_unit} per (batch, kv head) evenly spaced over its valid rows, each with its "
+                      f"{G} query heads; dt over all tokens prorated to that share; fp64; median of {reps} "
+                      f"runs after one warm-up",
+            "sample_kept_flops": sample_flops,
+            "stage_s": {"dt_all_tokens": round(t_dt, 4), "select_sample": round(t_sel, 4),
+                        "attn_sample": round(t_attn, 4)},
+            "est_full_prefill_s": round(t_dt + t_sel / share + t_attn * total_flops / sample_flops, 2),
+            "host": {**host_cpu_info(), "omp_threads": threads}}
 
-    def c_select():
-        s_ = nxt()
-        dma.select(s_[3], wl.w, seq, tau=s_[4], tie=s_[5])
 
-    def c_attn():
-        s_ = nxt()
-        dma.attn_fwd(*s_, wl.w, seq, out=O)
-
-    res = {}
-    for n, f in (("dt", c_dt), ("select", c_select), ("attn_fwd", c_attn)):
-        pairs = []
+def per_launch_ms(calls, evict, R, rounds):
+    """Average GPU time per launch of each call: after an eviction, R
+    back-to-back launches between two events, `rounds` times."""
+    res, host = {}, {}
+    for n, f in calls:
+        f()                         # the first launch of a kernel loads its code
+        torch.cuda.synchronize()
+        pairs, hs = [], []
         for _ in range(rounds):
             evict()
+            evict()                 # keeps the GPU busy while the host enqueues the R launches
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
+            h0 = time.perf_counter()
             for _ in range(R):
                 f()
+            hs.append((time.perf_counter() - h0) * 1e3 / R)
             b.record()
             pairs.append((a, b))
         torch.cuda.synchronize()
         res[n] = float(np.mean([a.elapsed_time(b) for a, b in pairs])) / R
-    del sets
-    flops = kept_flops(wl.B, wl.Hq, wl.S, wl.d, wl.w, inp["seqlens"])
-    tot = sum(res.values())
-    return {"ms": {k: round(v, 5) for k, v in res.items()}, "kept_flops": flops, "input_copies": nsets,
-            "tflops_prefill": round(flops / (tot * 1e-3) / 1e12, 2),
-            "tflops_attn": round(flops / (res["attn_fwd"] * 1e-3) / 1e12, 2),
-            "attn_frac_of_peak": round(flops / (res["attn_fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        host[n] = float(np.mean(hs))
+    return res, host
+
+
+class Prefill:
+    """One prefill workload on the device, with rotating copies of its
+    inputs (enough that the data read between two launches of a call exceeds
+    the 256 MB last-level cache, so every launch reads from HBM)."""
+
+    def __init__(self, dma, name, dev, inp=None):
+        self.dma, self.name = dma, name
+        self.wl = wl = si.WORKLOADS[name]
+        self.inp = inp = si.make_inputs(wl) if inp is None else inp
+        self.Q, self.K, self.V = to_dev(inp["Q"], dev), to_dev(inp["K"], dev), to_dev(inp["V"], dev)
+        self.W, self.A, self.bias = to_dev(inp["W"], dev), to_dev(inp["A"], dev), to_dev(inp["bias"], dev)
+        self.seq = None if inp["seqlens"] is None else to_dev(inp["seqlens"], dev)
+        self.dt = torch.empty((wl.B, wl.Hkv, wl.S), dtype=torch.float32, device=dev)
+        self.tau = torch.empty_like(self.dt)
+        self.tie = torch.empty(self.dt.shape, dtype=torch.int32, device=dev)
+        self.O = torch.empty_like(self.Q)
+        dma.dt(self.V, self.W, self.A, self.bias, out=self.dt)
+        dma.select(self.dt, wl.w, self.seq, tau=self.tau, tie=self.tie)
+        self.flops = kept_flops(wl.B, wl.Hq, wl.S, wl.d, wl.w, inp["seqlens"])
+        self.sets, self.rot, self.ncopies = None, 0, 1
+
+    def make_sets(self, min_bytes=300 * 2**20):
+        first = (self.Q, self.K, self.V, self.dt, self.tau, self.tie)
+        set_bytes = sum(t.numel() * t.element_size() for t in first)
+        n = 1 + -(-min_bytes // set_bytes)
+        self.sets = [first] + [tuple(t.clone() for t in first) for _ in range(n - 1)]
+        self.ncopies = n
+
+    def drop_sets(self):
+        self.sets = None
+
+    def nxt(self):
+        self.rot += 1
+        return self.sets[self.rot % len(self.sets)]
+
+    # the three calls of the path on the resident inputs (no rotation)
+    def g_dt(self):
+        self.dma.dt(self.V, self.W, self.A, self.bias, out=self.dt)
+
+    def g_select(self):
+        self.dma.select(self.dt, self.wl.w, self.seq, tau=self.tau, tie=self.tie)
+
+    def g_attn(self):
+        self.dma.attn_fwd(self.Q, self.K, self.V, self.dt, self.tau, self.tie, self.wl.w, self.seq, out=self.O)
+
+    # the same calls, each on the next copy of the inputs
+    def c_dt(self):
+        s_ = self.nxt()
+        self.dma.dt(s_[2], self.W, self.A, self.bias, out=s_[3])
+
+    def c_select(self):
+        s_ = self.nxt()
+        self.dma.select(s_[3], self.wl.w, self.seq, tau=s_[4], tie=s_[5])
+
+    def c_attn(self):
+        s_ = self.nxt()
+        self.dma.attn_fwd(*s_, self.wl.w, self.seq, out=self.O)
+
+    def summary(self, ms):
+        tot = ms["dt"] + ms["select"] + ms["attn_fwd"]
+        wl = self.wl
+        att = self.flops / (ms["attn_fwd"] * 1e-3) / 1e12
+        return {"workload": workload_name(wl), "ms": {k: round(v, 5) for k, v in ms.items()},
+                "kept_flops": self.flops, "input_copies": self.ncopies,
+                "tflops_prefill": round(self.flops / (tot * 1e-3) / 1e12, 2), "tflops_attn": round(att, 2),
+                "attn_frac_of_peak": round(att / PEAK_BF16_TFLOPS, 4),
+                "select_share_of_prefill": round(ms["select"] / tot, 4)}
+
+
+def workload_name(wl):
+    pad = f", right-padded lengths ~U[{wl.pad_lo},{wl.pad_hi}]" if wl.pad_hi else ""
+    return f"prefill B{wl.B} Hq{wl.Hq} Hkv{wl.Hkv} S{wl.S} d{wl.d} w{wl.w} {wl.dtype}{pad}"
+
+
+def attn_only(name, launches):
+    """A few attention launches of one prefill workload (for counter runs):
+    the inputs are built, dt and the thresholds computed once, then
+    `launches` launches of dma_attn_fwd on rotating input copies."""
+    import doge_dynamic_mask_amd as dma
+    dma.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    P = Prefill(dma, name, dev)
+    P.make_sets()
+    for _ in range(launches):
+        P.c_attn()
+    torch.cuda.synchronize()
+    print(json.dumps({"attn_only": name, "launches": launches, "kept_flops": P.flops}), flush=True)
 
 
 def window_breakdown(dma, dev, evict, win=4096, R=6, rounds=3):
@@ -300,13 +394,15 @@ def cdmoe_breakdown(dma, dev, evict, T=8192, H=1024, nk=128, k=64, R=6, rounds=3
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--other-configs", action="store_true",
-                    help="also time the other prefill workloads (long, padded, tiny) per kernel")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the sliding-window and CDMoE measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain copies of known size (counter calibration)")
+    ap.add_argument("--attn-only", default=None, help="only run attention launches of this prefill workload")
+    ap.add_argument("--launches", type=int, default=5)
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
@@ -315,24 +411,24 @@ def main():
         print("bench.py measures one GPU: the DMA hot path here has no cross-GPU step "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
+    if args.attn_only:
+        attn_only(args.attn_only, args.launches)
+        return
+
+    def progress(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     import doge_dynamic_mask_amd as dma
     dma.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    wl_p = si.WORKLOADS["c2"]
+    progress("inputs: padded prefill")
+    P5 = Prefill(dma, "padded", dev)
+    wl_p = P5.wl
     wl_d = si.WORKLOADS["decode"]
-    pre = si.make_inputs(wl_p)
+    progress("inputs: decode")
     dec = si.make_inputs(wl_d)
-
-    Q, K, V = to_dev(pre["Q"], dev), to_dev(pre["K"], dev), to_dev(pre["V"], dev)
-    W, A, bias = to_dev(pre["W"], dev), to_dev(pre["A"], dev), to_dev(pre["bias"], dev)
-    dt = torch.empty((wl_p.B, wl_p.Hkv, wl_p.S), dtype=torch.float32, device=dev)
-    tau = torch.empty_like(dt)
-    tie = torch.empty(dt.shape, dtype=torch.int32, device=dev)
-    O = torch.empty_like(Q)
-
     q, Kc, Vc = to_dev(dec["q"], dev), to_dev(dec["Kc"], dev), to_dev(dec["Vc"], dev)
     Wd, Ad, biasd = to_dev(dec["W"], dev), to_dev(dec["A"], dev), to_dev(dec["bias"], dev)
     lens = to_dev(dec["cache_lens"], dev)
@@ -350,42 +446,18 @@ def main():
 
     torch.cuda.synchronize()
 
-    # The stages, each one call of the C ABI through the binding, which
-    # launches on torch's current stream (the stream the events record on).
-    def g_dt():
-        dma.dt(V, W, A, bias, out=dt)
-
-    def g_select():
-        dma.select(dt, wl_p.w, tau=tau, tie=tie)
-
-    def g_attn():
-        dma.attn_fwd(Q, K, V, dt, tau, tie, wl_p.w, out=O)
-
     def g_dt_append():
         dma.dt(v_new, Wd, Ad, biasd, out=dt_cache, out_pos=pos)
 
     def g_decode():
         dma.decode(q, Kc, Vc, dt_cache, lens, wl_d.w, out=out, workspace=ws)
 
-    def capture(*fns):
-        for f in fns:
-            f()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for f in fns:
-                f()
-        torch.cuda.synchronize()
-        return g
-
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
     # One step: evict, the three prefill calls back to back, evict, the two
-    # decode calls.  The eviction keeps the GPU busy for ~0.14 ms while Python
-    # enqueues what follows, so the events see GPU work rather than host
-    # launch latency (host_enqueue_ms_per_step reports the enqueue time).
-    PRE = (g_dt, g_select, g_attn)
+    # decode calls.
+    PRE = (P5.g_dt, P5.g_select, P5.g_attn)
     DEC = (g_dt_append, g_decode)
     host_ms = []
 
@@ -407,6 +479,7 @@ def main():
             e[3].record()
         host_ms.append((time.perf_counter() - h0) * 1e3)
 
+    progress(f"steps: {args.warmup} warm-up, {args.steps} timed")
     for _ in range(args.warmup):
         step()
     evs = [[ev() for _ in range(4)] for _ in range(args.steps)]
@@ -422,69 +495,35 @@ def main():
     ms_pre = float(np.mean(pre_each))
     ms_dec = float(np.mean(dec_each))
 
-    # Average launch duration per call: after an eviction, R back-to-back
-    # launches of one call between two events, ROUNDS times.  Each launch
-    # reads its own copy of the inputs, rotating over enough copies that the
-    # data read in between exceeds the 256 MB last-level cache, so that every
-    # launch reads from HBM as in the steps above.
-    R, ROUNDS = 12, 5
-    NPRE = 20    # prefill input sets of ~16.4 MB
+    # Per-launch times of every call (rotating input copies, see Prefill).
+    progress("per-launch: padded prefill")
+    P5.make_sets()
+    avg5, host5 = per_launch_ms((("dt", P5.c_dt), ("select", P5.c_select), ("attn_fwd", P5.c_attn)),
+                                evict, R=6, rounds=4)
+    # the prologue upstream of dt (Q/K RMSNorm + rotary, then dt), in place on
+    # the rotating copies; timed after attn_fwd, whose inputs it rewrites
+    wq5, wk5 = (to_dev(x, dev) for x in si.make_norm_weights(wl_p.d, wl_p.dtype, wl_p.seed + 7))
+
+    def c_prologue5():
+        q_, k_, v_, d, _, _ = P5.nxt()
+        dma.prologue(q_, k_, v_, wq5, wk5, P5.W, P5.A, P5.bias, Q_out=q_, K_out=k_, dt_out=d)
+    pro5, _ = per_launch_ms((("prologue", c_prologue5),), evict, R=6, rounds=3)
+    P5.drop_sets()
+
+    progress("per-launch: decode")
     NDEC = 4     # decode caches (~134 MB of kept rows each)
-    pre_sets = [(Q, K, V, dt, tau, tie)] + [
-        tuple(t.clone() for t in (Q, K, V, dt, tau, tie)) for _ in range(NPRE - 1)]
-    dec_sets = [(Kc, Vc, dt_cache)] + [
-        tuple(t.clone() for t in (Kc, Vc, dt_cache)) for _ in range(NDEC - 1)]
+    dec_sets = [(Kc, Vc, dt_cache)] + [tuple(t.clone() for t in (Kc, Vc, dt_cache)) for _ in range(NDEC - 1)]
     rot = [0]
 
-    def nxt(sets):
+    def nxt_dec():
         rot[0] += 1
-        return sets[rot[0] % len(sets)]
-
-    def c_dt():
-        _, _, v, d, _, _ = nxt(pre_sets)
-        dma.dt(v, W, A, bias, out=d)
-
-    def c_select():
-        _, _, _, d, ta, ti = nxt(pre_sets)
-        dma.select(d, wl_p.w, tau=ta, tie=ti)
-
-    def c_attn():
-        q_, k_, v_, d, ta, ti = nxt(pre_sets)
-        dma.attn_fwd(q_, k_, v_, d, ta, ti, wl_p.w, out=O)
+        return dec_sets[rot[0] % NDEC]
 
     def c_dt_append():
-        dma.dt(v_new, Wd, Ad, biasd, out=nxt(dec_sets)[2], out_pos=pos)
-
-    # The prologue upstream of dt (Q/K RMSNorm + rotary, then dt), in place on
-    # the rotating input sets; timed after attn_fwd, whose inputs it rewrites.
-    wq, wk = (to_dev(x, dev) for x in si.make_norm_weights(wl_p.d, wl_p.dtype, wl_p.seed + 7))
-
-    def c_qk_norm_rope():
-        q_, k_, _, _, _, _ = nxt(pre_sets)
-        dma.qk_norm_rope(q_, k_, wq, wk, Q_out=q_, K_out=k_)
-
-    def c_prologue():
-        q_, k_, v_, d, _, _ = nxt(pre_sets)
-        dma.prologue(q_, k_, v_, wq, wk, W, A, bias, Q_out=q_, K_out=k_, dt_out=d)
-
-    # The backward of the prefill (attention gradients, then the dt chain's),
-    # on the rotating input sets with one upstream gradient dO.
-    dO = torch.randn_like(Q)
-    ws_b = torch.empty(dma.attn_bwd_workspace_bytes(wl_p.B, wl_p.S, wl_p.Hq, wl_p.Hkv, wl_p.d, wl_p.w),
-                       dtype=torch.uint8, device=dev)
-    ws_db = torch.empty(dma.dt_bwd_workspace_bytes(wl_p.B, wl_p.S, wl_p.Hkv, wl_p.d), dtype=torch.uint8, device=dev)
-    g_out = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V), torch.empty_like(dt))
-
-    def c_attn_bwd():
-        q_, k_, v_, d, ta, ti = nxt(pre_sets)
-        dma.attn_bwd(q_, k_, v_, d, ta, ti, wl_p.w, dO, workspace=ws_b, out=g_out)
-
-    def c_dt_bwd():
-        _, _, v_, _, _, _ = nxt(pre_sets)
-        dma.dt_bwd(v_, W, A, g_out[3], bias, dV=g_out[2], workspace=ws_db)
+        dma.dt(v_new, Wd, Ad, biasd, out=nxt_dec()[2], out_pos=pos)
 
     def c_decode():
-        kc, vc, dc = nxt(dec_sets)
+        kc, vc, dc = nxt_dec()
         dma.decode(q, kc, vc, dc, lens, wl_d.w, out=out, workspace=ws)
 
     # The incremental decode: the state of the cache without its last token
@@ -503,37 +542,61 @@ def main():
         rot_st[0] += 1
         dma.decode_step(q, k_last, v_last, dt_last, states[rot_st[0] % NST], out=out, workspace=ws_step)
 
-    calls = (("dt", c_dt), ("select", c_select), ("attn_fwd", c_attn),
-             ("dt_append", c_dt_append), ("decode", c_decode), ("decode_step", c_decode_step),
-             ("attn_bwd", c_attn_bwd), ("dt_bwd", c_dt_bwd),
-             ("qk_norm_rope", c_qk_norm_rope), ("prologue", c_prologue))
-    avg, host_launch_ms = {}, {}
-    for n, f in calls:
-        f()                         # the first launch of a kernel loads its code
-        torch.cuda.synchronize()
-        pairs = []
-        hs = []
-        for _ in range(ROUNDS):
-            evict()
-            evict()                 # ~0.28 ms for the host to enqueue the R launches
-            a, b = ev(), ev()
-            a.record()
-            h0 = time.perf_counter()
-            for _ in range(R):
-                f()
-            hs.append((time.perf_counter() - h0) * 1e3 / R)
-            b.record()
-            pairs.append((a, b))
-        torch.cuda.synchronize()
-        avg[n] = float(np.mean([a.elapsed_time(b) for a, b in pairs])) / R
-        host_launch_ms[n] = float(np.mean(hs))
-    del pre_sets, dec_sets, states
+    avg_d, host_d = per_launch_ms((("dt_append", c_dt_append), ("decode", c_decode),
+                                   ("decode_step", c_decode_step)), evict, R=12, rounds=5)
+    del dec_sets, states
 
-    # The same prefill replayed as one HIP graph (one launch for three
+    progress("per-launch: long and c2 prefill, backward, prologue")
+    P3 = Prefill(dma, "long", dev)
+    P3.make_sets()
+    avg3, _ = per_launch_ms((("dt", P3.c_dt), ("select", P3.c_select), ("attn_fwd", P3.c_attn)),
+                            evict, R=8, rounds=4)
+    P3.drop_sets()
+    P2 = Prefill(dma, "c2", dev)
+    P2.make_sets()
+    wl2 = P2.wl
+    wq, wk = (to_dev(x, dev) for x in si.make_norm_weights(wl2.d, wl2.dtype, wl2.seed + 7))
+
+    def c_qk_norm_rope():
+        q_, k_, _, _, _, _ = P2.nxt()
+        dma.qk_norm_rope(q_, k_, wq, wk, Q_out=q_, K_out=k_)
+
+    def c_prologue():
+        q_, k_, v_, d, _, _ = P2.nxt()
+        dma.prologue(q_, k_, v_, wq, wk, P2.W, P2.A, P2.bias, Q_out=q_, K_out=k_, dt_out=d)
+
+    dO = torch.randn_like(P2.Q)
+    ws_b = torch.empty(dma.attn_bwd_workspace_bytes(wl2.B, wl2.S, wl2.Hq, wl2.Hkv, wl2.d, wl2.w),
+                       dtype=torch.uint8, device=dev)
+    ws_db = torch.empty(dma.dt_bwd_workspace_bytes(wl2.B, wl2.S, wl2.Hkv, wl2.d), dtype=torch.uint8, device=dev)
+    g_out = (torch.empty_like(P2.Q), torch.empty_like(P2.K), torch.empty_like(P2.V), torch.empty_like(P2.dt))
+
+    def c_attn_bwd():
+        q_, k_, v_, d, ta, ti = P2.nxt()
+        dma.attn_bwd(q_, k_, v_, d, ta, ti, wl2.w, dO, workspace=ws_b, out=g_out)
+
+    def c_dt_bwd():
+        _, _, v_, _, _, _ = P2.nxt()
+        dma.dt_bwd(v_, P2.W, P2.A, g_out[3], P2.bias, dV=g_out[2], workspace=ws_db)
+
+    avg2, host2 = per_launch_ms((("dt", P2.c_dt), ("select", P2.c_select), ("attn_fwd", P2.c_attn),
+                                 ("attn_bwd", c_attn_bwd), ("dt_bwd", c_dt_bwd),
+                                 ("qk_norm_rope", c_qk_norm_rope), ("prologue", c_prologue)),
+                                evict, R=12, rounds=5)
+    P2.drop_sets()
+
+    # The padded prefill replayed as one HIP graph (one launch for three
     # kernels), timed after an eviction in the same way; reported beside.
-    G_pre = capture(g_dt, g_select, g_attn)
+    for f in PRE:
+        f()
+    torch.cuda.synchronize()
+    G_pre = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(G_pre):
+        for f in PRE:
+            f()
+    torch.cuda.synchronize()
     gpairs = []
-    for _ in range(args.steps):
+    for _ in range(max(3, args.steps // 2)):
         evict()
         a, b = ev(), ev()
         a.record()
@@ -543,17 +606,19 @@ def main():
     torch.cuda.synchronize()
     ms_pre_graph = float(np.mean([a.elapsed_time(b) for a, b in gpairs]))
 
-    flops = kept_flops(wl_p.B, wl_p.Hq, wl_p.S, wl_p.d, wl_p.w)
+    flops = P5.flops
     value = flops / (ms_pre * 1e-3) / 1e12
     dbytes = decode_bytes(wl_d.B, wl_d.Hq, wl_d.Hkv, wl_d.d, wl_d.w, dec["cache_lens"])
-    dec_gbs = dbytes / (avg["decode"] * 1e-3) / 1e9
-    attn_tflops = flops / (avg["attn_fwd"] * 1e-3) / 1e12
+    dec_gbs = dbytes / (avg_d["decode"] * 1e-3) / 1e9
+    attn_tflops = flops / (avg5["attn_fwd"] * 1e-3) / 1e12
     sbytes = decode_state_bytes_moved(wl_d.B, wl_d.Hq, wl_d.Hkv, wl_d.d, wl_d.w, pos.cpu().numpy())
-    step_gbs = sbytes / (avg["decode_step"] * 1e-3) / 1e9
-    pbytes = prologue_bytes(wl_p.B, wl_p.S, wl_p.Hq, wl_p.Hkv, wl_p.d)
-    pro_gbs = pbytes / (avg["prologue"] * 1e-3) / 1e9
-    ms_bwd = avg["attn_bwd"] + avg["dt_bwd"]
-    bwd_tflops = 2.5 * flops / (ms_bwd * 1e-3) / 1e12
+    step_gbs = sbytes / (avg_d["decode_step"] * 1e-3) / 1e9
+    pbytes2 = prologue_bytes(wl2.B, wl2.S, wl2.Hq, wl2.Hkv, wl2.d)
+    pbytes5 = prologue_bytes(wl_p.B, wl_p.S, wl_p.Hq, wl_p.Hkv, wl_p.d)
+    ms_bwd = avg2["attn_bwd"] + avg2["dt_bwd"]
+    bwd_tflops = 2.5 * P2.flops / (ms_bwd * 1e-3) / 1e12
+    traffic_ok = ATTN_TRAFFIC["bytes"] is not None and \
+        ATTN_TRAFFIC["sources_sha256"] == sources_sha256(ATTN_SOURCES)
 
     line = {
         "metric": "DMA prefill kept-key TFLOP/s + decode GB/s, % of MI355X roofline",
@@ -567,59 +632,72 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) Q/K/V, N(0,0.02) dt_proj, A~U(-2,2))",
+        "data": "synthetic (seeded N(0,1) Q/K/V, N(0,0.02) dt_proj, A~U(-2,2), lengths ~U[16384,32768])",
         "config": {
-            "workload": "prefill B4 Hq8 Hkv4 S2048 d64 w512 (dt+select+attn) + decode B64 L16384 Hq8 Hkv2 "
-                        "d128 w2048 (dt append + decode)",
+            "workload": workload_name(wl_p) + " (dt+select+attn) + decode B64 L16384 Hq8 Hkv2 d128 w2048 "
+                        "(dt append + decode)",
             "prefill_kept_flops": flops,
+            "prefill_lengths": [int(x) for x in P5.inp["seqlens"]],
             "decode_bytes": dbytes,
         },
         "roofline": {
-            "bound": "mfma", "kernel": "dma_attn_fwd (attn_bf16_kernel<64>)",
+            "bound": "mfma", "kernel": "dma_attn_fwd (attn_bf16_kernel<128>) on the padded workload",
             "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "ms_per_launch": round(avg["attn_fwd"], 5), "flop_per_launch": flops,
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 5),
-            "traffic": (ATTN_TRAFFIC["bytes"]
-                        if ATTN_TRAFFIC["sources_sha256"] == sources_sha256(ATTN_SOURCES) else None),
+            "traffic": ATTN_TRAFFIC["bytes"] if traffic_ok else None,
+            "ms_per_launch": round(avg5["attn_fwd"], 5), "flop_per_launch": flops,
         },
+        "prefill_configs": {"padded": P5.summary(avg5), "long": P3.summary(avg3),
+                            "c2": P2.summary({k: avg2[k] for k in ("dt", "select", "attn_fwd")})},
         "decode": {
             "value": round(dec_gbs, 2), "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS,
-            "frac": round(dec_gbs / PEAK_HBM_GBS, 5),
+            "frac": round(dec_gbs / PEAK_HBM_GBS, 5), "bytes": dbytes, "ms": round(avg_d["decode"], 5),
         },
         "decode_incremental": {
             "value": round(step_gbs, 2), "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS,
-            "frac": round(step_gbs / PEAK_HBM_GBS, 5), "bytes": sbytes, "ms": round(avg["decode_step"], 5),
-            "tokens_per_s": round(wl_d.B / (avg["decode_step"] * 1e-3), 1),
+            "frac": round(step_gbs / PEAK_HBM_GBS, 5), "bytes": sbytes, "ms": round(avg_d["decode_step"], 5),
+            "tokens_per_s": round(wl_d.B / (avg_d["decode_step"] * 1e-3), 1),
             "note": "dma_decode_step: kept set carried across steps, the kept K/V rows stored compactly",
         },
         "prologue": {
-            "value": round(pro_gbs, 2), "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS,
-            "frac": round(pro_gbs / PEAK_HBM_GBS, 5), "bytes": pbytes, "ms": round(avg["prologue"], 5),
-            "note": "dma_prologue on the prefill workload, in place: Q/K RMSNorm + rotary, then dt",
+            "padded": {"value": round(pbytes5 / (pro5["prologue"] * 1e-3) / 1e9, 2), "unit": "GB/s",
+                       "frac": round(pbytes5 / (pro5["prologue"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
+                       "bytes": pbytes5, "ms": round(pro5["prologue"], 5)},
+            "c2": {"value": round(pbytes2 / (avg2["prologue"] * 1e-3) / 1e9, 2), "unit": "GB/s",
+                   "frac": round(pbytes2 / (avg2["prologue"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
+                   "bytes": pbytes2, "ms": round(avg2["prologue"], 5)},
+            "bound": "hbm", "peak": PEAK_HBM_GBS,
+            "note": "dma_prologue in place: Q/K RMSNorm + rotary, then dt",
         },
         "backward": {
             "value": round(bwd_tflops, 3), "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
-            "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 5), "flops": 2.5 * flops, "ms": round(ms_bwd, 5),
-            "note": "dma_attn_bwd + dma_dt_bwd on the prefill workload; kept-key flops of the five products "
+            "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 5), "flops": 2.5 * P2.flops, "ms": round(ms_bwd, 5),
+            "note": "dma_attn_bwd + dma_dt_bwd on the c2 workload; kept-key flops of the five products "
                     "(scores, dp, dq, dk, dv) = 2.5x the forward's",
         },
         "ms_prefill": round(ms_pre, 5),
         "ms_decode_step": round(ms_dec, 5),
         "step_ms_percentiles": {
-            n: {q: round(float(np.percentile(v, int(q[1:]))), 5) for q in ("p10", "p50", "p90")}
+            n: {q_: round(float(np.percentile(v, int(q_[1:]))), 5) for q_ in ("p10", "p50", "p90")}
             for n, v in (("prefill", pre_each), ("decode", dec_each))},
-        "kernel_ms_avg": {n: round(v, 5) for n, v in avg.items()},
+        "kernel_ms_avg": {"padded": {k: round(v, 5) for k, v in avg5.items()},
+                          "decode": {k: round(v, 5) for k, v in avg_d.items()},
+                          "c2": {k: round(v, 5) for k, v in avg2.items()}},
         "ms_prefill_as_one_graph": round(ms_pre_graph, 5),
         "host_enqueue_ms_per_step": round(float(np.mean(host_ms)), 4),
-        "host_ms_per_launch": {n: round(v, 5) for n, v in host_launch_ms.items()},
+        "host_ms_per_launch": {**{f"padded_{k}": round(v, 5) for k, v in host5.items()},
+                               **{f"decode_{k}": round(v, 5) for k, v in host_d.items()},
+                               **{f"c2_{k}": round(v, 5) for k, v in host2.items()}},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
     }
-    line["window_variant"] = window_breakdown(dma, dev, evict)
-    line["cdmoe"] = cdmoe_breakdown(dma, dev, evict)
-    if args.other_configs:
-        line["other_configs"] = {n: prefill_breakdown(dma, n, dev, evict) for n in ("long", "padded")}
+    del P3, P2
+    if not args.no_variants:
+        progress("variants: sliding window, CDMoE")
+        line["window_variant"] = window_breakdown(dma, dev, evict)
+        line["cdmoe"] = cdmoe_breakdown(dma, dev, evict)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(pre, wl_p)
+        progress("cpu baseline: the oracle on a row sample of the padded prefill")
+        line["cpu_baseline"] = cpu_baseline(P5.inp, wl_p)
     print(json.dumps(line), flush=True)
 
 
