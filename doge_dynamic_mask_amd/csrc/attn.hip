@@ -97,12 +97,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     static_assert(kBK * RV % kThreads == 0, "block staging split");
     static_assert(4 * (kCarrySlots + 1) <= 64 && 4 * (kCarrySlots + 1) <= 4 * kMaxSteps, "carry scan");
     __shared__ __align__(16) int c_idx[kCap];
-    __shared__ __align__(16) float c_dtl[kCap];     // dt * log2(e)
+    __shared__ __align__(16) float c_dtl[kCap];     // (dt - dref) * log2(e); raw dt while filling
     __shared__ __align__(16) int c_lo[kPartCap];    // masked region: first tile row keeping the key
     __shared__ __align__(16) int c_span[kPartCap];  // masked region: rows keeping it
     __shared__ uint64_t thr[kRowsPerWG];            // threshold key of each tile row
     __shared__ uint32_t cnt[kMaxSteps * 4];         // per (fill step, wave): full | partial << 16
     __shared__ int fill_info[3];                    // steps used, full count, partial count
+    __shared__ float red_max[kThreads / 64];        // per-wave maxima of the candidates' dt
     __shared__ __align__(16) uint16_t Ks[kBK * T::KP];
     __shared__ __align__(16) uint16_t Vs[kBK * T::VP];
 
@@ -225,6 +226,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         for (int t = tid; t < nrows; t += kThreads) thr[t] = selkey(tau[urow + i0 + t], (uint32_t)tie[urow + i0 + t]);
 
         float mrow = -INFINITY, lrow = 0.f;
+        float dref = 0.f;  // reference dt of the tile (set with its first round of candidates)
         f32x16 oacc[D / 32];
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
@@ -281,10 +283,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                     const int op = nF + (int)(base >> 16) + (int)__popcll(__ballot(cc[q] == 2) & lt_mask);
                     if (cc[q] == 1) {
                         c_idx[of] = jc[q];
-                        c_dtl[of] = dc[q] * kLog2e;
+                        c_dtl[of] = dc[q];
                     } else if (cc[q] == 2) {
                         c_idx[op] = jc[q];
-                        c_dtl[op] = dc[q] * kLog2e;
+                        c_dtl[op] = dc[q];
                     }
                 }
                 scan = i_last + 1;
@@ -360,11 +362,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                         const int j = jb + e;
                         if (c[e] == 1) {
                             c_idx[of] = j;
-                            c_dtl[of] = dv[bb][e] * kLog2e;
+                            c_dtl[of] = dv[bb][e];
                             ++of;
                         } else if (c[e] == 2) {
                             c_idx[op] = j;
-                            c_dtl[op] = dv[bb][e] * kLog2e;
+                            c_dtl[op] = dv[bb][e];
                             ++op;
                         }
                     }
@@ -386,6 +388,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
             const int pbase = nF / kBK * kBK;           // first block holding a partial key
             const int npad = (n + kBK - 1) / kBK * kBK;
             __syncthreads();
+            // The dt bias enters each score relative to dref, the largest dt
+            // among the keys kept by every row of the tile (a shift common to
+            // every key of a row leaves its softmax unchanged).  Every row
+            // keeps that key, so its own largest kept dt is at least dref:
+            // the keys that carry a row's weight have dt - dref small (exact
+            // in float32 when within a factor 2 of dref) and never larger
+            // than dt itself, so a large dt shared by the kept keys does not
+            // swallow the query-key term.  dref is fixed by the tile's first
+            // round of candidates (every round of a row must use one shift;
+            // the first round's full keys are still kept by every row).
+            if (rounds == 1) {
+                float mx = -INFINITY;
+                for (int k = tid; k < nF; k += kThreads) mx = fmaxf(mx, c_dtl[k]);
+                mx = wave_max(mx);
+                if (lane == 0) red_max[wave] = mx;
+                __syncthreads();
+                dref = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
+                if (!(dref > -INFINITY && dref < INFINITY)) dref = 0.f;
+            }
+            for (int k = tid; k < n; k += kThreads) c_dtl[k] = (c_dtl[k] - dref) * kLog2e;
             // row runs of the masked region: a partial key j is kept on the tile
             // rows [lo, lo + span) (by nesting a run: from its own row, or from
             // i0, until the first row whose threshold passes it); full keys
@@ -584,6 +606,16 @@ __global__ __launch_bounds__(kThreads) void attn_rowwise_kernel(
         qv[u] = e < d ? Elem<Tin>::load(Q, obase + e) : 0.f;
         acc[u] = 0.f;
     }
+    // the bias enters relative to the largest kept dt of the row (a shift
+    // common to all its keys leaves the softmax unchanged), so a large dt
+    // shared by the kept keys does not swallow q.k in float32
+    float dref = -INFINITY;
+    for (int j = lane; j <= i; j += 64) {
+        const float dj = dt[urow + j];
+        if (kept_test(dj, j, ti, ki)) dref = fmaxf(dref, dj);
+    }
+    dref = wave_max(dref);
+    if (!(dref > -INFINITY && dref < INFINITY)) dref = 0.f;
     float mrow = -INFINITY, lrow = 0.f;
     for (int j = 0; j <= i; ++j) {
         const float dj = dt[urow + j];
@@ -595,7 +627,7 @@ __global__ __launch_bounds__(kThreads) void attn_rowwise_kernel(
             const int e = lane + 64 * u;
             if (e < d) part = fmaf(qv[u], Elem<Tin>::load(K, kb + e), part);
         }
-        const float zz = fmaf(wave_sum(part), qscale, dj * kLog2e);
+        const float zz = fmaf(wave_sum(part), qscale, (dj - dref) * kLog2e);
         const float mnew = fmaxf(mrow, zz);
         const float alpha = exp2f(mrow - mnew);
         const float p = exp2f(zz - mnew);

@@ -137,6 +137,8 @@ def make_dt(shape, kind: str, seed: int) -> np.ndarray:
       const      every value 1.0 (all keys tie)
       few        values from a set of 5: heavy ties
       wide       log-uniform over [2^-20, 2^20]
+      shared     2^18 + U(0, 4): a large dt common to every key, so the
+                 scores' differences come from q.k and a small spread of dt
     """
     rng = np.random.default_rng(seed)
     if kind == "lognormal":
@@ -149,6 +151,8 @@ def make_dt(shape, kind: str, seed: int) -> np.ndarray:
         x = rng.choice(np.array([0.25, 0.5, 1.0, 1.5, 3.0]), size=shape)
     elif kind == "wide":
         x = 2.0 ** rng.uniform(-20.0, 20.0, size=shape)
+    elif kind == "shared":
+        x = 2.0 ** 18 + rng.uniform(0.0, 4.0, size=shape)
     else:
         raise ValueError(kind)
     return np.ascontiguousarray(x, dtype=np.float32)

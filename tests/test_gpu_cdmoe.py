@@ -64,9 +64,15 @@ def test_experts(dma, oracle_mod, T, H, nk, k):
 
 def test_chain_at_config_size(dma, oracle_mod):
     """logits -> route -> experts at the DogeConfig sizes (hidden 1024,
-    16384 experts, 64 per token) against the whole oracle.  Tokens whose
-    expert list depends on a logit difference below float32 resolution may
-    differ; every other token must match the oracle's list exactly."""
+    16384 experts, 64 per token) against the whole fp64 oracle.
+    The routing decision is taken in float32 on both sides: the oracle's
+    routing of the GPU's float32 logits must give the GPU's expert lists
+    for every token.  Against the fp64 chain, a token's list may differ only
+    where the fp64 pair scores leave no float32-resolvable gap at the k-th
+    place: its k-th and (k+1)-th best pair scores (over all nk*nk pairs) lie
+    within twice the token's largest logit error plus float32 rounding, and
+    every expert in only one of the two lists scores within that margin of
+    the k-th.  Every token whose list agrees is output-checked."""
     T, H, nk, k = 256, 1024, 128, 64
     h, router, down, up = si.make_cdmoe(T, H, nk, "bf16", seed=12)
     hd = to_dev(h)
@@ -74,9 +80,23 @@ def test_chain_at_config_size(dma, oracle_mod):
     idx, w = dma.cdmoe_route(lg, k)
     out = dma.cdmoe_experts(hd, to_dev(down), to_dev(up), idx, w)
     torch.cuda.synchronize()
+    gl, gi, go = to_host(lg), to_host(idx), to_host(out)
+    # the decision in the kernel's precision: exact for every token
+    fi, _ = oracle_mod.cdmoe_route(gl, k)
+    np.testing.assert_array_equal(gi, fi)
+    # against the fp64 chain
     ri, rw, ro = oracle_mod.cdmoe(h, router, down, up, k)
-    gi, go = to_host(idx), to_host(out)
+    rl = oracle_mod.cdmoe_logits(h, router)
     same = (gi == ri).all(axis=1)
-    assert same.mean() >= 0.95, same.mean()
+    for t in np.nonzero(~same)[0]:
+        x, y = rl[t, :nk], rl[t, nk:]
+        scores = (x[:, None] + y[None, :]).ravel()          # expert a*nk + b scores x_a + y_b
+        srt = np.sort(scores)[::-1]
+        err = np.abs(gl[t].astype(np.float64) - rl[t]).max()
+        margin = 2.0 * err + 4.0 * np.spacing(np.float32(abs(srt[k - 1])))
+        assert srt[k - 1] - srt[k] <= margin, (t, srt[k - 1] - srt[k], margin)
+        diff = np.setxor1d(gi[t], ri[t])
+        assert (np.abs(scores[diff] - srt[k - 1]) <= margin).all(), (t, diff)
+    assert same.sum() > 0
     bound = 2.0 ** -8 * np.abs(ro[same]) + 1e-4 * np.abs(ro).max()
     assert (np.abs(go[same] - ro[same]) <= bound).all()

@@ -128,6 +128,18 @@ def test_select_bit_exact(dma, oracle_mod, B, Hkv, S, w, kind, padded):
     np.testing.assert_array_equal(to_host(tau), rt)
 
 
+def test_select_long_every_row(dma, oracle_mod):
+    """The long workload (B1 Hkv8 S8192 w2048) from its own value states: the
+    threshold pair of every row against the oracle fed the GPU's dt."""
+    wl = si.WORKLOADS["long"]
+    inp = full_inputs("long")
+    dt = dma.dt(to_dev(inp["V"]), to_dev(inp["W"]), to_dev(inp["A"]), to_dev(inp["bias"]))
+    tau, tie = dma.select(dt, wl.w)
+    rt, ri = oracle_mod.select(to_host(dt), wl.w)
+    np.testing.assert_array_equal(to_host(tie), ri)
+    np.testing.assert_array_equal(to_host(tau), rt)
+
+
 @pytest.mark.parametrize("name,kind", [("c2", "lognormal"), ("long", "dyadic"), ("padded", "lognormal"),
                                        ("long", "few")])
 def test_select_full_size_sampled(dma, oracle_mod, name, kind):
@@ -170,6 +182,14 @@ ATTN_CASES = [
     ("bf16", 3, 257, 2, 2, 64, 20, "wide", False),
     ("bf16", 2, 700, 8, 2, 128, 33, "wide", True),
     ("bf16", 1, 2600, 4, 1, 64, 2500, "lognormal", True),
+    # a large dt shared by every key (2^18 + U(0, 4)): a score formed as
+    # q.k + dt in float32 keeps q.k only to about 0.03, so the bias must
+    # enter relative to a reference near the kept keys' dt
+    ("bf16", 2, 600, 8, 2, 128, 64, "shared", True),
+    ("bf16", 1, 500, 4, 4, 64, 100, "shared", False),
+    ("bf16", 1, 1200, 8, 1, 128, 1000, "shared", False),
+    ("f32", 1, 300, 2, 1, 64, 64, "shared", False),
+    ("f32", 2, 200, 4, 2, 128, 150, "shared", True),
 ]
 
 
@@ -395,8 +415,9 @@ def test_decode_state_steps(dma, oracle_mod, B, Hq, Hkv, d, w, lens, kind):
 
 def test_decode_state_full_size(dma, oracle_mod):
     """The decode workload: the state of the cache without its last token, then
-    one step with that token, against dma_decode of the whole cache (kept sets
-    exactly, outputs within tolerance) and the oracle on sampled batches."""
+    one step with that token, against dma_decode of the whole cache and the
+    oracle's decode of it, every batch (kept sets exactly, outputs within
+    tolerance)."""
     wl = si.WORKLOADS["decode"]
     inp = full_inputs("decode")
     dtc = si.make_dt((wl.B, wl.Hkv, wl.S), "lognormal", seed=91)
@@ -414,9 +435,11 @@ def test_decode_state_full_size(dma, oracle_mod):
     assert (slens == lens[:, None]).all()
     got = to_host(out).astype(np.float64)
     assert np.abs(got - to_host(ref)).max() <= 2e-2
-    bs = [0, 17, 63]
-    r, _ = oracle_mod.decode(inp["q"][bs], inp["Kc"][bs], inp["Vc"][bs], dtc[bs], lens[bs], wl.w)
-    assert np.abs(got[bs] - r).max() <= 2e-2
+    # every batch against the oracle's decode of the whole cache: kept sets
+    # exactly, outputs within the bf16 bar
+    r, rkept = oracle_mod.decode(inp["q"], inp["Kc"], inp["Vc"], dtc, lens, wl.w)
+    np.testing.assert_array_equal(kept, rkept)
+    assert np.abs(got - r).max() <= 2e-2
 
 
 def test_decode_matches_last_prefill_row(dma, oracle_mod):
