@@ -329,7 +329,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
         fetch(x0 + kBlk < n ? x0 + kBlk : 0);  // the next block, or pass 2's first
         float z[4][4];
         f32x4 dp[4];
+        // wave priority 3 while forming scores, 1 for the gradient products,
+        // 0 in the vector work between them (the waves of a SIMD then
+        // interleave their phases)
+        __builtin_amdgcn_s_setprio(3);
         scores(x0 + kBlk <= nF, z, dp);  // rows past the length: results unused
+        __builtin_amdgcn_s_setprio(0);
         float mb = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -380,7 +385,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
         if (x0 + kBlk < n) fetch(x0 + kBlk);
         float z[4][4];
         f32x4 dp[4], ds[4];
+        __builtin_amdgcn_s_setprio(3);
         scores(x0 + kBlk <= nF, z, dp);
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -389,12 +396,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
                 ds[mt][r] = p * (dp[mt][r] - dd);
             }
         }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const bf16x8 bop = acc_operand(ds[2 * s2], ds[2 * s2 + 1]);
 #pragma unroll
             for (int t = 0; t < D / 16; ++t) dq[t] = mfma16(tr_operand<P>(Ks, 32 * s2, 16 * t, lane), bop, dq[t]);
         }
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();
     }
 
@@ -571,11 +580,13 @@ __global__ __launch_bounds__(NG * kThreads) void attn_bwd_kv_kernel(
             for (int th = 0; th < 2; ++th) {
                 const int t = 2 * s2 + th;
                 f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+                __builtin_amdgcn_s_setprio(3);
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
                     sacc = mfma16(ld8(&Qg[(16 * t + kk) * P + 32 * s + 8 * q]), kb[s], sacc);
                     dp = mfma16(ld8(&Og[(16 * t + kk) * P + 32 * s + 8 * q]), vb[s], dp);
                 }
+                __builtin_amdgcn_s_setprio(0);
                 const float4 l4 = *reinterpret_cast<const float4 *>(&lse_g[16 * t + 4 * q]);
                 const float4 d4 = *reinterpret_cast<const float4 *>(&dd_g[16 * t + 4 * q]);
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
@@ -590,11 +601,13 @@ __global__ __launch_bounds__(NG * kThreads) void attn_bwd_kv_kernel(
             }
             const bf16x8 pbf = acc_operand(pm[0], pm[1]);
             const bf16x8 sbf = acc_operand(dsm[0], dsm[1]);
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 dva[t] = mfma16(tr_operand<P>(Og, 32 * s2, 16 * t, lane), pbf, dva[t]);
                 dka[t] = mfma16(tr_operand<P>(Qg, 32 * s2, 16 * t, lane), sbf, dka[t]);
             }
+            __builtin_amdgcn_s_setprio(0);
         }
     };
 
