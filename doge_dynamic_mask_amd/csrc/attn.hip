@@ -51,7 +51,6 @@ constexpr int kBatchSteps = 8;   // fill steps whose loads are issued together
 constexpr int kPartCap = 2 * kRowsPerWG + 2 * kBK;  // slots of the masked region
 constexpr int kCarrySlots = kCap / kThreads;         // carried candidates per thread
 constexpr int kTargetItems = 4096;                   // work items a launch aims for
-constexpr int kChunk = 8;                            // consecutive groups of one unit per XCD chunk
 
 template <int D>
 struct Tiles {
@@ -75,6 +74,43 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t *p) {
         (__attribute__((address_space(3))) i16x4 *)(p));
 }
 
+// Valid tile groups of batch b (those holding a row below L_b).
+__device__ __forceinline__ int valid_groups(const int32_t *seqlens, int b, int S, int Bq, int tpw) {
+    const int Lb = clamp_len(seqlens, b, S);
+    return ((Lb + Bq - 1) / Bq + tpw - 1) / tpw;
+}
+
+// Wave 0: the batch holding item k when batch b holds cnt(b) * Hkv items
+// (items ordered by batch, then kv head, then group), and k's place in it.
+template <typename F>
+__device__ __forceinline__ void locate_item(long long k, int B, int Hkv, int lane, F cnt, int &b_out,
+                                            long long &off_out) {
+    long long base = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        const int bb = b0 + lane;
+        long long c = bb < B ? (long long)cnt(bb) * Hkv : 0;
+        long long incl = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const long long y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        const long long tot = __shfl(incl, 63, 64);
+        if (k < base + tot) {
+            // the first lane whose inclusive count passes k
+            const unsigned long long m = __ballot(bb < B && base + incl > k);
+            const int src = __ffsll((long long)m) - 1;
+            const long long excl = __shfl(incl - c, src, 64);
+            b_out = b0 + src;
+            off_out = k - base - excl;
+            return;
+        }
+        base += tot;
+    }
+    b_out = -1;
+    off_out = 0;
+}
+
 // Upper bound: first t in [lo, n) with thr[t] > key (thr nondecreasing), else n.
 __device__ __forceinline__ int first_row_above(const uint64_t *thr, int lo, int n, uint64_t key) {
     int a = lo, b = n;
@@ -90,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const float *__restrict__ dt, const float *__restrict__ tau, const int32_t *__restrict__ tie,
     const int32_t *__restrict__ seqlens, int S, int Hq, int Hkv, int G, int Bq, int ntiles, int tpw,
-    int nunits, uint16_t *__restrict__ O, float qscale) {
+    int B, uint16_t *__restrict__ O, float qscale) {
     using T = Tiles<D>;
     constexpr int RV = D / 8;                    // 16-byte vectors per K/V row
     constexpr int NL = kBK * RV / kThreads;      // K (and V) vectors per thread per block
@@ -109,27 +145,64 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int h = lane >> 5, ql = lane & 31;
-    // Work item = (unit (batch, kv head), group of tpw consecutive query
-    // tiles).  Each unit's groups are cut into chunks of kChunk consecutive
-    // groups, and workgroup ids go round-robin over the 8 XCDs, so the k-th
-    // workgroup of XCD x takes group k % kChunk of the chunk with rank
-    // 8 * (k / kChunk) + x.  Chunk ranks run over row position first and
-    // rotate the unit with it, so every XCD gets an equal share of every
-    // unit's rows (padded units, whose later groups are empty, do not load
-    // one XCD more than another), the groups of a chunk share their
-    // candidate K/V rows in one XCD's L2, and items are many more than the
-    // XCD's workgroup slots, so the last round of slow items stays short.
+    // Work items: the tile groups (tpw consecutive query tiles of one
+    // (batch, kv head)) that hold a valid row, ordered by batch, kv head and
+    // row.  XCD x (workgroup ids go round-robin over the 8 XCDs) takes the
+    // x-th eighth of that list, in row order, on its own workgroup slots: the
+    // work is balanced over the XCDs whatever the lengths, and each XCD works
+    // on one or two kv heads at a time, whose candidate K/V rows stay in its
+    // L2.  Each workgroup finds its item from the lengths; slots past the
+    // XCD's share write the zeros of the groups that hold only padded rows.
     const int ngroups = (ntiles + tpw - 1) / tpw;
-    const int nchunk_u = (ngroups + kChunk - 1) / kChunk;
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int qch = (slot / kChunk) * 8 + xcd;  // chunk rank
-    if (qch >= nunits * nchunk_u) return;
-    const int cch = qch / nunits;               // chunk position in its unit
-    const int unit = (qch - cch * nunits + cch) % nunits;
-    const int grp = cch * kChunk + slot % kChunk;
-    if (grp >= ngroups) return;
-    const int g = unit % Hkv;
-    const int b = unit / Hkv;
+    __shared__ int wmap[4];  // batch, kv head, first group, group count (-1: none)
+    if (wave == 0) {
+        long long T = 0;  // valid items
+        for (int b0 = 0; b0 < B; b0 += 64) {
+            const int bb = b0 + lane;
+            long long c = bb < B ? (long long)valid_groups(seqlens, bb, S, Bq, tpw) * Hkv : 0;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, 64);
+            T += c;
+        }
+        const long long qx = (T + 7) / 8;  // items per XCD
+        const long long per_xcd = gridDim.x >> 3;
+        const long long slot = blockIdx.x >> 3, xcd = blockIdx.x & 7;
+        int bsel = -1, gsel = 0, gfirst = 0, gcount = 0;
+        long long off = 0;
+        if (slot < qx) {
+            const long long k = xcd * qx + slot;
+            if (k < T) {
+                locate_item(k, B, Hkv, lane, [&](int bb) { return valid_groups(seqlens, bb, S, Bq, tpw); }, bsel, off);
+                const int vg = valid_groups(seqlens, bsel, S, Bq, tpw);
+                gsel = (int)(off / vg);
+                gfirst = (int)(off % vg);
+                gcount = 1;
+            }
+        } else {
+            // padded groups, one per spare slot (spare slots: 8 (per_xcd - qx)
+            // >= all groups - T + 1)
+            const long long e = xcd * (per_xcd - qx) + (slot - qx);
+            const long long P = (long long)B * Hkv * ngroups - T;
+            if (e < P) {
+                // one padded item: (batch, kv head, group) past the valid groups
+                locate_item(e, B, Hkv, lane, [&](int bb) { return ngroups - valid_groups(seqlens, bb, S, Bq, tpw); },
+                            bsel, off);
+                const int pg = ngroups - valid_groups(seqlens, bsel, S, Bq, tpw);
+                gsel = (int)(off / pg);
+                gfirst = valid_groups(seqlens, bsel, S, Bq, tpw) + (int)(off % pg);
+                gcount = 1;
+            }
+        }
+        if (lane == 0) {
+            wmap[0] = bsel;
+            wmap[1] = gsel;
+            wmap[2] = gfirst;
+            wmap[3] = gcount;
+        }
+    }
+    __syncthreads();
+    if (wmap[0] < 0) return;
+    const int b = wmap[0], g = wmap[1], grp = wmap[2];
     const int L = clamp_len(seqlens, b, S);
 
     const int m = wave * 32 + ql;  // stacked (row, head) pair of this lane
@@ -675,19 +748,20 @@ hipError_t launch_attn(const void *Q, const void *K, const void *V, int dtype, c
         const int64_t total = (int64_t)ntiles * Hkv * B;
         const int tpw = (int)std::max<int64_t>(1, std::min<int64_t>(total / kTargetItems, ntiles));
         const int64_t ngroups = (ntiles + tpw - 1) / tpw;
-        const int64_t nchunks = (int64_t)B * Hkv * ((ngroups + kChunk - 1) / kChunk);
-        const int64_t items = 8 * (int64_t)kChunk * ((nchunks + 7) / 8);
+        const int64_t all_groups = (int64_t)B * Hkv * ngroups;
+        // one slot per group, plus one spare per XCD: the slots past each
+        // XCD's share of the valid groups then outnumber the padded groups
+        const int64_t items = 8 * ((all_groups + 7) / 8 + 1);
         if (items > 0x7fffffff) return hipErrorInvalidValue;
         const dim3 grid((unsigned)items);
-        const int nunits = B * Hkv;
         if (d == 128)
             hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(kThreads), 0, stream,
                                (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau,
-                               tie, seqlens, S, Hq, Hkv, G, Bq, ntiles, tpw, nunits, (uint16_t *)O, qscale);
+                               tie, seqlens, S, Hq, Hkv, G, Bq, ntiles, tpw, B, (uint16_t *)O, qscale);
         else
             hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(kThreads), 0, stream,
                                (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau,
-                               tie, seqlens, S, Hq, Hkv, G, Bq, ntiles, tpw, nunits, (uint16_t *)O, qscale);
+                               tie, seqlens, S, Hq, Hkv, G, Bq, ntiles, tpw, B, (uint16_t *)O, qscale);
     } else {
         const int64_t waves = (int64_t)B * Hq * S;
         const int64_t blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);

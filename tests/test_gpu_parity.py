@@ -190,6 +190,10 @@ ATTN_CASES = [
     ("bf16", 1, 1200, 8, 1, 128, 1000, "shared", False),
     ("f32", 1, 300, 2, 1, 64, 64, "shared", False),
     ("f32", 2, 200, 4, 2, 128, 150, "shared", True),
+    # more than 64 batches of varied lengths: work items are found by a scan
+    # over the lengths in steps of 64 batches
+    ("bf16", 70, 150, 4, 2, 64, 30, "lognormal", True),
+    ("bf16", 67, 90, 8, 1, 128, 40, "dyadic", True),
 ]
 
 
