@@ -18,6 +18,19 @@ bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? DMA_OK : DMA_ERR_HIP; }
 
+int qk_norm_rope_check(const void *Q, const void *K, int dtype, const void *q_norm_w, const void *k_norm_w, float eps,
+                       double rope_theta, int B, int S, int Hq, int Hkv, int d, const void *Q_out, const void *K_out) {
+    if (!Q || !K || !q_norm_w || !k_norm_w || !Q_out || !K_out) return DMA_ERR_NULL;
+    if (!dtype_ok(dtype)) return DMA_ERR_DTYPE;
+    if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || d < 1) return DMA_ERR_SHAPE;
+    if (!(eps >= 0.f) || !(rope_theta > 1.0) || (int64_t)B * S > 0x7fffffff) return DMA_ERR_SHAPE;
+    if (!head_dim_ok(d)) return DMA_ERR_UNSUPPORTED;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(q_norm_w) || !aligned16(k_norm_w) || !aligned16(Q_out) ||
+        !aligned16(K_out))
+        return DMA_ERR_UNSUPPORTED;
+    return DMA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -177,14 +190,9 @@ int dma_decode_state_kept(const void *state, size_t state_bytes, int B, int Hkv,
 int dma_qk_norm_rope(const void *Q, const void *K, int dtype, const void *q_norm_w, const void *k_norm_w, float eps,
                      double rope_theta, const int32_t *positions, int B, int S, int Hq, int Hkv, int d, void *Q_out,
                      void *K_out, void *stream) {
-    if (!Q || !K || !q_norm_w || !k_norm_w || !Q_out || !K_out) return DMA_ERR_NULL;
-    if (!dtype_ok(dtype)) return DMA_ERR_DTYPE;
-    if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || d < 1) return DMA_ERR_SHAPE;
-    if (!(eps >= 0.f) || !(rope_theta > 1.0) || (int64_t)B * S > 0x7fffffff) return DMA_ERR_SHAPE;
-    if (!head_dim_ok(d)) return DMA_ERR_UNSUPPORTED;
-    if (!aligned16(Q) || !aligned16(K) || !aligned16(q_norm_w) || !aligned16(k_norm_w) || !aligned16(Q_out) ||
-        !aligned16(K_out))
-        return DMA_ERR_UNSUPPORTED;
+    const int st = qk_norm_rope_check(Q, K, dtype, q_norm_w, k_norm_w, eps, rope_theta, B, S, Hq, Hkv, d, Q_out,
+                                      K_out);
+    if (st != DMA_OK) return st;
     return from_hip(dma::launch_qk_norm_rope(Q, K, dtype, q_norm_w, k_norm_w, eps, rope_theta, positions, B, S, Hq,
                                              Hkv, d, Q_out, K_out, (hipStream_t)stream));
 }
@@ -201,9 +209,15 @@ int dma_prologue(const void *Q, const void *K, const void *V, int dtype, const v
         if (!aligned16(V) || !aligned16(W)) return DMA_ERR_UNSUPPORTED;
     }
     // every argument is checked before the first launch
-    const int st = dma_qk_norm_rope(Q, K, dtype, q_norm_w, k_norm_w, eps, rope_theta, positions, B, S, Hq, Hkv, d,
-                                    Q_out, K_out, stream);
+    const int st = qk_norm_rope_check(Q, K, dtype, q_norm_w, k_norm_w, eps, rope_theta, B, S, Hq, Hkv, d, Q_out,
+                                      K_out);
     if (st != DMA_OK) return st;
+    if (dtype == DMA_BF16)  // one launch: dt's tiles and the Q/K rows side by side
+        return from_hip(dma::launch_prologue_bf16(Q, K, q_norm_w, k_norm_w, eps, rope_theta, positions, B, S, Hq, Hkv,
+                                                  d, Q_out, K_out, V, W, bias, A, dt_out, (hipStream_t)stream));
+    const hipError_t e = dma::launch_qk_norm_rope(Q, K, dtype, q_norm_w, k_norm_w, eps, rope_theta, positions, B, S,
+                                                  Hq, Hkv, d, Q_out, K_out, (hipStream_t)stream);
+    if (e != hipSuccess) return DMA_ERR_HIP;
     return from_hip(dma::launch_dt(V, W, bias, A, dtype, B, S, Hkv, d, dt_out, S, nullptr, (hipStream_t)stream));
 }
 

@@ -14,6 +14,7 @@
 // float32 uses VALU: eight lanes per token, 16-byte vectors, xor-shuffle
 // reduction.  softplus and exp run in float32 in both.
 #include "common.hpp"
+#include "dt_mfma.hpp"
 #include "launch.hpp"
 
 namespace dma {
@@ -114,103 +115,14 @@ __global__ __launch_bounds__(kThreads) void dt_kernel(const T *__restrict__ V, c
 }
 
 constexpr int kMfmaThreads = 128;     // two waves, one 16-token tile each
-constexpr int kChunk = 128;           // channels per lane group pass (4 lanes x 32)
-constexpr int kChunksPerBatch = 4;    // chunks loaded before the first multiply
 
-// softplus and exp on the hardware exp2 / log2: softplus(x) = max(x, 0) +
-// ln(1 + e^-|x|) and e^y, with an absolute error in softplus of a few 1e-8
-// and a relative error in e^y of about |y| * 2^-23, far inside the float32
-// tolerance of dt (which is relative to exp of their product).
-__device__ __forceinline__ float dt_from_x(float a, float x) {
-    constexpr float kLn2 = 0.6931471805599453f;
-    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
-    const float sp = fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + e) * kLn2;
-    return __builtin_amdgcn_exp2f(a * sp * kLog2e);
-}
-
-// bf16 dt on matrix cores.  16x16x32 bf16 operand layouts (l = lane):
-//   A[m = l%16][k = 8*(l/16) + j], B[k = 8*(l/16) + j][n = l%16],
-//   C[m = 4*(l/16) + i][n = l%16], i = 0..3.
-// Channel of k-slot (kg = l/16, j) in step s of chunk c: c*128 + 32*kg + 8*s + j.
-// Both operands come straight from global memory (W is small and stays in
-// the caches), so no LDS and no barrier stand between the loads and the math.
 __global__ __launch_bounds__(kMfmaThreads) void dt_mfma_kernel(
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ W, const uint16_t *__restrict__ bias,
     const float *__restrict__ A, int S, int Hkv, int width, int64_t ntok,
     float *__restrict__ out, int64_t ld, const int32_t *__restrict__ out_pos) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int mr = lane & 15, kg = lane >> 4;
-    const int nchunk = (width + kChunk - 1) / kChunk;
-    const bool head_ok = mr < Hkv;
-    const int hc = head_ok ? mr : 0;  // clamped head for the (unused) W loads
-    const int64_t ntiles = (ntok + 15) / 16;
-    const int64_t stride = (int64_t)gridDim.x * (kMfmaThreads / 64);
-    const float a_h = A[hc];
-    const float b_h = bias ? bf16_to_f32(bias[hc]) : 0.f;
-
-    // this lane's 16-byte vectors of chunks c0 .. c0 + kChunksPerBatch - 1 of
-    // its token row and of W's row for head l%16 (zeros past the row, the last
-    // token or the last head).  Requests are unconditional from clamped, valid
-    // addresses: a conditional load would be a branch of its own.
-    uint4 va[kChunksPerBatch][4], wa[kChunksPerBatch][4];
-    auto load_batch = [&](int64_t tile, int c0) __attribute__((always_inline)) {
-        const int64_t t = tile * 16 + mr;
-        const bool tok_ok = t < ntok;
-        const uint16_t *vrow = V + (tok_ok ? t : ntok - 1) * (int64_t)width;
-        const uint16_t *wrow = W + (size_t)hc * width;
-#pragma unroll
-        for (int cc = 0; cc < kChunksPerBatch; ++cc) {
-            const int base = (c0 + cc) * kChunk + 32 * kg;
-            const bool in = base < width;
-            const int cb = in ? base : width - 32;
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const uint4 x = *reinterpret_cast<const uint4 *>(vrow + cb + 8 * st);
-                const uint4 y = *reinterpret_cast<const uint4 *>(wrow + cb + 8 * st);
-                va[cc][st] = (tok_ok && in) ? x : make_uint4(0, 0, 0, 0);
-                wa[cc][st] = (head_ok && in) ? y : make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-
-    int64_t tile = (int64_t)blockIdx.x * (kMfmaThreads / 64) + wave;
-    if (tile < ntiles) load_batch(tile, 0);
-    for (; tile < ntiles; tile += stride) {
-        // batch and column of this lane's four output tokens, out_pos loaded
-        // now so that its latency hides behind the products
-        int ob[4], os[4];
-        int64_t ocol[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t tok = tile * 16 + 4 * kg + i;
-            const int64_t tc = tok < ntok ? tok : ntok - 1;
-            ob[i] = ntok <= 0x7fffffff ? (int)((uint32_t)tc / (uint32_t)S) : (int)(tc / S);
-            os[i] = (int)(tc - (int64_t)ob[i] * S);
-            ocol[i] = out_pos ? (int64_t)out_pos[ob[i]] : 0;
-        }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int c0 = 0; c0 < nchunk; c0 += kChunksPerBatch) {
-            if (c0 > 0) load_batch(tile, c0);  // the first batch is already in flight
-#pragma unroll
-            for (int cc = 0; cc < kChunksPerBatch; ++cc) {
-                if (c0 + cc >= nchunk) break;
-#pragma unroll
-                for (int st = 0; st < 4; ++st)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va[cc][st]),
-                                                                  __builtin_bit_cast(bf16x8, wa[cc][st]), acc, 0, 0, 0);
-            }
-        }
-        if (tile + stride < ntiles) load_batch(tile + stride, 0);  // next tile's rows in flight
-        if (head_ok) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t tok = tile * 16 + 4 * kg + i;
-                // a column outside [0, ld) (an out_pos past the row) is not written
-                if (tok < ntok && (uint64_t)(ocol[i] + os[i]) < (uint64_t)ld)
-                    out[((int64_t)ob[i] * Hkv + mr) * ld + ocol[i] + os[i]] = dt_from_x(a_h, acc[i] + b_h);
-            }
-        }
-    }
+    constexpr int kWavesPerBlock = kMfmaThreads / 64;
+    dt_mfma_tiles<4>((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6), (int64_t)gridDim.x * kWavesPerBlock,
+                  V, W, bias, A, S, Hkv, width, ntok, out, ld, out_pos);
 }
 
 }  // namespace

@@ -55,6 +55,13 @@ hipError_t launch_qk_norm_rope(const void *Q, const void *K, int dtype, const vo
                                double rope_theta, const int32_t *positions, int B, int S, int Hq, int Hkv, int d,
                                void *Qo, void *Ko, hipStream_t stream);
 
+// The bf16 prologue in one launch: Q/K RMSNorm + rotary and dt from V
+// (dt_out [B][Hkv][S], no out_pos), prologue.hip.
+hipError_t launch_prologue_bf16(const void *Q, const void *K, const void *wq, const void *wk, float eps,
+                                double rope_theta, const int32_t *positions, int B, int S, int Hq, int Hkv, int d,
+                                void *Qo, void *Ko, const void *V, const void *W, const void *bias, const float *A,
+                                float *dt_out, hipStream_t stream);
+
 // Backward of the prefill attention (bwd.hip), bf16.
 size_t attn_bwd_ws_bytes(int B, int S, int Hq);
 hipError_t launch_attn_bwd(const void *Q, const void *K, const void *V, const float *dt, const float *tau,

@@ -18,6 +18,7 @@
 // the outputs may alias the inputs (each lane writes only the 16 bytes it
 // read, after reading them).
 #include "common.hpp"
+#include "dt_mfma.hpp"
 #include "launch.hpp"
 
 namespace dma {
@@ -93,9 +94,9 @@ template <int LR> __device__ __forceinline__ float group_mirror(float v) {
 // partner of every element then sits in the mirror lane LR - 1 - i, one DPP
 // move away.
 template <int D, typename T, int NS, bool MULTI>
-__global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
-    const T *Q, const T *K, const T *__restrict__ wq, const T *__restrict__ wk, float eps, double log2_theta,
-    const int32_t *__restrict__ positions, int S, int Hq, int Hkv, int ntok, T *Qo, T *Ko) {
+__device__ __forceinline__ void qk_norm_rope_block(
+    int blk, const T *Q, const T *K, const T *__restrict__ wq, const T *__restrict__ wk, float eps,
+    double log2_theta, const int32_t *__restrict__ positions, int S, int Hq, int Hkv, int ntok, T *Qo, T *Ko) {
     using L = Lanes<T>;
     constexpr int E = L::kElems;   // elements per lane
     constexpr int LR = D / E;      // lanes per row
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
     const int e0 = E * (low ? li : LR / 2 + (LR - 1 - li));  // this lane's first element
     const int nrows = Hq + Hkv;
     const int nch = (nrows + NS * RW - 1) / (NS * RW);  // chunks per token
-    const int t_raw = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wv);
+    const int t_raw = __builtin_amdgcn_readfirstlane(blk * kWaves + wv);
     const int t = min(t_raw, ntok - 1);  // the wave's token
 
     // Element offset of this lane's 16 bytes of row r of token t in Q (r < Hq)
@@ -211,15 +212,86 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
     }
 }
 
+template <int D, typename T, int NS, bool MULTI>
+__global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
+    const T *Q, const T *K, const T *__restrict__ wq, const T *__restrict__ wk, float eps, double log2_theta,
+    const int32_t *__restrict__ positions, int S, int Hq, int Hkv, int ntok, T *Qo, T *Ko) {
+    qk_norm_rope_block<D, T, NS, MULTI>(blockIdx.x, Q, K, wq, wk, eps, log2_theta, positions, S, Hq, Hkv, ntok,
+                                        Qo, Ko);
+}
+
+// The whole prologue of bf16 projections in one launch: the first ndt
+// workgroups run dt's matrix-core tiles over V (four waves, a 16-token tile
+// each, striding over the tiles), the rest normalise and rotate Q and K one
+// token per wave.  The two streams read disjoint inputs and write disjoint
+// outputs, so they run side by side instead of one after the other.  dt
+// keeps one 128-channel chunk of loads in flight here (not four as in
+// dma_dt's kernel), so that the kernel's register count stays that of the
+// Q/K part and its memory-bound waves keep their occupancy.
+template <int D, int NS, bool MULTI>
+__global__ __launch_bounds__(kThreads) void prologue_kernel(
+    const uint16_t *Q, const uint16_t *K, const uint16_t *__restrict__ wq, const uint16_t *__restrict__ wk,
+    float eps, double log2_theta, const int32_t *__restrict__ positions, int S, int Hq, int Hkv, int ntok,
+    uint16_t *Qo, uint16_t *Ko, const uint16_t *__restrict__ V, const uint16_t *__restrict__ W,
+    const uint16_t *__restrict__ bias, const float *__restrict__ A, float *__restrict__ dt_out, int ndt) {
+    if ((int)blockIdx.x < ndt) {
+        dt_mfma_tiles<1>((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6), (int64_t)ndt * kWaves, V, W, bias, A, S, Hkv,
+                      Hkv * D, ntok, dt_out, S, nullptr);
+        return;  // uniform per workgroup
+    }
+    qk_norm_rope_block<D, uint16_t, NS, MULTI>(blockIdx.x - ndt, Q, K, wq, wk, eps, log2_theta, positions, S, Hq, Hkv,
+                                               ntok, Qo, Ko);
+}
+
+// rows per chunk step and chunk layout of a token's Q and K rows: as few
+// chunks of at most 4 steps as possible, each of equal size
+template <int D, typename T>
+inline void qk_chunks(int Hq, int Hkv, int &nchunk, int &ns) {
+    constexpr int RW = 64 / (D / Lanes<T>::kElems);
+    const int steps = (Hq + Hkv + RW - 1) / RW;
+    nchunk = (steps + 3) / 4;
+    ns = (steps + nchunk - 1) / nchunk;
+}
+
+template <int D>
+void launch_prologue_t(const void *Q, const void *K, const void *wq, const void *wk, float eps, double log2_theta,
+                       const int32_t *positions, int S, int Hq, int Hkv, int ntok, void *Qo, void *Ko,
+                       const void *V, const void *W, const void *bias, const float *A, float *dt_out,
+                       hipStream_t stream) {
+    int nchunk, ns;
+    qk_chunks<D, uint16_t>(Hq, Hkv, nchunk, ns);
+    const int nqk = (ntok + kWaves - 1) / kWaves;
+    const int64_t ntiles = (ntok + 15) / 16;
+    const int64_t want = (ntiles + kWaves - 1) / kWaves;
+    const int ndt = (int)(want < 2048 ? want : 2048);
+    const dim3 grid((unsigned)(ndt + nqk));
+#define DMA_PRO(NS, MULTI)                                                                                          \
+    hipLaunchKernelGGL((prologue_kernel<D, NS, MULTI>), grid, dim3(kThreads), 0, stream, (const uint16_t *)Q,          \
+                       (const uint16_t *)K, (const uint16_t *)wq, (const uint16_t *)wk, eps, log2_theta, positions, S, \
+                       Hq, Hkv, ntok, (uint16_t *)Qo, (uint16_t *)Ko, (const uint16_t *)V, (const uint16_t *)W,        \
+                       (const uint16_t *)bias, A, dt_out, ndt)
+    if (nchunk == 1) {
+        switch (ns) {
+            case 1: DMA_PRO(1, false); break;
+            case 2: DMA_PRO(2, false); break;
+            case 3: DMA_PRO(3, false); break;
+            default: DMA_PRO(4, false); break;
+        }
+    } else {
+        switch (ns) {
+            case 2: DMA_PRO(2, true); break;
+            case 3: DMA_PRO(3, true); break;
+            default: DMA_PRO(4, true); break;
+        }
+    }
+#undef DMA_PRO
+}
+
 template <int D, typename T>
 void launch_t(const void *Q, const void *K, const void *wq, const void *wk, float eps, double log2_theta,
               const int32_t *positions, int S, int Hq, int Hkv, int ntok, void *Qo, void *Ko, hipStream_t stream) {
-    constexpr int RW = 64 / (D / Lanes<T>::kElems);
-    const int steps = (Hq + Hkv + RW - 1) / RW;
-    // a token's rows in as few chunks of at most 4 steps as possible, each
-    // of equal size
-    const int nchunk = (steps + 3) / 4;
-    const int ns = (steps + nchunk - 1) / nchunk;
+    int nchunk, ns;
+    qk_chunks<D, T>(Hq, Hkv, nchunk, ns);
     const unsigned grid = (unsigned)((ntok + kWaves - 1) / kWaves);
 #define DMA_QKNR(NS, MULTI)                                                                                   \
     hipLaunchKernelGGL((qk_norm_rope_kernel<D, T, NS, MULTI>), dim3(grid), dim3(kThreads), 0, stream,         \
@@ -243,6 +315,21 @@ void launch_t(const void *Q, const void *K, const void *wq, const void *wk, floa
 }
 
 }  // namespace
+
+hipError_t launch_prologue_bf16(const void *Q, const void *K, const void *wq, const void *wk, float eps,
+                                double rope_theta, const int32_t *positions, int B, int S, int Hq, int Hkv, int d,
+                                void *Qo, void *Ko, const void *V, const void *W, const void *bias, const float *A,
+                                float *dt_out, hipStream_t stream) {
+    const int ntok = B * S;
+    const double log2_theta = __builtin_log2(rope_theta);
+    if (d == 128)
+        launch_prologue_t<128>(Q, K, wq, wk, eps, log2_theta, positions, S, Hq, Hkv, ntok, Qo, Ko, V, W, bias, A,
+                               dt_out, stream);
+    else
+        launch_prologue_t<64>(Q, K, wq, wk, eps, log2_theta, positions, S, Hq, Hkv, ntok, Qo, Ko, V, W, bias, A,
+                              dt_out, stream);
+    return hipGetLastError();
+}
 
 hipError_t launch_qk_norm_rope(const void *Q, const void *K, int dtype, const void *wq, const void *wk, float eps,
                                double rope_theta, const int32_t *positions, int B, int S, int Hq, int Hkv, int d,
