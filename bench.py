@@ -137,7 +137,7 @@ def host_cpu_info():
     return {"cpu_model": model, "sockets": max(1, len(phys)), "nproc": os.cpu_count(), "usable_cpus": usable}
 
 
-def cpu_baseline(inp, wl, rows_per_unit=768, reps=3):
+def cpu_baseline(inp, wl, rows_per_unit=1024, reps=3):
     """The oracle (plain C, fp64, OpenMP over rows) timed on the host on a
     stratified sample of the prefill workload: dt over every token, then the
     selection and the attention of rows_per_unit rows per (batch, kv head),

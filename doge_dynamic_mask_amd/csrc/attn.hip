@@ -50,7 +50,7 @@ constexpr int kMaxSteps = 32;    // fill steps counted per round (32768 keys)
 constexpr int kBatchSteps = 8;   // fill steps whose loads are issued together
 constexpr int kPartCap = 2 * kRowsPerWG + 2 * kBK;  // slots of the masked region
 constexpr int kCarrySlots = kCap / kThreads;         // carried candidates per thread
-constexpr int kTargetItems = 4096;                   // work items a launch aims for
+constexpr int kTargetItems = 2048;                   // work items a launch aims for
 
 template <int D>
 struct Tiles {

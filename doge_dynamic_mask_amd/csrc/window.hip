@@ -352,6 +352,9 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
         if (x0 + kBlk < n) fetch(x0 + kBlk);
         float z[4][4];
         float mb = -INFINITY;
+        // wave priority 3 while forming scores, 1 for the weighted sum of V,
+        // 0 in the softmax (the waves of a SIMD then interleave their phases)
+        __builtin_amdgcn_s_setprio(3);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -366,6 +369,7 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
                 mb = fmaxf(mb, z[mt][r]);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // the running max is shared by the four lanes of a pair, so that
         // every weight of the pair's row has the same scale
         mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
@@ -383,6 +387,7 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) pm[mt][r] = __builtin_amdgcn_exp2f(z[mt][r] - msub);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             bf16x8 pb;
@@ -399,6 +404,7 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
 #pragma unroll
             for (int t = 0; t < D / 16; ++t) oacc[t] = mfma16(tr_operand<P>(Vs, 32 * s2, 16 * t, lane), pb, oacc[t]);
         }
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();
     }
     l += __shfl_xor(l, 16, 64);
