@@ -45,6 +45,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kCollectCap = 512;    // boundary-bin keys ranked exactly in LDS
 constexpr int kUnroll = 16;         // prefix keys per thread per pass step (loads in flight)
+constexpr int kUnroll4 = 8;         // float4 loads per thread per pass step
+constexpr int kSampleKeys = 1024;   // keys whose range bins a prefix too long to stage
 
 // STAGE: prefixes up to this many keys are kept in LDS for the second and
 // third passes (longer ones are read again from memory).  The workgroups are
@@ -69,11 +71,37 @@ __device__ __forceinline__ float order_value(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-// f(j, dt[j]) for every prefix position j < P, kUnroll positions per thread
-// per step with all of their loads issued before any is used.
+// f(j, dt[j]) for every prefix position j < P.  A 16-byte aligned row is read
+// in float4 loads, kUnroll4 of them per thread per step (32 positions), all
+// issued before any is used; the last P % 4 positions, and rows that are not
+// 16-byte aligned, go key by key, kUnroll per thread per step.  The passes
+// are bound by the latency of these reads, so the fewer steps the better.
 template <typename F>
 __device__ __forceinline__ void for_prefix(const float *__restrict__ row, int P, F f) {
-    for (int j0 = 0; j0 < P; j0 += kUnroll * kThreads) {
+    int jt = 0;  // first position left to the key-by-key loop
+    if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0) {
+        const int P4 = P & ~3;
+        for (int j0 = 0; j0 < P4; j0 += 4 * kUnroll4 * kThreads) {
+            float4 v[kUnroll4];
+#pragma unroll
+            for (int u = 0; u < kUnroll4; ++u) {
+                const int j = j0 + 4 * (u * kThreads + (int)threadIdx.x);
+                v[u] = j < P4 ? *reinterpret_cast<const float4 *>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll4; ++u) {
+                const int j = j0 + 4 * (u * kThreads + (int)threadIdx.x);
+                if (j < P4) {
+                    f(j, v[u].x);
+                    f(j + 1, v[u].y);
+                    f(j + 2, v[u].z);
+                    f(j + 3, v[u].w);
+                }
+            }
+        }
+        jt = P4;
+    }
+    for (int j0 = jt; j0 < P; j0 += kUnroll * kThreads) {
         float v[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -148,15 +176,39 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
     const int nb = min(P, w) - A0;  // band size, 0 when the prefix is empty
     if (nb > 0) {
         const uint32_t rankA = (uint32_t)A0, rankB = (uint32_t)(A0 + nb - 1);
-        // ---- a1: key range of the prefix
+        // ---- a1: key range of the prefix.  A staged prefix is read whole
+        // (into LDS).  A longer one takes its range from kSampleKeys keys in
+        // blocks of 64 consecutive positions spread evenly over it; keys
+        // outside that range go to the end bins, so the histogram is still a
+        // monotone bucketing of the keys and the ranks it gives are exact.
+        // Only when a rank of the band falls in a clamped end bin (which the
+        // spread sample makes unlikely: the band sits w keys below the top)
+        // does the collect step overflow and take the exact fallback.
         const bool staged = P <= STAGE;
         uint32_t kmin = 0xffffffffu, kmax = 0u;
-        for_prefix(row, P, [&](int j, float x) {
-            const uint32_t k = ordkey(x);
-            kmin = min(kmin, k);
-            kmax = max(kmax, k);
-            if (staged) sh.keys[j] = k;
-        });
+        if (staged) {
+            for_prefix(row, P, [&](int j, float x) {
+                const uint32_t k = ordkey(x);
+                kmin = min(kmin, k);
+                kmax = max(kmax, k);
+                sh.keys[j] = k;
+            });
+        } else {
+            static_assert(STAGE >= kSampleKeys, "a sampled prefix holds every sample block");
+            constexpr int kBlocks = kSampleKeys / 64;
+            float v[kSampleKeys / kThreads];
+#pragma unroll
+            for (int u = 0; u < kSampleKeys / kThreads; ++u) {
+                const int x = tid + u * kThreads, blk = x >> 6;
+                v[u] = row[(int)((int64_t)blk * (P - 64) / (kBlocks - 1)) + (x & 63)];
+            }
+#pragma unroll
+            for (int u = 0; u < kSampleKeys / kThreads; ++u) {
+                const uint32_t k = ordkey(v[u]);
+                kmin = min(kmin, k);
+                kmax = max(kmax, k);
+            }
+        }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) {
             kmin = min(kmin, (uint32_t)__shfl_xor(kmin, o, 64));
@@ -183,11 +235,16 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
         const int bw = range == 0u ? 0 : 32 - __clz(range);
         constexpr int kLogBins = __builtin_ctz(NB);
         const int shift = bw > kLogBins ? bw - kLogBins : 0;
+        // bin of a key: keys outside [kmin, kmax] (only a sampled range has
+        // them) go to the end bins
+        auto bin_of = [=](uint32_t k) -> uint32_t {
+            return k < kmin ? 0u : min((k - kmin) >> shift, (uint32_t)(NB - 1));
+        };
         // ---- a2: histogram, then the bins of ranks A0 and w-1 (descending)
         if (staged)
             for_staged(sh.keys, P, [&](int, uint32_t k) { atomicAdd(&sh.hist[(k - kmin) >> shift], 1u); });
         else
-            for_prefix(row, P, [&](int, float x) { atomicAdd(&sh.hist[(ordkey(x) - kmin) >> shift], 1u); });
+            for_prefix(row, P, [&](int, float x) { atomicAdd(&sh.hist[bin_of(ordkey(x))], 1u); });
         __syncthreads();
         {
             constexpr int PER = NB / kThreads;  // bins per thread, descending
@@ -223,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
         const uint32_t binA = sh.binA, binB = sh.binB, aboveA = sh.aboveA;
         // ---- a3: keys of bins [binB, binA] into LDS, ranked exactly
         auto collect = [&](int j, uint32_t k) {
-            const uint32_t bin = (k - kmin) >> shift;
+            const uint32_t bin = bin_of(k);
             if (bin >= binB && bin <= binA) {
                 const uint32_t at = atomicAdd(&sh.ncol, 1u);
                 if (at < (uint32_t)kCollectCap) sh.col[at] = ((uint64_t)k << 32) | (uint64_t)(~(uint32_t)j);

@@ -139,6 +139,10 @@ def make_dt(shape, kind: str, seed: int) -> np.ndarray:
       wide       log-uniform over [2^-20, 2^20]
       shared     2^18 + U(0, 4): a large dt common to every key, so the
                  scores' differences come from q.k and a small spread of dt
+      spiky      lognormal with one key in 500 raised 10^6-fold: a few keys
+                 far above the rest, easily missed by a sample of positions
+      rising     position / n + U(0, 0.05) along the last axis: the largest
+                 keys are the latest ones
     """
     rng = np.random.default_rng(seed)
     if kind == "lognormal":
@@ -153,6 +157,12 @@ def make_dt(shape, kind: str, seed: int) -> np.ndarray:
         x = 2.0 ** rng.uniform(-20.0, 20.0, size=shape)
     elif kind == "shared":
         x = 2.0 ** 18 + rng.uniform(0.0, 4.0, size=shape)
+    elif kind == "spiky":
+        x = rng.lognormal(0.0, 0.8, size=shape)
+        x = np.where(rng.uniform(size=shape) < 1.0 / 500, x * 1e6, x)
+    elif kind == "rising":
+        n = shape[-1]
+        x = np.arange(n) / n + rng.uniform(0.0, 0.05, size=shape)
     else:
         raise ValueError(kind)
     return np.ascontiguousarray(x, dtype=np.float32)

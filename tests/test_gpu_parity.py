@@ -115,6 +115,15 @@ SELECT_CASES = [
     (1, 1, 3000, 700, "dyadic", False),   # a prefix key of rank w-C-1 can be the threshold
     (2, 2, 2000, 129, "few", True),
     (1, 2, 4000, 1000, "lognormal", False),
+    # rows past 4096 keys: prefixes longer than the selector stages in LDS,
+    # binned over the range of a sample of their positions
+    (1, 1, 5000, 64, "const", False),
+    (1, 2, 6000, 1500, "wide", True),
+    (2, 1, 4500, 300, "few", True),
+    (1, 1, 4200, 4000, "dyadic", False),
+    (1, 1, 6000, 2048, "spiky", False),
+    (1, 1, 5000, 8, "spiky", False),
+    (1, 1, 6000, 700, "rising", False),
 ]
 
 
