@@ -48,7 +48,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 # known size (--copy-calibration); the runs and their readings are in
 # profiles/.  The figure holds only for the attention source it was measured
 # on: when the hash of those files differs, traffic is reported as null.
-ATTN_TRAFFIC = {"bytes": None, "sources_sha256": ""}
+ATTN_TRAFFIC = {"bytes": 748728790,
+                "sources_sha256": "52ba66234fc23bd92d60e60a36fd47f8b722bc1ac57ab8ff90d3ff3ff3e7d500"}
 ATTN_SOURCES = ("doge_dynamic_mask_amd/csrc/attn.hip", "doge_dynamic_mask_amd/csrc/common.hpp")
 COPY_CAL_BYTES = 256 * 1024 * 1024
 
@@ -120,16 +121,22 @@ def to_dev(x, dev):
 
 def host_cpu_info():
     """CPU model, sockets and core counts of this host."""
-    model, phys = "", set()
+    model, phys, ids = "", set(), {}
     try:
         with open("/proc/cpuinfo") as f:
             for ln in f:
-                if ln.startswith("model name") and not model:
+                key = ln.split(":", 1)[0].strip()
+                if key == "model name" and not model:
                     model = ln.split(":", 1)[1].strip()
-                elif ln.startswith("physical id"):
+                elif key == "physical id":
                     phys.add(ln.split(":", 1)[1].strip())
+                elif key in ("cpu family", "model", "stepping") and key not in ids:
+                    ids[key] = ln.split(":", 1)[1].strip()
     except OSError:
         pass
+    if ids:  # a virtualised host may name only the product line
+        model += " (family %s, model %s, stepping %s)" % (ids.get("cpu family", "?"), ids.get("model", "?"),
+                                                         ids.get("stepping", "?"))
     try:
         usable = len(os.sched_getaffinity(0))
     except AttributeError:

@@ -67,7 +67,7 @@ int dma_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, i
                int32_t *tie, void *stream) {
     if (!dt || !tau || !tie) return DMA_ERR_NULL;
     if (B < 1 || Hkv < 1 || S < 1 || w < 1) return DMA_ERR_SHAPE;
-    if (B > 65535 || Hkv > 65535) return DMA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hkv * ((S + 63) / 64) >= ((int64_t)1 << 31) - 8) return DMA_ERR_UNSUPPORTED;
     return from_hip(dma::launch_select(dt, seqlens, B, Hkv, S, w, 0, tau, tie, (hipStream_t)stream));
 }
 
@@ -267,6 +267,7 @@ int dma_select_window(const float *dt, const int32_t *seqlens, int B, int Hkv, i
     if (!dt || !tau || !tie) return DMA_ERR_NULL;
     if (B < 1 || Hkv < 1 || S < 1 || w < 1 || win < 1) return DMA_ERR_SHAPE;
     if ((int64_t)B * Hkv * S > ((int64_t)1 << 40)) return DMA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hkv * ((S + 63) / 64) >= ((int64_t)1 << 31) - 8) return DMA_ERR_UNSUPPORTED;
     return from_hip(dma::launch_select_window(dt, seqlens, B, Hkv, S, w, win, tau, tie, (hipStream_t)stream));
 }
 

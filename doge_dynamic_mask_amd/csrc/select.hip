@@ -15,9 +15,11 @@
 //       plus the chunk's own keys: at most 2C+1 candidates.
 // One workgroup per (batch, kv head, chunk of C rows), C = 64 (128 for a
 // sliding window over rows longer than 4096 with win >= 128):
-//   a. finds the band: min/max of the prefix keys, one histogram pass with
-//      1024 bins (4096 for the 128-row chunks) spanning that range, the bins
-//      holding ranks A0 and w-1, and
+//   a. finds the band: the key range of the prefix (of all of it when it is
+//      staged in LDS, else of 1024 keys sampled in blocks spread over it,
+//      keys outside the sampled range counting in the end bins), one
+//      histogram pass with 1024 bins (4096 for the 128-row chunks) spanning
+//      that range, the bins holding ranks A0 and w-1, and
 //      an exact rank of the keys gathered from those bins (a multi-pass radix
 //      select over the prefix when those bins hold too many keys, e.g. under
 //      heavy ties);
@@ -128,14 +130,28 @@ __device__ __forceinline__ void for_staged(const uint32_t *keys, int P, F f) {
 template <int C, int NB, int STAGE, bool WIN>
 __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restrict__ dt,
                                                           const int32_t *__restrict__ seqlens,
-                                                          int Hkv, int S, int w, int win,
+                                                          int Hkv, int S, int w, int win, int nb_total,
                                                           float *__restrict__ tau,
                                                           int32_t *__restrict__ tie) {
     constexpr int kChunk = C;
     __shared__ SelectShared<C, NB, STAGE, WIN> sh;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = blockIdx.y, b = blockIdx.z;
-    const int r0 = blockIdx.x * kChunk;
+    // Work item of this workgroup, items ordered by (batch, kv head, chunk).
+    // Rows of one length (no seqlens): workgroup ids go round-robin over the
+    // 8 XCDs, so XCD x takes items x*per_xcd .. (x+1)*per_xcd - 1 and the
+    // chunks of one row run on one XCD, whose L2 then holds that row's dt for
+    // all of them.  Rows of different lengths carry different work (it grows
+    // with the square of the length), so there the items stay in id order,
+    // spread evenly over the XCDs.  The grid is padded to a multiple of 8;
+    // items past the last return at once.
+    // (items < 2^31: B * Hkv * S is bounded so on the host)
+    const uint32_t per_xcd = gridDim.x >> 3;
+    const uint32_t item = seqlens ? blockIdx.x : (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
+    const uint32_t nchunks = (uint32_t)((S + kChunk - 1) / kChunk);
+    const uint32_t unit = item / nchunks;  // b * Hkv + g
+    if (unit >= (uint32_t)(nb_total * Hkv)) return;  // uniform across the workgroup
+    const int g = (int)(unit % (uint32_t)Hkv), b = (int)(unit / (uint32_t)Hkv);
+    const int r0 = (int)(item - unit * nchunks) * kChunk;
     const int L = clamp_len(seqlens, b, S);
     const size_t base = ((size_t)b * Hkv + g) * S;
     const float *row = dt + base;
@@ -428,6 +444,13 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
 
 }  // namespace
 
+// A 1-D grid of at least nchunks * Hkv * B workgroups, a multiple of 8 (one
+// share per XCD).
+static unsigned xcd_grid(int nchunks, int Hkv, int B) {
+    const int64_t items = (int64_t)nchunks * Hkv * B;
+    return (unsigned)(8 * ((items + 7) / 8));
+}
+
 hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w, int win,
                          float *tau, int32_t *tie, hipStream_t stream) {
     // Full causal range: chunks of 64 rows (more workgroups; they are
@@ -435,8 +458,8 @@ hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv
     // staging beyond.  Sliding window: short windows take 64-row chunks,
     // longer rows and windows 128-row chunks (a window needs win >= C).
 #define DMA_SEL(C, NB, STAGE, WIN)                                                                               \
-    hipLaunchKernelGGL((select_kernel<C, NB, STAGE, WIN>), dim3((S + C - 1) / C, Hkv, B), dim3(kThreads), 0,    \
-                       stream, dt, seqlens, Hkv, S, w, win, tau, tie)
+    hipLaunchKernelGGL((select_kernel<C, NB, STAGE, WIN>), dim3(xcd_grid((S + C - 1) / C, Hkv, B)), dim3(kThreads), \
+                       0, stream, dt, seqlens, Hkv, S, w, win, B, tau, tie)
     if (win > 0) {
         if (S <= 4096 || win < 128) DMA_SEL(64, 1024, 8192, true);
         else DMA_SEL(128, 4096, 8192, true);

@@ -125,7 +125,8 @@ int dma_dt(const void *V, const void *W, const void *bias, const float *A, int d
  *   dt      [B][Hkv][S] float32
  *   seqlens [B] int32 or NULL
  *   tau     [B][Hkv][S] float32 (out), tie [B][Hkv][S] int32 (out)
- * Needs no workspace.
+ * Needs no workspace.  B * Hkv * ceil(S / 64) must stay below 2^31 (else
+ * DMA_ERR_UNSUPPORTED).
  */
 int dma_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w,
                float *tau, int32_t *tie, void *stream);
@@ -366,7 +367,8 @@ int dma_dt_bwd(const void *V, const void *W, const void *bias, const float *A, i
  * dma_select_window -- the threshold pair of every row over its window, with
  * the conventions of dma_select: (tau, tie) is the w-th kept key under (dt
  * desc, index asc); (-inf, -1) when the row sees at most w keys; (+inf, -1)
- * for a padded row.  Exact (comparisons only).  win >= 1.
+ * for a padded row.  Exact (comparisons only).  win >= 1; B * Hkv *
+ * ceil(S / 64) below 2^31 as for dma_select.
  */
 int dma_select_window(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w, int win, float *tau,
                       int32_t *tie, void *stream);
