@@ -122,8 +122,11 @@ __global__ __launch_bounds__(kMfmaThreads) void dt_mfma_kernel(
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ W, const uint16_t *__restrict__ bias,
     const float *__restrict__ A, int S, int Hkv, int width, int64_t ntok,
     float *__restrict__ out, int64_t ld, const int32_t *__restrict__ out_pos) {
+    // one 128-channel chunk per batch of loads: fewer registers, so more
+    // waves in flight, beat fewer rounds (padded 26 -> 22 us, c2 6.0 -> 5.5 us
+    // against four chunks per batch)
     constexpr int kWavesPerBlock = kMfmaThreads / 64;
-    dt_mfma_tiles<4>((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6), (int64_t)gridDim.x * kWavesPerBlock,
+    dt_mfma_tiles<1>((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6), (int64_t)gridDim.x * kWavesPerBlock,
                   V, W, bias, A, S, Hkv, width, ntok, out, ld, out_pos);
 }
 
