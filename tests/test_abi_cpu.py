@@ -71,6 +71,10 @@ def test_select_validation(dma):
     assert dma.dma_select(FAKE, None, 1, 1, 8, 0, FAKE, FAKE, None) == -2
     assert dma.dma_select(FAKE, None, 0, 1, 8, 2, FAKE, FAKE, None) == -2
     assert dma.dma_select(FAKE, None, 1, 1, 0, 2, FAKE, FAKE, None) == -2
+    # one workgroup per (batch, kv head, 64-row chunk) on a 1-D grid: more
+    # than 2^31 - 8 of them is refused before any launch
+    assert dma.dma_select(FAKE, None, 65536, 512, 4096, 2, FAKE, FAKE, None) == -4
+    assert dma.dma_select_window(FAKE, None, 65536, 512, 4096, 2, 64, FAKE, FAKE, None) == -4
 
 
 def test_attn_validation(dma):

@@ -124,6 +124,8 @@ SELECT_CASES = [
     (1, 1, 6000, 2048, "spiky", False),
     (1, 1, 5000, 8, "spiky", False),
     (1, 1, 6000, 700, "rising", False),
+    (2, 3, 5001, 500, "lognormal", True),   # rows not 16-byte aligned: key-by-key passes
+    (1, 2, 4097, 2048, "few", False),       # the shortest rows past the staged length
 ]
 
 

@@ -35,6 +35,10 @@ SEL_CASES = [
     (1, 2, 900, 120, 130, "dyadic", True),
     (2, 2, 5000, 500, 700, "few", True),
     (1, 1, 4200, 127, 128, "const", False),
+    # windows longer than the selector stages in LDS (8192 keys): the common
+    # range is binned by a sample of its keys; rows 9001 long, so the second
+    # row is not 16-byte aligned
+    (1, 2, 9001, 1000, 8700, "spiky", False),
 ]
 
 
