@@ -13,8 +13,9 @@
 //       are never its w-th key, prefix keys of rank >= w are kept by none, and
 //       each row's threshold key lies in the "band" of prefix ranks [A0, w)
 //       plus the chunk's own keys: at most 2C+1 candidates.
-// One workgroup per (batch, kv head, chunk of C rows), C = 64 (128 for a
-// sliding window over rows longer than 4096 with win >= 128):
+// One workgroup per (batch, kv head, chunk of C rows), C = 32 for rows up to
+// 4096 keys, 64 beyond (128 for a sliding window over rows longer than 4096
+// with win >= 128):
 //   a. finds the band: the key range of the prefix (of all of it when it is
 //      staged in LDS, else of 1024 keys sampled in blocks spread over it,
 //      keys outside the sampled range counting in the end bins), one
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
     // with the square of the length), so there the items stay in id order,
     // spread evenly over the XCDs.  The grid is padded to a multiple of 8;
     // items past the last return at once.
-    // (items < 2^31: B * Hkv * S is bounded so on the host)
+    // (the host keeps B * Hkv * ceil(S / 64), the item count, below 2^31)
     const uint32_t per_xcd = gridDim.x >> 3;
     const uint32_t item = seqlens ? blockIdx.x : (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
     const uint32_t nchunks = (uint32_t)((S + kChunk - 1) / kChunk);
@@ -453,9 +454,10 @@ static unsigned xcd_grid(int nchunks, int Hkv, int B) {
 
 hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w, int win,
                          float *tau, int32_t *tie, hipStream_t stream) {
-    // Full causal range: chunks of 64 rows (more workgroups; they are
-    // latency-bound), whole rows staged in LDS up to 4096 keys, 1024-key
-    // staging beyond.  Sliding window: short windows take 64-row chunks,
+    // Full causal range: chunks of 32 rows for rows up to 4096 keys, staged
+    // whole in LDS (more, shorter workgroups: 7 % faster at S = 2048 than 64
+    // rows), chunks of 64 rows with 1024-key staging beyond (the prefix passes
+    // then dominate, and 32-row chunks would double them).  Sliding window: short windows take 64-row chunks,
     // longer rows and windows 128-row chunks (a window needs win >= C).
 #define DMA_SEL(C, NB, STAGE, WIN)                                                                               \
     hipLaunchKernelGGL((select_kernel<C, NB, STAGE, WIN>), dim3(xcd_grid((S + C - 1) / C, Hkv, B)), dim3(kThreads), \
@@ -464,7 +466,7 @@ hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv
         if (S <= 4096 || win < 128) DMA_SEL(64, 1024, 8192, true);
         else DMA_SEL(128, 4096, 8192, true);
     } else {
-        if (S <= 4096) DMA_SEL(64, 1024, 4096, false);
+        if (S <= 4096) DMA_SEL(32, 1024, 4096, false);
         else DMA_SEL(64, 1024, 1024, false);
     }
 #undef DMA_SEL
