@@ -130,50 +130,16 @@ __global__ __launch_bounds__(kMfmaThreads) void dt_mfma_kernel(
                   V, W, bias, A, S, Hkv, width, ntok, out, ld, out_pos);
 }
 
-// A few tokens (a decode step's append form): one wave per (token, kv head),
-// the dot product of the width-long rows of V and W split over the lanes in
-// 16-byte vectors, all loaded before any is used, a butterfly sum, then
-// softplus and exp as on the matrix-core path.  One round of loads: a launch
-// over a handful of 16-token tiles would be bound by their latency chain.
-constexpr int kSmallTokens = 256;  // bf16 calls with at most this many tokens
+// A few tokens (a decode step's append form): one wave per (token, kv head)
+// with a single round of loads (dt_pair); a launch over a handful of 16-token
+// tiles would be bound by their latency chain.
 __global__ __launch_bounds__(kThreads) void dt_small_kernel(
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ W, const uint16_t *__restrict__ bias,
     const float *__restrict__ A, int S, int Hkv, int width, int64_t ntok,
     float *__restrict__ out, int64_t ld, const int32_t *__restrict__ out_pos) {
-    constexpr int kMaxVec = kMaxHkvDt * 128 / 8 / 64;  // vectors per lane at the widest row
-    const int lane = threadIdx.x & 63;
     const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     if (wid >= ntok * Hkv) return;  // whole waves
-    const int64_t t = wid / Hkv;
-    const int h = (int)(wid - t * Hkv);
-    const int b = (int)(t / S), s = (int)(t - (int64_t)b * S);
-    const int64_t col = (out_pos ? (int64_t)out_pos[b] : 0) + s;
-    const float a_h = A[h];  // requested with the rows, not after the sum
-    const float b_h = bias ? bf16_to_f32(bias[h]) : 0.f;
-    const int nvec = width / 8;
-    const uint4 *vrow = reinterpret_cast<const uint4 *>(V + t * width);
-    const uint4 *wrow = reinterpret_cast<const uint4 *>(W + (size_t)h * width);
-    uint4 vv[kMaxVec], wv[kMaxVec];
-#pragma unroll
-    for (int u = 0; u < kMaxVec; ++u) {
-        const int v = lane + 64 * u;
-        vv[u] = v < nvec ? vrow[v] : make_uint4(0, 0, 0, 0);
-        wv[u] = v < nvec ? wrow[v] : make_uint4(0, 0, 0, 0);
-    }
-    float acc = 0.f;
-#pragma unroll
-    for (int u = 0; u < kMaxVec; ++u) {
-        const uint32_t a[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
-        const uint32_t c[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            acc = fmaf(__uint_as_float(a[k] << 16), __uint_as_float(c[k] << 16), acc);
-            acc = fmaf(__uint_as_float(a[k] & 0xffff0000u), __uint_as_float(c[k] & 0xffff0000u), acc);
-        }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (lane == 0 && (uint64_t)col < (uint64_t)ld) out[((int64_t)b * Hkv + h) * ld + col] = dt_from_x(a_h, acc + b_h);
+    dt_pair(wid, V, W, bias, A, S, Hkv, width, out, ld, out_pos);
 }
 
 }  // namespace
@@ -182,7 +148,7 @@ hipError_t launch_dt(const void *V, const void *W, const void *bias, const float
                      int B, int S, int Hkv, int d, float *dt_out, int64_t ld_out,
                      const int32_t *out_pos, hipStream_t stream) {
     const int64_t ntok = (int64_t)B * S;
-    if (dtype == 1 && ntok <= kSmallTokens) {
+    if (dtype == 1 && ntok <= kDtSmallTokens) {
         const int64_t waves = ntok * Hkv;
         hipLaunchKernelGGL(dt_small_kernel, dim3((unsigned)((waves + kThreads / 64 - 1) / (kThreads / 64))),
                            dim3(kThreads), 0, stream, (const uint16_t *)V, (const uint16_t *)W,

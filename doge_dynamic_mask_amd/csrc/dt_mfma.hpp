@@ -1,5 +1,6 @@
-// dt on matrix cores for bf16 value states: the per-wave tile loop, shared by
-// dma_dt's kernel and the fused prologue kernel.
+// dt for bf16 value states: the per-wave matrix-core tile loop and the
+// per-pair path of small calls, shared by dma_dt's kernels and the fused
+// prologue kernel.
 // Doge guide (gitcode), DMA section, forward step 3: dt_proj over the value
 // states of all kv heads of a token (input width Hkv*d, head-major), then
 // exp(A * softplus(.)).
@@ -108,6 +109,51 @@ __device__ __forceinline__ void dt_mfma_tiles(int64_t first, int64_t stride, con
             }
         }
     }
+}
+
+// A few tokens (a decode step's append form): dt of pair wid = token * Hkv +
+// head by one wave, the dot product of the width-long rows of V and W split
+// over the lanes in 16-byte vectors, all loaded before any is used, a
+// butterfly sum, then softplus and exp as on the matrix-core path.  Calls with
+// at most kDtSmallTokens tokens take this path in dma_dt and in the fused
+// prologue alike, so both give the same bits.  Width <= 16 heads x 128.
+constexpr int kDtSmallTokens = 256;
+__device__ __forceinline__ void dt_pair(int64_t wid, const uint16_t *__restrict__ V, const uint16_t *__restrict__ W,
+                                        const uint16_t *__restrict__ bias, const float *__restrict__ A, int S,
+                                        int Hkv, int width, float *__restrict__ out, int64_t ld,
+                                        const int32_t *__restrict__ out_pos) {
+    constexpr int kMaxVec = 16 * 128 / 8 / 64;  // vectors per lane at the widest row
+    const int lane = threadIdx.x & 63;
+    const int64_t t = wid / Hkv;
+    const int h = (int)(wid - t * Hkv);
+    const int b = (int)(t / S), s = (int)(t - (int64_t)b * S);
+    const int64_t col = (out_pos ? (int64_t)out_pos[b] : 0) + s;
+    const float a_h = A[h];  // requested with the rows, not after the sum
+    const float b_h = bias ? bf16_to_f32(bias[h]) : 0.f;
+    const int nvec = width / 8;
+    const uint4 *vrow = reinterpret_cast<const uint4 *>(V + t * width);
+    const uint4 *wrow = reinterpret_cast<const uint4 *>(W + (size_t)h * width);
+    uint4 vv[kMaxVec], wv[kMaxVec];
+#pragma unroll
+    for (int u = 0; u < kMaxVec; ++u) {
+        const int v = lane + 64 * u;
+        vv[u] = v < nvec ? vrow[v] : make_uint4(0, 0, 0, 0);
+        wv[u] = v < nvec ? wrow[v] : make_uint4(0, 0, 0, 0);
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < kMaxVec; ++u) {
+        const uint32_t a[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+        const uint32_t c[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc = fmaf(__uint_as_float(a[k] << 16), __uint_as_float(c[k] << 16), acc);
+            acc = fmaf(__uint_as_float(a[k] & 0xffff0000u), __uint_as_float(c[k] & 0xffff0000u), acc);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0 && (uint64_t)col < (uint64_t)ld) out[((int64_t)b * Hkv + h) * ld + col] = dt_from_x(a_h, acc + b_h);
 }
 
 }  // namespace dma

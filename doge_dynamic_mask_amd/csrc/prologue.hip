@@ -221,13 +221,13 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
 }
 
 // The whole prologue of bf16 projections in one launch: the first ndt
-// workgroups run dt's matrix-core tiles over V (four waves, a 16-token tile
-// each, striding over the tiles), the rest normalise and rotate Q and K one
-// token per wave.  The two streams read disjoint inputs and write disjoint
-// outputs, so they run side by side instead of one after the other.  dt
-// keeps one 128-channel chunk of loads in flight here (not four as in
-// dma_dt's kernel), so that the kernel's register count stays that of the
-// Q/K part and its memory-bound waves keep their occupancy.
+// workgroups run dt over V — matrix-core tiles (four waves, a 16-token tile
+// each, striding over the tiles, one 128-channel chunk of loads in flight so
+// that the kernel's register count stays that of the Q/K part), or for calls
+// of at most kDtSmallTokens tokens one wave per (token, kv head), exactly as
+// dma_dt does, so both give the same dt — and the rest normalise and rotate
+// Q and K one token per wave.  The two streams read disjoint inputs and write
+// disjoint outputs, so they run side by side instead of one after the other.
 template <int D, int NS, bool MULTI>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(
     const uint16_t *Q, const uint16_t *K, const uint16_t *__restrict__ wq, const uint16_t *__restrict__ wk,
@@ -235,8 +235,13 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(
     uint16_t *Qo, uint16_t *Ko, const uint16_t *__restrict__ V, const uint16_t *__restrict__ W,
     const uint16_t *__restrict__ bias, const float *__restrict__ A, float *__restrict__ dt_out, int ndt) {
     if ((int)blockIdx.x < ndt) {
-        dt_mfma_tiles<1>((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6), (int64_t)ndt * kWaves, V, W, bias, A, S, Hkv,
-                      Hkv * D, ntok, dt_out, S, nullptr);
+        const int64_t first = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+        if (ntok <= kDtSmallTokens) {
+            if (first < (int64_t)ntok * Hkv) dt_pair(first, V, W, bias, A, S, Hkv, Hkv * D, dt_out, S, nullptr);
+        } else {
+            dt_mfma_tiles<1>(first, (int64_t)ndt * kWaves, V, W, bias, A, S, Hkv, Hkv * D, ntok, dt_out, S,
+                             nullptr);
+        }
         return;  // uniform per workgroup
     }
     qk_norm_rope_block<D, uint16_t, NS, MULTI>(blockIdx.x - ndt, Q, K, wq, wk, eps, log2_theta, positions, S, Hq, Hkv,
@@ -262,7 +267,8 @@ void launch_prologue_t(const void *Q, const void *K, const void *wq, const void 
     qk_chunks<D, uint16_t>(Hq, Hkv, nchunk, ns);
     const int nqk = (ntok + kWaves - 1) / kWaves;
     const int64_t ntiles = (ntok + 15) / 16;
-    const int64_t want = (ntiles + kWaves - 1) / kWaves;
+    const int64_t want = ntok <= kDtSmallTokens ? ((int64_t)ntok * Hkv + kWaves - 1) / kWaves  // a wave per pair
+                                                : (ntiles + kWaves - 1) / kWaves;                 // a wave per tile
     const int ndt = (int)(want < 2048 ? want : 2048);
     const dim3 grid((unsigned)(ndt + nqk));
 #define DMA_PRO(NS, MULTI)                                                                                          \

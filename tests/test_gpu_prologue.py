@@ -168,3 +168,27 @@ def test_prologue_decode_token(dma, oracle_mod):
     _check("bf16", to_host(Qo), _expect(oracle_mod, Q, wq, lens), "q")
     _check("bf16", to_host(Ko), _expect(oracle_mod, K, wk, lens), "k")
     _dt_check(oracle_mod, {"V": V, "W": inp["W"], "A": inp["A"], "bias": None}, to_host(dt))
+    # a call this small takes the one-wave-per-(token, head) dt path in both
+    # entry points: the same bits
+    dt_plain = dma.dt(to_dev(V), to_dev(inp["W"]), to_dev(inp["A"]), None)
+    torch.cuda.synchronize()
+    assert torch.equal(dt, dt_plain)
+
+
+@pytest.mark.parametrize("B,S,Hkv,d", [(2, 50, 4, 64), (1, 256, 16, 128), (1, 257, 3, 128)])
+def test_prologue_dt_matches_dma_dt_small(dma, oracle_mod, B, S, Hkv, d):
+    """Calls around the small-call threshold (256 tokens): dma_prologue's dt
+    is bit-identical to dma_dt's and within the oracle's tolerance."""
+    Hq = 2 * Hkv
+    Q, K, V = si.make_qkv(B, S, Hq, Hkv, d, "bf16", 93 + S)
+    wq, wk = si.make_norm_weights(d, "bf16", 94)
+    rng = np.random.default_rng(95 + S)
+    W = si.to_bf16_bits(rng.normal(0, 0.02, (Hkv, Hkv * d)).astype(np.float32))
+    A = rng.uniform(-2, 2, Hkv).astype(np.float32)
+    bias = si.to_bf16_bits(rng.normal(0, 0.5, Hkv).astype(np.float32))
+    _, _, dt = dma.prologue(to_dev(Q), to_dev(K), to_dev(V), to_dev(wq), to_dev(wk), to_dev(W), to_dev(A),
+                            to_dev(bias))
+    dt_plain = dma.dt(to_dev(V), to_dev(W), to_dev(A), to_dev(bias))
+    torch.cuda.synchronize()
+    assert torch.equal(dt, dt_plain)
+    _dt_check(oracle_mod, {"V": V, "W": W, "A": A, "bias": bias}, to_host(dt))
