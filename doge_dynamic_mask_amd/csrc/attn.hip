@@ -4,9 +4,10 @@
 // float32, o_i = sum_j p_ij v_j; query head hq reads kv head hq / G.
 //
 // bf16 kernel (matrix cores).  One workgroup = one (batch, kv head, tile of
-// Bq query rows); its 4 waves hold the G*Bq <= 128 stacked (row, head) pairs,
-// 32 per wave, so the G query heads of a kv head share every K/V tile and the
-// mask (which depends only on the kv head and the row).
+// Bq query rows); its NW waves (8 at d = 128, 4 at d = 64) hold the
+// G*Bq <= 32*NW stacked (row, head) pairs, 32 per wave, so the G query heads
+// of a kv head share every K/V tile and the mask (which depends only on the
+// kv head and the row).
 //
 // Gathered keys instead of dense key tiles: by nesting, the union of the kept
 // sets of rows [i0, i_last] lies inside K_{i0} plus the keys (i0, i_last].
@@ -40,17 +41,31 @@
 namespace dma {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowsPerWG = 128;  // stacked (row, head) pairs per workgroup
 constexpr int kBK = 64;          // keys per block
 constexpr int kCap = 2560;       // candidate slots in LDS (multiple of kBK)
 constexpr int kFillKeys = 4;     // consecutive keys per thread per fill step
-constexpr int kStepKeys = kThreads * kFillKeys;  // keys per fill step
-constexpr int kMaxSteps = 32;    // fill steps counted per round (32768 keys)
 constexpr int kBatchSteps = 8;   // fill steps whose loads are issued together
-constexpr int kPartCap = 2 * kRowsPerWG + 2 * kBK;  // slots of the masked region
-constexpr int kCarrySlots = kCap / kThreads;         // carried candidates per thread
-constexpr int kTargetItems = 2048;                   // work items a launch aims for
+constexpr int kRowThreads = 256; // the float32 row kernel's workgroup
+
+// Workgroup shape: NW waves of 32 stacked (row, head) pairs each.  d = 128
+// runs eight waves, one workgroup per CU (256 pairs a tile: half the K/V
+// staging per flop and half the candidate fills per row of the four-wave
+// shape; measured 4.4 % faster at the padded and 3.3 % at the long
+// workload), d = 64 four, two workgroups per CU (eight were 4 % slower on the
+// small c2 workload).
+template <int NW>
+struct Shape {
+    static constexpr int kThreads = 64 * NW;
+    static constexpr int kRowsPerWG = 32 * NW;                 // stacked (row, head) pairs per workgroup
+    static constexpr int kStepKeys = kThreads * kFillKeys;     // keys per fill step
+    static constexpr int kMaxSteps = 128 / NW;                 // fill steps counted per round (two scan entries a lane)
+    static constexpr int kPartCap = 2 * kRowsPerWG + 2 * kBK;  // slots of the masked region
+    static constexpr int kCarrySlots = kCap / kThreads;        // carried candidates per thread
+    // work items a launch aims for: enough for balance, few enough that
+    // each group's one full candidate scan serves several tiles
+    static constexpr int kTargetItems = NW == 4 ? 2048 : 1024;
+};
+template <int D> constexpr int waves_for() { return D == 128 ? 8 : 4; }
 
 template <int D>
 struct Tiles {
@@ -121,23 +136,27 @@ __device__ __forceinline__ int first_row_above(const uint64_t *thr, int lo, int 
     return a;
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const float *__restrict__ dt, const float *__restrict__ tau, const int32_t *__restrict__ tie,
     const int32_t *__restrict__ seqlens, int S, int Hq, int Hkv, int G, int Bq, int ntiles, int tpw,
     int B, uint16_t *__restrict__ O, float qscale) {
     using T = Tiles<D>;
+    using SH = Shape<NW>;
+    constexpr int kThreads = SH::kThreads, kRowsPerWG = SH::kRowsPerWG, kStepKeys = SH::kStepKeys,
+                  kMaxSteps = SH::kMaxSteps, kPartCap = SH::kPartCap, kCarrySlots = SH::kCarrySlots;
     constexpr int RV = D / 8;                    // 16-byte vectors per K/V row
     constexpr int NL = kBK * RV / kThreads;      // K (and V) vectors per thread per block
     static_assert(kBK * RV % kThreads == 0, "block staging split");
-    static_assert(4 * (kCarrySlots + 1) <= 64 && 4 * (kCarrySlots + 1) <= 4 * kMaxSteps, "carry scan");
+    static_assert(NW * (kCarrySlots + 1) <= 64 && kCarrySlots + 1 <= kMaxSteps, "carry scan");
+    static_assert(NW * kMaxSteps == 128, "two (step, wave) entries per lane in the fill scan");
     __shared__ __align__(16) int c_idx[kCap];
     __shared__ __align__(16) float c_dtl[kCap];     // (dt - dref) * log2(e); raw dt while filling
     __shared__ __align__(16) int c_lo[kPartCap];    // masked region: first tile row keeping the key
     __shared__ __align__(16) int c_span[kPartCap];  // masked region: rows keeping it
     __shared__ uint64_t thr[kRowsPerWG];            // threshold key of each tile row
-    __shared__ uint32_t cnt[kMaxSteps * 4];         // per (fill step, wave): full | partial << 16
+    __shared__ uint32_t cnt[kMaxSteps * NW];        // per (fill step, wave): full | partial << 16
     __shared__ int fill_info[3];                    // steps used, full count, partial count
     __shared__ float red_max[kThreads / 64];        // per-wave maxima of the candidates' dt
     __shared__ __align__(16) uint16_t Ks[kBK * T::KP];
@@ -327,11 +346,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                     cc[q] = jc[q] >= 0 ? cls_of(dc[q], jc[q]) : 0;
                     const uint32_t nf = (uint32_t)__popcll(__ballot(cc[q] == 1));
                     const uint32_t np = (uint32_t)__popcll(__ballot(cc[q] == 2));
-                    if (lane == 0) cnt[q * 4 + wave] = nf | (np << 16);
+                    if (lane == 0) cnt[q * NW + wave] = nf | (np << 16);
                 }
                 __syncthreads();  // counts visible; every read of the old list done
                 if (wave == 0) {
-                    constexpr int ne = 4 * (kCarrySlots + 1);
+                    constexpr int ne = NW * (kCarrySlots + 1);
                     const uint32_t v = lane < ne ? cnt[lane] : 0u;
                     uint32_t incl = v;
 #pragma unroll
@@ -351,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 n = nF + fill_info[2];
 #pragma unroll
                 for (int q = 0; q <= kCarrySlots; ++q) {
-                    const uint32_t base = cnt[q * 4 + wave];
+                    const uint32_t base = cnt[q * NW + wave];
                     const int of = (int)(base & 0xffffu) + (int)__popcll(__ballot(cc[q] == 1) & lt_mask);
                     const int op = nF + (int)(base >> 16) + (int)__popcll(__ballot(cc[q] == 2) & lt_mask);
                     if (cc[q] == 1) {
@@ -383,14 +402,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                         nf += (uint32_t)__popcll(__ballot(c == 1));
                         np += (uint32_t)__popcll(__ballot(c == 2));
                     }
-                    if (lane == 0) cnt[(s0 + bb) * 4 + wave] = nf | (np << 16);
+                    if (lane == 0) cnt[(s0 + bb) * NW + wave] = nf | (np << 16);
                 }
             }
             __syncthreads();
             // ---- exclusive scan over (step, wave) in key order; the steps whose
             // candidates fit in kCap are used this round
             if (wave == 0) {
-                const int e0 = 2 * lane, ne = 4 * nsteps;
+                const int e0 = 2 * lane, ne = NW * nsteps;
                 const uint32_t v0 = e0 < ne ? cnt[e0] : 0u, v1 = e0 + 1 < ne ? cnt[e0 + 1] : 0u;
                 uint32_t incl = v0 + v1;
 #pragma unroll
@@ -400,10 +419,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 }
                 if (e0 < ne) cnt[e0] = incl - v0 - v1;
                 if (e0 + 1 < ne) cnt[e0 + 1] = incl - v1;
-                // lane 2s+1 holds the running total through the end of step s
-                const bool fits = (lane & 1) && (lane >> 1) < nsteps && (incl & 0xffffu) + (incl >> 16) <= (uint32_t)kCap;
+                // the last of step s's LPS lanes holds the running total
+                // through the end of step s
+                constexpr int LPS = NW / 2;  // lanes per step
+                const bool fits = (lane % LPS) == LPS - 1 && (lane / LPS) < nsteps &&
+                                  (incl & 0xffffu) + (incl >> 16) <= (uint32_t)kCap;
                 const int used = __popcll(__ballot(fits));  // >= 1: one step never exceeds kCap
-                const uint32_t tot = __shfl(incl, 2 * used - 1, 64);
+                const uint32_t tot = __shfl(incl, LPS * used - 1, 64);
                 if (lane == 0) {
                     fill_info[0] = used;
                     fill_info[1] = (int)(tot & 0xffffu);
@@ -420,7 +442,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 #pragma unroll
                 for (int bb = 0; bb < kBatchSteps; ++bb) {
                     if (s0 + bb >= used) break;
-                    const uint32_t base = cnt[(s0 + bb) * 4 + wave];
+                    const uint32_t base = cnt[(s0 + bb) * NW + wave];
                     int of = (int)(base & 0xffffu), op = nF + (int)(base >> 16);
                     const int jb = scan + (s0 + bb) * kStepKeys + kFillKeys * tid;
                     int c[kFillKeys];
@@ -477,7 +499,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 mx = wave_max(mx);
                 if (lane == 0) red_max[wave] = mx;
                 __syncthreads();
-                dref = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
+                dref = red_max[0];
+#pragma unroll
+                for (int w2 = 1; w2 < NW; ++w2) dref = fmaxf(dref, red_max[w2]);
                 if (!(dref > -INFINITY && dref < INFINITY)) dref = 0.f;
             }
             for (int k = tid; k < n; k += kThreads) c_dtl[k] = (c_dtl[k] - dref) * kLog2e;
@@ -659,13 +683,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 // Scans the row's causal keys, applies the kept test and runs the online
 // softmax in float32.  Serves the fp32 workloads (small shapes).
 template <typename Tin>
-__global__ __launch_bounds__(kThreads) void attn_rowwise_kernel(
+__global__ __launch_bounds__(kRowThreads) void attn_rowwise_kernel(
     const Tin *__restrict__ Q, const Tin *__restrict__ K, const Tin *__restrict__ V,
     const float *__restrict__ dt, const float *__restrict__ tau, const int32_t *__restrict__ tie,
     const int32_t *__restrict__ seqlens, int B, int S, int Hq, int Hkv, int d,
     Tin *__restrict__ O, float qscale) {
     const int lane = threadIdx.x & 63;
-    const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int64_t wid = (int64_t)blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
     if (wid >= (int64_t)B * Hq * S) return;
     const int i = (int)(wid % S);
     const int hq = (int)((wid / S) % Hq);
@@ -730,6 +754,38 @@ __global__ __launch_bounds__(kThreads) void attn_rowwise_kernel(
     }
 }
 
+
+// bf16 launch of one head_dim: the workgroup shape of that head_dim, its
+// tile groups, and a grid of one slot per group plus spares.
+template <int D>
+void launch_attn_bf16(const void *Q, const void *K, const void *V, const float *dt, const float *tau,
+                      const int32_t *tie, const int32_t *seqlens, int B, int S, int Hq, int Hkv, void *O,
+                      float qscale, hipStream_t stream, hipError_t &err) {
+    constexpr int NW = waves_for<D>();
+    using SH = Shape<NW>;
+    const int G = Hq / Hkv;
+    const int Bq = SH::kRowsPerWG / G;
+    const int ntiles = (S + Bq - 1) / Bq;
+    // consecutive tiles per workgroup: enough work items to fill the chip's
+    // workgroup slots several times over (a short last round), and the prefix
+    // scan of a group's first candidate list amortised over the rest of its
+    // group
+    const int64_t total = (int64_t)ntiles * Hkv * B;
+    const int tpw = (int)std::max<int64_t>(1, std::min<int64_t>(total / SH::kTargetItems, ntiles));
+    const int64_t ngroups = (ntiles + tpw - 1) / tpw;
+    const int64_t all_groups = (int64_t)B * Hkv * ngroups;
+    // one slot per group, plus one spare per XCD: the slots past each XCD's
+    // share of the valid groups then outnumber the padded groups
+    const int64_t items = 8 * ((all_groups + 7) / 8 + 1);
+    if (items > 0x7fffffff) {
+        err = hipErrorInvalidValue;
+        return;
+    }
+    hipLaunchKernelGGL((attn_bf16_kernel<D, NW>), dim3((unsigned)items), dim3(SH::kThreads), 0, stream,
+                       (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau, tie, seqlens, S,
+                       Hq, Hkv, G, Bq, ntiles, tpw, B, (uint16_t *)O, qscale);
+}
+
 }  // namespace
 
 hipError_t launch_attn(const void *Q, const void *K, const void *V, int dtype, const float *dt,
@@ -738,34 +794,16 @@ hipError_t launch_attn(const void *Q, const void *K, const void *V, int dtype, c
     (void)w;
     const float qscale = (float)(1.0 / __builtin_sqrt((double)d) * 1.4426950408889634);
     if (dtype == 1) {
-        const int G = Hq / Hkv;
-        const int Bq = kRowsPerWG / G;
-        const int ntiles = (S + Bq - 1) / Bq;
-        // consecutive tiles per workgroup: enough work items to fill the
-        // chip's workgroup slots several times over (a short last round),
-        // and the prefix scan of a group's first candidate list amortised
-        // over the rest of its group
-        const int64_t total = (int64_t)ntiles * Hkv * B;
-        const int tpw = (int)std::max<int64_t>(1, std::min<int64_t>(total / kTargetItems, ntiles));
-        const int64_t ngroups = (ntiles + tpw - 1) / tpw;
-        const int64_t all_groups = (int64_t)B * Hkv * ngroups;
-        // one slot per group, plus one spare per XCD: the slots past each
-        // XCD's share of the valid groups then outnumber the padded groups
-        const int64_t items = 8 * ((all_groups + 7) / 8 + 1);
-        if (items > 0x7fffffff) return hipErrorInvalidValue;
-        const dim3 grid((unsigned)items);
+        hipError_t err = hipSuccess;
         if (d == 128)
-            hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(kThreads), 0, stream,
-                               (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau,
-                               tie, seqlens, S, Hq, Hkv, G, Bq, ntiles, tpw, B, (uint16_t *)O, qscale);
+            launch_attn_bf16<128>(Q, K, V, dt, tau, tie, seqlens, B, S, Hq, Hkv, O, qscale, stream, err);
         else
-            hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(kThreads), 0, stream,
-                               (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau,
-                               tie, seqlens, S, Hq, Hkv, G, Bq, ntiles, tpw, B, (uint16_t *)O, qscale);
+            launch_attn_bf16<64>(Q, K, V, dt, tau, tie, seqlens, B, S, Hq, Hkv, O, qscale, stream, err);
+        if (err != hipSuccess) return err;
     } else {
         const int64_t waves = (int64_t)B * Hq * S;
-        const int64_t blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);
-        hipLaunchKernelGGL(attn_rowwise_kernel<float>, dim3((unsigned)blocks), dim3(kThreads), 0,
+        const int64_t blocks = (waves + kRowThreads / 64 - 1) / (kRowThreads / 64);
+        hipLaunchKernelGGL(attn_rowwise_kernel<float>, dim3((unsigned)blocks), dim3(kRowThreads), 0,
                            stream, (const float *)Q, (const float *)K, (const float *)V, dt, tau, tie,
                            seqlens, B, S, Hq, Hkv, d, (float *)O, qscale);
     }
