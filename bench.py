@@ -48,8 +48,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 # known size (--copy-calibration); the runs and their readings are in
 # profiles/.  The figure holds only for the attention source it was measured
 # on: when the hash of those files differs, traffic is reported as null.
-ATTN_TRAFFIC = {"bytes": 748728790,
-                "sources_sha256": "52ba66234fc23bd92d60e60a36fd47f8b722bc1ac57ab8ff90d3ff3ff3e7d500"}
+ATTN_TRAFFIC = {"bytes": 764028560,
+                "sources_sha256": "f1c362fdd71636b1014a78cf79c65f603b3f79ae33466e765560def647773da2"}
 ATTN_SOURCES = ("doge_dynamic_mask_amd/csrc/attn.hip", "doge_dynamic_mask_amd/csrc/common.hpp")
 COPY_CAL_BYTES = 256 * 1024 * 1024
 
