@@ -15,8 +15,8 @@
 // that value goes to the lower index, found by a ballot scan in index order.
 // Exact: comparisons and integer arithmetic only.
 //
-// attn_window_kernel: one workgroup per (batch, kv head, tile of 64 / G rows),
-// 16 (row, head) pairs per wave in lane columns.  The candidate keys of the
+// attn_window_kernel: one workgroup per (batch, kv head, tile of 128 / G
+// rows), eight waves of 16 (row, head) pairs in lane columns.  The candidate keys of the
 // tile's window range [i0 - win + 1, last row] (those at or above the
 // smallest threshold of its rows; no other key is kept by any of them) are
 // compacted into an LDS list, and blocks of 64 candidates are gathered into
@@ -33,10 +33,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 256;
-constexpr int kPairs = 64;
+// window attention: eight waves of 16 (row, head) pairs, 128 pairs a tile
+// (the K/V tiles in LDS serve twice the pairs of four waves: 0.34 -> 0.24 ms
+// on the long workload with a 4096-key window)
+constexpr int kAttnThreads = 512;
+constexpr int kPairs = kAttnThreads / 4;
 constexpr int kBlk = 64;
 constexpr int kWinCap = 4224;            // candidate keys of a query tile held in LDS
-constexpr int kScanKeys = 4 * kThreads;  // keys classified per scan step
+constexpr int kScanKeys = 4 * kAttnThreads;  // keys the attention classifies per scan step
 
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -190,22 +194,22 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t *T, int base, int c0
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_window_kernel(
+__global__ __launch_bounds__(kAttnThreads) void attn_window_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const float *__restrict__ dt, const float *__restrict__ tau, const int32_t *__restrict__ tie,
     const int32_t *__restrict__ seqlens, int S, int Hq, int Hkv, int G, int ntq, int win, float qscale,
     uint16_t *__restrict__ O) {
     constexpr int P = D + 32;
     constexpr int NS = D / 32;
-    constexpr int NV = kBlk * D / 8 / kThreads;
+    constexpr int NV = kBlk * D / 8 / kAttnThreads;
     __shared__ __align__(16) uint16_t Ks[kBlk * P];
     __shared__ __align__(16) uint16_t Vs[kBlk * P];
     __shared__ float dtl_s[kBlk];
     __shared__ uint64_t skey_s[kBlk];
     __shared__ int jk_s[kBlk];
     __shared__ int c_idx[kWinCap];
-    __shared__ uint32_t wcnt[kThreads / 64];
-    __shared__ uint64_t tmin[kThreads / 64];
+    __shared__ uint32_t wcnt[kAttnThreads / 64];
+    __shared__ uint64_t tmin[kAttnThreads / 64];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int q = lane >> 4, pq = lane & 15;
@@ -253,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
     int n;
     {
         uint64_t tm = ~0ull;
-        for (int r = tid; r < kmax - i0 + 1; r += kThreads) {
+        for (int r = tid; r < kmax - i0 + 1; r += kAttnThreads) {
             const uint64_t t = selkey(tau[urow + i0 + r], (uint32_t)tie[urow + i0 + r]);
             tm = t < tm ? t : tm;
         }
@@ -266,18 +270,18 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
         __syncthreads();
         tm = tmin[0];
 #pragma unroll
-        for (int w2 = 1; w2 < kThreads / 64; ++w2) tm = tmin[w2] < tm ? tmin[w2] : tm;
+        for (int w2 = 1; w2 < kAttnThreads / 64; ++w2) tm = tmin[w2] < tm ? tmin[w2] : tm;
         const uint64_t lt_mask = (1ull << lane) - 1ull;
         int base = 0;
         for (int c0 = kmin; c0 <= kmax; c0 += kScanKeys) {
             float dv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dv[e] = drow[min(c0 + tid + kThreads * e, kmax)];
+            for (int e = 0; e < 4; ++e) dv[e] = drow[min(c0 + tid + kAttnThreads * e, kmax)];
             bool pr[4];
             uint32_t nw = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int j = c0 + tid + kThreads * e;
+                const int j = c0 + tid + kAttnThreads * e;
                 pr[e] = j <= kmax && selkey(dv[e], (uint32_t)j) >= tm;
                 nw += (uint32_t)__popcll(__ballot(pr[e]));
             }
@@ -285,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
             __syncthreads();
             int off = base, tot = 0;
 #pragma unroll
-            for (int w2 = 0; w2 < kThreads / 64; ++w2) {
+            for (int w2 = 0; w2 < kAttnThreads / 64; ++w2) {
                 const int cw = (int)wcnt[w2];
                 off += w2 < wave ? cw : 0;
                 tot += cw;
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
             for (int e = 0; e < 4; ++e) {
                 const uint64_t bl = __ballot(pr[e]);
                 const int pos = off + (int)__popcll(bl & lt_mask);
-                if (pr[e] && pos < kWinCap) c_idx[pos] = c0 + tid + kThreads * e;
+                if (pr[e] && pos < kWinCap) c_idx[pos] = c0 + tid + kAttnThreads * e;
                 off += (int)__popcll(bl);
             }
             base += tot;
@@ -317,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
     auto fetch = [&](int x0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int v = tid + u * kThreads;
+            const int v = tid + u * kAttnThreads;
             const size_t off = (size_t)(uint32_t)key_at(min(x0 + v / (D / 8), n - 1)) * kvs + 8 * (v % (D / 8));
             rk[u] = *reinterpret_cast<const u32x4 *>(Kb + off);
             rv[u] = *reinterpret_cast<const u32x4 *>(Vb + off);
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void attn_window_kernel(
     auto put = [&](int x0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int v = tid + u * kThreads;
+            const int v = tid + u * kAttnThreads;
             const int kk = v / (D / 8), cv = v % (D / 8);
             *reinterpret_cast<u32x4 *>(&Ks[kk * P + 8 * cv]) = rk[u];
             *reinterpret_cast<u32x4 *>(&Vs[kk * P + 8 * cv]) = rv[u];
@@ -443,11 +447,11 @@ hipError_t launch_attn_window(const void *Q, const void *K, const void *V, const
     const unsigned grid = (unsigned)(B * Hkv * ntq);
     const float qscale = (1.0f / sqrtf((float)d)) * kLog2e;
     if (d == 128)
-        hipLaunchKernelGGL((attn_window_kernel<128>), dim3(grid), dim3(kThreads), 0, stream, (const uint16_t *)Q,
+        hipLaunchKernelGGL((attn_window_kernel<128>), dim3(grid), dim3(kAttnThreads), 0, stream, (const uint16_t *)Q,
                            (const uint16_t *)K, (const uint16_t *)V, dt, tau, tie, seqlens, S, Hq, Hkv, G, ntq, win,
                            qscale, (uint16_t *)O);
     else
-        hipLaunchKernelGGL((attn_window_kernel<64>), dim3(grid), dim3(kThreads), 0, stream, (const uint16_t *)Q,
+        hipLaunchKernelGGL((attn_window_kernel<64>), dim3(grid), dim3(kAttnThreads), 0, stream, (const uint16_t *)Q,
                            (const uint16_t *)K, (const uint16_t *)V, dt, tau, tie, seqlens, S, Hq, Hkv, G, ntq, win,
                            qscale, (uint16_t *)O);
     return hipGetLastError();
