@@ -12,10 +12,10 @@
 // Two kernels, neither with atomics, so every result is deterministic.
 //
 // Query side (attn_bwd_q_kernel): one workgroup per (batch, kv head, tile of
-// 64 / G query rows), its four waves holding 16 (row, head) pairs each, one
+// 128 / G query rows), its eight waves holding 16 (row, head) pairs each, one
 // pair per lane column.  Only candidate keys are walked: by nesting, those
 // kept by row i0 (the tile's first row) and the tile's own keys, about
-// w + 64/G of them, compacted into an LDS list (the causal range when they
+// w + 128/G of them, compacted into an LDS list (the causal range when they
 // overflow it).  Key blocks of 64 candidates are gathered into LDS and every
 // kept test is evaluated (key j is kept by row i when j <= i < L and
 // selkey(dt_j, j) >= selkey(tau_i, tie_i)).  Pass 1 finds
@@ -66,7 +66,12 @@ constexpr int kThreads = 256;
 constexpr int kPairs = 64;   // (row, head) pairs per query tile and per row block
 constexpr int kBlk = 64;     // keys per block on the query side
 constexpr int kCandCap = 3072;  // candidate keys of a query tile held in LDS
-constexpr int kScanKeys = 4 * kThreads;  // prefix keys classified per scan step
+// The query side runs eight waves of 16 pairs (128 pairs a tile): each
+// gathered key block in LDS serves twice the pairs of four waves, and half
+// as many tiles scan the prefix for candidates (c2 backward 139 -> 132 us).
+constexpr int kQThreads = 512;
+constexpr int kQPairs = kQThreads / 4;
+constexpr int kQScanKeys = 4 * kQThreads;  // prefix keys classified per scan step
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -113,7 +118,7 @@ __device__ __forceinline__ bf16x8 ld8(const uint16_t *p) { return *reinterpret_c
 
 // ---------------------------------------------------------------- query side
 template <int D>
-__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
+__global__ __launch_bounds__(kQThreads, D == 64 ? 2 : 1) void attn_bwd_q_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const float *__restrict__ dt, const float *__restrict__ tau, const int32_t *__restrict__ tie,
     const int32_t *__restrict__ seqlens, const uint16_t *__restrict__ dO, int S, int Hq, int Hkv, int G, int ntq,
@@ -121,14 +126,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
     float *__restrict__ dd_ws) {
     constexpr int P = pitch<D>();
     constexpr int NS = D / 32;          // k-steps of 32 over head_dim
-    constexpr int NV = kBlk * D / 8 / kThreads;  // 16-byte vectors per thread per tile
+    constexpr int NV = kBlk * D / 8 / kQThreads;  // 16-byte vectors per thread per tile
     __shared__ __align__(16) uint16_t Ks[kBlk * P];
     __shared__ __align__(16) uint16_t Vs[kBlk * P];
     __shared__ float dtl_s[kBlk];
     __shared__ uint64_t skey_s[kBlk];
     __shared__ int jk_s[kBlk];
     __shared__ int c_idx[kCandCap];
-    __shared__ uint32_t wcnt[kThreads / 64];
+    __shared__ uint32_t wcnt[kQThreads / 64];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int q = lane >> 4, pq = lane & 15;
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
     const int g = (item / ntq) % Hkv;
     const int b = item / (ntq * Hkv);
     const int L = clamp_len(seqlens, b, S);
-    const int RB = kPairs / G;
+    const int RB = kQPairs / G;
     const int i0 = tq * RB;
     const int pr = 16 * wave + pq;      // this lane's pair
     const int i = i0 + pr / G, hq = g * G + pr % G;
@@ -196,15 +201,15 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
         const uint64_t thrl = selkey(tau[urow + kmax], (uint32_t)tie[urow + kmax]);
         const uint64_t lt_mask = (1ull << lane) - 1ull;
         int baseF = 0, baseP = 0;
-        for (int c0 = 0; c0 <= i0; c0 += kScanKeys) {
+        for (int c0 = 0; c0 <= i0; c0 += kQScanKeys) {
             float dv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dv[e] = drow[min(c0 + tid + kThreads * e, i0)];
+            for (int e = 0; e < 4; ++e) dv[e] = drow[min(c0 + tid + kQThreads * e, i0)];
             bool pf[4], pp[4];
             uint32_t nfw = 0, npw = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int j = c0 + tid + kThreads * e;
+                const int j = c0 + tid + kQThreads * e;
                 const uint64_t sk = selkey(dv[e], (uint32_t)j);
                 const bool cand = j <= i0 && sk >= thr0;
                 pf[e] = cand && sk >= thrl;
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
             __syncthreads();
             int offF = baseF, offP = baseP, totF = 0, totP = 0;
 #pragma unroll
-            for (int w2 = 0; w2 < kThreads / 64; ++w2) {
+            for (int w2 = 0; w2 < kQThreads / 64; ++w2) {
                 const int cf = (int)(wcnt[w2] & 0xffffu), cp = (int)(wcnt[w2] >> 16);
                 offF += w2 < wave ? cf : 0;
                 offP += w2 < wave ? cp : 0;
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int j = c0 + tid + kThreads * e;
+                const int j = c0 + tid + kQThreads * e;
                 const uint64_t bf = __ballot(pf[e]), bp = __ballot(pp[e]);
                 const int posF = offF + (int)__popcll(bf & lt_mask);
                 const int posP = offP + (int)__popcll(bp & lt_mask);
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
             baseP += totP;
             __syncthreads();  // wcnt is rewritten by the next step
         }
-        for (int x = tid; x < kmax - i0; x += kThreads)
+        for (int x = tid; x < kmax - i0; x += kQThreads)
             if (baseP + x < kCandCap) c_idx[kCandCap - 1 - (baseP + x)] = i0 + 1 + x;
         nF = baseF;
         n = baseF + baseP + (kmax - i0);
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
     auto fetch = [&](int x0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int v = tid + u * kThreads;
+            const int v = tid + u * kQThreads;
             const size_t off = (size_t)(uint32_t)key_at(min(x0 + v / (D / 8), n - 1)) * kvs + 8 * (v % (D / 8));
             rk[u] = *reinterpret_cast<const u32x4 *>(Kb + off);
             rv[u] = *reinterpret_cast<const u32x4 *>(Vb + off);
@@ -275,7 +280,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_bwd_q_kernel(
     auto put = [&](int x0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int v = tid + u * kThreads;
+            const int v = tid + u * kQThreads;
             const int kk = v / (D / 8), cv = v % (D / 8);
             *reinterpret_cast<u32x4 *>(&Ks[kk * P + 8 * cv]) = rk[u];
             *reinterpret_cast<u32x4 *>(&Vs[kk * P + 8 * cv]) = rv[u];
@@ -706,13 +711,13 @@ hipError_t launch_bwd_d(const void *Q, const void *K, const void *V, const float
                         const int32_t *tie, const int32_t *seqlens, const void *dO, int B, int S,
                         int Hq, int Hkv, void *dQ, void *dK, void *dV, float *ddt, void *ws, hipStream_t stream) {
     const int G = Hq / Hkv;
-    const int RB = kPairs / G;
+    const int RB = kQPairs / G;
     const int ntq = (S + RB - 1) / RB;
     const float c = 1.0f / sqrtf((float)D);
     const float qscale = c * kLog2e;
     float *lse_ws = (float *)ws;
     float *dd_ws = lse_ws + (size_t)B * Hq * S;
-    hipLaunchKernelGGL((attn_bwd_q_kernel<D>), dim3((unsigned)(B * Hkv * ntq)), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((attn_bwd_q_kernel<D>), dim3((unsigned)(B * Hkv * ntq)), dim3(kQThreads), 0, stream,
                        (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau, tie, seqlens,
                        (const uint16_t *)dO, S, Hq, Hkv, G, ntq, qscale, c, (uint16_t *)dQ, lse_ws, dd_ws);
     const int nkt = (S + 63) / 64;
