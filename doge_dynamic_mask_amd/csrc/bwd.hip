@@ -29,8 +29,9 @@
 // key side.
 //
 // Key side (attn_bwd_kv_kernel): one workgroup per (batch, kv head, tile of
-// 64 keys), row groups of four waves (three at d = 64, two at d = 128, as
-// registers and LDS allow); every wave holds 16 keys, one key per lane
+// 16 KW keys), NG row groups of KW waves (three groups of four at d = 64; one
+// group of eight at d = 128, so each staged row block serves 128 keys: long
+// backward 1.37 -> 1.26 ms); every wave holds 16 keys, one key per lane
 // column, with their K and V rows as MFMA operands in registers.  By nesting
 // the rows that keep key j form a run [j, e_j), and the thresholds grow with
 // the row, so the workgroup walks row blocks of 64 pairs from its first key
@@ -43,7 +44,8 @@
 // where the key drops out), so the element test is one unsigned compare.
 // dV^T += dO^T P and dK^T += Q^T dS accumulate in registers, ddt is the
 // column sum of dS; the other groups hand their sums to the first through
-// LDS, in group order.
+// LDS, in group order (in passes of as many rank blocks as the free row
+// tiles hold).
 //
 // The key side touches every (pair, key) of the row range it walks, not only
 // the kept ones: its work grows like the dense causal attention rather than
@@ -62,7 +64,6 @@
 namespace dma {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kPairs = 64;   // (row, head) pairs per query tile and per row block
 constexpr int kBlk = 64;     // keys per block on the query side
 constexpr int kCandCap = 3072;  // candidate keys of a query tile held in LDS
@@ -427,9 +428,9 @@ __global__ __launch_bounds__(kQThreads, D == 64 ? 2 : 1) void attn_bwd_q_kernel(
 }
 
 // ------------------------------------------------------------------ key side
-// NG row groups of four waves (kThreads threads each)
-template <int D, int NG>
-__global__ __launch_bounds__(NG * kThreads) void attn_bwd_kv_kernel(
+// NG row groups of KW waves (64 KW threads each)
+template <int D, int NG, int KW>
+__global__ __launch_bounds__(NG * KW * 64) void attn_bwd_kv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const float *__restrict__ dt, const float *__restrict__ tau, const int32_t *__restrict__ tie,
     const int32_t *__restrict__ seqlens, const uint16_t *__restrict__ dO, const float *__restrict__ lse_ws,
@@ -438,17 +439,23 @@ __global__ __launch_bounds__(NG * kThreads) void attn_bwd_kv_kernel(
     constexpr int P = pitch<D>();
     constexpr int NS = D / 32;
     constexpr int NT = D / 16;
-    constexpr int NV = kPairs * D / 8 / kThreads;  // 16-byte vectors per group thread per tile
-    static_assert(2 * NG * kPairs * P * 2 >= 4 * (2 * NT + 1) * 4 * 64 * 4, "the exchange fits in the row tiles");
+    constexpr int GT = KW * 64;                   // threads per row group
+    constexpr int KT = 16 * KW;                   // keys per tile
+    constexpr int NV = kPairs * D / 8 / GT;       // 16-byte vectors per group thread per tile
+    static_assert(NV >= 1 && kPairs * D / 8 % GT == 0, "row block staging split");
+    // rank blocks whose sums the row tiles hold at once for the exchange
+    constexpr int XB = (2 * NG * kPairs * P * 2) / ((2 * NT + 1) * 4 * 64 * 4);
+    static_assert(XB >= 1, "the exchange fits in the row tiles");
+    constexpr int NPASS = (KW + XB - 1) / XB;
     // Q of each group's row block, then dO of each ([NG + h])
     __shared__ __align__(16) uint16_t tiles[2 * NG][kPairs * P];
     __shared__ __align__(16) float lse_s[NG][kPairs], dd_s[NG][kPairs];
     __shared__ uint64_t thr_s[NG][kPairs];
-    __shared__ uint64_t kmax_s[4];
+    __shared__ uint64_t kmax_s[KW];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int hg = wave >> 2, kw = wave & 3;  // row group; key wave within it
-    const int gt = tid & (kThreads - 1);      // thread index within the row group
+    const int hg = wave / KW, kw = wave % KW;  // row group; key wave within it
+    const int gt = tid % GT;                   // thread index within the row group
     const int q = lane >> 4, kk = lane & 15;
     // Early key tiles (the longest row ranges) are dispatched first.  Ids go
     // round-robin over the 8 XCDs, so with a multiple of 8 (batch, kv head)
@@ -457,35 +464,35 @@ __global__ __launch_bounds__(NG * kThreads) void attn_bwd_kv_kernel(
     const int kt = blockIdx.x / nbg, bg = blockIdx.x % nbg;
     const int g = bg % Hkv, b = bg / Hkv;
     const int L = clamp_len(seqlens, b, S);
-    const int j0 = kt * 64;
+    const int j0 = kt * KT;
     const uint32_t kvs = (uint32_t)(Hkv * D);
     const size_t urow = ((size_t)b * Hkv + g) * S;
 
-    // The tile's keys ordered by selection key, best first, in four rank
+    // The tile's keys ordered by selection key, best first, in KW rank
     // blocks of 16: the waves holding the lower keys, which leave the rows'
     // kept sets first, stop working early (a wave skips the blocks where none
-    // of its keys is kept).  Every row group holds the same 64 keys, group h
-    // key wave kw the rank block (kw + h) mod 4, so that the long-lived blocks
+    // of its keys is kept).  Every row group holds the same 16 KW keys, group
+    // h key wave kw the rank block (kw + h) mod KW, so that the long-lived blocks
     // of the groups sit on different SIMDs (wave i of a workgroup runs on
     // SIMD i mod 4).
-    __shared__ uint64_t tsk[64];
-    __shared__ int perm[64];
-    if (tid < 64) {
+    __shared__ uint64_t tsk[KT];
+    __shared__ int perm[KT];
+    if (tid < KT) {
         const int j = j0 + tid;
         tsk[tid] = j < L ? selkey(dt[urow + min(j, S - 1)], (uint32_t)j) : 0ull;
     }
     __syncthreads();
-    if (tid < 64) {
+    if (tid < KT) {
         const uint64_t mine = tsk[tid];
         int r = 0;
-        for (int u = 0; u < 64; ++u) {
+        for (int u = 0; u < KT; ++u) {
             const uint64_t o = tsk[u];
             r += (int)((o > mine) | ((o == mine) & (u < tid)));
         }
         perm[r] = tid;
     }
     __syncthreads();
-    const int rb = (kw + hg) & 3;  // rank block of this wave's keys
+    const int rb = (kw + hg) % KW;  // rank block of this wave's keys
     const int jk = j0 + perm[16 * rb + kk];
     const bool kvalid = jk < L;
     const int jc = min(jk, S - 1);
@@ -515,7 +522,7 @@ __global__ __launch_bounds__(NG * kThreads) void attn_bwd_kv_kernel(
     __syncthreads();
     kmax = kmax_s[0];
 #pragma unroll
-    for (int w2 = 1; w2 < 4; ++w2) kmax = kmax_s[w2] > kmax ? kmax_s[w2] : kmax;
+    for (int w2 = 1; w2 < KW; ++w2) kmax = kmax_s[w2] > kmax ? kmax_s[w2] : kmax;
 
     f32x4 dka[NT], dva[NT];
     float dsum = 0.f;
@@ -539,7 +546,7 @@ __global__ __launch_bounds__(NG * kThreads) void attn_bwd_kv_kernel(
     auto fetch = [&](int r0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int v = gt + u * kThreads;
+            const int v = gt + u * GT;
             const int p = v / (D / 8), cv = v % (D / 8);
             const int row = min(r0 + p / G, S - 1), hq = g * G + p % G;
             const size_t off = (((size_t)b * S + row) * Hq + hq) * D + 8 * cv;
@@ -557,7 +564,7 @@ __global__ __launch_bounds__(NG * kThreads) void attn_bwd_kv_kernel(
     auto put = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int v = gt + u * kThreads;
+            const int v = gt + u * GT;
             const int p = v / (D / 8), cv = v % (D / 8);
             *reinterpret_cast<u32x4 *>(&Qg[p * P + 8 * cv]) = rq[u];
             *reinterpret_cast<u32x4 *>(&Og[p * P + 8 * cv]) = ro[u];
@@ -658,32 +665,37 @@ __global__ __launch_bounds__(NG * kThreads) void attn_bwd_kv_kernel(
     // the other groups hand their sums to group 0 through LDS (the row tiles
     // are free now), one group at a time in group order, and group 0 writes
     // the key's gradients
-    float *xw = reinterpret_cast<float *>(&tiles[0][0]) + rb * (2 * NT + 1) * 4 * 64;  // [4 rank blocks][2 NT + 1][4][64]
+    // in passes of XB rank blocks when the row tiles cannot hold all of them
 #pragma unroll
-    for (int h2 = 1; h2 < NG; ++h2) {
-        __syncthreads();
-        if (hg == h2) {
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const bool mine = rb / XB == pass;
+        float *xw = reinterpret_cast<float *>(&tiles[0][0]) + (rb - pass * XB) * (2 * NT + 1) * 4 * 64;
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
+        for (int h2 = 1; h2 < NG; ++h2) {
+            __syncthreads();
+            if (hg == h2 && mine) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    xw[((2 * t) * 4 + i) * 64 + lane] = dka[t][i];
-                    xw[((2 * t + 1) * 4 + i) * 64 + lane] = dva[t][i];
+                for (int t = 0; t < NT; ++t) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        xw[((2 * t) * 4 + i) * 64 + lane] = dka[t][i];
+                        xw[((2 * t + 1) * 4 + i) * 64 + lane] = dva[t][i];
+                    }
                 }
+                xw[(2 * NT * 4) * 64 + lane] = dsum;
             }
-            xw[(2 * NT * 4) * 64 + lane] = dsum;
-        }
-        __syncthreads();
-        if (hg == 0) {
+            __syncthreads();
+            if (hg == 0 && mine) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
+                for (int t = 0; t < NT; ++t) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    dka[t][i] += xw[((2 * t) * 4 + i) * 64 + lane];
-                    dva[t][i] += xw[((2 * t + 1) * 4 + i) * 64 + lane];
+                    for (int i = 0; i < 4; ++i) {
+                        dka[t][i] += xw[((2 * t) * 4 + i) * 64 + lane];
+                        dva[t][i] += xw[((2 * t + 1) * 4 + i) * 64 + lane];
+                    }
                 }
+                dsum += xw[(2 * NT * 4) * 64 + lane];
             }
-            dsum += xw[(2 * NT * 4) * 64 + lane];
         }
     }
     if (hg > 0) return;
@@ -720,9 +732,10 @@ hipError_t launch_bwd_d(const void *Q, const void *K, const void *V, const float
     hipLaunchKernelGGL((attn_bwd_q_kernel<D>), dim3((unsigned)(B * Hkv * ntq)), dim3(kQThreads), 0, stream,
                        (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau, tie, seqlens,
                        (const uint16_t *)dO, S, Hq, Hkv, G, ntq, qscale, c, (uint16_t *)dQ, lse_ws, dd_ws);
-    const int nkt = (S + 63) / 64;
-    constexpr int NG = D == 64 ? 3 : 2;  // row groups the registers and LDS allow
-    hipLaunchKernelGGL((attn_bwd_kv_kernel<D, NG>), dim3((unsigned)(B * Hkv * nkt)), dim3(NG * kThreads), 0, stream,
+    constexpr int KW = D == 64 ? 4 : 8;  // key waves per row group (16 keys each)
+    constexpr int NG = D == 64 ? 3 : 1;  // row groups the registers and LDS allow
+    const int nkt = (S + 16 * KW - 1) / (16 * KW);
+    hipLaunchKernelGGL((attn_bwd_kv_kernel<D, NG, KW>), dim3((unsigned)(B * Hkv * nkt)), dim3(NG * KW * 64), 0, stream,
                        (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, dt, tau, tie, seqlens,
                        (const uint16_t *)dO, lse_ws, dd_ws, S, Hq, Hkv, G, nkt, qscale, c, (uint16_t *)dK,
                        (uint16_t *)dV, ddt);
