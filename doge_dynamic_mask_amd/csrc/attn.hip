@@ -164,7 +164,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int h = lane >> 5, ql = lane & 31;
-    const float bscale = kLog2e / qscale;  // dt bias in units of the raw q.k product
     // Work items: the tile groups (tpw consecutive query tiles of one
     // (batch, kv head)) that hold a valid row, ordered by batch, kv head and
     // row.  XCD x (workgroup ids go round-robin over the 8 XCDs) takes the
@@ -505,9 +504,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(
                 for (int w2 = 1; w2 < NW; ++w2) dref = fmaxf(dref, red_max[w2]);
                 if (!(dref > -INFINITY && dref < INFINITY)) dref = 0.f;
             }
-            // stored in units of the raw q.k product (divided by the score
-            // scale), so that it can seed the score accumulators
-            for (int k = tid; k < n; k += kThreads) c_dtl[k] = (c_dtl[k] - dref) * bscale;
+            for (int k = tid; k < n; k += kThreads) c_dtl[k] = (c_dtl[k] - dref) * kLog2e;
             // row runs of the masked region: a partial key j is kept on the tile
             // rows [lo, lo + span) (by nesting a run: from its own row, or from
             // i0, until the first row whose threshold passes it); full keys
@@ -544,20 +541,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(
                 // sum of V comes next and one in its softmax yields; measured
                 // 5-18 % faster than equal priorities.
                 __builtin_amdgcn_s_setprio(3);
-                // the accumulators start at the keys' dt bias, so that they end
-                // at the score over the score scale
-                f32x16 sacc[2];
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const float4 dl4 = *reinterpret_cast<const float4 *>(&c_dtl[blk + 32 * kt + 8 * r4 + 4 * h]);
-                        sacc[kt][4 * r4 + 0] = dl4.x;
-                        sacc[kt][4 * r4 + 1] = dl4.y;
-                        sacc[kt][4 * r4 + 2] = dl4.z;
-                        sacc[kt][4 * r4 + 3] = dl4.w;
-                    }
-                }
+                f32x16 sacc[2] = {f32x16{}, f32x16{}};
                 const uint16_t *kp0 = &Ks[ql * T::KP + 8 * h];
                 const uint16_t *kp1 = &Ks[(32 + ql) * T::KP + 8 * h];
                 bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kp0);
@@ -576,9 +560,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(
                 }
 
                 __builtin_amdgcn_s_setprio(0);
-                // the row-run test where partial keys are, then the online
-                // softmax in base 2 (scores z = sacc * qscale)
-                if (blk >= pbase) {
+                // dt bias (and, where partial keys are, the row-run test), then
+                // the online softmax in base 2
+                float z[2][16];
+                float mloc = -INFINITY;
+                if (blk < pbase) {
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const int pos = blk + 32 * kt + 8 * r4 + 4 * h;
+                            const float4 dl4 = *reinterpret_cast<const float4 *>(&c_dtl[pos]);
+                            const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float zz = fmaf(sacc[kt][4 * r4 + e], qscale, dls[e]);
+                                z[kt][4 * r4 + e] = zz;
+                                mloc = fmaxf(mloc, zz);
+                            }
+                        }
+                    }
+                } else {
 #pragma unroll
                     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -586,27 +588,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(
                             const int pos = blk + 32 * kt + 8 * r4 + 4 * h;
                             const int4 lo4 = *reinterpret_cast<const int4 *>(&c_lo[pos - pbase]);
                             const int4 sp4 = *reinterpret_cast<const int4 *>(&c_span[pos - pbase]);
+                            const float4 dl4 = *reinterpret_cast<const float4 *>(&c_dtl[pos]);
                             const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
                             const int sps[4] = {sp4.x, sp4.y, sp4.z, sp4.w};
+                            const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const bool ok = (unsigned)(r - los[e]) < (unsigned)sps[e];
-                                sacc[kt][4 * r4 + e] = ok ? sacc[kt][4 * r4 + e] : -INFINITY;
+                                const float zz = fmaf(sacc[kt][4 * r4 + e], qscale, ok ? dls[e] : -INFINITY);
+                                z[kt][4 * r4 + e] = zz;
+                                mloc = fmaxf(mloc, zz);
                             }
                         }
                     }
-                }
-                float mloc = -INFINITY;
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[kt][e]);
                 }
                 // Lazy rescale: the running max only moves when a block raises it
                 // by more than 8 (base 2), so p stays <= 256 and most blocks skip
                 // the O rescale.  The final normalisation uses the same max, so
                 // the result is the softmax whatever max was used.
-                const float mblk = half_swap_max(mloc) * qscale;
+                const float mblk = half_swap_max(mloc);
                 const bool upd = mblk > mrow + 8.f;
                 if (__any(upd)) {
                     const float mnew = upd ? mblk : mrow;
@@ -617,11 +617,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(
                     for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
                 }
                 const float msub = (mrow == -INFINITY) ? 0.f : mrow;
-                float z[2][16];
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) z[kt][e] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][e], qscale, -msub));
+                    for (int e = 0; e < 16; ++e) z[kt][e] = __builtin_amdgcn_exp2f(z[kt][e] - msub);
                 }
 
                 // O^T += V^T P^T.  PV call c covers keys 16c..16c+15; lane half h
