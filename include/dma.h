@@ -318,11 +318,11 @@ size_t dma_attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int d, int w)
  *   ws, ws_bytes: device workspace of at least dma_attn_bwd_workspace_bytes()
  * bf16 only; d in {64, 128}; Hq/Hkv in {1, 2, 4, 8}.  Products on matrix
  * cores with float32 accumulation (p and ds rounded to bf16 as operands);
- * deterministic (no atomics).  The query side walks about w + 64/(Hq/Hkv)
- * candidate keys per tile of rows; the key side walks, for each tile of 64
- * keys, the rows from its first key to the last row that keeps any of them
- * (with dt drawn independently per key that is often most of the causal
- * range).
+ * deterministic (no atomics).  The query side walks about w + 128/(Hq/Hkv)
+ * candidate keys per tile of rows; the key side walks, for each tile of keys
+ * (64 at d = 64, 128 at d = 128), the rows from its first key to the last
+ * row that keeps any of them (with dt drawn independently per key that is
+ * often most of the causal range).
  */
 int dma_attn_bwd(const void *Q, const void *K, const void *V, int dtype, const float *dt, const float *tau,
                  const int32_t *tie, const int32_t *seqlens, const void *dO, int B, int S, int Hq, int Hkv, int d,
