@@ -49,7 +49,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 # profiles/.  The figure holds only for the attention source it was measured
 # on: when the hash of those files differs, traffic is reported as null.
 ATTN_TRAFFIC = {"bytes": 764028560,
-                "sources_sha256": "f1c362fdd71636b1014a78cf79c65f603b3f79ae33466e765560def647773da2"}
+                "sources_sha256": "e8dfaa6b23cacf0d2b3eacf113e4081132fc6af9b47e2c2700fdc34400d03b8e"}
 ATTN_SOURCES = ("doge_dynamic_mask_amd/csrc/attn.hip", "doge_dynamic_mask_amd/csrc/common.hpp")
 COPY_CAL_BYTES = 256 * 1024 * 1024
 

@@ -12,8 +12,9 @@
 // Gathered keys instead of dense key tiles: by nesting, the union of the kept
 // sets of rows [i0, i_last] lies inside K_{i0} plus the keys (i0, i_last].
 // The workgroup scans dt[0..i_last] and compacts those candidate keys into
-// LDS in two passes (count per wave and 1024-key step with all loads in
-// flight, one scan, then write with ballot offsets), in index order and split
+// LDS in two passes (count per wave and step of four keys a thread, with the
+// loads of eight steps in flight, one scan, then write with ballot offsets),
+// in index order and split
 // in two groups: "full" keys, kept by every row of the tile (a key j <= i0
 // kept by i_last is kept by every row in between, by nesting), first, and the
 // "partial" rest after them (at most 2*Bq keys: each row drops at most one
