@@ -45,6 +45,7 @@ BWD_CASES = [
     (1, 190, 1, 1, 64, 64, None, "const"),           # G = 1, all dt equal
     (2, 97, 16, 2, 128, 33, (97, 1), "lognormal"),   # G = 8, a batch of length 1
     (2, 700, 4, 2, 128, 90, (700, 515), "wide"),     # several 128-key tiles, a length ending inside one
+    (1, 300, 2, 2, 128, 40, None, "lognormal"),      # G = 1 at d = 128: row blocks of 64 rows
     (1, 2600, 4, 2, 64, 300, None, "lognormal"),     # query tiles past 1024 keys: several scan steps
     # late query tiles have more candidate keys than the query kernel's LDS
     # list holds and walk the causal range instead
