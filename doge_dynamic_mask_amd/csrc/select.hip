@@ -138,17 +138,30 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
     __shared__ SelectShared<C, NB, STAGE, WIN> sh;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // Work item of this workgroup, items ordered by (batch, kv head, chunk).
-    // Rows of one length (no seqlens): workgroup ids go round-robin over the
-    // 8 XCDs, so XCD x takes items x*per_xcd .. (x+1)*per_xcd - 1 and the
-    // chunks of one row run on one XCD, whose L2 then holds that row's dt for
-    // all of them.  Rows of different lengths carry different work (it grows
-    // with the square of the length), so there the items stay in id order,
-    // spread evenly over the XCDs.  The grid is padded to a multiple of 8;
-    // items past the last return at once.
-    // (the host keeps B * Hkv * ceil(S / 64), the item count, below 2^31)
+    // Workgroup ids go round-robin over the 8 XCDs (XCD x = id mod 8).  Rows
+    // of one length (no seqlens): XCD x takes items x*per_xcd ..
+    // (x+1)*per_xcd - 1, so the chunks of one row run on one XCD, whose L2
+    // then holds that row's dt for all of them.  Rows of different lengths
+    // carry different work (it grows with the square of the length): with at
+    // least four rows, row u goes to the XCD pair u mod 4 and its chunks
+    // alternate between the pair's two XCDs, so each row is read into two L2s
+    // and the two XCDs of a pair carry the same work; with fewer rows the
+    // items stay in id order, spread over all the XCDs.  Slots past an XCD's
+    // items return at once (select_grid sizes the grid for the fullest XCD).
     const uint32_t per_xcd = gridDim.x >> 3;
-    const uint32_t item = seqlens ? blockIdx.x : (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
     const uint32_t nchunks = (uint32_t)((S + kChunk - 1) / kChunk);
+    const uint32_t nunits = (uint32_t)(nb_total * Hkv);
+    uint32_t item;
+    if (seqlens && nunits >= 4u) {
+        const uint32_t x = blockIdx.x & 7u, slot = blockIdx.x >> 3, par = x & 1u;
+        const uint32_t per_row = (nchunks + 1u - par) >> 1;  // chunks par, par + 2, ... of a row
+        if (per_row == 0u) return;
+        const uint32_t m = slot / per_row, u = (x >> 1) + 4u * m;
+        if (u >= nunits) return;
+        item = u * nchunks + par + 2u * (slot - m * per_row);
+    } else {
+        item = seqlens ? blockIdx.x : (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
+    }
     const uint32_t unit = item / nchunks;  // b * Hkv + g
     if (unit >= (uint32_t)(nb_total * Hkv)) return;  // uniform across the workgroup
     const int g = (int)(unit % (uint32_t)Hkv), b = (int)(unit / (uint32_t)Hkv);
@@ -445,11 +458,15 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const float *__restric
 
 }  // namespace
 
-// A 1-D grid of at least nchunks * Hkv * B workgroups, a multiple of 8 (one
-// share per XCD).
-static unsigned xcd_grid(int nchunks, int Hkv, int B) {
-    const int64_t items = (int64_t)nchunks * Hkv * B;
-    return (unsigned)(8 * ((items + 7) / 8));
+// The 1-D grid of select_kernel, a multiple of 8 (one share per XCD): at
+// least nchunks * Hkv * B workgroups, and with seqlens and four or more rows
+// the fullest XCD's share (ceil(rows / 4) rows of ceil(nchunks / 2) chunks).
+// 0 when it would not fit a grid dimension.
+static unsigned select_grid(int nchunks, int Hkv, int B, bool pairs) {
+    const int64_t units = (int64_t)Hkv * B;
+    const int64_t per_xcd = pairs && units >= 4 ? ((units + 3) / 4) * ((nchunks + 1) / 2)
+                                                 : (units * nchunks + 7) / 8;
+    return 8 * per_xcd > 0x7fffffff ? 0u : (unsigned)(8 * per_xcd);
 }
 
 hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv, int S, int w, int win,
@@ -459,9 +476,13 @@ hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv
     // rows), chunks of 64 rows with 1024-key staging beyond (the prefix passes
     // then dominate, and 32-row chunks would double them).  Sliding window: short windows take 64-row chunks,
     // longer rows and windows 128-row chunks (a window needs win >= C).
-#define DMA_SEL(C, NB, STAGE, WIN)                                                                               \
-    hipLaunchKernelGGL((select_kernel<C, NB, STAGE, WIN>), dim3(xcd_grid((S + C - 1) / C, Hkv, B)), dim3(kThreads), \
-                       0, stream, dt, seqlens, Hkv, S, w, win, B, tau, tie)
+#define DMA_SEL(C, NB, STAGE, WIN)                                                                                \
+    do {                                                                                                          \
+        const unsigned grid = select_grid((S + C - 1) / C, Hkv, B, seqlens != nullptr);                           \
+        if (grid == 0u) return hipErrorInvalidValue;                                                              \
+        hipLaunchKernelGGL((select_kernel<C, NB, STAGE, WIN>), dim3(grid), dim3(kThreads), 0, stream, dt, seqlens, \
+                           Hkv, S, w, win, B, tau, tie);                                                          \
+    } while (0)
     if (win > 0) {
         if (S <= 4096 || win < 128) DMA_SEL(64, 1024, 8192, true);
         else DMA_SEL(128, 4096, 8192, true);
