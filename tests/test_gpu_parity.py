@@ -113,6 +113,9 @@ SELECT_CASES = [
     (1, 2, 2500, 63, "wide", True),
     (1, 1, 1200, 65, "lognormal", False),
     (1, 1, 3000, 700, "dyadic", False),   # a prefix key of rank w-C-1 can be the threshold
+    # rows of different lengths spread over XCD pairs: five and nine rows
+    (5, 1, 1500, 200, "lognormal", True),
+    (3, 3, 700, 50, "wide", True),
     (2, 2, 2000, 129, "few", True),
     (1, 2, 4000, 1000, "lognormal", False),
     # rows past 4096 keys: prefixes longer than the selector stages in LDS,
