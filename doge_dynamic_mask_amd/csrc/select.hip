@@ -474,7 +474,9 @@ hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv
     // Full causal range: chunks of 32 rows for rows up to 4096 keys, staged
     // whole in LDS (more, shorter workgroups: 7 % faster at S = 2048 than 64
     // rows), chunks of 64 rows with 1024-key staging beyond (the prefix passes
-    // then dominate, and 32-row chunks would double them).  Sliding window: short windows take 64-row chunks,
+    // then dominate, and 32-row chunks would double them), 128 rows past
+    // 16384 keys (half the prefix passes again: 55.0 -> 51.5 us at the
+    // padded size).  Sliding window: short windows take 64-row chunks,
     // longer rows and windows 128-row chunks (a window needs win >= C).
 #define DMA_SEL(C, NB, STAGE, WIN)                                                                                \
     do {                                                                                                          \
@@ -488,7 +490,8 @@ hipError_t launch_select(const float *dt, const int32_t *seqlens, int B, int Hkv
         else DMA_SEL(128, 4096, 8192, true);
     } else {
         if (S <= 4096) DMA_SEL(32, 1024, 4096, false);
-        else DMA_SEL(64, 1024, 1024, false);
+        else if (S <= 16384) DMA_SEL(64, 1024, 1024, false);
+        else DMA_SEL(128, 1024, 1024, false);
     }
 #undef DMA_SEL
     return hipGetLastError();

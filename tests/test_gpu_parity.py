@@ -113,11 +113,11 @@ SELECT_CASES = [
     (1, 2, 2500, 63, "wide", True),
     (1, 1, 1200, 65, "lognormal", False),
     (1, 1, 3000, 700, "dyadic", False),   # a prefix key of rank w-C-1 can be the threshold
+    (2, 2, 2000, 129, "few", True),
+    (1, 2, 4000, 1000, "lognormal", False),
     # rows of different lengths spread over XCD pairs: five and nine rows
     (5, 1, 1500, 200, "lognormal", True),
     (3, 3, 700, 50, "wide", True),
-    (2, 2, 2000, 129, "few", True),
-    (1, 2, 4000, 1000, "lognormal", False),
     # rows past 4096 keys: prefixes longer than the selector stages in LDS,
     # binned over the range of a sample of their positions
     (1, 1, 5000, 64, "const", False),
@@ -173,6 +173,31 @@ def test_select_full_size_sampled(dma, oracle_mod, name, kind):
         for gg in range(wl.Hkv):
             t = tau[bb, gg, wl.w:L].astype(np.float64)
             k = tie[bb, gg, wl.w:L].astype(np.int64)
+            assert ((t[1:] > t[:-1]) | ((t[1:] == t[:-1]) & (k[1:] <= k[:-1]))).all()
+            assert (tau[bb, gg, L:] == np.inf).all()
+
+
+# Rows past 16384 keys (128-row chunks): a ragged last chunk, rows of
+# different lengths over XCD pairs, ties and a wide key range.
+@pytest.mark.parametrize("B,Hkv,S,w,kind,padded", [(1, 1, 16385, 64, "const", False),
+                                                   (2, 3, 20001, 1500, "lognormal", True),
+                                                   (3, 2, 18000, 700, "dyadic", True),
+                                                   (1, 2, 17000, 2048, "wide", False)])
+def test_select_long_rows_sampled(dma, oracle_mod, B, Hkv, S, w, kind, padded):
+    seq = si.make_lengths(B, S // 2, S, seed=S) if padded else None
+    dt = si.make_dt((B, Hkv, S), kind, seed=S + w)
+    tau, tie = dma.select(to_dev(dt), w, to_dev(seq))
+    tau, tie = to_host(tau), to_host(tie)
+    rows = sample_rows(B, Hkv, S, seq, 600, seed=2, w=w)
+    rt, ri = oracle_mod.select(dt, w, seq, rows=rows)
+    b, g, i = rows.T
+    np.testing.assert_array_equal(tie[b, g, i], ri)
+    np.testing.assert_array_equal(tau[b, g, i], rt)
+    for bb in range(B):
+        L = S if seq is None else int(seq[bb])
+        for gg in range(Hkv):
+            t = tau[bb, gg, w:L].astype(np.float64)
+            k = tie[bb, gg, w:L].astype(np.int64)
             assert ((t[1:] > t[:-1]) | ((t[1:] == t[:-1]) & (k[1:] <= k[:-1]))).all()
             assert (tau[bb, gg, L:] == np.inf).all()
 
